@@ -1,0 +1,218 @@
+"""Benchmark: GatedDeltaNet speculative verify + commit on one MI355X.
+
+A step is one pass of the whole path over one batch: gdn_spec_verify of every
+request's k+1 rows, then gdn_spec_commit of its accepted rows. The default
+workload is the saturated batch: 64 requests, 9 verify rows (k = 8), a
+Qwen3-Next-shaped layer (16 key / 32 value heads, d = 128, conv width 4 over
+8192 channels, bf16 inputs, fp32 state), a 256-slot pool and geometric(0.3)
+accept lengths capped at 9.
+
+Steps rotate over several independent copies of the workload (as the layers of
+a hybrid stack would), verifying a group of copies and then committing them,
+so no kernel finds its state still in the 256 MB Infinity Cache from the
+previous kernel on the same copy. All inputs are resident in HBM before the
+timed region.
+
+Prints one JSON line. value = verify rows per second (batch x rows per step);
+gbps = algorithmic HBM bytes per second: per request, verify reads the state,
+the conv history, x and the gates and writes o and a stash of the rows' raw
+inputs; commit reads and writes the state and the conv history and reads the
+accepted rows' stash.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+sys.path.insert(0, os.path.join(ROOT, "tests"))
+
+METRIC = "GDN verify+commit rows/s and achieved HBM GB/s (% of MI355X peak)"
+HBM_PEAK_GBPS = 8000.0
+
+
+def algorithmic_bytes(w, accept):
+    """(verify bytes, commit bytes) per launch for workload w and accept lengths."""
+    s = w.shape
+    E, HV, D, C, W, R = s.elem_bytes, s.num_v_heads, s.d_k, s.conv_channels, s.conv_width, w.rows
+    state = HV * D * D * 4
+    hist = (W - 1) * C * E
+    row_stash = (C + 2 * HV) * E
+    per_verify = state + hist + R * C * E + 2 * R * HV * E + R * HV * D * E + R * row_stash
+    verify = w.batch * per_verify
+    commit = 0
+    for n in accept:
+        if n > 0:
+            commit += 2 * state + 2 * hist + int(n) * row_stash
+    return verify, commit
+
+
+def cpu_baseline(w, budget_s=12.0):
+    """The oracle (as it stands) on the same workload, on this host's cores."""
+    import numpy as np
+
+    import oracle
+    from linear_attention_verify_amd import workloads as wl
+
+    cores = len(os.sched_getaffinity(0))
+    cores = max(1, min(cores, 16))
+    orc = oracle.Oracle()
+    _, accept = wl.draw_requests(w)
+    d = wl.draw_layer(w)
+    # compact pool: request b in slot b (the oracle's cost does not depend on slot ids)
+    compact = wl.Workload(name=w.name, shape=w.shape, batch=w.batch, rows=w.rows,
+                          num_slots=w.batch)
+    slot_ids = np.arange(w.batch, dtype=np.int32)
+    ssm, conv = wl.build_pools(compact, d, slot_ids)
+    s = w.shape
+    reps, rows = 0, 0
+    t0 = time.perf_counter()
+    while True:
+        # verify, then commit in place: the state moves on as in a decode loop
+        orc.verify(s, ssm, conv, d["conv_w"], d["x"], d["alpha"], d["beta"], slot_ids, w.rows,
+                   nthreads=cores)
+        orc.commit(s, ssm, conv, d["conv_w"], d["x"], d["alpha"], d["beta"], slot_ids, accept,
+                   w.rows, nthreads=cores)
+        reps += 1
+        rows += w.batch * w.rows
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": rows / dt, "unit": "rows/s", "cores": cores, "kind": "oracle",
+            "sample": "%d full verify+commit passes of the %s batch (%d requests x %d rows), fp64"
+                      % (reps, w.name, w.batch, w.rows)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="saturated-b64")
+    ap.add_argument("--mode", default="replay", choices=["replay", "snapshot"])
+    ap.add_argument("--copies", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py runs on one GPU: the verify/commit path has no cross-GPU step "
+              "(requests and value heads shard with no exchange); --gpus %d is not supported"
+              % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gpu_harness as gh
+    from linear_attention_verify_amd import binding as bd
+    from linear_attention_verify_amd import workloads as wl
+
+    w = wl.WORKLOADS[args.workload]
+    if w.layers != 1:
+        raise SystemExit("bench workloads are single-layer configurations")
+    torch.cuda.init()
+    M = max(1, args.copies)
+    base = gh.make_case(w, mode=args.mode)
+    cases = [base]
+    for _ in range(M - 1):
+        c = gh.make_case(w, mode=args.mode, draw=base.draw)
+        cases.append(c)
+    stream = torch.cuda.current_stream()
+    prepared = [bd.Prepared(c.desc, c.ssm, c.conv, c.conv_w, c.x, c.alpha, c.beta, c.slot_ids,
+                            c.accept, w.rows, c.mode, c.scratch, c.out, c.err, stream)
+                for c in cases]
+    torch.cuda.synchronize()
+
+    def run(nsteps, events=None):
+        s = 0
+        while s < nsteps:
+            group = list(range(s, min(s + M, nsteps)))
+            for k in group:
+                p = prepared[k % M]
+                if events is not None:
+                    events["v"].append((torch.cuda.Event(enable_timing=True),
+                                        torch.cuda.Event(enable_timing=True)))
+                    events["v"][-1][0].record(stream)
+                p.verify()
+                if events is not None:
+                    events["v"][-1][1].record(stream)
+            for k in group:
+                p = prepared[k % M]
+                if events is not None:
+                    events["c"].append((torch.cuda.Event(enable_timing=True),
+                                        torch.cuda.Event(enable_timing=True)))
+                    events["c"][-1][0].record(stream)
+                p.commit()
+                if events is not None:
+                    events["c"][-1][1].record(stream)
+            s += len(group)
+
+    run(args.warmup)
+    torch.cuda.synchronize()
+    errs = [int(c.err.item()) for c in cases]
+    if any(errs):
+        raise SystemExit("device error flags set: %s" % errs)
+
+    # timed region: exactly K steps, wall clock bracketed by synchronisation
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(args.steps)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # same K steps again with per-kernel HIP events on the launch stream
+    events = {"v": [], "c": []}
+    run(args.steps, events)
+    torch.cuda.synchronize()
+    tv = np.array([a.elapsed_time(b) for a, b in events["v"]]) * 1e-3
+    tc = np.array([a.elapsed_time(b) for a, b in events["c"]]) * 1e-3
+
+    vbytes, cbytes = algorithmic_bytes(w, base.accept_np)
+    rows_per_step = w.batch * w.rows
+    value = rows_per_step * args.steps / wall
+    gbps = (vbytes + cbytes) * args.steps / wall / 1e9
+    kernels = {
+        "verify": {"avg_us": float(tv.mean() * 1e6), "bytes": vbytes,
+                   "gbps": float(vbytes / tv.mean() / 1e9)},
+        "commit": {"avg_us": float(tc.mean() * 1e6), "bytes": cbytes,
+                   "gbps": float(cbytes / tc.mean() / 1e9)},
+    }
+    dom = "verify" if tv.mean() >= tc.mean() else "commit"
+    ach = kernels[dom]["gbps"]
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "rows": w.rows,
+                   "key_heads": w.shape.num_k_heads, "value_heads": w.shape.num_v_heads,
+                   "head_dim": w.shape.d_k, "conv_width": w.shape.conv_width,
+                   "storage": w.shape.dtype, "state": "f32", "pool_slots": w.num_slots,
+                   "commit_mode": args.mode, "accept_mean": float(np.mean(base.accept_np)),
+                   "rotating_copies": M},
+        "gbps": gbps,
+        "hbm_frac": gbps / HBM_PEAK_GBPS,
+        "kernels": kernels,
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS, "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,152 @@
+/*
+ * gdn_spec.h -- C ABI of the MI355X (gfx950) GatedDeltaNet speculative
+ * verify / commit library (libgdn_spec.so).
+ *
+ * The step: for every request, the target model scores k+1 verify rows (the
+ * pending token and k draft tokens, k <= 8) through each GatedDeltaNet layer,
+ * then keeps the first n of them (FreeToken PR #844 "MTP drafts for the
+ * Qwen3.5 family and Flash-Next", Summary and Design; the accept length n is
+ * the number of committed tokens per request per verify step, at most k+1,
+ * same page, End-to-end). Per layer this library does:
+ *
+ *   gdn_spec_verify  the spec-decode causal conv over [history | rows], SiLU,
+ *                    per-key-head L2 norm of q and k, and the gated delta rule
+ *                        S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T,
+ *                        o_t = scale * S_t q_t
+ *                    on every value head, for all rows; the committed state is
+ *                    only read (FreeToken issue #828 "Speculative decoding: MTP
+ *                    and DFlash", Design: a verify is a uniform extend of k+1
+ *                    rows and only reads the GatedDeltaNet state);
+ *   gdn_spec_commit  once the accept lengths are known, writes each request's
+ *                    conv history and state as they stand after its n accepted
+ *                    rows: by replaying the accepted rows (same Design section)
+ *                    or by selecting the state the verify saved after row n-1
+ *                    (LightLLM PR #1330 "Qwen3.5 / Qwen3.5-MoE MTP speculative
+ *                    decoding", Summary: snapshot/restore of committed state).
+ *
+ * Conventions carried from the pages:
+ *  - per-request state lives in a pool of slots addressed through a slot-id
+ *    table (FreeToken PR #844, Design: pools keyed by the target's slot ids;
+ *    one upload of the slot and count indices shared by every handler);
+ *  - verify request i's scratch is row i of the scratch buffer (same page,
+ *    "Flash-Next target verify");
+ *  - accept lengths stay on the device and nothing here reads device memory on
+ *    the host, so both calls are capture-safe (LightLLM PR #1330, Summary: no
+ *    device-to-host syncs, accept_len passed by device pointer);
+ *  - arguments that cannot work are refused before anything is launched
+ *    (FreeToken PR #844, Summary: rejection at config time).
+ *
+ * Readings where the pages are silent: x holds the mixed channels
+ * [q (HK*d_k) | k (HK*d_k) | v (HV*d_v)]; the conv is depthwise with no bias,
+ * conv_w[c][W-1] multiplying the newest input; the conv history holds the
+ * last W-1 raw inputs, oldest first; q and k are normalised as
+ * x / sqrt(sum x^2 + l2_eps) per key head; value head h uses key head
+ * h / (HV/HK); alpha and beta arrive already activated, per (row, value head).
+ *
+ * Ownership: the caller allocates every buffer (device memory unless stated);
+ * the library allocates nothing, keeps no state between calls, never
+ * synchronises and never reads device memory on the host. All work is
+ * enqueued on `stream` (a hipStream_t; NULL = the null stream).
+ */
+#ifndef GDN_SPEC_H
+#define GDN_SPEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_INVALID_ARG = 1,       /* null pointer, bad count, misaligned buffer */
+    GDN_ERR_UNSUPPORTED = 2,       /* a shape this build has no kernel for */
+    GDN_ERR_SCRATCH_TOO_SMALL = 3, /* scratch_bytes below gdn_spec_scratch_bytes() */
+    GDN_ERR_HIP = 4                /* the HIP runtime refused a launch */
+} gdn_status;
+
+/* Storage type of x, conv history, conv weights, alpha, beta and out. The SSM
+ * state is always fp32. bf16 is the upper half of an IEEE fp32 word. */
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+typedef enum { GDN_COMMIT_REPLAY = 0, GDN_COMMIT_SNAPSHOT = 1 } gdn_commit_mode;
+
+typedef enum { GDN_ACT_SILU = 0, GDN_ACT_NONE = 1 } gdn_act;
+
+typedef struct {
+    int32_t num_k_heads;  /* HK >= 1 */
+    int32_t num_v_heads;  /* HV, a multiple of HK */
+    int32_t d_k;          /* key head dim; this build: d_k == d_v in {32, 64, 128} */
+    int32_t d_v;          /* value head dim */
+    int32_t conv_width;   /* W; this build: 4 */
+    int32_t dtype;        /* gdn_dtype */
+    int32_t act;          /* gdn_act applied after the conv */
+    float scale;          /* o = scale * S q */
+    float l2_eps;         /* q / sqrt(sum q^2 + l2_eps) */
+} gdn_layer_desc;
+
+/*
+ * One layer's state pool.
+ *  ssm   fp32 [num_slots][HV][d_k][d_v]: head h of slot s stores its d_v x d_k
+ *        state S transposed, S[i][j] at ssm[((s*HV + h)*d_k + j)*d_v + i]
+ *        (d_v contiguous). 16-byte aligned.
+ *  conv  dtype [num_slots][W-1][C], C = 2*HK*d_k + HV*d_v, oldest input first.
+ */
+typedef struct {
+    float *ssm;
+    void *conv;
+    int32_t num_slots;
+} gdn_pool;
+
+/*
+ * Bytes of scratch a verify of `batch` requests x `rows` rows needs in `mode`
+ * (the commit reads the same buffer). Request b's part is row b. Host only.
+ * Returns GDN_ERR_INVALID_ARG / GDN_ERR_UNSUPPORTED for arguments the verify
+ * would refuse.
+ */
+gdn_status gdn_spec_scratch_bytes(const gdn_layer_desc *desc, int32_t batch, int32_t rows,
+                                  gdn_commit_mode mode, size_t *bytes);
+
+/*
+ * Verify `rows` rows (1..9) of `batch` requests; the pool is only read.
+ *  conv_w    dtype [C][W]
+ *  x         dtype [batch][rows][C]      pre-conv inputs of the verify rows
+ *  alpha     dtype [batch][rows][HV]     decay gate a_t
+ *  beta      dtype [batch][rows][HV]     write strength b_t
+ *  slot_ids  int32 [batch]               slot of each request, -1 = padding;
+ *                                        distinct within one call
+ *  scratch   device buffer of scratch_bytes >= gdn_spec_scratch_bytes(), 16-byte
+ *            aligned, left untouched by the caller until the commit
+ *  out       dtype [batch][rows][HV][d_v] o of every row (zeros for padding and
+ *            bad slots)
+ *  err_flag  int32, nullable: bit 0 is OR-ed in when a slot id is outside
+ *            [-1, num_slots); that request is skipped.
+ */
+gdn_status gdn_spec_verify(const gdn_layer_desc *desc, const gdn_pool *pool, const void *conv_w,
+                           const void *x, const void *alpha, const void *beta,
+                           const int32_t *slot_ids, int32_t batch, int32_t rows,
+                           gdn_commit_mode mode, void *scratch, size_t scratch_bytes, void *out,
+                           int32_t *err_flag, void *stream);
+
+/*
+ * Commit accept_len[b] rows (0..rows; 0 = nothing) of each request verified by
+ * the last gdn_spec_verify on this scratch, which must have used the same
+ * desc, batch, rows, mode and slot_ids. Writes the pool's conv history and
+ * state of each request's slot. Bad slot ids (bit 0) and accept lengths
+ * outside [0, rows] (bit 1) are OR-ed into *err_flag and leave that slot
+ * untouched. The result is the same in both modes, bit for bit.
+ */
+gdn_status gdn_spec_commit(const gdn_layer_desc *desc, const gdn_pool *pool,
+                           const int32_t *slot_ids, const int32_t *accept_len, int32_t batch,
+                           int32_t rows, gdn_commit_mode mode, const void *scratch,
+                           size_t scratch_bytes, int32_t *err_flag, void *stream);
+
+/* Static description of a status code. */
+const char *gdn_strerror(gdn_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_SPEC_H */

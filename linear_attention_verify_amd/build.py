@@ -1,0 +1,40 @@
+"""Build the HIP library (libgdn_spec.so) for gfx950 in-tree with hipcc."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+SOURCES = [os.path.join(PKG, "csrc", "gdn_spec.hip")]
+INCLUDE = os.path.join(ROOT, "include")
+LIBRARY = os.path.join(PKG, "libgdn_spec.so")
+ARCH = "gfx950"
+
+# Packed fp32 arithmetic (v_pk_*_f32) is kept out of every kernel.
+HIPCC_FLAGS = [
+    "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def hipcc() -> str:
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    return os.path.join(rocm, "bin", "hipcc")
+
+
+def build(output: str = LIBRARY, extra=(), verbose: bool = False) -> str:
+    tmp = output + ".tmp%d" % os.getpid()
+    cmd = [hipcc()] + HIPCC_FLAGS + list(extra) + ["-I" + INCLUDE, "-o", tmp] + SOURCES
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, output)
+    return output
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    print(LIBRARY)

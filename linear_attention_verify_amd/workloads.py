@@ -169,7 +169,7 @@ def build_pools(w: Workload, layer_draw: dict, slot_ids: np.ndarray):
     s = w.shape
     ssm = sentinel_fill((w.num_slots, s.num_v_heads, s.d_k, s.d_v), "f32")
     conv = sentinel_fill((w.num_slots, s.conv_width - 1, s.conv_channels), s.dtype)
-    valid = slot_ids >= 0
+    valid = (slot_ids >= 0) & (slot_ids < w.num_slots)
     ssm[slot_ids[valid]] = layer_draw["ssm_active"][valid]
     conv[slot_ids[valid]] = layer_draw["conv_active"][valid]
     return ssm, conv

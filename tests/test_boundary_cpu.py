@@ -1,0 +1,154 @@
+"""The C ABI on the host: the library loads, exports every declared symbol and
+refuses bad arguments before anything reaches the GPU (FreeToken PR #844,
+Summary: rejection at config time). No call here launches a kernel: every
+argument set is one the library must reject, or has batch 0."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_attention_verify_amd import binding as bd
+from linear_attention_verify_amd import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn_spec.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bd.LIBRARY):
+        from linear_attention_verify_amd import build
+        build.build()
+    return bd.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(gdn_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(bd.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError):
+        bd.load_library(str(tmp_path / "absent.so"))
+
+
+def _align(v):
+    return (v + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("name", wl.WORKLOAD_ORDER)
+@pytest.mark.parametrize("mode", ["replay", "snapshot"])
+def test_scratch_bytes(lib, name, mode):
+    w = wl.WORKLOADS[name]
+    s = w.shape
+    B, R, HK, HV, D, C = w.batch, w.rows, s.num_k_heads, s.num_v_heads, s.d_k, s.conv_channels
+    want = (_align(B * R * C * s.elem_bytes) + _align(B * R * HV * D * 4) + _align(B * R * HK * D * 4)
+            + _align(B * R * HV * 4))
+    if mode == "snapshot":
+        want += _align(B * R * HV * D * D * 4)
+    assert bd.gdn_spec_scratch_bytes(bd.layer_desc(s), B, R, mode) == want
+
+
+def _status_verify(lib, desc, pool, batch=2, rows=3, mode=0, scratch=4096, nbytes=1 << 30,
+                   ptr=4096, slot=4096):
+    return lib.gdn_spec_verify(ctypes.byref(desc) if desc is not None else None,
+                               ctypes.byref(pool) if pool is not None else None,
+                               ptr, ptr, ptr, ptr, slot, batch, rows, mode, scratch, nbytes, ptr,
+                               None, None)
+
+
+def _status_commit(lib, desc, pool, batch=2, rows=3, mode=0, scratch=4096, nbytes=1 << 30,
+                   ptr=4096):
+    return lib.gdn_spec_commit(ctypes.byref(desc) if desc is not None else None,
+                               ctypes.byref(pool) if pool is not None else None,
+                               ptr, ptr, batch, rows, mode, scratch, nbytes, None, None)
+
+
+def good_desc(**kw):
+    s = wl.LayerShape(num_k_heads=2, num_v_heads=4, d_k=32, d_v=32, dtype="f32")
+    d = bd.layer_desc(s)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def good_pool():
+    return bd.GdnPool(4096, 4096, 8)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("num_k_heads", 0, bd.GDN_ERR_INVALID_ARG),
+    ("num_v_heads", 3, bd.GDN_ERR_INVALID_ARG),      # not a multiple of HK = 2
+    ("d_k", 96, bd.GDN_ERR_UNSUPPORTED),
+    ("d_v", 64, bd.GDN_ERR_UNSUPPORTED),              # d_k != d_v
+    ("conv_width", 3, bd.GDN_ERR_UNSUPPORTED),
+    ("dtype", 7, bd.GDN_ERR_INVALID_ARG),
+    ("act", 5, bd.GDN_ERR_INVALID_ARG),
+])
+def test_bad_descriptor_is_refused(lib, field, value, status):
+    d = good_desc(**{field: value})
+    assert _status_verify(lib, d, good_pool()) == status
+    assert _status_commit(lib, d, good_pool()) == status
+    out = ctypes.c_size_t(0)
+    assert lib.gdn_spec_scratch_bytes(ctypes.byref(d), 2, 3, 0, ctypes.byref(out)) == status
+
+
+def test_bad_arguments_are_refused(lib):
+    d, p = good_desc(), good_pool()
+    inv = bd.GDN_ERR_INVALID_ARG
+    assert _status_verify(lib, None, p) == inv
+    assert _status_verify(lib, d, None) == inv
+    assert _status_verify(lib, d, bd.GdnPool(None, 4096, 8)) == inv
+    assert _status_verify(lib, d, bd.GdnPool(4096, 4096, 0)) == inv
+    assert _status_verify(lib, d, bd.GdnPool(4100, 4096, 8)) == inv      # ssm not 16-byte aligned
+    assert _status_verify(lib, d, p, rows=0) == inv
+    assert _status_verify(lib, d, p, rows=10) == inv
+    assert _status_verify(lib, d, p, batch=-1) == inv
+    assert _status_verify(lib, d, p, mode=2) == inv
+    assert _status_verify(lib, d, p, scratch=None) == inv
+    assert _status_verify(lib, d, p, scratch=4104) == inv                # misaligned scratch
+    assert _status_verify(lib, d, p, slot=None) == inv
+    assert _status_verify(lib, d, p, ptr=None) == inv
+    assert _status_commit(lib, d, p, ptr=None) == inv
+    assert _status_commit(lib, d, p, rows=10) == inv
+
+
+def test_small_scratch_is_refused(lib):
+    d, p = good_desc(), good_pool()
+    need = bd.gdn_spec_scratch_bytes(d, 2, 3, "replay")
+    assert _status_verify(lib, d, p, nbytes=need - 1) == bd.GDN_ERR_SCRATCH_TOO_SMALL
+    assert _status_commit(lib, d, p, nbytes=need - 1) == bd.GDN_ERR_SCRATCH_TOO_SMALL
+    snap = bd.gdn_spec_scratch_bytes(d, 2, 3, "snapshot")
+    assert _status_verify(lib, d, p, mode=1, nbytes=snap - 1) == bd.GDN_ERR_SCRATCH_TOO_SMALL
+
+
+def test_empty_batch_returns_before_launching(lib):
+    d, p = good_desc(), good_pool()
+    assert _status_verify(lib, d, p, batch=0, scratch=None, nbytes=0, ptr=None, slot=None) == bd.GDN_OK
+    assert _status_commit(lib, d, p, batch=0, scratch=None, nbytes=0, ptr=None) == bd.GDN_OK
+
+
+def test_strerror(lib):
+    for st in range(5):
+        assert bd.gdn_strerror(st)
+    assert bd.gdn_strerror(99) == "unknown status"
+
+
+def test_product_code_never_touches_the_oracle():
+    pkg = os.path.join(ROOT, "linear_attention_verify_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle", text, re.M), f
+                assert "gdn_oracle" not in text, f
