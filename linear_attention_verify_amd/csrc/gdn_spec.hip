@@ -1,13 +1,11 @@
 // gdn_spec.hip -- GatedDeltaNet speculative verify / commit for MI355X (gfx950).
 //
-// Implements the C ABI of include/gdn_spec.h. One workgroup of 256 threads
-// (four wave64s) owns one (request, value head) tile: its d x d fp32 state,
-// its value channels and its key head's q/k channels.
+// Implements the C ABI of include/gdn_spec.h.
 //
 // Verify (FreeToken issue #828, Design: the verify rows run as a uniform
 // extend and only read the GatedDeltaNet state). Rather than stepping the
-// state row by row (4 multiply-adds per state element per row), the kernel
-// uses the exact unrolled form of the gated delta rule. With e_t the row's
+// state row by row (4 multiply-adds per state element per row), the kernels
+// use the exact unrolled form of the gated delta rule. With e_t the row's
 // correction vector and g(t,u) = a_{u+1} ... a_t (g(t,t) = 1):
 //
 //     S_t     = g(t,-1) S_0 + sum_{u<=t} g(t,u) e_u k_u^T
@@ -15,9 +13,22 @@
 //             = b_t (v_t - g(t,-1) S_0 k_t - sum_{u<t} g(t,u) (k_u . k_t) e_u)
 //     o_t     = scale (g(t,-1) S_0 q_t + sum_{u<=t} g(t,u) (k_u . q_t) e_u)
 //
-// so one pass over S_0 computing the 2R products S_0 k_t and S_0 q_t (2
-// multiply-adds per element per row) plus R x R scalar algebra per row of S
-// gives every o_t. The state is streamed once from HBM and never written.
+// One pass over S_0 computing the 2R products S_0 k_t and S_0 q_t, plus R x R
+// scalar algebra per state row, gives every o_t. The state is streamed once
+// from HBM and never written.
+//
+// For d = 128 the verify is two launches:
+//   gdn_prep_kernel    one workgroup per (request, key head): conv + SiLU of the
+//                      q/k channels, L2 norms, the normalised column table
+//                      [k_0..k_{R-1} | q_0..q_{R-1}], its Gram entries and,
+//                      for each value head of the key head, the scalar
+//                      coefficients g(t,-1), b_t, g(t,u) k_u.k_t, g(t,u) k_u.q_t;
+//   gdn_stream_d128    one workgroup per (request, value head): streams S_0,
+//                      runs S_0 [K | Q] on the matrix cores, the value conv in
+//                      registers and the triangular solve for e_t and o_t.
+// Keeping the latency-bound per-key-head work out of the streaming kernel lets
+// the state stream of one round of workgroups overlap the compute of another.
+// Other head dims use one fused kernel (gdn_verify_kernel) on the VALU.
 //
 // Commit (same Design section: the commit replays the accepted rows). The
 // verify leaves each row's e_t and normalised k_t in scratch, so replaying
@@ -44,7 +55,10 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWidth = 4;    // conv width this build supports
 constexpr int kMaxRows = 9;  // k + 1 with k <= 8 drafts
+constexpr int kMaxGroup = 16; // value heads per key head
 constexpr size_t kAlign = 256;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // ---- storage types -------------------------------------------------------
 
@@ -75,12 +89,32 @@ __device__ __forceinline__ void lds_barrier()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+template <int CTRL> __device__ __forceinline__ float dpp_mov(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+__device__ __forceinline__ float lane_value(float v, int lane)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// Sum over the 64 lanes of a wave, returned to every lane. DPP butterflies
+// within each 16-lane row (xor 1 and xor 2 by quad permutes, then the half-row
+// and row mirrors), then the four row sums in a fixed order: every lane gets
+// the same bits on every run.
 __device__ __forceinline__ float wave_sum(float v)
 {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1)
-        v += __shfl_xor(v, m, 64);
-    return v;
+    v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp_mov<0x141>(v);  // row_half_mirror
+    v += dpp_mov<0x140>(v);  // row_mirror
+    return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
+}
+
+__device__ __forceinline__ float silu(float y)
+{
+    return y * __builtin_amdgcn_rcpf(1.0f + __expf(-y));
 }
 
 // One accepted row replayed on one state element: S <- a S + e k.
@@ -89,21 +123,36 @@ __device__ __forceinline__ float row_update(float s, float a, float e, float k)
     return __builtin_fmaf(e, k, a * s);
 }
 
+// Triangular index of a pair (t, u), u <= t, enumerated row by row.
+__device__ __forceinline__ void tri_decode(int idx, int &t, int &u)
+{
+    t = 0;
+    while (idx > t) {
+        idx -= t + 1;
+        ++t;
+    }
+    u = idx;
+}
+
 // ---- scratch layout (shared by host and device code) -----------------------
 
+// Scalar coefficients per (request, value head): a_t, g(t,-1), b_t, then the
+// R x R blocks g(t,u) k_u.k_t (u < t) and g(t,u) k_u.q_t (u <= t).
+__host__ __device__ constexpr int coef_count(int R) { return 3 * R + 2 * R * R; }
+
 struct ScratchLayout {
-    size_t xs, es, ks, as, snap, total;
+    size_t xs, es, tab, coef, snap, total;
 };
 
 __host__ __device__ inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 // Per request b (row b of every part):
-//   xs   [B][R][C]       raw verify inputs (storage type), for the conv commit
-//   es   [B][R][HV][D]   fp32 correction vector e_t of each row and value head
-//   ks   [B][R][HK][D]   fp32 normalised key of each row and key head
-//   as   [B][R][HV]      fp32 decay gate a_t
-//   snap [B][R][HV][D][D] fp32 S_t after each row (snapshot mode only),
-//                         same per-head layout as the pool
+//   xs   [B][R][C]          raw verify inputs (storage type), for the conv commit
+//   es   [B][R][HV][D]      fp32 correction vector e_t of each row and value head
+//   tab  [B][HK][2R][D]     fp32 normalised k_0..k_{R-1}, q_0..q_{R-1} per key head
+//   coef [B][HV][3R + 2R^2] fp32 scalar coefficients (a_t first)
+//   snap [B][R][HV][D][D]   fp32 S_t after each row (snapshot mode only), same
+//                           per-head layout as the pool
 __host__ inline ScratchLayout scratch_layout(int HK, int HV, int D, int C, size_t esize, int B,
                                               int R, bool snapshot)
 {
@@ -113,10 +162,10 @@ __host__ inline ScratchLayout scratch_layout(int HK, int HV, int D, int C, size_
     off = align_up(off + (size_t)B * R * C * esize);
     L.es = off;
     off = align_up(off + (size_t)B * R * HV * D * sizeof(float));
-    L.ks = off;
-    off = align_up(off + (size_t)B * R * HK * D * sizeof(float));
-    L.as = off;
-    off = align_up(off + (size_t)B * R * HV * sizeof(float));
+    L.tab = off;
+    off = align_up(off + (size_t)B * HK * 2 * R * D * sizeof(float));
+    L.coef = off;
+    off = align_up(off + (size_t)B * HV * coef_count(R) * sizeof(float));
     L.snap = off;
     if (snapshot)
         off = align_up(off + (size_t)B * R * HV * D * D * sizeof(float));
@@ -124,7 +173,7 @@ __host__ inline ScratchLayout scratch_layout(int HK, int HV, int D, int C, size_
     return L;
 }
 
-// ---- verify ----------------------------------------------------------------
+// ---- verify: shared pieces ---------------------------------------------------
 
 template <typename T> struct VerifyParams {
     const float *ssm;
@@ -138,8 +187,8 @@ template <typename T> struct VerifyParams {
     int32_t *err;
     T *xs;
     float *es;
-    float *ks;
-    float *as;
+    float *tab;
+    float *coef;
     float *snap;
     int HK, HV, C, P;
     int act;
@@ -187,10 +236,75 @@ __device__ __forceinline__ void conv_rows(const ChanIn<NR, T> &in, int act, floa
 #pragma unroll
         for (int k = 0; k < kWidth; ++k)
             acc = __builtin_fmaf(to_f32(in.w[k]), win[t + k], acc);
-        y[t] = act == GDN_ACT_SILU ? acc / (1.0f + __expf(-acc)) : acc;
+        y[t] = act == GDN_ACT_SILU ? silu(acc) : acc;
     }
 }
 
+template <typename T>
+__device__ __forceinline__ void zero_outputs(const VerifyParams<T> &p, int b, int h, int NR, int D)
+{
+    for (int idx = threadIdx.x; idx < NR * D; idx += kThreads) {
+        const int t = idx / D, i = idx % D;
+        p.out[(((size_t)b * NR + t) * p.HV + h) * D + i] = from_f32<T>(0.0f);
+    }
+}
+
+// Per state row i (thread i): e_t and o_t from S_0 k_t (pk) and S_0 q_t (pq),
+// the row's values v_t and the scalar coefficients cf (coef_count(NR) floats).
+template <int NR, typename T>
+__device__ __forceinline__ void solve_row(const VerifyParams<T> &p, const float *cf, const float (&pk)[NR],
+                                          const float (&pq)[NR], const float (&v)[NR], float (&e)[NR],
+                                          int b, int h, int i, int D)
+{
+    const float *gam = cf + NR, *bet = cf + 2 * NR, *cA = cf + 3 * NR, *cB = cf + 3 * NR + NR * NR;
+#pragma unroll
+    for (int t = 0; t < NR; ++t) {
+        float sres = __builtin_fmaf(-gam[t], pk[t], v[t]);
+#pragma unroll
+        for (int u = 0; u < t; ++u)
+            sres = __builtin_fmaf(-cA[t * NR + u], e[u], sres);
+        e[t] = bet[t] * sres;
+        float o = gam[t] * pq[t];
+#pragma unroll
+        for (int u = 0; u <= t; ++u)
+            o = __builtin_fmaf(cB[t * NR + u], e[u], o);
+        const size_t oi = (((size_t)b * NR + t) * p.HV + h) * D + i;
+        p.out[oi] = from_f32<T>(p.scale * o);
+        p.es[oi] = e[t];
+    }
+}
+
+// Coefficient idx (< NR*NR + NR) of one value head from the Gram entries
+// gkk[t][u] = k_u.k_t and gkq[t][u] = k_u.q_t (u <= t) and the head's gates
+// al[t], be[t] (LDS); written to cf.
+template <int NR>
+__device__ __forceinline__ void write_coefficients(const float *gkk, const float *gkq, const float *al,
+                                                   const float *be, int idx, float *cf)
+{
+    if (idx < NR * NR) {
+        const int t = idx / NR, u = idx % NR;
+        float gtu = 1.0f;
+        for (int q = u + 1; q <= t; ++q)
+            gtu *= al[q];
+        cf[3 * NR + idx] = (u < t) ? gtu * gkk[idx] : 0.0f;
+        cf[3 * NR + NR * NR + idx] = (u <= t) ? gtu * gkq[idx] : 0.0f;
+    } else if (idx < NR * NR + NR) {
+        const int t = idx - NR * NR;
+        float gt = 1.0f;
+        for (int q = 0; q <= t; ++q)
+            gt *= al[q];
+        cf[t] = al[t];
+        cf[NR + t] = gt;
+        cf[2 * NR + t] = be[t];
+    }
+}
+
+// ---- verify, d = 32 / 64: one fused kernel on the VALU ----------------------
+//
+// One workgroup per (request, value head). Lane (rq, g) holds state rows
+// 4rq..4rq+3 at key indices jj*GJ + g and accumulates their products with the
+// 2R columns from LDS; the partial sums of the key-index groups are added
+// across lanes and waves.
 template <int D, int NR, typename T, bool SNAP>
 __global__ __launch_bounds__(kThreads) void gdn_verify_kernel(const VerifyParams<T> p)
 {
@@ -201,14 +315,15 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_kernel(const VerifyParams
     constexpr int JPER = D / GJ;            // key indices per lane
     static_assert(JPER >= 1 && LPJ <= 64, "unsupported head dim");
     constexpr int NPAIR = NR * (NR + 1) / 2;
+    constexpr int NCF = coef_count(NR);
 
     __shared__ __align__(16) float Mt[D * MS];    // [j][c]: k_hat_t[j] (c < NR), q_hat_t[j]
-    __shared__ float vb[NR * D];                  // v_t[i]
-    __shared__ __align__(16) float red[4 * D * NC];  // per-wave partial products; later e_t
+    __shared__ __align__(16) float vb[NR * D];    // v_t[i]; e_t in snapshot mode
+    __shared__ __align__(16) float red[4 * D * NC];  // per-wave partial products
     __shared__ float inv[NC];
     __shared__ float gkk[NR * NR], gkq[NR * NR];
-    __shared__ float cA[NR * NR], cB[NR * NR];
-    __shared__ float gam[NR], bet[NR], alp[NR];
+    __shared__ float cf[NCF];
+    __shared__ float al[NR], be[NR];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -223,33 +338,22 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_kernel(const VerifyParams
     if (slot < 0 || slot >= p.P) {
         if (slot != -1 && tid == 0 && p.err)
             atomicOr(p.err, 1);
-        for (int idx = tid; idx < NR * D; idx += kThreads) {
-            const int t = idx / D, i = idx % D;
-            p.out[(((size_t)b * NR + t) * HV + h) * D + i] = from_f32<T>(0.0f);
-        }
+        zero_outputs(p, b, h, NR, D);
         return;
     }
 
-    // Small loads first: vmcnt retires in issue order, so anything issued
-    // after the state stream would wait for all of it. They are branch-free
-    // (clamped indices) so that they share one basic block with the stream.
-    const int tr = tid < NR ? tid : NR - 1;
-    const size_t gi = ((size_t)b * NR + tr) * HV + h;
-    const T ga = p.alpha[gi];
-    const T gb = p.beta[gi];
+    const size_t gi = ((size_t)b * NR + min(tid, NR - 1)) * HV + h;
+    const T ga = p.alpha[gi], gb = p.beta[gi];
+
     // channels: threads < D take the key head's q and k channel `tid`,
-    // threads D..2D-1 the value channel tid - D of this head (loaded twice)
+    // threads D..2D-1 the value channel tid - D of this head
     const int tc = tid < 2 * D ? tid : 0;
     const int nch = tid < D ? 2 : (tid < 2 * D ? 1 : 0);
     const int chan0 = tid < D ? kh * D + tc : 2 * HK * D + h * D + (tc - D + (tid >= 2 * D ? D : 0));
     const int chan1 = tid < D ? HK * D + kh * D + tc : chan0;
-    const int chan[2] = {chan0, chan1};
-    ChanIn<NR, T> cin[2];
-    cin[0] = load_channel<NR>(p, slot, b, chan0);
-    cin[1] = load_channel<NR>(p, slot, b, chan1);
+    ChanIn<NR, T> cin0 = load_channel<NR>(p, slot, b, chan0);
+    ChanIn<NR, T> cin1 = load_channel<NR>(p, slot, b, chan1);
 
-    // The whole state slice: lane (rq, g) holds rows 4rq..4rq+3 at key
-    // indices j = jj*GJ + g. The prologue below runs while it lands.
     const int rq = tid % LPJ;
     const int g = tid / LPJ;
     const float *S0 = p.ssm + ((size_t)slot * HV + h) * D * D;
@@ -260,22 +364,22 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_kernel(const VerifyParams
     __builtin_amdgcn_sched_barrier(0);
 
     if (tid < NR) {
-        alp[tid] = to_f32(ga);
-        bet[tid] = to_f32(gb);
+        al[tid] = to_f32(ga);
+        be[tid] = to_f32(gb);
     }
     if (nch == 2) {
         float y[NR];
-        conv_rows(cin[0], p.act, y);
+        conv_rows(cin0, p.act, y);
 #pragma unroll
         for (int t = 0; t < NR; ++t)
             Mt[tid * MS + NR + t] = y[t];
-        conv_rows(cin[1], p.act, y);
+        conv_rows(cin1, p.act, y);
 #pragma unroll
         for (int t = 0; t < NR; ++t)
             Mt[tid * MS + t] = y[t];
     } else if (nch == 1) {
         float y[NR];
-        conv_rows(cin[0], p.act, y);
+        conv_rows(cin0, p.act, y);
 #pragma unroll
         for (int t = 0; t < NR; ++t)
             vb[t * D + (tid - D)] = y[t];
@@ -303,12 +407,8 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_kernel(const VerifyParams
     // Gram entries k_hat_u . k_hat_t and k_hat_u . q_hat_t for u <= t
     for (int idx = tid; idx < 2 * NPAIR; idx += kThreads) {
         const int which = idx / NPAIR;
-        int pr = idx % NPAIR, t = 0;
-        while (pr > t) {
-            pr -= t + 1;
-            ++t;
-        }
-        const int u = pr;
+        int t, u;
+        tri_decode(idx % NPAIR, t, u);
         const int ca = which ? NR + t : t;
         float acc = 0.0f;
         for (int j = 0; j < D; ++j)
@@ -316,22 +416,8 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_kernel(const VerifyParams
         (which ? gkq : gkk)[t * NR + u] = acc;
     }
     lds_barrier();
-
-    // scalar coefficients: gam[t] = a_0...a_t; cA = g(t,u) k_u.k_t; cB = g(t,u) k_u.q_t
-    if (tid < NR * NR) {
-        const int t = tid / NR, u = tid % NR;
-        float gtu = 1.0f;
-        for (int m = u + 1; m <= t; ++m)
-            gtu *= alp[m];
-        cA[tid] = (u < t) ? gtu * gkk[tid] : 0.0f;
-        cB[tid] = (u <= t) ? gtu * gkq[tid] : 0.0f;
-    }
-    if (tid < NR) {
-        float gt = 1.0f;
-        for (int m = 0; m <= tid; ++m)
-            gt *= alp[m];
-        gam[tid] = gt;
-    }
+    for (int idx = tid; idx < NR * NR + NR; idx += kThreads)
+        write_coefficients<NR>(gkk, gkq, al, be, idx, cf);
 
     // S_0 times the 2*NR column vectors
     float acc[4][NC];
@@ -369,29 +455,30 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_kernel(const VerifyParams
                 red[(wave * D + 4 * rq + r) * NC + c] = acc[r][c];
     }
 
-    // Scratch for the commit; stores start only now that the state has landed.
-    const bool owner = (h % G) == 0;  // one value head per key head stores q/k inputs
+    // scratch for the commit; stores start only now that the state has landed
+    const bool owner = (h % G) == 0;  // one value head per key head stores q/k inputs and the table
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        if (k < nch && (nch == 1 || owner)) {
-#pragma unroll
-            for (int t = 0; t < NR; ++t)
-                p.xs[((size_t)b * NR + t) * p.C + chan[k]] = cin[k].x[t];
+    for (int t = 0; t < NR; ++t) {
+        if (nch == 1 || (nch == 2 && owner)) {
+            p.xs[((size_t)b * NR + t) * p.C + chan0] = cin0.x[t];
+            if (nch == 2)
+                p.xs[((size_t)b * NR + t) * p.C + chan1] = cin1.x[t];
         }
     }
-    if (tid < NR)
-        p.as[((size_t)b * NR + tid) * HV + h] = alp[tid];
     if (owner) {
-        for (int idx = tid; idx < NR * D; idx += kThreads) {
-            const int t = idx / D, j = idx % D;
-            p.ks[(((size_t)b * NR + t) * HK + kh) * D + j] = Mt[j * MS + t];
+        float *tab = p.tab + ((size_t)b * HK + kh) * NC * D;
+        for (int idx = tid; idx < NC * D; idx += kThreads) {
+            const int c = idx / D, j = idx % D;
+            tab[idx] = Mt[j * MS + c];
         }
     }
     lds_barrier();
+    if (tid < NR)
+        p.coef[((size_t)b * HV + h) * NCF + tid] = cf[tid];  // a_t, for the commit
 
     // per state row i: correction vectors and outputs
-    float pk[NR], pq[NR];
     if (tid < D) {
+        float pk[NR], pq[NR], v[NR], e[NR];
 #pragma unroll
         for (int c = 0; c < NR; ++c) {
             float a = 0.0f, q = 0.0f;
@@ -402,29 +489,14 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_kernel(const VerifyParams
             }
             pk[c] = a;
             pq[c] = q;
+            v[c] = vb[c * D + tid];
         }
-    }
-    if (SNAP)
-        lds_barrier();  // red is reused for e_t below
-    if (tid < D) {
-        const int i = tid;
-        float e[NR];
+        solve_row<NR>(p, cf, pk, pq, v, e, b, h, tid, D);
+        if (SNAP) {
+            // entries of column tid of vb are read and written by this thread only
 #pragma unroll
-        for (int t = 0; t < NR; ++t) {
-            float sres = __builtin_fmaf(-gam[t], pk[t], vb[t * D + i]);
-#pragma unroll
-            for (int u = 0; u < t; ++u)
-                sres = __builtin_fmaf(-cA[t * NR + u], e[u], sres);
-            e[t] = bet[t] * sres;
-            float o = gam[t] * pq[t];
-#pragma unroll
-            for (int u = 0; u <= t; ++u)
-                o = __builtin_fmaf(cB[t * NR + u], e[u], o);
-            const size_t oi = (((size_t)b * NR + t) * HV + h) * D + i;
-            p.out[oi] = from_f32<T>(p.scale * o);
-            p.es[oi] = e[t];
-            if (SNAP)
-                red[t * D + i] = e[t];
+            for (int t = 0; t < NR; ++t)
+                vb[t * D + tid] = e[t];
         }
     }
 
@@ -433,8 +505,8 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_kernel(const VerifyParams
         // S_t for every row, by the same update the replay commit applies
 #pragma unroll 1
         for (int t = 0; t < NR; ++t) {
-            const float a = alp[t];
-            const float4 ev = *reinterpret_cast<const float4 *>(&red[t * D + 4 * rq]);
+            const float a = cf[t];
+            const float4 ev = *reinterpret_cast<const float4 *>(&vb[t * D + 4 * rq]);
             float *dst = p.snap + (((size_t)b * NR + t) * HV + h) * D * D;
 #pragma unroll
             for (int jj = 0; jj < JPER; ++jj) {
@@ -450,6 +522,280 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_kernel(const VerifyParams
     }
 }
 
+// ---- verify, d = 128, launch 1: per key head ---------------------------------
+//
+// Thread j < 128 runs the conv of q channel j, thread 128 + j that of k
+// channel j. Writes the normalised column table, the raw q/k inputs of the
+// rows (for the conv commit) and the coefficients of each value head.
+template <int NR, typename T>
+__global__ __launch_bounds__(kThreads) void gdn_prep_kernel(const VerifyParams<T> p)
+{
+    constexpr int D = 128;
+    constexpr int NC = 2 * NR;
+    constexpr int QS = NC + 1;               // LDS row stride (odd)
+    constexpr int NPAIR = NR * (NR + 1) / 2;
+    constexpr int PAIRS = 2 * NPAIR;
+    constexpr int SPLIT = 4;                 // Gram dots in 4 partial sums
+    constexpr int NCF = coef_count(NR);
+
+    __shared__ float qk[D * QS];             // [j][c]: k (c < NR), q (c >= NR); normalised in place
+    __shared__ float inv[NC];
+    __shared__ float gpart[PAIRS * SPLIT];
+    __shared__ float gkk[NR * NR], gkq[NR * NR];
+    __shared__ float al[kMaxGroup * NR], be[kMaxGroup * NR];  // gates of the key head's value heads
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int HV = p.HV, HK = p.HK;
+    const int G = HV / HK;
+    const int b = blockIdx.x / HK;
+    const int kh = blockIdx.x % HK;
+    const int slot = p.slot_ids[b];
+    if (slot < 0 || slot >= p.P)
+        return;  // padding or a bad slot: the stream kernel flags and zeroes it
+
+    // gate g*NR + t of value head kh*G + g, clamped so the loads need no branch
+    const int gq = min(tid, G * NR - 1);
+    const size_t gi = ((size_t)b * NR + gq % NR) * HV + kh * G + gq / NR;
+    const T ga = p.alpha[gi], gb = p.beta[gi];
+    const int j = tid & (D - 1);
+    const bool isq = tid < D;
+    const int c = isq ? kh * D + j : HK * D + kh * D + j;
+    const ChanIn<NR, T> in = load_channel<NR>(p, slot, b, c);
+    if (tid < G * NR) {
+        al[tid] = to_f32(ga);
+        be[tid] = to_f32(gb);
+    }
+    {
+        float y[NR];
+        conv_rows(in, p.act, y);
+#pragma unroll
+        for (int t = 0; t < NR; ++t)
+            qk[j * QS + (isq ? NR + t : t)] = y[t];
+    }
+#pragma unroll
+    for (int t = 0; t < NR; ++t)
+        p.xs[((size_t)b * NR + t) * p.C + c] = in.x[t];
+    lds_barrier();
+
+    for (int col = wave; col < NC; col += 4) {
+        const float v0 = qk[lane * QS + col], v1 = qk[(lane + 64) * QS + col];
+        const float ss = wave_sum(__builtin_fmaf(v0, v0, v1 * v1));
+        if (lane == 0)
+            inv[col] = 1.0f / sqrtf(ss + p.eps);
+    }
+    lds_barrier();
+    float *tab = p.tab + ((size_t)b * HK + kh) * NC * D;
+    for (int idx = tid; idx < NC * D; idx += kThreads) {
+        const int col = idx / D, jj = idx % D;
+        const float v = qk[jj * QS + col] * inv[col];
+        qk[jj * QS + col] = v;
+        tab[idx] = v;
+    }
+    lds_barrier();
+
+    for (int idx = tid; idx < PAIRS * SPLIT; idx += kThreads) {
+        const int pair = idx / SPLIT, part = idx % SPLIT;
+        int t, u;
+        tri_decode(pair % NPAIR, t, u);
+        const int ca = pair >= NPAIR ? NR + t : t;
+        float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll 8
+        for (int jj = part * (D / SPLIT); jj < (part + 1) * (D / SPLIT); jj += 2) {
+            a0 = __builtin_fmaf(qk[jj * QS + ca], qk[jj * QS + u], a0);
+            a1 = __builtin_fmaf(qk[(jj + 1) * QS + ca], qk[(jj + 1) * QS + u], a1);
+        }
+        gpart[idx] = a0 + a1;
+    }
+    lds_barrier();
+    if (tid < PAIRS) {
+        int t, u;
+        tri_decode(tid % NPAIR, t, u);
+        float acc = 0.0f;
+#pragma unroll
+        for (int q = 0; q < SPLIT; ++q)
+            acc += gpart[tid * SPLIT + q];
+        (tid >= NPAIR ? gkq : gkk)[t * NR + u] = acc;
+    }
+    lds_barrier();
+
+    for (int idx = tid; idx < G * (NR * NR + NR); idx += kThreads) {
+        const int gh = idx / (NR * NR + NR);
+        const int h = kh * G + gh;
+        write_coefficients<NR>(gkk, gkq, al + gh * NR, be + gh * NR, idx % (NR * NR + NR),
+                               p.coef + ((size_t)b * HV + h) * NCF);
+    }
+}
+
+// ---- verify, d = 128, launch 2: per value head ------------------------------
+//
+// The 2R products S_0 k_t, S_0 q_t are a dense (128 x 128) x (128 x 2R)
+// contraction, run with v_mfma_f32_16x16x4_f32 (fp32 in, fp32 accumulate).
+// Wave w owns state rows 32w..32w+31 as two 16-row tiles: lane l (kg = l/16,
+// m = l%16) loads rows 32w+2m and 32w+2m+1 at key index j = 4*ks + kg for each
+// of the 32 K-steps ks, which is exactly the A operand of both tiles
+// (A[m][k] = S[row][4ks+k]). The first 16 columns of [K | Q] go through one
+// 16-wide B tile; with R = 9 the last two (q_7, q_8) are done on the VALU from
+// the same registers, so no matrix-core work is spent on padding.
+template <int NR, typename T, bool SNAP>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void gdn_stream_d128_kernel(const VerifyParams<T> p)
+{
+    constexpr int D = 128;
+    constexpr int NC = 2 * NR;
+    constexpr int NMF = NC < 16 ? NC : 16;   // columns on the matrix cores
+    constexpr int NVL = NC - NMF;            // columns on the VALU (0, or 2 when NR = 9)
+    static_assert(NVL == 0 || NVL == 2, "unsupported row count");
+    constexpr int MS = NVL ? 20 : 16;        // column-table row stride
+    constexpr int PS = NC + 1;               // product-table row stride (odd)
+    constexpr int KS = D / 4;                // K-steps of 4 key indices
+    constexpr int NCF = coef_count(NR);
+    constexpr int TABN = NC * D;
+    constexpr int TPT = (TABN + kThreads - 1) / kThreads;  // table floats per thread
+
+    __shared__ __align__(16) float Mt[D * MS];   // [j][c]: k_hat_c[j] (c < NR), q_hat_{c-NR}[j]; 0 beyond NC
+    __shared__ __align__(16) float P[D * PS];    // [i][c]: (S_0 k_hat_c)[i], then (S_0 q_hat)[i]; later e_t
+    __shared__ float cf[NCF];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int HV = p.HV, HK = p.HK;
+    const int G = HV / HK;
+    const int b = blockIdx.x / HV;
+    const int h = blockIdx.x % HV;
+    const int kh = h / G;
+    const int slot = p.slot_ids[b];
+
+    if (slot < 0 || slot >= p.P) {
+        if (slot != -1 && tid == 0 && p.err)
+            atomicOr(p.err, 1);
+        zero_outputs(p, b, h, NR, D);
+        return;
+    }
+
+    // small loads first (branch-free: vmcnt retires in issue order), then the state
+    const int i = tid & (D - 1);
+    const int cv = 2 * HK * D + h * D + i;
+    const ChanIn<NR, T> vin = load_channel<NR>(p, slot, b, cv);
+    const float *tab = p.tab + ((size_t)b * HK + kh) * TABN;
+    float tv[TPT];
+#pragma unroll
+    for (int q = 0; q < TPT; ++q)
+        tv[q] = tab[min(q * kThreads + tid, TABN - 1)];
+    const float cfv = p.coef[((size_t)b * HV + h) * NCF + min(tid, NCF - 1)];
+
+    const int kg = lane >> 4;
+    const int m = lane & 15;
+    const int row0 = 32 * wave + 2 * m;            // this lane's two state rows: row0, row0 + 1
+    const float *S0 = p.ssm + ((size_t)slot * HV + h) * D * D;
+    float2 s[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+        s[ks] = *reinterpret_cast<const float2 *>(S0 + (size_t)(4 * ks + kg) * D + row0);
+    __builtin_amdgcn_sched_barrier(0);
+
+#pragma unroll
+    for (int q = 0; q < TPT; ++q) {
+        const int idx = q * kThreads + tid;
+        if (idx < TABN)
+            Mt[(idx % D) * MS + idx / D] = tv[q];
+    }
+    for (int idx = tid; idx < D * (MS - NC); idx += kThreads)
+        Mt[(idx / (MS - NC)) * MS + NC + idx % (MS - NC)] = 0.0f;
+    if (tid < NCF)
+        cf[tid] = cfv;
+    float v[NR];
+    conv_rows(vin, p.act, v);
+    lds_barrier();
+
+    // S_0 [K | Q]: one 16-column tile on the matrix cores, the rest on the VALU
+    f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4 acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+    float pv[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const int j = 4 * ks + kg;
+        const float bm = Mt[j * MS + m];
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(s[ks].x, bm, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(s[ks].y, bm, acc1, 0, 0, 0);
+        if (NVL) {
+            const float2 mv = *reinterpret_cast<const float2 *>(&Mt[j * MS + 16]);
+            pv[0][0] = __builtin_fmaf(s[ks].x, mv.x, pv[0][0]);
+            pv[0][1] = __builtin_fmaf(s[ks].x, mv.y, pv[0][1]);
+            pv[1][0] = __builtin_fmaf(s[ks].y, mv.x, pv[1][0]);
+            pv[1][1] = __builtin_fmaf(s[ks].y, mv.y, pv[1][1]);
+        }
+    }
+    // tile r, register q of lane (kg, m): row 32w + 2(4kg + q) + r, column m
+    if (m < NMF) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            P[(32 * wave + 2 * (4 * kg + q)) * PS + m] = acc0[q];
+            P[(32 * wave + 2 * (4 * kg + q) + 1) * PS + m] = acc1[q];
+        }
+    }
+    if (NVL) {
+        // the four key-index groups kg hold partial sums: add lanes l^16 and l^32
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                float x = pv[r][c];
+                x += __shfl_xor(x, 16, 64);
+                x += __shfl_xor(x, 32, 64);
+                pv[r][c] = x;
+            }
+        if (kg == 0) {
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+                    P[(row0 + r) * PS + NMF + c] = pv[r][c];
+        }
+    }
+    lds_barrier();
+
+    // per state row i: correction vectors and outputs
+    if (tid < D) {
+        float pk[NR], pq[NR], e[NR];
+#pragma unroll
+        for (int c = 0; c < NR; ++c) {
+            pk[c] = P[tid * PS + c];
+            pq[c] = P[tid * PS + NR + c];
+        }
+        solve_row<NR>(p, cf, pk, pq, v, e, b, h, tid, D);
+#pragma unroll
+        for (int t = 0; t < NR; ++t)
+            p.xs[((size_t)b * NR + t) * p.C + cv] = vin.x[t];
+        if (SNAP) {
+            // row tid of P is read only by this thread: reuse it for e_t
+#pragma unroll
+            for (int t = 0; t < NR; ++t)
+                P[tid * PS + t] = e[t];
+        }
+    }
+
+    if (SNAP) {
+        lds_barrier();
+        // S_t for every row, by the same update the replay commit applies
+#pragma unroll 1
+        for (int t = 0; t < NR; ++t) {
+            const float a = cf[t];
+            const float e0 = P[row0 * PS + t], e1 = P[(row0 + 1) * PS + t];
+            float *dst = p.snap + (((size_t)b * NR + t) * HV + h) * D * D;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int j = 4 * ks + kg;
+                const float k = Mt[j * MS + t];
+                s[ks].x = row_update(s[ks].x, a, e0, k);
+                s[ks].y = row_update(s[ks].y, a, e1, k);
+                *reinterpret_cast<float2 *>(dst + (size_t)j * D + row0) = s[ks];
+            }
+        }
+    }
+}
+
 // ---- commit ----------------------------------------------------------------
 
 template <typename T> struct CommitParams {
@@ -460,8 +806,8 @@ template <typename T> struct CommitParams {
     int32_t *err;
     const T *xs;
     const float *es;
-    const float *ks;
-    const float *as;
+    const float *tab;
+    const float *coef;
     const float *snap;
     int HK, HV, C, P, R;
 };
@@ -518,15 +864,16 @@ __global__ __launch_bounds__(kThreads) void gdn_commit_kernel(const CommitParams
         // staging loads first (fixed count, clamped indices, no branches),
         // then the state stream
         constexpr int NSTAGE = (kMaxRows * D + kThreads - 1) / kThreads;
+        const float *tab = p.tab + ((size_t)b * HK + kh) * 2 * R * D;  // k_t at tab[t*D + j]
         float ev_in[NSTAGE], kv_in[NSTAGE];
 #pragma unroll
         for (int q = 0; q < NSTAGE; ++q) {
             const int idx = min(q * kThreads + tid, n * D - 1);
             const int t = idx / D, i = idx % D;
             ev_in[q] = p.es[(((size_t)b * R + t) * HV + h) * D + i];
-            kv_in[q] = p.ks[(((size_t)b * R + t) * HK + kh) * D + i];
+            kv_in[q] = tab[idx];
         }
-        const float a_in = p.as[((size_t)b * R + min(tid, n - 1)) * HV + h];
+        const float a_in = p.coef[((size_t)b * HV + h) * coef_count(R) + min(tid, n - 1)];
         float4 s[JPER];
 #pragma unroll
         for (int jj = 0; jj < JPER; ++jj)
@@ -607,7 +954,7 @@ gdn_status check_desc(const gdn_layer_desc *d, Checked *c)
         return GDN_ERR_INVALID_ARG;
     if (d->d_k != d->d_v || (d->d_k != 32 && d->d_k != 64 && d->d_k != 128))
         return GDN_ERR_UNSUPPORTED;
-    if (d->conv_width != kWidth)
+    if (d->conv_width != kWidth || d->num_v_heads / d->num_k_heads > kMaxGroup)
         return GDN_ERR_UNSUPPORTED;
     c->HK = d->num_k_heads;
     c->HV = d->num_v_heads;
@@ -619,37 +966,49 @@ gdn_status check_desc(const gdn_layer_desc *d, Checked *c)
 
 bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
+struct VerifyLaunch {
+    int batch, HK, HV;
+    hipStream_t st;
+};
+
 template <int D, int NR, typename T, bool SNAP>
-hipError_t launch_verify(const VerifyParams<T> &vp, int blocks, hipStream_t st)
+hipError_t launch_verify(const VerifyParams<T> &vp, const VerifyLaunch &l)
 {
-    hipLaunchKernelGGL((gdn_verify_kernel<D, NR, T, SNAP>), dim3(blocks), dim3(kThreads), 0, st, vp);
+    if (D == 128) {
+        hipLaunchKernelGGL((gdn_prep_kernel<NR, T>), dim3(l.batch * l.HK), dim3(kThreads), 0, l.st, vp);
+        hipLaunchKernelGGL((gdn_stream_d128_kernel<NR, T, SNAP>), dim3(l.batch * l.HV), dim3(kThreads),
+                           0, l.st, vp);
+    } else {
+        hipLaunchKernelGGL((gdn_verify_kernel<D, NR, T, SNAP>), dim3(l.batch * l.HV), dim3(kThreads),
+                           0, l.st, vp);
+    }
     return hipGetLastError();
 }
 
 template <int D, typename T, bool SNAP>
-hipError_t verify_rows(int rows, const VerifyParams<T> &vp, int blocks, hipStream_t st)
+hipError_t verify_rows(int rows, const VerifyParams<T> &vp, const VerifyLaunch &l)
 {
     switch (rows) {
-    case 1: return launch_verify<D, 1, T, SNAP>(vp, blocks, st);
-    case 2: return launch_verify<D, 2, T, SNAP>(vp, blocks, st);
-    case 3: return launch_verify<D, 3, T, SNAP>(vp, blocks, st);
-    case 4: return launch_verify<D, 4, T, SNAP>(vp, blocks, st);
-    case 5: return launch_verify<D, 5, T, SNAP>(vp, blocks, st);
-    case 6: return launch_verify<D, 6, T, SNAP>(vp, blocks, st);
-    case 7: return launch_verify<D, 7, T, SNAP>(vp, blocks, st);
-    case 8: return launch_verify<D, 8, T, SNAP>(vp, blocks, st);
-    case 9: return launch_verify<D, 9, T, SNAP>(vp, blocks, st);
+    case 1: return launch_verify<D, 1, T, SNAP>(vp, l);
+    case 2: return launch_verify<D, 2, T, SNAP>(vp, l);
+    case 3: return launch_verify<D, 3, T, SNAP>(vp, l);
+    case 4: return launch_verify<D, 4, T, SNAP>(vp, l);
+    case 5: return launch_verify<D, 5, T, SNAP>(vp, l);
+    case 6: return launch_verify<D, 6, T, SNAP>(vp, l);
+    case 7: return launch_verify<D, 7, T, SNAP>(vp, l);
+    case 8: return launch_verify<D, 8, T, SNAP>(vp, l);
+    case 9: return launch_verify<D, 9, T, SNAP>(vp, l);
     default: return hipErrorInvalidValue;
     }
 }
 
 template <typename T, bool SNAP>
-hipError_t verify_dim(int D, int rows, const VerifyParams<T> &vp, int blocks, hipStream_t st)
+hipError_t verify_dim(int D, int rows, const VerifyParams<T> &vp, const VerifyLaunch &l)
 {
     switch (D) {
-    case 32: return verify_rows<32, T, SNAP>(rows, vp, blocks, st);
-    case 64: return verify_rows<64, T, SNAP>(rows, vp, blocks, st);
-    case 128: return verify_rows<128, T, SNAP>(rows, vp, blocks, st);
+    case 32: return verify_rows<32, T, SNAP>(rows, vp, l);
+    case 64: return verify_rows<64, T, SNAP>(rows, vp, l);
+    case 128: return verify_rows<128, T, SNAP>(rows, vp, l);
     default: return hipErrorInvalidValue;
     }
 }
@@ -673,8 +1032,8 @@ hipError_t verify_typed(const Checked &c, const gdn_layer_desc *d, const gdn_poo
     vp.err = err;
     vp.xs = reinterpret_cast<T *>(base + L.xs);
     vp.es = reinterpret_cast<float *>(base + L.es);
-    vp.ks = reinterpret_cast<float *>(base + L.ks);
-    vp.as = reinterpret_cast<float *>(base + L.as);
+    vp.tab = reinterpret_cast<float *>(base + L.tab);
+    vp.coef = reinterpret_cast<float *>(base + L.coef);
     vp.snap = snapshot ? reinterpret_cast<float *>(base + L.snap) : nullptr;
     vp.HK = c.HK;
     vp.HV = c.HV;
@@ -683,9 +1042,8 @@ hipError_t verify_typed(const Checked &c, const gdn_layer_desc *d, const gdn_poo
     vp.act = d->act;
     vp.scale = d->scale;
     vp.eps = d->l2_eps;
-    const int blocks = batch * c.HV;
-    return snapshot ? verify_dim<T, true>(c.D, rows, vp, blocks, st)
-                    : verify_dim<T, false>(c.D, rows, vp, blocks, st);
+    const VerifyLaunch l{batch, c.HK, c.HV, st};
+    return snapshot ? verify_dim<T, true>(c.D, rows, vp, l) : verify_dim<T, false>(c.D, rows, vp, l);
 }
 
 template <int D, typename T, bool SNAP>
@@ -720,8 +1078,8 @@ hipError_t commit_typed(const Checked &c, const gdn_pool *pool, const int32_t *s
     cp.err = err;
     cp.xs = reinterpret_cast<const T *>(base + L.xs);
     cp.es = reinterpret_cast<const float *>(base + L.es);
-    cp.ks = reinterpret_cast<const float *>(base + L.ks);
-    cp.as = reinterpret_cast<const float *>(base + L.as);
+    cp.tab = reinterpret_cast<const float *>(base + L.tab);
+    cp.coef = reinterpret_cast<const float *>(base + L.coef);
     cp.snap = snapshot ? reinterpret_cast<const float *>(base + L.snap) : nullptr;
     cp.HK = c.HK;
     cp.HV = c.HV;
