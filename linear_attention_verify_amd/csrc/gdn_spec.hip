@@ -17,18 +17,9 @@
 // scalar algebra per state row, gives every o_t. The state is streamed once
 // from HBM and never written.
 //
-// For d = 128 the verify is two launches:
-//   gdn_prep_kernel    one workgroup per (request, key head): conv + SiLU of the
-//                      q/k channels, L2 norms, the normalised column table
-//                      [k_0..k_{R-1} | q_0..q_{R-1}], its Gram entries and,
-//                      for each value head of the key head, the scalar
-//                      coefficients g(t,-1), b_t, g(t,u) k_u.k_t, g(t,u) k_u.q_t;
-//   gdn_stream_d128    one workgroup per (request, value head): streams S_0,
-//                      runs S_0 [K | Q] on the matrix cores, the value conv in
-//                      registers and the triangular solve for e_t and o_t.
-// Keeping the latency-bound per-key-head work out of the streaming kernel lets
-// the state stream of one round of workgroups overlap the compute of another.
-// Other head dims use one fused kernel (gdn_verify_kernel) on the VALU.
+// For d = 128 (gdn_verify_d128_kernel) the 2R products, and the Gram entries
+// k_u.k_t and k_u.q_t the scalar algebra needs, come out of one pass on the
+// matrix cores; other head dims use a VALU kernel (gdn_verify_kernel).
 //
 // Commit (same Design section: the commit replays the accepted rows). The
 // verify leaves each row's e_t and normalised k_t in scratch, so replaying
@@ -78,6 +69,29 @@ template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v)
         return bf16_t{(uint16_t)((u >> 16) | 0x40u)};  // stay NaN
     u += 0x7fffu + ((u >> 16) & 1u);                     // nearest, ties to even
     return bf16_t{(uint16_t)(u >> 16)};
+}
+
+// Buffer loads: an SGPR resource (base, size in bytes), a 32-bit per-lane
+// byte offset and a uniform byte offset. Keeps address registers to one per
+// lane, and the hardware returns zero for any byte outside the resource.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+template <typename T> __device__ __forceinline__ T buf_load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff);
+template <> __device__ __forceinline__ float buf_load<float>(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0));
+}
+template <> __device__ __forceinline__ bf16_t buf_load<bf16_t>(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return bf16_t{__builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0)};
+}
+
+__device__ __forceinline__ float2 buf_load_f2(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0));
 }
 
 // Barrier that orders LDS only: global loads already in flight (the state
@@ -136,12 +150,13 @@ __device__ __forceinline__ void tri_decode(int idx, int &t, int &u)
 
 // ---- scratch layout (shared by host and device code) -----------------------
 
-// Scalar coefficients per (request, value head): a_t, g(t,-1), b_t, then the
-// R x R blocks g(t,u) k_u.k_t (u < t) and g(t,u) k_u.q_t (u <= t).
+// Scalar coefficients of one value head, as the verify kernels keep them in
+// LDS: a_t, g(t,-1), b_t, then the R x R blocks g(t,u) k_u.k_t (u < t) and
+// g(t,u) k_u.q_t (u <= t).
 __host__ __device__ constexpr int coef_count(int R) { return 3 * R + 2 * R * R; }
 
 struct ScratchLayout {
-    size_t xs, es, tab, coef, snap, total;
+    size_t xs, es, ks, as, snap, total;
 };
 
 __host__ __device__ inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -149,8 +164,8 @@ __host__ __device__ inline size_t align_up(size_t v) { return (v + kAlign - 1) /
 // Per request b (row b of every part):
 //   xs   [B][R][C]          raw verify inputs (storage type), for the conv commit
 //   es   [B][R][HV][D]      fp32 correction vector e_t of each row and value head
-//   tab  [B][HK][2R][D]     fp32 normalised k_0..k_{R-1}, q_0..q_{R-1} per key head
-//   coef [B][HV][3R + 2R^2] fp32 scalar coefficients (a_t first)
+//   ks   [B][HK][R][D]      fp32 normalised k_t of each row and key head
+//   as   [B][HV][R]         fp32 decay gate a_t
 //   snap [B][R][HV][D][D]   fp32 S_t after each row (snapshot mode only), same
 //                           per-head layout as the pool
 __host__ inline ScratchLayout scratch_layout(int HK, int HV, int D, int C, size_t esize, int B,
@@ -162,10 +177,10 @@ __host__ inline ScratchLayout scratch_layout(int HK, int HV, int D, int C, size_
     off = align_up(off + (size_t)B * R * C * esize);
     L.es = off;
     off = align_up(off + (size_t)B * R * HV * D * sizeof(float));
-    L.tab = off;
-    off = align_up(off + (size_t)B * HK * 2 * R * D * sizeof(float));
-    L.coef = off;
-    off = align_up(off + (size_t)B * HV * coef_count(R) * sizeof(float));
+    L.ks = off;
+    off = align_up(off + (size_t)B * HK * R * D * sizeof(float));
+    L.as = off;
+    off = align_up(off + (size_t)B * HV * R * sizeof(float));
     L.snap = off;
     if (snapshot)
         off = align_up(off + (size_t)B * R * HV * D * D * sizeof(float));
@@ -187,8 +202,8 @@ template <typename T> struct VerifyParams {
     int32_t *err;
     T *xs;
     float *es;
-    float *tab;
-    float *coef;
+    float *ks;
+    float *as;
     float *snap;
     int HK, HV, C, P;
     int act;
@@ -202,19 +217,26 @@ template <int NR, typename T> struct ChanIn {
     T x[NR];
 };
 
+// Row bases are uniform across the workgroup and the channel is the only
+// per-lane part, so every load is an SGPR base plus one 32-bit lane offset.
 template <int NR, typename T>
 __device__ __forceinline__ ChanIn<NR, T> load_channel(const VerifyParams<T> &p, int slot, int b, int c)
 {
     ChanIn<NR, T> in;
+    const uint32_t E = sizeof(T);
+    const uint32_t row = (uint32_t)p.C * E;
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.conv_w, row * kWidth);
+    const __amdgpu_buffer_rsrc_t rh = make_rsrc(p.conv + (size_t)slot * (kWidth - 1) * p.C, row * (kWidth - 1));
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x + (size_t)b * NR * p.C, row * NR);
 #pragma unroll
     for (int k = 0; k < kWidth; ++k)
-        in.w[k] = p.conv_w[(size_t)c * kWidth + k];
+        in.w[k] = buf_load<T>(rw, (uint32_t)c * kWidth * E, k * E);
 #pragma unroll
     for (int k = 0; k < kWidth - 1; ++k)
-        in.hist[k] = p.conv[((size_t)slot * (kWidth - 1) + k) * p.C + c];
+        in.hist[k] = buf_load<T>(rh, (uint32_t)c * E, k * row);
 #pragma unroll
     for (int t = 0; t < NR; ++t)
-        in.x[t] = p.x[((size_t)b * NR + t) * p.C + c];
+        in.x[t] = buf_load<T>(rx, (uint32_t)c * E, t * row);
     return in;
 }
 
@@ -271,6 +293,7 @@ __device__ __forceinline__ void solve_row(const VerifyParams<T> &p, const float 
         const size_t oi = (((size_t)b * NR + t) * p.HV + h) * D + i;
         p.out[oi] = from_f32<T>(p.scale * o);
         p.es[oi] = e[t];
+        __builtin_amdgcn_sched_barrier(0);  // one row at a time: bounds the hoisted coefficient reads
     }
 }
 
@@ -466,15 +489,13 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_kernel(const VerifyParams
         }
     }
     if (owner) {
-        float *tab = p.tab + ((size_t)b * HK + kh) * NC * D;
-        for (int idx = tid; idx < NC * D; idx += kThreads) {
-            const int c = idx / D, j = idx % D;
-            tab[idx] = Mt[j * MS + c];
-        }
+        float *ks = p.ks + ((size_t)b * HK + kh) * NR * D;
+        for (int idx = tid; idx < NR * D; idx += kThreads)
+            ks[idx] = Mt[(idx % D) * MS + idx / D];
     }
-    lds_barrier();
     if (tid < NR)
-        p.coef[((size_t)b * HV + h) * NCF + tid] = cf[tid];  // a_t, for the commit
+        p.as[((size_t)b * HV + h) * NR + tid] = al[tid];
+    lds_barrier();
 
     // per state row i: correction vectors and outputs
     if (tid < D) {
@@ -522,124 +543,21 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_kernel(const VerifyParams
     }
 }
 
-// ---- verify, d = 128, launch 1: per key head ---------------------------------
-//
-// Thread j < 128 runs the conv of q channel j, thread 128 + j that of k
-// channel j. Writes the normalised column table, the raw q/k inputs of the
-// rows (for the conv commit) and the coefficients of each value head.
-template <int NR, typename T>
-__global__ __launch_bounds__(kThreads) void gdn_prep_kernel(const VerifyParams<T> p)
-{
-    constexpr int D = 128;
-    constexpr int NC = 2 * NR;
-    constexpr int QS = NC + 1;               // LDS row stride (odd)
-    constexpr int NPAIR = NR * (NR + 1) / 2;
-    constexpr int PAIRS = 2 * NPAIR;
-    constexpr int SPLIT = 4;                 // Gram dots in 4 partial sums
-    constexpr int NCF = coef_count(NR);
-
-    __shared__ float qk[D * QS];             // [j][c]: k (c < NR), q (c >= NR); normalised in place
-    __shared__ float inv[NC];
-    __shared__ float gpart[PAIRS * SPLIT];
-    __shared__ float gkk[NR * NR], gkq[NR * NR];
-    __shared__ float al[kMaxGroup * NR], be[kMaxGroup * NR];  // gates of the key head's value heads
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int HV = p.HV, HK = p.HK;
-    const int G = HV / HK;
-    const int b = blockIdx.x / HK;
-    const int kh = blockIdx.x % HK;
-    const int slot = p.slot_ids[b];
-    if (slot < 0 || slot >= p.P)
-        return;  // padding or a bad slot: the stream kernel flags and zeroes it
-
-    // gate g*NR + t of value head kh*G + g, clamped so the loads need no branch
-    const int gq = min(tid, G * NR - 1);
-    const size_t gi = ((size_t)b * NR + gq % NR) * HV + kh * G + gq / NR;
-    const T ga = p.alpha[gi], gb = p.beta[gi];
-    const int j = tid & (D - 1);
-    const bool isq = tid < D;
-    const int c = isq ? kh * D + j : HK * D + kh * D + j;
-    const ChanIn<NR, T> in = load_channel<NR>(p, slot, b, c);
-    if (tid < G * NR) {
-        al[tid] = to_f32(ga);
-        be[tid] = to_f32(gb);
-    }
-    {
-        float y[NR];
-        conv_rows(in, p.act, y);
-#pragma unroll
-        for (int t = 0; t < NR; ++t)
-            qk[j * QS + (isq ? NR + t : t)] = y[t];
-    }
-#pragma unroll
-    for (int t = 0; t < NR; ++t)
-        p.xs[((size_t)b * NR + t) * p.C + c] = in.x[t];
-    lds_barrier();
-
-    for (int col = wave; col < NC; col += 4) {
-        const float v0 = qk[lane * QS + col], v1 = qk[(lane + 64) * QS + col];
-        const float ss = wave_sum(__builtin_fmaf(v0, v0, v1 * v1));
-        if (lane == 0)
-            inv[col] = 1.0f / sqrtf(ss + p.eps);
-    }
-    lds_barrier();
-    float *tab = p.tab + ((size_t)b * HK + kh) * NC * D;
-    for (int idx = tid; idx < NC * D; idx += kThreads) {
-        const int col = idx / D, jj = idx % D;
-        const float v = qk[jj * QS + col] * inv[col];
-        qk[jj * QS + col] = v;
-        tab[idx] = v;
-    }
-    lds_barrier();
-
-    for (int idx = tid; idx < PAIRS * SPLIT; idx += kThreads) {
-        const int pair = idx / SPLIT, part = idx % SPLIT;
-        int t, u;
-        tri_decode(pair % NPAIR, t, u);
-        const int ca = pair >= NPAIR ? NR + t : t;
-        float a0 = 0.0f, a1 = 0.0f;
-#pragma unroll 8
-        for (int jj = part * (D / SPLIT); jj < (part + 1) * (D / SPLIT); jj += 2) {
-            a0 = __builtin_fmaf(qk[jj * QS + ca], qk[jj * QS + u], a0);
-            a1 = __builtin_fmaf(qk[(jj + 1) * QS + ca], qk[(jj + 1) * QS + u], a1);
-        }
-        gpart[idx] = a0 + a1;
-    }
-    lds_barrier();
-    if (tid < PAIRS) {
-        int t, u;
-        tri_decode(tid % NPAIR, t, u);
-        float acc = 0.0f;
-#pragma unroll
-        for (int q = 0; q < SPLIT; ++q)
-            acc += gpart[tid * SPLIT + q];
-        (tid >= NPAIR ? gkq : gkk)[t * NR + u] = acc;
-    }
-    lds_barrier();
-
-    for (int idx = tid; idx < G * (NR * NR + NR); idx += kThreads) {
-        const int gh = idx / (NR * NR + NR);
-        const int h = kh * G + gh;
-        write_coefficients<NR>(gkk, gkq, al + gh * NR, be + gh * NR, idx % (NR * NR + NR),
-                               p.coef + ((size_t)b * HV + h) * NCF);
-    }
-}
-
-// ---- verify, d = 128, launch 2: per value head ------------------------------
+// ---- verify, d = 128: one pass on the matrix cores --------------------------
 //
 // The 2R products S_0 k_t, S_0 q_t are a dense (128 x 128) x (128 x 2R)
 // contraction, run with v_mfma_f32_16x16x4_f32 (fp32 in, fp32 accumulate).
 // Wave w owns state rows 32w..32w+31 as two 16-row tiles: lane l (kg = l/16,
 // m = l%16) loads rows 32w+2m and 32w+2m+1 at key index j = 4*ks + kg for each
 // of the 32 K-steps ks, which is exactly the A operand of both tiles
-// (A[m][k] = S[row][4ks+k]). The first 16 columns of [K | Q] go through one
+// (A[m][k] = S[row][4ks+k]). The first 16 columns of M = [K | Q] go through one
 // 16-wide B tile; with R = 9 the last two (q_7, q_8) are done on the VALU from
-// the same registers, so no matrix-core work is spent on padding.
+// the same registers. A third tile has the keys themselves as rows
+// (A[m][k] = k_m[4ks+k], the same LDS value as the B operand of column m): it
+// yields K^T M, i.e. every Gram entry k_u.k_t and k_u.q_t, with each wave
+// covering 8 of the 32 K-steps.
 template <int NR, typename T, bool SNAP>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void gdn_stream_d128_kernel(const VerifyParams<T> p)
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NR == 9 ? 3 : 4))) void gdn_verify_d128_kernel(const VerifyParams<T> p)
 {
     constexpr int D = 128;
     constexpr int NC = 2 * NR;
@@ -649,13 +567,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     constexpr int MS = NVL ? 20 : 16;        // column-table row stride
     constexpr int PS = NC + 1;               // product-table row stride (odd)
     constexpr int KS = D / 4;                // K-steps of 4 key indices
+    constexpr int KSW = KS / 4;              // K-steps of the Gram tile per wave
     constexpr int NCF = coef_count(NR);
-    constexpr int TABN = NC * D;
-    constexpr int TPT = (TABN + kThreads - 1) / kThreads;  // table floats per thread
 
-    __shared__ __align__(16) float Mt[D * MS];   // [j][c]: k_hat_c[j] (c < NR), q_hat_{c-NR}[j]; 0 beyond NC
-    __shared__ __align__(16) float P[D * PS];    // [i][c]: (S_0 k_hat_c)[i], then (S_0 q_hat)[i]; later e_t
+    __shared__ __align__(16) float Mt[D * MS];   // [j][c]: k_c[j] (c < NR), q_{c-NR}[j]; 0 beyond NC
+    __shared__ __align__(16) float P[D * PS];    // [i][c]: (S_0 M)[i][c]; later e_t in snapshot mode
+    __shared__ float gp[4 * NR * NC];            // [w][u][c]: wave w's share of (K^T M)[u][c]
+    __shared__ float inv[NC];
     __shared__ float cf[NCF];
+    __shared__ float al[NR], be[NR];
+    __shared__ T xr[NR * kThreads];              // raw q/k inputs of each thread's channel, by row
+    __shared__ T xv[NR * D];                     // raw value inputs, by row
+    __shared__ float vb[NR * D];                 // v_t[i] after the conv
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -674,65 +597,126 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         return;
     }
 
-    // small loads first (branch-free: vmcnt retires in issue order), then the state
-    const int i = tid & (D - 1);
-    const int cv = 2 * HK * D + h * D + i;
-    const ChanIn<NR, T> vin = load_channel<NR>(p, slot, b, cv);
-    const float *tab = p.tab + ((size_t)b * HK + kh) * TABN;
-    float tv[TPT];
-#pragma unroll
-    for (int q = 0; q < TPT; ++q)
-        tv[q] = tab[min(q * kThreads + tid, TABN - 1)];
-    const float cfv = p.coef[((size_t)b * HV + h) * NCF + min(tid, NCF - 1)];
+    // Small loads first, branch-free, so they share a block with the state
+    // stream and retire ahead of it. Threads < 128 take q channel `tid` and
+    // value channel `tid`; threads 128.. take k channel tid-128 (and load the
+    // value channel again, unused).
+    const size_t gi = ((size_t)b * NR + min(tid, NR - 1)) * HV + h;
+    const T ga = p.alpha[gi], gb = p.beta[gi];
+    const int jc = tid & (D - 1);
+    const bool isq = tid < D;
+    const int chA = isq ? kh * D + jc : HK * D + kh * D + jc;
+    const int chV = 2 * HK * D + h * D + jc;
+    const ChanIn<NR, T> cinA = load_channel<NR>(p, slot, b, chA);
+    const ChanIn<NR, T> cinV = load_channel<NR>(p, slot, b, chV);
 
+    // The state slice in two halves: the first goes out with the small loads,
+    // the second once the convs have freed their input registers.
     const int kg = lane >> 4;
     const int m = lane & 15;
     const int row0 = 32 * wave + 2 * m;            // this lane's two state rows: row0, row0 + 1
-    const float *S0 = p.ssm + ((size_t)slot * HV + h) * D * D;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.ssm + ((size_t)slot * HV + h) * D * D, D * D * 4);
+    const uint32_t soff = (kg * D + row0) * 4;      // lane byte offset within each K-step block
     float2 s[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-        s[ks] = *reinterpret_cast<const float2 *>(S0 + (size_t)(4 * ks + kg) * D + row0);
+    for (int ks = 0; ks < KS / 2; ++ks)
+        s[ks] = buf_load_f2(rs, soff, ks * 4 * D * 4);
     __builtin_amdgcn_sched_barrier(0);
 
-#pragma unroll
-    for (int q = 0; q < TPT; ++q) {
-        const int idx = q * kThreads + tid;
-        if (idx < TABN)
-            Mt[(idx % D) * MS + idx / D] = tv[q];
+    if (tid < NR) {
+        al[tid] = to_f32(ga);
+        be[tid] = to_f32(gb);
     }
-    for (int idx = tid; idx < D * (MS - NC); idx += kThreads)
-        Mt[(idx / (MS - NC)) * MS + NC + idx % (MS - NC)] = 0.0f;
-    if (tid < NCF)
-        cf[tid] = cfv;
-    float v[NR];
-    conv_rows(vin, p.act, v);
+    {
+        float y[NR];
+        conv_rows(cinA, p.act, y);
+#pragma unroll
+        for (int t = 0; t < NR; ++t) {
+            Mt[jc * MS + (isq ? NR + t : t)] = y[t];
+            xr[t * kThreads + tid] = cinA.x[t];
+        }
+        if (isq) {
+#pragma unroll
+            for (int c = NC; c < MS; ++c)
+                Mt[jc * MS + c] = 0.0f;
+#pragma unroll
+            for (int t = 0; t < NR; ++t)
+                xv[t * D + jc] = cinV.x[t];
+        }
+        conv_rows(cinV, p.act, y);
+        if (isq) {
+#pragma unroll
+            for (int t = 0; t < NR; ++t)
+                vb[t * D + jc] = y[t];
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = KS / 2; ks < KS; ++ks)
+        s[ks] = buf_load_f2(rs, soff, ks * 4 * D * 4);
+    __builtin_amdgcn_sched_barrier(0);
     lds_barrier();
 
-    // S_0 [K | Q]: one 16-column tile on the matrix cores, the rest on the VALU
+    // L2 norms of the 2R columns, one wave per column
+    for (int col = wave; col < NC; col += 4) {
+        const float v0 = Mt[lane * MS + col], v1 = Mt[(lane + 64) * MS + col];
+        const float ss = wave_sum(__builtin_fmaf(v0, v0, v1 * v1));
+        if (lane == 0)
+            inv[col] = 1.0f / sqrtf(ss + p.eps);
+    }
+    lds_barrier();
+    for (int idx = tid; idx < D * NC; idx += kThreads) {
+        const int j = idx / NC, c = idx % NC;
+        Mt[j * MS + c] *= inv[c];
+    }
+    lds_barrier();
+
+    // S_0 M (two state tiles) and K^T M (one key tile, this wave's K-steps)
     f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f};
     f32x4 acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
-    float pv[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
+    f32x4 accg = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
         const int j = 4 * ks + kg;
         const float bm = Mt[j * MS + m];
         acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(s[ks].x, bm, acc0, 0, 0, 0);
         acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(s[ks].y, bm, acc1, 0, 0, 0);
-        if (NVL) {
+        if (ks / KSW == wave) {
+            const float ak = m < NR ? bm : 0.0f;   // row m of the key tile: k_m[j]
+            accg = __builtin_amdgcn_mfma_f32_16x16x4f32(ak, bm, accg, 0, 0, 0);
+        }
+        if (ks % 4 == 3)
+            __builtin_amdgcn_sched_barrier(0);  // bound the operand lookahead (register pressure)
+    }
+    // the VALU columns in a second pass over the same registers
+    float pv[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
+    float gv[2] = {0.0f, 0.0f};
+    if (NVL) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int j = 4 * ks + kg;
             const float2 mv = *reinterpret_cast<const float2 *>(&Mt[j * MS + 16]);
             pv[0][0] = __builtin_fmaf(s[ks].x, mv.x, pv[0][0]);
             pv[0][1] = __builtin_fmaf(s[ks].x, mv.y, pv[0][1]);
             pv[1][0] = __builtin_fmaf(s[ks].y, mv.x, pv[1][0]);
             pv[1][1] = __builtin_fmaf(s[ks].y, mv.y, pv[1][1]);
+            if (ks / KSW == wave && m < NR) {
+                const float ak = Mt[j * MS + m];
+                gv[0] = __builtin_fmaf(ak, mv.x, gv[0]);
+                gv[1] = __builtin_fmaf(ak, mv.y, gv[1]);
+            }
+            if (ks % 4 == 3)
+                __builtin_amdgcn_sched_barrier(0);
         }
     }
-    // tile r, register q of lane (kg, m): row 32w + 2(4kg + q) + r, column m
+    // tile register q of lane (kg, m): row 4kg + q of the tile, column m
     if (m < NMF) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             P[(32 * wave + 2 * (4 * kg + q)) * PS + m] = acc0[q];
             P[(32 * wave + 2 * (4 * kg + q) + 1) * PS + m] = acc1[q];
+            if (4 * kg + q < NR)
+                gp[(wave * NR + 4 * kg + q) * NC + m] = accg[q];
         }
     }
     if (NVL) {
@@ -746,28 +730,79 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
                 x += __shfl_xor(x, 32, 64);
                 pv[r][c] = x;
             }
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            float x = gv[c];
+            x += __shfl_xor(x, 16, 64);
+            x += __shfl_xor(x, 32, 64);
+            gv[c] = x;
+        }
         if (kg == 0) {
 #pragma unroll
             for (int r = 0; r < 2; ++r)
 #pragma unroll
                 for (int c = 0; c < 2; ++c)
                     P[(row0 + r) * PS + NMF + c] = pv[r][c];
+            if (m < NR) {
+                gp[(wave * NR + m) * NC + NMF] = gv[0];
+                gp[(wave * NR + m) * NC + NMF + 1] = gv[1];
+            }
+        }
+    }
+
+    // scratch for the commit; stores start only now that the state has landed
+    const bool owner = (h % G) == 0;  // one value head per key head stores the q/k inputs and k_t
+#pragma unroll
+    for (int t = 0; t < NR; ++t) {
+        if (owner)
+            p.xs[((size_t)b * NR + t) * p.C + chA] = xr[t * kThreads + tid];
+        if (isq)
+            p.xs[((size_t)b * NR + t) * p.C + chV] = xv[t * D + jc];
+    }
+    if (owner) {
+        float *ks = p.ks + ((size_t)b * HK + kh) * NR * D;
+        for (int idx = tid; idx < NR * D; idx += kThreads)
+            ks[idx] = Mt[(idx % D) * MS + idx / D];
+    }
+    if (tid < NR)
+        p.as[((size_t)b * HV + h) * NR + tid] = al[tid];
+    lds_barrier();
+
+    // scalar coefficients; (K^T M)[u][c] is the sum of the four waves' shares
+    for (int idx = tid; idx < NR * NR + NR; idx += kThreads) {
+        auto gram = [&](int u, int c) {
+            return (gp[(0 * NR + u) * NC + c] + gp[(1 * NR + u) * NC + c]) +
+                   (gp[(2 * NR + u) * NC + c] + gp[(3 * NR + u) * NC + c]);
+        };
+        if (idx < NR * NR) {
+            const int t = idx / NR, u = idx % NR;
+            float gtu = 1.0f;
+            for (int q = u + 1; q <= t; ++q)
+                gtu *= al[q];
+            cf[3 * NR + idx] = (u < t) ? gtu * gram(u, t) : 0.0f;
+            cf[3 * NR + NR * NR + idx] = (u <= t) ? gtu * gram(u, NR + t) : 0.0f;
+        } else {
+            const int t = idx - NR * NR;
+            float gt = 1.0f;
+            for (int q = 0; q <= t; ++q)
+                gt *= al[q];
+            cf[t] = al[t];
+            cf[NR + t] = gt;
+            cf[2 * NR + t] = be[t];
         }
     }
     lds_barrier();
 
     // per state row i: correction vectors and outputs
     if (tid < D) {
-        float pk[NR], pq[NR], e[NR];
+        float pk[NR], pq[NR], v[NR], e[NR];
 #pragma unroll
         for (int c = 0; c < NR; ++c) {
             pk[c] = P[tid * PS + c];
             pq[c] = P[tid * PS + NR + c];
+            v[c] = vb[c * D + tid];
         }
         solve_row<NR>(p, cf, pk, pq, v, e, b, h, tid, D);
-#pragma unroll
-        for (int t = 0; t < NR; ++t)
-            p.xs[((size_t)b * NR + t) * p.C + cv] = vin.x[t];
         if (SNAP) {
             // row tid of P is read only by this thread: reuse it for e_t
 #pragma unroll
@@ -781,7 +816,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         // S_t for every row, by the same update the replay commit applies
 #pragma unroll 1
         for (int t = 0; t < NR; ++t) {
-            const float a = cf[t];
+            const float a = al[t];
             const float e0 = P[row0 * PS + t], e1 = P[(row0 + 1) * PS + t];
             float *dst = p.snap + (((size_t)b * NR + t) * HV + h) * D * D;
 #pragma unroll
@@ -806,8 +841,8 @@ template <typename T> struct CommitParams {
     int32_t *err;
     const T *xs;
     const float *es;
-    const float *tab;
-    const float *coef;
+    const float *ks;
+    const float *as;
     const float *snap;
     int HK, HV, C, P, R;
 };
@@ -864,16 +899,16 @@ __global__ __launch_bounds__(kThreads) void gdn_commit_kernel(const CommitParams
         // staging loads first (fixed count, clamped indices, no branches),
         // then the state stream
         constexpr int NSTAGE = (kMaxRows * D + kThreads - 1) / kThreads;
-        const float *tab = p.tab + ((size_t)b * HK + kh) * 2 * R * D;  // k_t at tab[t*D + j]
+        const float *kt = p.ks + ((size_t)b * HK + kh) * R * D;  // k_t at kt[t*D + j]
         float ev_in[NSTAGE], kv_in[NSTAGE];
 #pragma unroll
         for (int q = 0; q < NSTAGE; ++q) {
             const int idx = min(q * kThreads + tid, n * D - 1);
             const int t = idx / D, i = idx % D;
             ev_in[q] = p.es[(((size_t)b * R + t) * HV + h) * D + i];
-            kv_in[q] = tab[idx];
+            kv_in[q] = kt[idx];
         }
-        const float a_in = p.coef[((size_t)b * HV + h) * coef_count(R) + min(tid, n - 1)];
+        const float a_in = p.as[((size_t)b * HV + h) * R + min(tid, n - 1)];
         float4 s[JPER];
 #pragma unroll
         for (int jj = 0; jj < JPER; ++jj)
@@ -975,8 +1010,7 @@ template <int D, int NR, typename T, bool SNAP>
 hipError_t launch_verify(const VerifyParams<T> &vp, const VerifyLaunch &l)
 {
     if (D == 128) {
-        hipLaunchKernelGGL((gdn_prep_kernel<NR, T>), dim3(l.batch * l.HK), dim3(kThreads), 0, l.st, vp);
-        hipLaunchKernelGGL((gdn_stream_d128_kernel<NR, T, SNAP>), dim3(l.batch * l.HV), dim3(kThreads),
+        hipLaunchKernelGGL((gdn_verify_d128_kernel<NR, T, SNAP>), dim3(l.batch * l.HV), dim3(kThreads),
                            0, l.st, vp);
     } else {
         hipLaunchKernelGGL((gdn_verify_kernel<D, NR, T, SNAP>), dim3(l.batch * l.HV), dim3(kThreads),
@@ -1032,8 +1066,8 @@ hipError_t verify_typed(const Checked &c, const gdn_layer_desc *d, const gdn_poo
     vp.err = err;
     vp.xs = reinterpret_cast<T *>(base + L.xs);
     vp.es = reinterpret_cast<float *>(base + L.es);
-    vp.tab = reinterpret_cast<float *>(base + L.tab);
-    vp.coef = reinterpret_cast<float *>(base + L.coef);
+    vp.ks = reinterpret_cast<float *>(base + L.ks);
+    vp.as = reinterpret_cast<float *>(base + L.as);
     vp.snap = snapshot ? reinterpret_cast<float *>(base + L.snap) : nullptr;
     vp.HK = c.HK;
     vp.HV = c.HV;
@@ -1078,8 +1112,8 @@ hipError_t commit_typed(const Checked &c, const gdn_pool *pool, const int32_t *s
     cp.err = err;
     cp.xs = reinterpret_cast<const T *>(base + L.xs);
     cp.es = reinterpret_cast<const float *>(base + L.es);
-    cp.tab = reinterpret_cast<const float *>(base + L.tab);
-    cp.coef = reinterpret_cast<const float *>(base + L.coef);
+    cp.ks = reinterpret_cast<const float *>(base + L.ks);
+    cp.as = reinterpret_cast<const float *>(base + L.as);
     cp.snap = snapshot ? reinterpret_cast<const float *>(base + L.snap) : nullptr;
     cp.HK = c.HK;
     cp.HV = c.HV;

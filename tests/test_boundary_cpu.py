@@ -52,10 +52,9 @@ def test_scratch_bytes(lib, name, mode):
     w = wl.WORKLOADS[name]
     s = w.shape
     B, R, HK, HV, D, C = w.batch, w.rows, s.num_k_heads, s.num_v_heads, s.d_k, s.conv_channels
-    # raw row inputs, e_t per value head, the [k | q] table per key head, the
-    # scalar coefficients (3R + 2R^2) per value head
-    want = (_align(B * R * C * s.elem_bytes) + _align(B * R * HV * D * 4) + _align(B * HK * 2 * R * D * 4)
-            + _align(B * HV * (3 * R + 2 * R * R) * 4))
+    # raw row inputs, e_t per value head, k_t per key head, a_t per value head
+    want = (_align(B * R * C * s.elem_bytes) + _align(B * R * HV * D * 4) + _align(B * HK * R * D * 4)
+            + _align(B * HV * R * 4))
     if mode == "snapshot":
         want += _align(B * R * HV * D * D * 4)
     assert bd.gdn_spec_scratch_bytes(bd.layer_desc(s), B, R, mode) == want
