@@ -548,16 +548,76 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_kernel(const VerifyParams
 // The 2R products S_0 k_t, S_0 q_t are a dense (128 x 128) x (128 x 2R)
 // contraction, run with v_mfma_f32_16x16x4_f32 (fp32 in, fp32 accumulate).
 // Wave w owns state rows 32w..32w+31 as two 16-row tiles: lane l (kg = l/16,
-// m = l%16) loads rows 32w+2m and 32w+2m+1 at key index j = 4*ks + kg for each
-// of the 32 K-steps ks, which is exactly the A operand of both tiles
-// (A[m][k] = S[row][4ks+k]). The first 16 columns of M = [K | Q] go through one
-// 16-wide B tile; with R = 9 the last two (q_7, q_8) are done on the VALU from
-// the same registers. A third tile has the keys themselves as rows
-// (A[m][k] = k_m[4ks+k], the same LDS value as the B operand of column m): it
-// yields K^T M, i.e. every Gram entry k_u.k_t and k_u.q_t, with each wave
-// covering 8 of the 32 K-steps.
+// m = l%16) holds rows 32w+2m and 32w+2m+1 at key index j = 4*ks + kg for a
+// K-step ks, which is exactly the A operand of both tiles
+// (A[m][k] = S[row][4ks+k]). The state streams through in four chunks of 8
+// K-steps, two chunks in flight, so a workgroup holds 32 registers of state
+// and five to six workgroups share a compute unit. The first 16 columns of
+// M = [K | Q] go through one 16-wide B tile; with R = 9 the last two
+// (q_7, q_8) are done on the VALU from the same registers. A third tile has the
+// keys themselves as rows (A[m][k] = k_m[4ks+k], the LDS value that is also
+// the B operand of column m): it yields K^T M, i.e. every Gram entry k_u.k_t
+// and k_u.q_t; wave w covers the K-steps of chunk w.
+//
+// The per-row recurrence for e_t is a unit lower-triangular system shared by
+// every state row, e = L^{-1} diag(b) (v - g S_0 k), L = I + diag(b) A with
+// A[t][u] = g(t,u) k_u.k_t (u < t). L^{-1} diag(b) is formed once per
+// workgroup, so each row's e_t and o_t are two small matrix-vector products.
+
+template <int CK, int NR, int NVL, int MS>
+__device__ __forceinline__ void mfma_chunk(const float2 (&sc)[CK], int c, int kg, int m, const float *Mt,
+                                           f32x4 &acc0, f32x4 &acc1, float (&pv)[2][2])
+{
+#pragma unroll
+    for (int k = 0; k < CK; ++k) {
+        const int j = 4 * (c * CK + k) + kg;
+        const float bm = Mt[j * MS + m];
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(sc[k].x, bm, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(sc[k].y, bm, acc1, 0, 0, 0);
+        if (NVL) {
+            const float2 mv = *reinterpret_cast<const float2 *>(&Mt[j * MS + 16]);
+            pv[0][0] = __builtin_fmaf(sc[k].x, mv.x, pv[0][0]);
+            pv[0][1] = __builtin_fmaf(sc[k].x, mv.y, pv[0][1]);
+            pv[1][0] = __builtin_fmaf(sc[k].y, mv.x, pv[1][0]);
+            pv[1][1] = __builtin_fmaf(sc[k].y, mv.y, pv[1][1]);
+        }
+    }
+}
+
+// This wave's share (K-steps 8w..8w+7) of K^T M: a 16-row tile whose row m
+// is key k_m (rows m >= R are zero), against the same B operand as the state.
+template <int CK, int NR, int NVL, int MS>
+__device__ __forceinline__ void gram_share(int wave, int kg, int m, const float *Mt, f32x4 &accg,
+                                           float (&gv)[2])
+{
+#pragma unroll
+    for (int k = 0; k < CK; ++k) {
+        const int j = 4 * (wave * CK + k) + kg;
+        const float bm = Mt[j * MS + m];
+        const float ak = m < NR ? bm : 0.0f;
+        accg = __builtin_amdgcn_mfma_f32_16x16x4f32(ak, bm, accg, 0, 0, 0);
+        if (NVL) {
+            const float2 mv = *reinterpret_cast<const float2 *>(&Mt[j * MS + 16]);
+            gv[0] = __builtin_fmaf(ak, mv.x, gv[0]);
+            gv[1] = __builtin_fmaf(ak, mv.y, gv[1]);
+        }
+    }
+}
+
+// Issue the loads of chunk c exactly here: the empty asm statements keep the
+// compiler from hoisting them (and the registers they fill) any earlier.
+template <int CK>
+__device__ __forceinline__ void load_chunk(float2 (&sc)[CK], __amdgpu_buffer_rsrc_t rs, uint32_t soff, int c)
+{
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int k = 0; k < CK; ++k)
+        sc[k] = buf_load_f2(rs, soff, (uint32_t)(c * CK + k) * 4 * 128 * 4);
+    asm volatile("" ::: "memory");
+}
+
 template <int NR, typename T, bool SNAP>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NR == 9 ? 3 : 4))) void gdn_verify_d128_kernel(const VerifyParams<T> p)
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5))) void gdn_verify_d128_kernel(const VerifyParams<T> p)
 {
     constexpr int D = 128;
     constexpr int NC = 2 * NR;
@@ -566,19 +626,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NR == 
     static_assert(NVL == 0 || NVL == 2, "unsupported row count");
     constexpr int MS = NVL ? 20 : 16;        // column-table row stride
     constexpr int PS = NC + 1;               // product-table row stride (odd)
-    constexpr int KS = D / 4;                // K-steps of 4 key indices
-    constexpr int KSW = KS / 4;              // K-steps of the Gram tile per wave
-    constexpr int NCF = coef_count(NR);
+    constexpr int CK = 8;                    // K-steps per chunk
+    constexpr int NCHUNK = D / 4 / CK;       // 4 chunks, one per wave for the key tile
 
     __shared__ __align__(16) float Mt[D * MS];   // [j][c]: k_c[j] (c < NR), q_{c-NR}[j]; 0 beyond NC
     __shared__ __align__(16) float P[D * PS];    // [i][c]: (S_0 M)[i][c]; later e_t in snapshot mode
     __shared__ float gp[4 * NR * NC];            // [w][u][c]: wave w's share of (K^T M)[u][c]
     __shared__ float inv[NC];
-    __shared__ float cf[NCF];
-    __shared__ float al[NR], be[NR];
-    __shared__ T xr[NR * kThreads];              // raw q/k inputs of each thread's channel, by row
-    __shared__ T xv[NR * D];                     // raw value inputs, by row
-    __shared__ float vb[NR * D];                 // v_t[i] after the conv
+    __shared__ float al[NR], be[NR], gam[NR];
+    __shared__ float Am[NR * NR];                // b_t g(t,u) k_u.k_t, u < t
+    __shared__ float Lb[NR * NR];                // L^{-1} diag(b)
+    __shared__ float Bm[NR * NR];                // g(t,u) k_u.q_t, u <= t
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -597,10 +655,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NR == 
         return;
     }
 
-    // Small loads first, branch-free, so they share a block with the state
-    // stream and retire ahead of it. Threads < 128 take q channel `tid` and
-    // value channel `tid`; threads 128.. take k channel tid-128 (and load the
-    // value channel again, unused).
+    // Small loads first, branch-free, so they retire ahead of the state
+    // stream. Threads < 128 take q channel `tid` and value channel `tid`;
+    // threads 128.. take k channel tid-128 (and load the value channel again, unused).
     const size_t gi = ((size_t)b * NR + min(tid, NR - 1)) * HV + h;
     const T ga = p.alpha[gi], gb = p.beta[gi];
     const int jc = tid & (D - 1);
@@ -610,50 +667,45 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NR == 
     const ChanIn<NR, T> cinA = load_channel<NR>(p, slot, b, chA);
     const ChanIn<NR, T> cinV = load_channel<NR>(p, slot, b, chV);
 
-    // The state slice in two halves: the first goes out with the small loads,
-    // the second once the convs have freed their input registers.
     const int kg = lane >> 4;
     const int m = lane & 15;
     const int row0 = 32 * wave + 2 * m;            // this lane's two state rows: row0, row0 + 1
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.ssm + ((size_t)slot * HV + h) * D * D, D * D * 4);
     const uint32_t soff = (kg * D + row0) * 4;      // lane byte offset within each K-step block
-    float2 s[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS / 2; ++ks)
-        s[ks] = buf_load_f2(rs, soff, ks * 4 * D * 4);
+    float2 c0[CK], c1[CK];
+    load_chunk(c0, rs, soff, 0);
     __builtin_amdgcn_sched_barrier(0);
 
     if (tid < NR) {
         al[tid] = to_f32(ga);
         be[tid] = to_f32(gb);
     }
+    float v[NR];
     {
         float y[NR];
         conv_rows(cinA, p.act, y);
 #pragma unroll
-        for (int t = 0; t < NR; ++t) {
+        for (int t = 0; t < NR; ++t)
             Mt[jc * MS + (isq ? NR + t : t)] = y[t];
-            xr[t * kThreads + tid] = cinA.x[t];
-        }
         if (isq) {
 #pragma unroll
             for (int c = NC; c < MS; ++c)
                 Mt[jc * MS + c] = 0.0f;
-#pragma unroll
-            for (int t = 0; t < NR; ++t)
-                xv[t * D + jc] = cinV.x[t];
         }
-        conv_rows(cinV, p.act, y);
-        if (isq) {
+        conv_rows(cinV, p.act, v);
+    }
+    // raw row inputs for the commit's conv history; one value head per key
+    // head stores the key head's q/k channels
+    const bool owner = (h % G) == 0;
 #pragma unroll
-            for (int t = 0; t < NR; ++t)
-                vb[t * D + jc] = y[t];
-        }
+    for (int t = 0; t < NR; ++t) {
+        if (owner)
+            p.xs[((size_t)b * NR + t) * p.C + chA] = cinA.x[t];
+        if (isq)
+            p.xs[((size_t)b * NR + t) * p.C + chV] = cinV.x[t];
     }
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int ks = KS / 2; ks < KS; ++ks)
-        s[ks] = buf_load_f2(rs, soff, ks * 4 * D * 4);
+    load_chunk(c1, rs, soff, 1);
     __builtin_amdgcn_sched_barrier(0);
     lds_barrier();
 
@@ -670,53 +722,58 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NR == 
         Mt[j * MS + c] *= inv[c];
     }
     lds_barrier();
+    if (owner) {
+        float *ks = p.ks + ((size_t)b * HK + kh) * NR * D;
+        for (int idx = tid; idx < NR * D; idx += kThreads)
+            ks[idx] = Mt[(idx % D) * MS + idx / D];
+    }
+    if (tid < NR)
+        p.as[((size_t)b * HV + h) * NR + tid] = al[tid];
 
-    // S_0 M (two state tiles) and K^T M (one key tile, this wave's K-steps)
+    // K^T M, this wave's share: only LDS operands, so it runs while the state streams in
+    {
+        f32x4 accg = {0.0f, 0.0f, 0.0f, 0.0f};
+        float gv[2] = {0.0f, 0.0f};
+        gram_share<CK, NR, NVL, MS>(wave, kg, m, Mt, accg, gv);
+        if (m < NMF) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (4 * kg + q < NR)
+                    gp[(wave * NR + 4 * kg + q) * NC + m] = accg[q];
+        }
+        if (NVL) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                float x = gv[c];
+                x += __shfl_xor(x, 16, 64);
+                x += __shfl_xor(x, 32, 64);
+                gv[c] = x;
+            }
+            if (kg == 0 && m < NR) {
+                gp[(wave * NR + m) * NC + NMF] = gv[0];
+                gp[(wave * NR + m) * NC + NMF + 1] = gv[1];
+            }
+        }
+    }
+
+    // S_0 M (two state tiles), chunk by chunk
     f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f};
     f32x4 acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
-    f32x4 accg = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        const int j = 4 * ks + kg;
-        const float bm = Mt[j * MS + m];
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(s[ks].x, bm, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(s[ks].y, bm, acc1, 0, 0, 0);
-        if (ks / KSW == wave) {
-            const float ak = m < NR ? bm : 0.0f;   // row m of the key tile: k_m[j]
-            accg = __builtin_amdgcn_mfma_f32_16x16x4f32(ak, bm, accg, 0, 0, 0);
-        }
-        if (ks % 4 == 3)
-            __builtin_amdgcn_sched_barrier(0);  // bound the operand lookahead (register pressure)
-    }
-    // the VALU columns in a second pass over the same registers
     float pv[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
-    float gv[2] = {0.0f, 0.0f};
-    if (NVL) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int j = 4 * ks + kg;
-            const float2 mv = *reinterpret_cast<const float2 *>(&Mt[j * MS + 16]);
-            pv[0][0] = __builtin_fmaf(s[ks].x, mv.x, pv[0][0]);
-            pv[0][1] = __builtin_fmaf(s[ks].x, mv.y, pv[0][1]);
-            pv[1][0] = __builtin_fmaf(s[ks].y, mv.x, pv[1][0]);
-            pv[1][1] = __builtin_fmaf(s[ks].y, mv.y, pv[1][1]);
-            if (ks / KSW == wave && m < NR) {
-                const float ak = Mt[j * MS + m];
-                gv[0] = __builtin_fmaf(ak, mv.x, gv[0]);
-                gv[1] = __builtin_fmaf(ak, mv.y, gv[1]);
-            }
-            if (ks % 4 == 3)
-                __builtin_amdgcn_sched_barrier(0);
-        }
-    }
+    mfma_chunk<CK, NR, NVL, MS>(c0, 0, kg, m, Mt, acc0, acc1, pv);
+    load_chunk(c0, rs, soff, 2);
+    mfma_chunk<CK, NR, NVL, MS>(c1, 1, kg, m, Mt, acc0, acc1, pv);
+    load_chunk(c1, rs, soff, 3);
+    mfma_chunk<CK, NR, NVL, MS>(c0, 2, kg, m, Mt, acc0, acc1, pv);
+    mfma_chunk<CK, NR, NVL, MS>(c1, 3, kg, m, Mt, acc0, acc1, pv);
+    static_assert(NCHUNK == 4, "chunk schedule written for four chunks");
+
     // tile register q of lane (kg, m): row 4kg + q of the tile, column m
     if (m < NMF) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             P[(32 * wave + 2 * (4 * kg + q)) * PS + m] = acc0[q];
             P[(32 * wave + 2 * (4 * kg + q) + 1) * PS + m] = acc1[q];
-            if (4 * kg + q < NR)
-                gp[(wave * NR + 4 * kg + q) * NC + m] = accg[q];
         }
     }
     if (NVL) {
@@ -730,42 +787,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NR == 
                 x += __shfl_xor(x, 32, 64);
                 pv[r][c] = x;
             }
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            float x = gv[c];
-            x += __shfl_xor(x, 16, 64);
-            x += __shfl_xor(x, 32, 64);
-            gv[c] = x;
-        }
         if (kg == 0) {
 #pragma unroll
             for (int r = 0; r < 2; ++r)
 #pragma unroll
                 for (int c = 0; c < 2; ++c)
                     P[(row0 + r) * PS + NMF + c] = pv[r][c];
-            if (m < NR) {
-                gp[(wave * NR + m) * NC + NMF] = gv[0];
-                gp[(wave * NR + m) * NC + NMF + 1] = gv[1];
-            }
         }
     }
-
-    // scratch for the commit; stores start only now that the state has landed
-    const bool owner = (h % G) == 0;  // one value head per key head stores the q/k inputs and k_t
-#pragma unroll
-    for (int t = 0; t < NR; ++t) {
-        if (owner)
-            p.xs[((size_t)b * NR + t) * p.C + chA] = xr[t * kThreads + tid];
-        if (isq)
-            p.xs[((size_t)b * NR + t) * p.C + chV] = xv[t * D + jc];
-    }
-    if (owner) {
-        float *ks = p.ks + ((size_t)b * HK + kh) * NR * D;
-        for (int idx = tid; idx < NR * D; idx += kThreads)
-            ks[idx] = Mt[(idx % D) * MS + idx / D];
-    }
-    if (tid < NR)
-        p.as[((size_t)b * HV + h) * NR + tid] = al[tid];
     lds_barrier();
 
     // scalar coefficients; (K^T M)[u][c] is the sum of the four waves' shares
@@ -779,30 +808,63 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NR == 
             float gtu = 1.0f;
             for (int q = u + 1; q <= t; ++q)
                 gtu *= al[q];
-            cf[3 * NR + idx] = (u < t) ? gtu * gram(u, t) : 0.0f;
-            cf[3 * NR + NR * NR + idx] = (u <= t) ? gtu * gram(u, NR + t) : 0.0f;
+            Am[idx] = (u < t) ? be[t] * (gtu * gram(u, t)) : 0.0f;
+            Bm[idx] = (u <= t) ? gtu * gram(u, NR + t) : 0.0f;
         } else {
             const int t = idx - NR * NR;
             float gt = 1.0f;
             for (int q = 0; q <= t; ++q)
                 gt *= al[q];
-            cf[t] = al[t];
-            cf[NR + t] = gt;
-            cf[2 * NR + t] = be[t];
+            gam[t] = gt;
         }
     }
     lds_barrier();
-
-    // per state row i: correction vectors and outputs
-    if (tid < D) {
-        float pk[NR], pq[NR], v[NR], e[NR];
+    // column j of L^{-1} diag(b) by forward substitution (thread j)
+    if (tid < NR) {
+        const int j = tid;
+        float a[NR * NR];
 #pragma unroll
-        for (int c = 0; c < NR; ++c) {
-            pk[c] = P[tid * PS + c];
-            pq[c] = P[tid * PS + NR + c];
-            v[c] = vb[c * D + tid];
+        for (int q = 0; q < NR * NR; ++q)
+            a[q] = Am[q];
+        float x[NR];
+#pragma unroll
+        for (int t = 0; t < NR; ++t) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int u = 0; u < t; ++u)
+                acc = __builtin_fmaf(a[t * NR + u], x[u], acc);
+            x[t] = t < j ? 0.0f : (t == j ? be[j] : -acc);
         }
-        solve_row<NR>(p, cf, pk, pq, v, e, b, h, tid, D);
+#pragma unroll
+        for (int t = 0; t < NR; ++t)
+            Lb[t * NR + j] = x[t];
+    }
+    lds_barrier();
+
+    // per state row i: e = L^{-1} diag(b) (v - g S_0 k), o = scale (g S_0 q + B e)
+    if (tid < D) {
+        float r[NR], e[NR];
+#pragma unroll
+        for (int u = 0; u < NR; ++u)
+            r[u] = __builtin_fmaf(-gam[u], P[tid * PS + u], v[u]);
+#pragma unroll
+        for (int t = 0; t < NR; ++t) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int u = 0; u <= t; ++u)
+                acc = __builtin_fmaf(Lb[t * NR + u], r[u], acc);
+            e[t] = acc;
+        }
+#pragma unroll
+        for (int t = 0; t < NR; ++t) {
+            float acc = gam[t] * P[tid * PS + NR + t];
+#pragma unroll
+            for (int u = 0; u <= t; ++u)
+                acc = __builtin_fmaf(Bm[t * NR + u], e[u], acc);
+            const size_t oi = (((size_t)b * NR + t) * HV + h) * D + tid;
+            p.out[oi] = from_f32<T>(p.scale * acc);
+            p.es[oi] = e[t];
+        }
         if (SNAP) {
             // row tid of P is read only by this thread: reuse it for e_t
 #pragma unroll
@@ -813,19 +875,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NR == 
 
     if (SNAP) {
         lds_barrier();
-        // S_t for every row, by the same update the replay commit applies
+        // S_t for every row, by the same update the replay commit applies,
+        // chunk by chunk from a second read of S_0
 #pragma unroll 1
-        for (int t = 0; t < NR; ++t) {
-            const float a = al[t];
-            const float e0 = P[row0 * PS + t], e1 = P[(row0 + 1) * PS + t];
-            float *dst = p.snap + (((size_t)b * NR + t) * HV + h) * D * D;
+        for (int c = 0; c < NCHUNK; ++c) {
+            load_chunk(c0, rs, soff, c);
+#pragma unroll 1
+            for (int t = 0; t < NR; ++t) {
+                const float a = al[t];
+                const float e0 = P[row0 * PS + t], e1 = P[(row0 + 1) * PS + t];
+                float *dst = p.snap + (((size_t)b * NR + t) * HV + h) * D * D;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int j = 4 * ks + kg;
-                const float k = Mt[j * MS + t];
-                s[ks].x = row_update(s[ks].x, a, e0, k);
-                s[ks].y = row_update(s[ks].y, a, e1, k);
-                *reinterpret_cast<float2 *>(dst + (size_t)j * D + row0) = s[ks];
+                for (int k = 0; k < CK; ++k) {
+                    const int j = 4 * (c * CK + k) + kg;
+                    const float kk = Mt[j * MS + t];
+                    c0[k].x = row_update(c0[k].x, a, e0, kk);
+                    c0[k].y = row_update(c0[k].y, a, e1, kk);
+                    *reinterpret_cast<float2 *>(dst + (size_t)j * D + row0) = c0[k];
+                }
             }
         }
     }
