@@ -89,9 +89,31 @@ template <> __device__ __forceinline__ bf16_t buf_load<bf16_t>(__amdgpu_buffer_r
     return bf16_t{__builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0)};
 }
 
-__device__ __forceinline__ float2 buf_load_f2(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+// State and snapshot traffic: every kernel streams it exactly once. The
+// nontemporal hint (cache-policy bit nt) keeps it from displacing the small
+// per-row inputs and the stash in the caches, and keeps dirty state lines from
+// piling up in the memory-side cache for the next kernel to write back.
+constexpr int kStreamPolicy = 2;
+
+__device__ __forceinline__ f32x4 buf_stream_load_f4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
 {
-    return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0));
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, kStreamPolicy));
+}
+
+__device__ __forceinline__ float4 stream_load(const float *ptr)
+{
+    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(ptr));
+    return float4{v[0], v[1], v[2], v[3]};
+}
+
+__device__ __forceinline__ void stream_store(float *ptr, f32x4 v)
+{
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(ptr));
+}
+
+__device__ __forceinline__ void stream_store(float *ptr, float4 v)
+{
+    stream_store(ptr, f32x4{v.x, v.y, v.z, v.w});
 }
 
 // Barrier that orders LDS only: global loads already in flight (the state
@@ -383,7 +405,7 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_kernel(const VerifyParams
     float4 s[JPER];
 #pragma unroll
     for (int jj = 0; jj < JPER; ++jj)
-        s[jj] = *reinterpret_cast<const float4 *>(S0 + (size_t)(jj * GJ + g) * D + 4 * rq);
+        s[jj] = stream_load(S0 + (size_t)(jj * GJ + g) * D + 4 * rq);
     __builtin_amdgcn_sched_barrier(0);
 
     if (tid < NR) {
@@ -537,7 +559,7 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_kernel(const VerifyParams
                 s[jj].y = row_update(s[jj].y, a, ev.y, k);
                 s[jj].z = row_update(s[jj].z, a, ev.z, k);
                 s[jj].w = row_update(s[jj].w, a, ev.w, k);
-                *reinterpret_cast<float4 *>(dst + (size_t)j * D + 4 * rq) = s[jj];
+                stream_store(dst + (size_t)j * D + 4 * rq, s[jj]);
             }
         }
     }
@@ -547,59 +569,62 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_kernel(const VerifyParams
 //
 // The 2R products S_0 k_t, S_0 q_t are a dense (128 x 128) x (128 x 2R)
 // contraction, run with v_mfma_f32_16x16x4_f32 (fp32 in, fp32 accumulate).
-// Wave w owns state rows 32w..32w+31 as two 16-row tiles: lane l (kg = l/16,
-// m = l%16) holds rows 32w+2m and 32w+2m+1 at key index j = 4*ks + kg for a
-// K-step ks, which is exactly the A operand of both tiles
-// (A[m][k] = S[row][4ks+k]). The state streams through in four chunks of 8
-// K-steps, two chunks in flight, so a workgroup holds 32 registers of state
-// and five to six workgroups share a compute unit. The first 16 columns of
-// M = [K | Q] go through one 16-wide B tile; with R = 9 the last two
-// (q_7, q_8) are done on the VALU from the same registers. A third tile has the
-// keys themselves as rows (A[m][k] = k_m[4ks+k], the LDS value that is also
-// the B operand of column m): it yields K^T M, i.e. every Gram entry k_u.k_t
-// and k_u.q_t; wave w covers the K-steps of chunk w.
+//
+// One workgroup per (request, pair of value heads on one key head): the conv
+// of the key head's q/k channels is done once for both heads, and with 4
+// workgroups per compute unit a 64-request batch is resident in one round.
+// Thread t convolves q/k channel t and value channel t of the pair; after
+// the column table M (the raw conv outputs [k_0..k_{R-1} | q_0..q_{R-1}]) is
+// in LDS there is no further workgroup barrier: wave w owns state rows
+// 64(w&1)..64(w&1)+63 of value head h0 + (w>>1), which are exactly the rows
+// whose value channels its own lanes convolved, and it finishes them alone.
+//
+// Per wave: lane l (kg = l/16, m = l%16) loads rows 4m..4m+3 of the block at
+// key index j = 4s + kg of K-step s as one 16-byte load, which is the A
+// operand of four 16-row tiles (tile v holds rows 4m + v: A[m][k] =
+// S[4m+v][4s+k]). The state streams in chunks of 4 K-steps, two chunks in
+// flight. The first 16 columns of M go through one 16-wide B tile; with
+// R = 9 the last two (q_7, q_8) are done on the VALU from the same registers.
+// Between chunks, the wave forms M^T M with a tile whose A operand is the B
+// value itself (A[m][k] = M[4s+k][m]), giving the column norms (diagonal) and
+// every Gram entry k_u.k_t, k_u.q_t; the L2 normalisation is then a column
+// scaling applied to the Gram entries and to S_0 M. Still between chunks it
+// forms its head's scalar coefficients and L^{-1} diag(b) (below), so after
+// the last chunk only the per-row solve remains.
 //
 // The per-row recurrence for e_t is a unit lower-triangular system shared by
 // every state row, e = L^{-1} diag(b) (v - g S_0 k), L = I + diag(b) A with
-// A[t][u] = g(t,u) k_u.k_t (u < t). L^{-1} diag(b) is formed once per
-// workgroup, so each row's e_t and o_t are two small matrix-vector products.
+// A[t][u] = g(t,u) k_u.k_t (u < t), so each row's e_t and o_t are two small
+// matrix-vector products.
 
-template <int CK, int NR, int NVL, int MS>
-__device__ __forceinline__ void mfma_chunk(const float2 (&sc)[CK], int c, int kg, int m, const float *Mt,
-                                           f32x4 &acc0, f32x4 &acc1, float (&pv)[2][2])
+// Orders this wave's LDS writes before its later LDS reads (one wave: no
+// workgroup barrier).
+__device__ __forceinline__ void wave_lds_sync()
 {
-#pragma unroll
-    for (int k = 0; k < CK; ++k) {
-        const int j = 4 * (c * CK + k) + kg;
-        const float bm = Mt[j * MS + m];
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(sc[k].x, bm, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(sc[k].y, bm, acc1, 0, 0, 0);
-        if (NVL) {
-            const float2 mv = *reinterpret_cast<const float2 *>(&Mt[j * MS + 16]);
-            pv[0][0] = __builtin_fmaf(sc[k].x, mv.x, pv[0][0]);
-            pv[0][1] = __builtin_fmaf(sc[k].x, mv.y, pv[0][1]);
-            pv[1][0] = __builtin_fmaf(sc[k].y, mv.x, pv[1][0]);
-            pv[1][1] = __builtin_fmaf(sc[k].y, mv.y, pv[1][1]);
-        }
-    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 }
 
-// This wave's share (K-steps 8w..8w+7) of K^T M: a 16-row tile whose row m
-// is key k_m (rows m >= R are zero), against the same B operand as the state.
-template <int CK, int NR, int NVL, int MS>
+// This wave's share (K-steps 8w..8w+7) of M^T M: tile rows are columns 0..15
+// of M; the VALU columns 16, 17 (NVL = 2) give gv (their products with the
+// tile rows) and dv (their own squared norms), as per-lane partial sums over
+// the lane's kg.
+template <int NVL, int MS>
 __device__ __forceinline__ void gram_share(int wave, int kg, int m, const float *Mt, f32x4 &accg,
-                                           float (&gv)[2])
+                                           float (&gv)[2], float (&dv)[2])
 {
 #pragma unroll
-    for (int k = 0; k < CK; ++k) {
-        const int j = 4 * (wave * CK + k) + kg;
+    for (int k = 0; k < 8; ++k) {
+        const int j = 4 * (8 * wave + k) + kg;
         const float bm = Mt[j * MS + m];
-        const float ak = m < NR ? bm : 0.0f;
-        accg = __builtin_amdgcn_mfma_f32_16x16x4f32(ak, bm, accg, 0, 0, 0);
+        accg = __builtin_amdgcn_mfma_f32_16x16x4f32(bm, bm, accg, 0, 0, 0);
         if (NVL) {
             const float2 mv = *reinterpret_cast<const float2 *>(&Mt[j * MS + 16]);
-            gv[0] = __builtin_fmaf(ak, mv.x, gv[0]);
-            gv[1] = __builtin_fmaf(ak, mv.y, gv[1]);
+            gv[0] = __builtin_fmaf(bm, mv.x, gv[0]);
+            gv[1] = __builtin_fmaf(bm, mv.y, gv[1]);
+            dv[0] = __builtin_fmaf(mv.x, mv.x, dv[0]);
+            dv[1] = __builtin_fmaf(mv.y, mv.y, dv[1]);
         }
     }
 }
@@ -607,17 +632,41 @@ __device__ __forceinline__ void gram_share(int wave, int kg, int m, const float 
 // Issue the loads of chunk c exactly here: the empty asm statements keep the
 // compiler from hoisting them (and the registers they fill) any earlier.
 template <int CK>
-__device__ __forceinline__ void load_chunk(float2 (&sc)[CK], __amdgpu_buffer_rsrc_t rs, uint32_t soff, int c)
+__device__ __forceinline__ void load_chunk(f32x4 (&sc)[CK], __amdgpu_buffer_rsrc_t rs, uint32_t soff, int c)
 {
     asm volatile("" ::: "memory");
 #pragma unroll
     for (int k = 0; k < CK; ++k)
-        sc[k] = buf_load_f2(rs, soff, (uint32_t)(c * CK + k) * 4 * 128 * 4);
+        sc[k] = buf_stream_load_f4(rs, soff, (uint32_t)(c * CK + k) * 4 * 128 * 4);
     asm volatile("" ::: "memory");
 }
 
+// Chunk c of the state against the column table: four tiles on the matrix
+// cores, and the two VALU columns (NVL = 2) as per-lane partial sums.
+template <int CK, int NVL, int MS>
+__device__ __forceinline__ void mfma_chunk(const f32x4 (&sc)[CK], int c, int kg, int m, const float *Mt,
+                                           f32x4 (&acc)[4], float (&pv)[4][2])
+{
+#pragma unroll
+    for (int k = 0; k < CK; ++k) {
+        const int j = 4 * (c * CK + k) + kg;
+        const float bm = Mt[j * MS + m];
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            acc[v] = __builtin_amdgcn_mfma_f32_16x16x4f32(sc[k][v], bm, acc[v], 0, 0, 0);
+        if (NVL) {
+            const float2 mv = *reinterpret_cast<const float2 *>(&Mt[j * MS + 16]);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                pv[v][0] = __builtin_fmaf(sc[k][v], mv.x, pv[v][0]);
+                pv[v][1] = __builtin_fmaf(sc[k][v], mv.y, pv[v][1]);
+            }
+        }
+    }
+}
+
 template <int NR, typename T, bool SNAP>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5))) void gdn_verify_d128_kernel(const VerifyParams<T> p)
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void gdn_verify_d128_kernel(const VerifyParams<T> p)
 {
     constexpr int D = 128;
     constexpr int NC = 2 * NR;
@@ -626,61 +675,65 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5))) v
     static_assert(NVL == 0 || NVL == 2, "unsupported row count");
     constexpr int MS = NVL ? 20 : 16;        // column-table row stride
     constexpr int PS = NC + 1;               // product-table row stride (odd)
-    constexpr int CK = 8;                    // K-steps per chunk
-    constexpr int NCHUNK = D / 4 / CK;       // 4 chunks, one per wave for the key tile
+    constexpr int CK = 4;                    // K-steps per chunk
+    constexpr int NCHUNK = D / 4 / CK;       // 8 chunks per wave
+    constexpr int CW = 3 * NR * NR + NR + NC;  // per-wave coefficients: Am, Lb, Bm, gam, inv
 
-    __shared__ __align__(16) float Mt[D * MS];   // [j][c]: k_c[j] (c < NR), q_{c-NR}[j]; 0 beyond NC
-    __shared__ __align__(16) float P[D * PS];    // [i][c]: (S_0 M)[i][c]; later e_t in snapshot mode
-    __shared__ float gp[4 * NR * NC];            // [w][u][c]: wave w's share of (K^T M)[u][c]
-    __shared__ float inv[NC];
-    __shared__ float al[NR], be[NR], gam[NR];
-    __shared__ float Am[NR * NR];                // b_t g(t,u) k_u.k_t, u < t
-    __shared__ float Lb[NR * NR];                // L^{-1} diag(b)
-    __shared__ float Bm[NR * NR];                // g(t,u) k_u.q_t, u <= t
+    __shared__ __align__(16) float Mt[D * MS];      // [j][c]: raw k_c[j] (c < NR), q_{c-NR}[j]; 0 beyond NC
+    __shared__ __align__(16) float P[4 * 64 * PS];  // per wave [i][c]: Gram table, then (S_0 M^)[i][c], then e_t
+    __shared__ float cf[4 * CW];
+    __shared__ float gp[4][NR * NC + NR];           // wave w's share: (M^T M)[u][c], u < NR; then |q_t|^2
+    __shared__ float al[2][NR], be[2][NR];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int HV = p.HV, HK = p.HK;
     const int G = HV / HK;
-    const int b = blockIdx.x / HV;
-    const int h = blockIdx.x % HV;
-    const int kh = h / G;
+    const int npair = HV / 2;
+    const int b = blockIdx.x / npair;
+    const int h0 = 2 * (blockIdx.x % npair);
+    const int kh = h0 / G;
     const int slot = p.slot_ids[b];
 
     if (slot < 0 || slot >= p.P) {
         if (slot != -1 && tid == 0 && p.err)
             atomicOr(p.err, 1);
-        zero_outputs(p, b, h, NR, D);
+        zero_outputs(p, b, h0, NR, D);
+        zero_outputs(p, b, h0 + 1, NR, D);
         return;
     }
 
     // Small loads first, branch-free, so they retire ahead of the state
-    // stream. Threads < 128 take q channel `tid` and value channel `tid`;
-    // threads 128.. take k channel tid-128 (and load the value channel again, unused).
-    const size_t gi = ((size_t)b * NR + min(tid, NR - 1)) * HV + h;
+    // stream. Threads < 128 take q channel `tid`, threads 128.. k channel
+    // tid-128; thread tid takes value channel tid of the pair (head h0 + tid/128).
+    const int gidx = min(tid, 2 * NR - 1);
+    const int ghh = gidx / NR, gtt = gidx % NR;
+    const size_t gi = ((size_t)b * NR + gtt) * HV + h0 + ghh;
     const T ga = p.alpha[gi], gb = p.beta[gi];
     const int jc = tid & (D - 1);
     const bool isq = tid < D;
     const int chA = isq ? kh * D + jc : HK * D + kh * D + jc;
-    const int chV = 2 * HK * D + h * D + jc;
+    const int chV = 2 * HK * D + h0 * D + tid;
     const ChanIn<NR, T> cinA = load_channel<NR>(p, slot, b, chA);
     const ChanIn<NR, T> cinV = load_channel<NR>(p, slot, b, chV);
 
     const int kg = lane >> 4;
     const int m = lane & 15;
-    const int row0 = 32 * wave + 2 * m;            // this lane's two state rows: row0, row0 + 1
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.ssm + ((size_t)slot * HV + h) * D * D, D * D * 4);
-    const uint32_t soff = (kg * D + row0) * 4;      // lane byte offset within each K-step block
-    float2 c0[CK], c1[CK];
+    const int hh = wave >> 1;                        // this wave's head: h0 + hh
+    const int rb = 64 * (wave & 1);                  // and its 64-row block
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.ssm + ((size_t)slot * HV + h0 + hh) * D * D, D * D * 4);
+    const uint32_t soff = (kg * D + rb + 4 * m) * 4;  // lane byte offset within each K-step block
+    f32x4 c0[CK], c1[CK], c2[CK];
     load_chunk(c0, rs, soff, 0);
     __builtin_amdgcn_sched_barrier(0);
 
-    if (tid < NR) {
-        al[tid] = to_f32(ga);
-        be[tid] = to_f32(gb);
+    if (tid < 2 * NR) {
+        al[ghh][gtt] = to_f32(ga);
+        be[ghh][gtt] = to_f32(gb);
+        p.as[((size_t)b * HV + h0 + ghh) * NR + gtt] = to_f32(ga);
     }
-    float v[NR];
+    float v[NR];   // value channel tid = row rb + lane of head h0 + hh
     {
         float y[NR];
         conv_rows(cinA, p.act, y);
@@ -694,204 +747,238 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5))) v
         }
         conv_rows(cinV, p.act, v);
     }
-    // raw row inputs for the commit's conv history; one value head per key
-    // head stores the key head's q/k channels
-    const bool owner = (h % G) == 0;
+    // raw row inputs for the commit's conv history; with more than two value
+    // heads per key head the first pair stores the key head's q/k channels
+    const bool owner = (h0 % G) == 0;
 #pragma unroll
     for (int t = 0; t < NR; ++t) {
         if (owner)
             p.xs[((size_t)b * NR + t) * p.C + chA] = cinA.x[t];
-        if (isq)
-            p.xs[((size_t)b * NR + t) * p.C + chV] = cinV.x[t];
+        p.xs[((size_t)b * NR + t) * p.C + chV] = cinV.x[t];
     }
     __builtin_amdgcn_sched_barrier(0);
     load_chunk(c1, rs, soff, 1);
+    load_chunk(c2, rs, soff, 2);
     __builtin_amdgcn_sched_barrier(0);
-    lds_barrier();
+    lds_barrier();   // the column table and the gates are complete
 
-    // L2 norms of the 2R columns, one wave per column
-    for (int col = wave; col < NC; col += 4) {
-        const float v0 = Mt[lane * MS + col], v1 = Mt[(lane + 64) * MS + col];
-        const float ss = wave_sum(__builtin_fmaf(v0, v0, v1 * v1));
-        if (lane == 0)
-            inv[col] = 1.0f / sqrtf(ss + p.eps);
-    }
-    lds_barrier();
-    for (int idx = tid; idx < D * NC; idx += kThreads) {
-        const int j = idx / NC, c = idx % NC;
-        Mt[j * MS + c] *= inv[c];
-    }
-    lds_barrier();
-    if (owner) {
-        float *ks = p.ks + ((size_t)b * HK + kh) * NR * D;
-        for (int idx = tid; idx < NR * D; idx += kThreads)
-            ks[idx] = Mt[(idx % D) * MS + idx / D];
-    }
-    if (tid < NR)
-        p.as[((size_t)b * HV + h) * NR + tid] = al[tid];
+    float *Pw = P + wave * 64 * PS;
+    float *cw = cf + wave * CW;
+    float *Amw = cw, *Lbw = cw + NR * NR, *Bmw = cw + 2 * NR * NR, *gamw = cw + 3 * NR * NR;
+    float *invw = gamw + NR;
+    const float *alw = al[hh], *bew = be[hh];
 
-    // K^T M, this wave's share: only LDS operands, so it runs while the state streams in
+    // M^T M, each wave a quarter of the key indices; then every wave adds the
+    // four shares in the same order, so all waves hold the same bits
     {
         f32x4 accg = {0.0f, 0.0f, 0.0f, 0.0f};
-        float gv[2] = {0.0f, 0.0f};
-        gram_share<CK, NR, NVL, MS>(wave, kg, m, Mt, accg, gv);
-        if (m < NMF) {
+        float gv[2] = {0.0f, 0.0f}, dv[2] = {0.0f, 0.0f};
+        gram_share<NVL, MS>(wave, kg, m, Mt, accg, gv, dv);
+        float *g = gp[wave];
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                if (4 * kg + q < NR)
-                    gp[(wave * NR + 4 * kg + q) * NC + m] = accg[q];
+        for (int q = 0; q < 4; ++q) {
+            const int u = 4 * kg + q;
+            if (u < NR && m < NMF)
+                g[u * NC + m] = accg[q];
+            if (u == m && m >= NR && m < NMF)
+                g[NR * NC + m - NR] = accg[q];   // |q_{m-NR}|^2
         }
         if (NVL) {
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
-                float x = gv[c];
+                float x = gv[c], y = dv[c];
                 x += __shfl_xor(x, 16, 64);
                 x += __shfl_xor(x, 32, 64);
+                y += __shfl_xor(y, 16, 64);
+                y += __shfl_xor(y, 32, 64);
                 gv[c] = x;
+                dv[c] = y;
             }
             if (kg == 0 && m < NR) {
-                gp[(wave * NR + m) * NC + NMF] = gv[0];
-                gp[(wave * NR + m) * NC + NMF + 1] = gv[1];
+                g[m * NC + NMF] = gv[0];
+                g[m * NC + NMF + 1] = gv[1];
+            }
+            if (lane == 0) {
+                g[NR * NC + NMF - NR] = dv[0];
+                g[NR * NC + NMF - NR + 1] = dv[1];
             }
         }
     }
+    lds_barrier();   // from here on each wave finishes its rows alone
+    auto gram = [&](int idx) { return (gp[0][idx] + gp[1][idx]) + (gp[2][idx] + gp[3][idx]); };
+    if (lane < NC) {
+        const float nn = lane < NR ? gram(lane * NC + lane) : gram(NR * NC + lane - NR);
+        invw[lane] = 1.0f / sqrtf(nn + p.eps);
+    }
+    wave_lds_sync();
 
-    // S_0 M (two state tiles), chunk by chunk
-    f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f};
-    f32x4 acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
-    float pv[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
-    mfma_chunk<CK, NR, NVL, MS>(c0, 0, kg, m, Mt, acc0, acc1, pv);
-    load_chunk(c0, rs, soff, 2);
-    mfma_chunk<CK, NR, NVL, MS>(c1, 1, kg, m, Mt, acc0, acc1, pv);
-    load_chunk(c1, rs, soff, 3);
-    mfma_chunk<CK, NR, NVL, MS>(c0, 2, kg, m, Mt, acc0, acc1, pv);
-    mfma_chunk<CK, NR, NVL, MS>(c1, 3, kg, m, Mt, acc0, acc1, pv);
-    static_assert(NCHUNK == 4, "chunk schedule written for four chunks");
-
-    // tile register q of lane (kg, m): row 4kg + q of the tile, column m
-    if (m < NMF) {
+    // this head's scalar coefficients from the normalised Gram entries; the
+    // decay products multiply a_{u+1} .. a_t in order (factors outside are 1)
+    {
+        float a[NR];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            P[(32 * wave + 2 * (4 * kg + q)) * PS + m] = acc0[q];
-            P[(32 * wave + 2 * (4 * kg + q) + 1) * PS + m] = acc1[q];
+        for (int q = 0; q < NR; ++q)
+            a[q] = alw[q];
+        for (int idx = lane; idx < NR * NR + NR; idx += 64) {
+            if (idx < NR * NR) {
+                const int t = idx / NR, u = idx % NR;
+                float gtu = 1.0f;
+#pragma unroll
+                for (int q = 1; q < NR; ++q)
+                    gtu *= (q > u && q <= t) ? a[q] : 1.0f;
+                const float iu = invw[u];
+                Amw[idx] = (u < t) ? bew[t] * (gtu * (gram(u * NC + t) * iu * invw[t])) : 0.0f;
+                Bmw[idx] = (u <= t) ? gtu * (gram(u * NC + NR + t) * iu * invw[NR + t]) : 0.0f;
+            } else {
+                const int t = idx - NR * NR;
+                float gt = 1.0f;
+#pragma unroll
+                for (int q = 0; q < NR; ++q)
+                    gt *= q <= t ? a[q] : 1.0f;
+                gamw[t] = gt;
+            }
         }
+    }
+    wave_lds_sync();
+
+    // column j of L^{-1} diag(b) by forward substitution (lane j)
+    if (lane < NR) {
+        const int j = lane;
+        float x[NR];
+#pragma unroll
+        for (int t = 0; t < NR; ++t) {
+            float s = 0.0f;
+#pragma unroll
+            for (int u = 0; u < t; ++u)
+                s = __builtin_fmaf(Amw[t * NR + u], x[u], s);
+            x[t] = t < j ? 0.0f : (t == j ? bew[j] : -s);
+        }
+#pragma unroll
+        for (int t = 0; t < NR; ++t)
+            Lbw[t * NR + j] = x[t];
+    }
+
+    f32x4 acc[4];
+    float pv[4][2];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        acc[q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        pv[q][0] = pv[q][1] = 0.0f;
+    }
+#pragma unroll
+    for (int c = 0; c < NCHUNK; ++c) {
+        if (c % 3 == 0) {
+            mfma_chunk<CK, NVL, MS>(c0, c, kg, m, Mt, acc, pv);
+            if (c + 3 < NCHUNK)
+                load_chunk(c0, rs, soff, c + 3);
+        } else if (c % 3 == 1) {
+            mfma_chunk<CK, NVL, MS>(c1, c, kg, m, Mt, acc, pv);
+            if (c + 3 < NCHUNK)
+                load_chunk(c1, rs, soff, c + 3);
+        } else {
+            mfma_chunk<CK, NVL, MS>(c2, c, kg, m, Mt, acc, pv);
+            if (c + 3 < NCHUNK)
+                load_chunk(c2, rs, soff, c + 3);
+        }
+    }
+
+    // (S_0 M^)[i][c] = (S_0 M)[i][c] inv_c. Tile v, register q of lane (kg, m):
+    // row 16kg + 4q + v of the block, column m.
+    if (m < NMF) {
+        const float ic = invw[m];
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                Pw[(16 * kg + 4 * q + v4) * PS + m] = acc[v4][q] * ic;
     }
     if (NVL) {
         // the four key-index groups kg hold partial sums: add lanes l^16 and l^32
 #pragma unroll
-        for (int r = 0; r < 2; ++r)
+        for (int v4 = 0; v4 < 4; ++v4)
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
-                float x = pv[r][c];
+                float x = pv[v4][c];
                 x += __shfl_xor(x, 16, 64);
                 x += __shfl_xor(x, 32, 64);
-                pv[r][c] = x;
+                pv[v4][c] = x;
             }
         if (kg == 0) {
+            const float i0 = invw[NMF], i1 = invw[NMF + 1];
 #pragma unroll
-            for (int r = 0; r < 2; ++r)
-#pragma unroll
-                for (int c = 0; c < 2; ++c)
-                    P[(row0 + r) * PS + NMF + c] = pv[r][c];
+            for (int v4 = 0; v4 < 4; ++v4) {
+                Pw[(4 * m + v4) * PS + NMF] = pv[v4][0] * i0;
+                Pw[(4 * m + v4) * PS + NMF + 1] = pv[v4][1] * i1;
+            }
         }
     }
-    lds_barrier();
+    wave_lds_sync();
 
-    // scalar coefficients; (K^T M)[u][c] is the sum of the four waves' shares
-    for (int idx = tid; idx < NR * NR + NR; idx += kThreads) {
-        auto gram = [&](int u, int c) {
-            return (gp[(0 * NR + u) * NC + c] + gp[(1 * NR + u) * NC + c]) +
-                   (gp[(2 * NR + u) * NC + c] + gp[(3 * NR + u) * NC + c]);
-        };
-        if (idx < NR * NR) {
-            const int t = idx / NR, u = idx % NR;
-            float gtu = 1.0f;
-            for (int q = u + 1; q <= t; ++q)
-                gtu *= al[q];
-            Am[idx] = (u < t) ? be[t] * (gtu * gram(u, t)) : 0.0f;
-            Bm[idx] = (u <= t) ? gtu * gram(u, NR + t) : 0.0f;
-        } else {
-            const int t = idx - NR * NR;
-            float gt = 1.0f;
-            for (int q = 0; q <= t; ++q)
-                gt *= al[q];
-            gam[t] = gt;
-        }
-    }
-    lds_barrier();
-    // column j of L^{-1} diag(b) by forward substitution (thread j)
-    if (tid < NR) {
-        const int j = tid;
-        float a[NR * NR];
-#pragma unroll
-        for (int q = 0; q < NR * NR; ++q)
-            a[q] = Am[q];
-        float x[NR];
-#pragma unroll
-        for (int t = 0; t < NR; ++t) {
-            float acc = 0.0f;
-#pragma unroll
-            for (int u = 0; u < t; ++u)
-                acc = __builtin_fmaf(a[t * NR + u], x[u], acc);
-            x[t] = t < j ? 0.0f : (t == j ? be[j] : -acc);
-        }
-#pragma unroll
-        for (int t = 0; t < NR; ++t)
-            Lb[t * NR + j] = x[t];
-    }
-    lds_barrier();
-
-    // per state row i: e = L^{-1} diag(b) (v - g S_0 k), o = scale (g S_0 q + B e)
-    if (tid < D) {
+    // row rb + lane: e = L^{-1} diag(b) (v - g S_0 k^), o = scale (g S_0 q^ + B e)
+    {
+        float *Pr = Pw + lane * PS;
         float r[NR], e[NR];
 #pragma unroll
         for (int u = 0; u < NR; ++u)
-            r[u] = __builtin_fmaf(-gam[u], P[tid * PS + u], v[u]);
+            r[u] = __builtin_fmaf(-gamw[u], Pr[u], v[u]);
 #pragma unroll
         for (int t = 0; t < NR; ++t) {
-            float acc = 0.0f;
+            float s = 0.0f;
 #pragma unroll
             for (int u = 0; u <= t; ++u)
-                acc = __builtin_fmaf(Lb[t * NR + u], r[u], acc);
-            e[t] = acc;
+                s = __builtin_fmaf(Lbw[t * NR + u], r[u], s);
+            e[t] = s;
         }
 #pragma unroll
         for (int t = 0; t < NR; ++t) {
-            float acc = gam[t] * P[tid * PS + NR + t];
+            float s = gamw[t] * Pr[NR + t];
 #pragma unroll
             for (int u = 0; u <= t; ++u)
-                acc = __builtin_fmaf(Bm[t * NR + u], e[u], acc);
-            const size_t oi = (((size_t)b * NR + t) * HV + h) * D + tid;
-            p.out[oi] = from_f32<T>(p.scale * acc);
+                s = __builtin_fmaf(Bmw[t * NR + u], e[u], s);
+            const size_t oi = (((size_t)b * NR + t) * HV + h0 + hh) * D + rb + lane;
+            p.out[oi] = from_f32<T>(p.scale * s);
             p.es[oi] = e[t];
         }
         if (SNAP) {
-            // row tid of P is read only by this thread: reuse it for e_t
+            // this row of the product table is read only by this lane: reuse it for e_t
 #pragma unroll
             for (int t = 0; t < NR; ++t)
-                P[tid * PS + t] = e[t];
+                Pr[t] = e[t];
         }
     }
 
+    // normalised keys for the commit (the key head's first pair of value heads)
+    if (owner) {
+        float *ks = p.ks + ((size_t)b * HK + kh) * NR * D;
+        for (int idx = tid; idx < NR * D; idx += kThreads)
+            ks[idx] = Mt[(idx % D) * MS + idx / D] * invw[idx / D];
+    }
+
     if (SNAP) {
-        lds_barrier();
+        wave_lds_sync();
         // S_t for every row, by the same update the replay commit applies,
         // chunk by chunk from a second read of S_0
+        float *snap_h = p.snap + ((size_t)b * NR * HV + h0 + hh) * D * D;
 #pragma unroll 1
         for (int c = 0; c < NCHUNK; ++c) {
             load_chunk(c0, rs, soff, c);
 #pragma unroll 1
             for (int t = 0; t < NR; ++t) {
-                const float a = al[t];
-                const float e0 = P[row0 * PS + t], e1 = P[(row0 + 1) * PS + t];
-                float *dst = p.snap + (((size_t)b * NR + t) * HV + h) * D * D;
+                const float a = alw[t];
+                const float it = invw[t];
+                float ev[4];
+#pragma unroll
+                for (int v4 = 0; v4 < 4; ++v4)
+                    ev[v4] = Pw[(4 * m + v4) * PS + t];
+                float *dst = snap_h + (size_t)t * HV * D * D;
 #pragma unroll
                 for (int k = 0; k < CK; ++k) {
                     const int j = 4 * (c * CK + k) + kg;
-                    const float kk = Mt[j * MS + t];
-                    c0[k].x = row_update(c0[k].x, a, e0, kk);
-                    c0[k].y = row_update(c0[k].y, a, e1, kk);
-                    *reinterpret_cast<float2 *>(dst + (size_t)j * D + row0) = c0[k];
+                    const float kk = Mt[j * MS + t] * it;
+#pragma unroll
+                    for (int v4 = 0; v4 < 4; ++v4)
+                        c0[k][v4] = row_update(c0[k][v4], a, ev[v4], kk);
+                    stream_store(dst + (size_t)j * D + rb + 4 * m, c0[k]);
                 }
             }
         }
@@ -952,16 +1039,14 @@ __global__ __launch_bounds__(kThreads) void gdn_commit_kernel(const CommitParams
     float *Sd = p.ssm + ((size_t)slot * HV + h) * D * D;
 
     if (SNAP) {
-        const float4 *src = reinterpret_cast<const float4 *>(
-            p.snap + (((size_t)b * R + (n - 1)) * HV + h) * D * D);
-        float4 *dst = reinterpret_cast<float4 *>(Sd);
+        const float *src = p.snap + (((size_t)b * R + (n - 1)) * HV + h) * D * D;
         float4 v[D * D / 4 / kThreads];
 #pragma unroll
         for (int q = 0; q < D * D / 4 / kThreads; ++q)
-            v[q] = src[q * kThreads + tid];
+            v[q] = stream_load(src + 4 * (q * kThreads + tid));
 #pragma unroll
         for (int q = 0; q < D * D / 4 / kThreads; ++q)
-            dst[q * kThreads + tid] = v[q];
+            stream_store(Sd + 4 * (q * kThreads + tid), v[q]);
     } else {
         // staging loads first (fixed count, clamped indices, no branches),
         // then the state stream
@@ -979,7 +1064,7 @@ __global__ __launch_bounds__(kThreads) void gdn_commit_kernel(const CommitParams
         float4 s[JPER];
 #pragma unroll
         for (int jj = 0; jj < JPER; ++jj)
-            s[jj] = *reinterpret_cast<const float4 *>(Sd + (size_t)(jj * GJ + g) * D + 4 * rq);
+            s[jj] = stream_load(Sd + (size_t)(jj * GJ + g) * D + 4 * rq);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int q = 0; q < NSTAGE; ++q) {
@@ -1006,7 +1091,7 @@ __global__ __launch_bounds__(kThreads) void gdn_commit_kernel(const CommitParams
         }
 #pragma unroll
         for (int jj = 0; jj < JPER; ++jj)
-            *reinterpret_cast<float4 *>(Sd + (size_t)(jj * GJ + g) * D + 4 * rq) = s[jj];
+            stream_store(Sd + (size_t)(jj * GJ + g) * D + 4 * rq, s[jj]);
     }
 
     // conv history: the last W-1 entries of [history | rows 0..n-1]; the value
@@ -1076,8 +1161,8 @@ struct VerifyLaunch {
 template <int D, int NR, typename T, bool SNAP>
 hipError_t launch_verify(const VerifyParams<T> &vp, const VerifyLaunch &l)
 {
-    if (D == 128) {
-        hipLaunchKernelGGL((gdn_verify_d128_kernel<NR, T, SNAP>), dim3(l.batch * l.HV), dim3(kThreads),
+    if (D == 128 && (l.HV / l.HK) % 2 == 0) {
+        hipLaunchKernelGGL((gdn_verify_d128_kernel<NR, T, SNAP>), dim3(l.batch * (l.HV / 2)), dim3(kThreads),
                            0, l.st, vp);
     } else {
         hipLaunchKernelGGL((gdn_verify_kernel<D, NR, T, SNAP>), dim3(l.batch * l.HV), dim3(kThreads),

@@ -177,6 +177,21 @@ def test_rows_and_head_dims(orc, rows, d, dtype):
     assert not bool(c.out[3].float().abs().sum())
 
 
+@pytest.mark.parametrize("mode", ["replay", "snapshot"])
+@pytest.mark.parametrize("rows", [3, 9])
+@pytest.mark.parametrize("hk,hv", [(3, 3), (2, 8), (3, 6)])
+def test_head_groups_at_d128(orc, hk, hv, rows, mode):
+    """Value heads per key head G = 1 (one head per workgroup), 4 (two pairs of
+    value heads per key head, only the first storing its q/k inputs) and 2
+    with an odd key-head count."""
+    shape = wl.LayerShape(num_k_heads=hk, num_v_heads=hv, d_k=128, d_v=128, dtype="bf16")
+    w = wl.small_workload(shape, batch=3, rows=rows, num_slots=7, seed=300 + rows + hv)
+    c = gh.make_case(w, mode=mode)
+    _log("G hk=%d hv=%d rows=%d %s" % (hk, hv, rows, mode))
+    check_layer(orc, c)
+    check_untouched(c)
+
+
 @pytest.mark.parametrize("name", ["tiny-fp32", "low-concurrency"])
 def test_replay_and_snapshot_agree_bitwise(name):
     w = wl.WORKLOADS[name]
