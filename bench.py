@@ -39,10 +39,10 @@ KERNEL_SOURCE = os.path.join(ROOT, "linear_attention_verify_amd", "csrc", "gdn_s
 # HBM bytes per launch read from rocprofv3 counters: FETCH_SIZE and WRITE_SIZE
 # (KiB per dispatch, one run each) of every launch of the kernel, averaged,
 # each scaled by known bytes / counter bytes of a plain 256 MiB device copy
-# in the same run. They hold only for the kernel source they were taken on
-# (its SHA-256); for any other source the bench reports null.
+# in the same run. They hold only for the kernel code they were taken on
+# (kernel_source_digest); for any other code the bench reports null.
 MEASURED_TRAFFIC = {
-    "source_sha256": "6835787f538121ca4db68165cd10b0304861ad2f579846b18ba8006ace10f0b8",
+    "source_sha256": "a5945ab26cc77b1b70a513b06814008fbec3734c1b6edf3bd30a00343114e2e1",
     "bytes": {   # (workload, mode, kernel) -> bytes per launch
         ("saturated-b64", "replay", "verify"): 176104574,
         ("saturated-b64", "replay", "commit"): 282765477,
@@ -50,10 +50,20 @@ MEASURED_TRAFFIC = {
 }
 
 
-def measured_traffic(workload, mode, kernel):
+def kernel_source_digest(path=KERNEL_SOURCE):
+    """SHA-256 of the kernel source with comments and whitespace removed, so
+    that only a change to the code itself invalidates measured figures."""
     import hashlib
-    digest = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
-    if digest != MEASURED_TRAFFIC["source_sha256"]:
+    import re
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = " ".join(text.split())
+    return hashlib.sha256(text.encode()).hexdigest()
+
+
+def measured_traffic(workload, mode, kernel):
+    if kernel_source_digest() != MEASURED_TRAFFIC["source_sha256"]:
         return None
     return MEASURED_TRAFFIC["bytes"].get((workload, mode, kernel))
 

@@ -61,7 +61,7 @@ extern "C" {
 typedef enum {
     GDN_OK = 0,
     GDN_ERR_INVALID_ARG = 1,       /* null pointer, bad count, misaligned buffer */
-    GDN_ERR_UNSUPPORTED = 2,       /* a shape this build has no kernel for */
+    GDN_ERR_UNSUPPORTED = 2,       /* a shape the library has no kernel for */
     GDN_ERR_SCRATCH_TOO_SMALL = 3, /* scratch_bytes below gdn_spec_scratch_bytes() */
     GDN_ERR_HIP = 4                /* the HIP runtime refused a launch */
 } gdn_status;
@@ -77,9 +77,9 @@ typedef enum { GDN_ACT_SILU = 0, GDN_ACT_NONE = 1 } gdn_act;
 typedef struct {
     int32_t num_k_heads;  /* HK >= 1 */
     int32_t num_v_heads;  /* HV, a multiple of HK */
-    int32_t d_k;          /* key head dim; this build: d_k == d_v in {32, 64, 128} */
+    int32_t d_k;          /* key head dim; supported: d_k == d_v in {32, 64, 128} */
     int32_t d_v;          /* value head dim */
-    int32_t conv_width;   /* W; this build: 4 */
+    int32_t conv_width;   /* W; supported: 4 */
     int32_t dtype;        /* gdn_dtype */
     int32_t act;          /* gdn_act applied after the conv */
     float scale;          /* o = scale * S q */

@@ -44,7 +44,7 @@
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kWidth = 4;    // conv width this build supports
+constexpr int kWidth = 4;    // the one conv width the kernels support
 constexpr int kMaxRows = 9;  // k + 1 with k <= 8 drafts
 constexpr int kMaxGroup = 16; // value heads per key head
 constexpr size_t kAlign = 256;
