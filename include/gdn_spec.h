@@ -92,6 +92,7 @@ typedef struct {
  *        state S transposed, S[i][j] at ssm[((s*HV + h)*d_k + j)*d_v + i]
  *        (d_v contiguous). 16-byte aligned.
  *  conv  dtype [num_slots][W-1][C], C = 2*HK*d_k + HV*d_v, oldest input first.
+ *        16-byte aligned.
  */
 typedef struct {
     float *ssm;

@@ -48,6 +48,7 @@ constexpr int kWidth = 4;    // the one conv width the kernels support
 constexpr int kMaxRows = 9;  // k + 1 with k <= 8 drafts
 constexpr int kMaxGroup = 16; // value heads per key head
 constexpr size_t kAlign = 256;
+constexpr int kXcds = 8;       // accelerator complex dies, each with its own L2
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -998,67 +999,127 @@ template <typename T> struct CommitParams {
     const float *ks;
     const float *as;
     const float *snap;
-    int HK, HV, C, P, R;
+    int HK, HV, C, P, R, B;
 };
+
+// Workgroups per head: each streams one part of at most 16 KiB of the
+// head's state (key rows j0 .. j0 + D/parts - 1, contiguous in the pool), in
+// four 16-byte accesses per lane. Small read-modify-write pieces keep enough
+// workgroups in flight to cover HBM latency with loads and stores interleaved.
+template <int D> __host__ __device__ constexpr int commit_parts() { return D * D * 4 > 16384 ? D * D * 4 / 16384 : 1; }
 
 template <int D, typename T, bool SNAP>
 __global__ __launch_bounds__(kThreads) void gdn_commit_kernel(const CommitParams<T> p)
 {
-    constexpr int LPJ = D / 4;
-    constexpr int GJ = kThreads / LPJ;
-    constexpr int JPER = D / GJ;
+    constexpr int NPART = commit_parts<D>();
+    constexpr int JW = D / NPART;          // key rows of this part
+    constexpr int LPJ = D / 4;             // lanes per key row, 4 state rows each
+    constexpr int GJ = kThreads / LPJ;     // key rows per pass
+    constexpr int JPER = JW / GJ;          // passes
+    static_assert(JPER >= 1 && JW % GJ == 0, "part must cover whole passes");
 
-    __shared__ __align__(16) float eb[kMaxRows * D];
-    __shared__ float kb[kMaxRows * D];
+    __shared__ __align__(16) float eb[kMaxRows * D];   // e_t[i]
+    __shared__ float kb[kMaxRows * JW];                // k_t[j0 + jl]
     __shared__ float al[kMaxRows];
 
     const int tid = threadIdx.x;
     const int HV = p.HV, HK = p.HK, R = p.R;
     const int G = HV / HK;
-    const int b = blockIdx.x / HV;
-    const int h = blockIdx.x % HV;
+    // Workgroups are dealt to the 8 XCDs round-robin by index: the parts of
+    // head bh take indices congruent to bh mod 8, so all of them run on one
+    // XCD and share its L2 copy of the head's stashed rows.
+    const int grp = blockIdx.x / (kXcds * NPART), rem = blockIdx.x % (kXcds * NPART);
+    const int part = rem / kXcds;
+    const int bh = grp * kXcds + rem % kXcds;
+    if (bh >= p.B * HV)
+        return;
+    const int b = bh / HV;
+    const int h = bh % HV;
     const int kh = h / G;
     const int slot = p.slot_ids[b];
     const int n = p.accept[b];
+    const bool report = tid == 0 && part == 0 && p.err;
 
     if (slot < -1 || slot >= p.P) {
-        if (tid == 0 && p.err)
+        if (report)
             atomicOr(p.err, 1);
         return;
     }
     if (n < 0 || n > R) {
-        if (tid == 0 && p.err)
+        if (report)
             atomicOr(p.err, 2);
         return;
     }
     if (slot == -1 || n == 0)
         return;
 
+    // Conv history: the last W-1 entries of [history | rows 0..n-1]. The value
+    // channels belong to this head, the key head's q/k channels to its first
+    // value head; one 16-byte unit of channels per thread, the parts of the
+    // head sharing the units out. Loaded first, stored last: each unit is
+    // read and written by its thread alone.
+    constexpr int EPU = 16 / sizeof(T);   // channels per unit
+    static_assert(D % EPU == 0, "units must not straddle channel groups");
+    const bool owner = (h % G) == 0;
+    const int nunit = (owner ? 3 * D : D) / EPU;
+    const int hu = part * kThreads + tid;
+    static_assert(kWidth == 4, "the history unit holds three rows");
+    T *hist = nullptr;
+    uint4 win0 = {}, win1 = {}, win2 = {};
+    if (hu < nunit) {
+        const int idx = hu * EPU;
+        int c;
+        if (idx < D)
+            c = 2 * HK * D + h * D + idx;
+        else if (idx < 2 * D)
+            c = kh * D + (idx - D);
+        else
+            c = HK * D + kh * D + (idx - 2 * D);
+        hist = p.conv + (size_t)slot * (kWidth - 1) * p.C + c;
+        // entry src of [history (W-1) | rows]
+        auto entry = [&](int src) {
+            const T *from = src < kWidth - 1 ? hist + (size_t)src * p.C
+                                             : p.xs + ((size_t)b * R + (src - (kWidth - 1))) * p.C + c;
+            return *reinterpret_cast<const uint4 *>(from);
+        };
+        win0 = entry(n);
+        win1 = entry(n + 1);
+        win2 = entry(n + 2);
+    }
+
+    const int j0 = part * JW;
     const int rq = tid % LPJ;
     const int g = tid / LPJ;
-    float *Sd = p.ssm + ((size_t)slot * HV + h) * D * D;
+    float *Sd = p.ssm + ((size_t)slot * HV + h) * D * D + (size_t)j0 * D;
 
     if (SNAP) {
-        const float *src = p.snap + (((size_t)b * R + (n - 1)) * HV + h) * D * D;
-        float4 v[D * D / 4 / kThreads];
+        const float *src = p.snap + (((size_t)b * R + (n - 1)) * HV + h) * D * D + (size_t)j0 * D;
+        constexpr int NV = JW * D / 4 / kThreads;
+        float4 v[NV];
 #pragma unroll
-        for (int q = 0; q < D * D / 4 / kThreads; ++q)
+        for (int q = 0; q < NV; ++q)
             v[q] = stream_load(src + 4 * (q * kThreads + tid));
 #pragma unroll
-        for (int q = 0; q < D * D / 4 / kThreads; ++q)
+        for (int q = 0; q < NV; ++q)
             stream_store(Sd + 4 * (q * kThreads + tid), v[q]);
     } else {
         // staging loads first (fixed count, clamped indices, no branches),
         // then the state stream
-        constexpr int NSTAGE = (kMaxRows * D + kThreads - 1) / kThreads;
+        constexpr int NSE = (kMaxRows * D + kThreads - 1) / kThreads;
+        constexpr int NSK = (kMaxRows * JW + kThreads - 1) / kThreads;
         const float *kt = p.ks + ((size_t)b * HK + kh) * R * D;  // k_t at kt[t*D + j]
-        float ev_in[NSTAGE], kv_in[NSTAGE];
+        float ev_in[NSE], kv_in[NSK];
 #pragma unroll
-        for (int q = 0; q < NSTAGE; ++q) {
+        for (int q = 0; q < NSE; ++q) {
             const int idx = min(q * kThreads + tid, n * D - 1);
             const int t = idx / D, i = idx % D;
             ev_in[q] = p.es[(((size_t)b * R + t) * HV + h) * D + i];
-            kv_in[q] = kt[idx];
+        }
+#pragma unroll
+        for (int q = 0; q < NSK; ++q) {
+            const int idx = min(q * kThreads + tid, n * JW - 1);
+            const int t = idx / JW, jl = idx % JW;
+            kv_in[q] = kt[t * D + j0 + jl];
         }
         const float a_in = p.as[((size_t)b * HV + h) * R + min(tid, n - 1)];
         float4 s[JPER];
@@ -1067,12 +1128,16 @@ __global__ __launch_bounds__(kThreads) void gdn_commit_kernel(const CommitParams
             s[jj] = stream_load(Sd + (size_t)(jj * GJ + g) * D + 4 * rq);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int q = 0; q < NSTAGE; ++q) {
+        for (int q = 0; q < NSE; ++q) {
             const int idx = q * kThreads + tid;
-            if (idx < n * D) {
+            if (idx < n * D)
                 eb[idx] = ev_in[q];
+        }
+#pragma unroll
+        for (int q = 0; q < NSK; ++q) {
+            const int idx = q * kThreads + tid;
+            if (idx < n * JW)
                 kb[idx] = kv_in[q];
-            }
         }
         if (tid < n)
             al[tid] = a_in;
@@ -1082,7 +1147,7 @@ __global__ __launch_bounds__(kThreads) void gdn_commit_kernel(const CommitParams
             const float4 ev = *reinterpret_cast<const float4 *>(&eb[t * D + 4 * rq]);
 #pragma unroll
             for (int jj = 0; jj < JPER; ++jj) {
-                const float k = kb[t * D + jj * GJ + g];
+                const float k = kb[t * JW + jj * GJ + g];
                 s[jj].x = row_update(s[jj].x, a, ev.x, k);
                 s[jj].y = row_update(s[jj].y, a, ev.y, k);
                 s[jj].z = row_update(s[jj].z, a, ev.z, k);
@@ -1094,30 +1159,11 @@ __global__ __launch_bounds__(kThreads) void gdn_commit_kernel(const CommitParams
             stream_store(Sd + (size_t)(jj * GJ + g) * D + 4 * rq, s[jj]);
     }
 
-    // conv history: the last W-1 entries of [history | rows 0..n-1]; the value
-    // channels belong to this head, the key head's q/k channels to its first
-    // value head
-    const bool owner = (h % G) == 0;
-    const int nch = owner ? 3 * D : D;
-    for (int idx = tid; idx < nch; idx += kThreads) {
-        int c;
-        if (idx < D)
-            c = 2 * HK * D + h * D + idx;
-        else if (idx < 2 * D)
-            c = kh * D + (idx - D);
-        else
-            c = HK * D + kh * D + (idx - 2 * D);
-        T *hist = p.conv + (size_t)slot * (kWidth - 1) * p.C + c;
-        T win[kWidth - 1];
-#pragma unroll
-        for (int w = 0; w < kWidth - 1; ++w) {
-            const int src = n + w;  // index into [history (W-1) | rows]
-            win[w] = src < kWidth - 1 ? hist[(size_t)src * p.C]
-                                      : p.xs[((size_t)b * R + (src - (kWidth - 1))) * p.C + c];
-        }
-#pragma unroll
-        for (int w = 0; w < kWidth - 1; ++w)
-            hist[(size_t)w * p.C] = win[w];
+    // conv history, stored after the state
+    if (hu < nunit) {
+        *reinterpret_cast<uint4 *>(hist) = win0;
+        *reinterpret_cast<uint4 *>(hist + (size_t)p.C) = win1;
+        *reinterpret_cast<uint4 *>(hist + 2 * (size_t)p.C) = win2;
     }
 }
 
@@ -1235,7 +1281,9 @@ hipError_t verify_typed(const Checked &c, const gdn_layer_desc *d, const gdn_poo
 template <int D, typename T, bool SNAP>
 hipError_t launch_commit(const CommitParams<T> &cp, int blocks, hipStream_t st)
 {
-    hipLaunchKernelGGL((gdn_commit_kernel<D, T, SNAP>), dim3(blocks), dim3(kThreads), 0, st, cp);
+    const int groups = (blocks + kXcds - 1) / kXcds;
+    hipLaunchKernelGGL((gdn_commit_kernel<D, T, SNAP>), dim3(groups * kXcds * commit_parts<D>()), dim3(kThreads), 0,
+                       st, cp);
     return hipGetLastError();
 }
 
@@ -1272,6 +1320,7 @@ hipError_t commit_typed(const Checked &c, const gdn_pool *pool, const int32_t *s
     cp.C = c.C;
     cp.P = pool->num_slots;
     cp.R = rows;
+    cp.B = batch;
     const int blocks = batch * c.HV;
     return snapshot ? commit_dim<T, true>(c.D, cp, blocks, st)
                     : commit_dim<T, false>(c.D, cp, blocks, st);
@@ -1284,7 +1333,8 @@ gdn_status check_common(const gdn_layer_desc *desc, const gdn_pool *pool, int32_
     gdn_status s = check_desc(desc, c);
     if (s != GDN_OK)
         return s;
-    if (!pool || !pool->ssm || !pool->conv || pool->num_slots < 1 || !aligned16(pool->ssm))
+    if (!pool || !pool->ssm || !pool->conv || pool->num_slots < 1 || !aligned16(pool->ssm) ||
+        !aligned16(pool->conv))
         return GDN_ERR_INVALID_ARG;
     if (batch < 0 || rows < 1 || rows > kMaxRows)
         return GDN_ERR_INVALID_ARG;

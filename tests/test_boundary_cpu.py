@@ -112,6 +112,8 @@ def test_bad_arguments_are_refused(lib):
     assert _status_verify(lib, d, bd.GdnPool(None, 4096, 8)) == inv
     assert _status_verify(lib, d, bd.GdnPool(4096, 4096, 0)) == inv
     assert _status_verify(lib, d, bd.GdnPool(4100, 4096, 8)) == inv      # ssm not 16-byte aligned
+    assert _status_verify(lib, d, bd.GdnPool(4096, 4100, 8)) == inv      # conv not 16-byte aligned
+    assert _status_commit(lib, d, bd.GdnPool(4096, 4104, 8)) == inv
     assert _status_verify(lib, d, p, rows=0) == inv
     assert _status_verify(lib, d, p, rows=10) == inv
     assert _status_verify(lib, d, p, batch=-1) == inv
