@@ -141,6 +141,9 @@ def main():
     ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of a captured HIP graph of each group of steps instead of "
+                         "eager launches (steps and warmup must be multiples of --copies)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 256 MiB device copy (the reference dispatch for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -183,7 +186,27 @@ def main():
                 for c in cases]
     torch.cuda.synchronize()
 
+    graph = None
+    if args.graph:
+        if args.steps % M or args.warmup % M:
+            raise SystemExit("--graph: --steps and --warmup must be multiples of --copies")
+        cap = torch.cuda.Stream()
+        on_cap = [bd.Prepared(c.desc, c.ssm, c.conv, c.conv_w, c.x, c.alpha, c.beta, c.slot_ids,
+                              c.accept, w.rows, c.mode, c.scratch, c.out, c.err, cap)
+                  for c in cases]
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=cap):
+            for p in on_cap:
+                p.verify()
+            for p in on_cap:
+                p.commit()
+        torch.cuda.synchronize()
+
     def run(nsteps, events=None):
+        if graph is not None and events is None:
+            for _ in range(nsteps // M):
+                graph.replay()
+            return
         s = 0
         while s < nsteps:
             group = list(range(s, min(s + M, nsteps)))
@@ -257,7 +280,7 @@ def main():
                    "head_dim": w.shape.d_k, "conv_width": w.shape.conv_width,
                    "storage": w.shape.dtype, "state": "f32", "pool_slots": w.num_slots,
                    "commit_mode": args.mode, "accept_mean": float(np.mean(base.accept_np)),
-                   "rotating_copies": M},
+                   "rotating_copies": M, "launch": "hip graph" if args.graph else "eager"},
         "gbps": gbps,
         "hbm_frac": gbps / HBM_PEAK_GBPS,
         "kernels": kernels,
