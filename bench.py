@@ -141,6 +141,10 @@ def main():
     ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--accept", default="given", choices=["given", "greedy"],
+                    help="given: the commit reads the workload's drawn accept lengths; greedy: each "
+                         "step runs device-side greedy acceptance on draft/target tokens that realise "
+                         "them, and the commit reads its output")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of a captured HIP graph of each group of steps instead of "
                          "eager launches (steps and warmup must be multiples of --copies)")
@@ -184,6 +188,15 @@ def main():
     prepared = [bd.Prepared(c.desc, c.ssm, c.conv, c.conv_w, c.x, c.alpha, c.beta, c.slot_ids,
                             c.accept, w.rows, c.mode, c.scratch, c.out, c.err, stream)
                 for c in cases]
+    accepts = [None] * M
+    if args.accept == "greedy":
+        draft, target = wl.draw_tokens(w, base.accept_np)
+        for k, c in enumerate(cases):
+            dt = torch.from_numpy(draft).cuda()
+            tt = torch.from_numpy(target).cuda()
+            nxt = torch.empty(w.batch, dtype=torch.int32, device="cuda")
+            c.accept.zero_()
+            accepts[k] = bd.PreparedAccept(dt, tt, c.slot_ids, w.rows, c.accept, nxt, stream)
     torch.cuda.synchronize()
 
     graph = None
@@ -194,10 +207,14 @@ def main():
         on_cap = [bd.Prepared(c.desc, c.ssm, c.conv, c.conv_w, c.x, c.alpha, c.beta, c.slot_ids,
                               c.accept, w.rows, c.mode, c.scratch, c.out, c.err, cap)
                   for c in cases]
+        acc_cap = [None if a is None else bd.PreparedAccept(*a._keep[:3], w.rows, *a._keep[3:], cap)
+                   for a in accepts]
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=cap):
-            for p in on_cap:
+            for p, a in zip(on_cap, acc_cap):
                 p.verify()
+                if a is not None:
+                    a()
             for p in on_cap:
                 p.commit()
         torch.cuda.synchronize()
@@ -219,6 +236,15 @@ def main():
                 p.verify()
                 if events is not None:
                     events["v"][-1][1].record(stream)
+                a = accepts[k % M]
+                if a is not None:
+                    if events is not None:
+                        events["a"].append((torch.cuda.Event(enable_timing=True),
+                                            torch.cuda.Event(enable_timing=True)))
+                        events["a"][-1][0].record(stream)
+                    a()
+                    if events is not None:
+                        events["a"][-1][1].record(stream)
             for k in group:
                 p = prepared[k % M]
                 if events is not None:
@@ -244,7 +270,7 @@ def main():
     wall = time.perf_counter() - t0
 
     # same K steps again with per-kernel HIP events on the launch stream
-    events = {"v": [], "c": []}
+    events = {"v": [], "c": [], "a": []}
     run(args.steps, events)
     torch.cuda.synchronize()
     tv = np.array([a.elapsed_time(b) for a, b in events["v"]]) * 1e-3
@@ -260,6 +286,9 @@ def main():
         "commit": {"avg_us": float(tc.mean() * 1e6), "bytes": cbytes,
                    "gbps": float(cbytes / tc.mean() / 1e9)},
     }
+    if events["a"]:
+        ta = np.array([a.elapsed_time(b) for a, b in events["a"]]) * 1e-3
+        kernels["accept_greedy"] = {"avg_us": float(ta.mean() * 1e6)}
     dom = "verify" if tv.mean() >= tc.mean() else "commit"
     ach = kernels[dom]["gbps"]
     line = {
@@ -280,7 +309,8 @@ def main():
                    "head_dim": w.shape.d_k, "conv_width": w.shape.conv_width,
                    "storage": w.shape.dtype, "state": "f32", "pool_slots": w.num_slots,
                    "commit_mode": args.mode, "accept_mean": float(np.mean(base.accept_np)),
-                   "rotating_copies": M, "launch": "hip graph" if args.graph else "eager"},
+                   "rotating_copies": M, "launch": "hip graph" if args.graph else "eager",
+                   "accept": args.accept},
         "gbps": gbps,
         "hbm_frac": gbps / HBM_PEAK_GBPS,
         "kernels": kernels,

@@ -143,6 +143,31 @@ gdn_status gdn_spec_commit(const gdn_layer_desc *desc, const gdn_pool *pool,
                            int32_t rows, gdn_commit_mode mode, const void *scratch,
                            size_t scratch_bytes, int32_t *err_flag, void *stream);
 
+/*
+ * Greedy acceptance on the device, producing the accept_len that
+ * gdn_spec_commit reads. Verify row 0 of request b holds the pending token and
+ * row t (1 <= t < rows) the draft token draft[b][t-1]; target[b][t] is the
+ * target's greedy token after row t (FreeToken PR #844, Design: the target
+ * scores [pending, d1..dk] and n tokens are accepted; FreeToken issue #828,
+ * Design: speculative decoding must reproduce greedy decoding token for
+ * token). Draft t is accepted while draft[b][t-1] == target[b][t-1] holds for
+ * it and every earlier draft, so
+ *     accept_len[b] = 1 + (number of leading drafts accepted), in [1, rows],
+ *     next_token[b] = target[b][accept_len[b] - 1], the new pending token.
+ * A request whose slot id is -1 (padding) gets accept_len 0 and next_token -1.
+ *
+ *  draft       int32 [batch][rows-1] (may be NULL when rows == 1)
+ *  target      int32 [batch][rows]
+ *  slot_ids    int32 [batch], nullable (NULL: no padding)
+ *  accept_len  int32 [batch], written
+ *  next_token  int32 [batch], nullable, written
+ * All device memory. Returns GDN_ERR_INVALID_ARG for rows outside [1, 9], a
+ * negative batch or a missing required pointer; batch 0 launches nothing.
+ */
+gdn_status gdn_spec_accept_greedy(const int32_t *draft, const int32_t *target,
+                                  const int32_t *slot_ids, int32_t batch, int32_t rows,
+                                  int32_t *accept_len, int32_t *next_token, void *stream);
+
 /* Static description of a status code. */
 const char *gdn_strerror(gdn_status status);
 

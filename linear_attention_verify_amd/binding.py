@@ -28,7 +28,8 @@ GDN_ACT_NONE = 1
 
 MODES = {"replay": GDN_COMMIT_REPLAY, "snapshot": GDN_COMMIT_SNAPSHOT}
 
-EXPORTS = ("gdn_spec_scratch_bytes", "gdn_spec_verify", "gdn_spec_commit", "gdn_strerror")
+EXPORTS = ("gdn_spec_scratch_bytes", "gdn_spec_verify", "gdn_spec_commit", "gdn_spec_accept_greedy",
+           "gdn_strerror")
 
 
 class GdnLayerDesc(ctypes.Structure):
@@ -81,6 +82,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                                     vp, sz, vp, vp, vp]
     lib.gdn_spec_commit.restype = ctypes.c_int
     lib.gdn_spec_commit.argtypes = [pdesc, ppool, vp, vp, i32, i32, ctypes.c_int, vp, sz, vp, vp]
+    lib.gdn_spec_accept_greedy.restype = ctypes.c_int
+    lib.gdn_spec_accept_greedy.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp]
     lib.gdn_strerror.restype = ctypes.c_char_p
     lib.gdn_strerror.argtypes = [ctypes.c_int]
     if path is None:
@@ -167,6 +170,16 @@ def gdn_spec_commit(desc, ssm, conv, slot_ids, accept_len, rows, mode, scratch, 
         raise GdnError(st, "gdn_spec_commit")
 
 
+def gdn_spec_accept_greedy(draft, target, slot_ids, rows, accept_len, next_token=None, stream=None,
+                           batch=None):
+    """accept_len (and next_token) from the draft and target greedy tokens, on the device."""
+    B = int(target.shape[0]) if batch is None else batch
+    st = load_library().gdn_spec_accept_greedy(_ptr(draft), _ptr(target), _ptr(slot_ids), B, rows,
+                                               _ptr(accept_len), _ptr(next_token), _stream(stream))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_spec_accept_greedy")
+
+
 class Prepared:
     """Verify and commit on fixed device tensors with the ctypes arguments built
     once, so that issuing a launch costs one foreign call."""
@@ -196,3 +209,18 @@ class Prepared:
         st = self.lib.gdn_spec_commit(*self.cargs)
         if st != GDN_OK:
             raise GdnError(st, "gdn_spec_commit")
+
+
+class PreparedAccept:
+    """gdn_spec_accept_greedy on fixed device tensors, ctypes arguments built once."""
+
+    def __init__(self, draft, target, slot_ids, rows, accept_len, next_token=None, stream=None):
+        self.lib = load_library()
+        self._keep = (draft, target, slot_ids, accept_len, next_token)
+        self.args = (_ptr(draft), _ptr(target), _ptr(slot_ids), int(target.shape[0]), rows,
+                     _ptr(accept_len), _ptr(next_token), _stream(stream))
+
+    def __call__(self):
+        st = self.lib.gdn_spec_accept_greedy(*self.args)
+        if st != GDN_OK:
+            raise GdnError(st, "gdn_spec_accept_greedy")

@@ -1167,6 +1167,33 @@ __global__ __launch_bounds__(kThreads) void gdn_commit_kernel(const CommitParams
     }
 }
 
+// ---- greedy acceptance --------------------------------------------------------
+
+// One thread per request: the first row whose draft differs from the target's
+// greedy token ends the accepted run.
+__global__ __launch_bounds__(kThreads) void gdn_accept_greedy_kernel(const int32_t *draft, const int32_t *target,
+                                                                     const int32_t *slot_ids, int B, int R,
+                                                                     int32_t *accept, int32_t *next)
+{
+    const int b = blockIdx.x * kThreads + threadIdx.x;
+    if (b >= B)
+        return;
+    if (slot_ids && slot_ids[b] == -1) {
+        accept[b] = 0;
+        if (next)
+            next[b] = -1;
+        return;
+    }
+    const int32_t *d = draft + (size_t)b * (R - 1);
+    const int32_t *g = target + (size_t)b * R;
+    int n = 1;
+    while (n < R && d[n - 1] == g[n - 1])
+        ++n;
+    accept[b] = n;
+    if (next)
+        next[b] = g[n - 1];
+}
+
 // ---- host side -------------------------------------------------------------
 
 struct Checked {
@@ -1413,6 +1440,22 @@ gdn_status gdn_spec_commit(const gdn_layer_desc *desc, const gdn_pool *pool,
         ? commit_typed<float>(c, pool, slot_ids, accept_len, batch, rows, snap, scratch, L, err_flag, st)
         : commit_typed<bf16_t>(c, pool, slot_ids, accept_len, batch, rows, snap, scratch, L, err_flag, st);
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+gdn_status gdn_spec_accept_greedy(const int32_t *draft, const int32_t *target,
+                                  const int32_t *slot_ids, int32_t batch, int32_t rows,
+                                  int32_t *accept_len, int32_t *next_token, void *stream)
+{
+    if (batch < 0 || rows < 1 || rows > kMaxRows)
+        return GDN_ERR_INVALID_ARG;
+    if (batch == 0)
+        return GDN_OK;
+    if (!target || !accept_len || (rows > 1 && !draft))
+        return GDN_ERR_INVALID_ARG;
+    hipLaunchKernelGGL(gdn_accept_greedy_kernel, dim3((batch + kThreads - 1) / kThreads), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), draft, target, slot_ids, batch, rows, accept_len,
+                       next_token);
+    return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
 const char *gdn_strerror(gdn_status status)

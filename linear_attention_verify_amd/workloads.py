@@ -175,6 +175,23 @@ def build_pools(w: Workload, layer_draw: dict, slot_ids: np.ndarray):
     return ssm, conv
 
 
+def draw_tokens(w: Workload, accept: np.ndarray, vocab: int = 151936, seed: int | None = None):
+    """Draft tokens [B][R-1] and target greedy tokens [B][R] (int32) under
+    which greedy acceptance yields exactly ``accept`` (entries 0 are treated
+    as 1: padding requests still get tokens): the first n-1 drafts equal the
+    target's tokens before them, and draft n (if any) differs."""
+    rng = np.random.default_rng([w.seed if seed is None else seed, 7919])
+    B, R = w.batch, w.rows
+    draft = rng.integers(0, vocab, size=(B, R - 1)).astype(np.int32)
+    target = rng.integers(0, vocab, size=(B, R)).astype(np.int32)
+    for b in range(B):
+        n = max(int(accept[b]), 1)
+        target[b, :n - 1] = draft[b, :n - 1]
+        if n - 1 < R - 1 and target[b, n - 1] == draft[b, n - 1]:
+            target[b, n - 1] = (draft[b, n - 1] + 1) % vocab
+    return draft, target
+
+
 def small_workload(shape: LayerShape, batch: int, rows: int, num_slots: int, seed: int,
                    name: str = "custom", **kw) -> Workload:
     return Workload(name=name, shape=shape, batch=batch, rows=rows, num_slots=num_slots,

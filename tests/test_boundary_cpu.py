@@ -126,6 +126,18 @@ def test_bad_arguments_are_refused(lib):
     assert _status_commit(lib, d, p, rows=10) == inv
 
 
+def test_accept_greedy_arguments_are_refused(lib):
+    inv = bd.GDN_ERR_INVALID_ARG
+    f = lib.gdn_spec_accept_greedy
+    assert f(4096, 4096, None, 2, 0, 4096, None, None) == inv      # rows 0
+    assert f(4096, 4096, None, 2, 10, 4096, None, None) == inv     # rows > 9
+    assert f(4096, 4096, None, -1, 3, 4096, None, None) == inv     # negative batch
+    assert f(None, 4096, None, 2, 3, 4096, None, None) == inv      # drafts needed when rows > 1
+    assert f(4096, None, None, 2, 3, 4096, None, None) == inv
+    assert f(4096, 4096, None, 2, 3, None, None, None) == inv
+    assert f(None, None, None, 0, 3, None, None, None) == bd.GDN_OK  # empty batch launches nothing
+
+
 def test_small_scratch_is_refused(lib):
     d, p = good_desc(), good_pool()
     need = bd.gdn_spec_scratch_bytes(d, 2, 3, "replay")
