@@ -131,6 +131,93 @@ def cpu_baseline(w, budget_s=12.0):
                       % (reps, w.name, w.batch, w.rows)}
 
 
+def run_stack(args, w):
+    """A hybrid stack slice: every step verifies the batch through each of the
+    w.layers GDN layers (one pool per layer) and then commits all layers, one
+    launch per layer (the default) or all in one launch (--stack-commit fused)."""
+    import numpy as np
+    import torch
+
+    import gpu_harness as gh
+    from linear_attention_verify_amd import binding as bd
+    from linear_attention_verify_amd import workloads as wl
+
+    if args.graph or args.accept != "given" or args.calibrate_copy:
+        raise SystemExit("--graph, --accept and --calibrate-copy apply to single-layer workloads")
+    sid, acc = wl.draw_requests(w)
+    stream = torch.cuda.current_stream()
+    layers = [gh.make_device_case(w, l, sid, acc, mode=args.mode) for l in range(w.layers)]
+    prepared = [bd.Prepared(c.desc, c.ssm, c.conv, c.conv_w, c.x, c.alpha, c.beta, c.slot_ids, c.accept,
+                            w.rows, c.mode, c.scratch, c.out, c.err, stream) for c in layers]
+    c0 = layers[0]
+    fused = bd.PreparedCommitLayers(c0.desc, [(c.ssm, c.conv, c.scratch) for c in layers], c0.slot_ids,
+                                    c0.accept, w.rows, args.mode, c0.err, stream)
+    torch.cuda.synchronize()
+
+    def step():
+        for p in prepared:
+            p.verify()
+        if args.stack_commit == "fused":
+            fused()
+        else:
+            for p in prepared:
+                p.commit()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if any(int(c.err.item()) for c in layers):
+        raise SystemExit("device error flags set")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # per-kernel durations in a second pass with HIP events on the launch stream
+    ev_v, ev_c = [], []
+    for _ in range(args.steps):
+        for p in prepared:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream); p.verify(); b.record(stream)
+            ev_v.append((a, b))
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        if args.stack_commit == "fused":
+            fused()
+        else:
+            for p in prepared:
+                p.commit()
+        b.record(stream)
+        ev_c.append((a, b))
+    torch.cuda.synchronize()
+    tv = np.array([a.elapsed_time(b) for a, b in ev_v]) * 1e-3
+    tc = np.array([a.elapsed_time(b) for a, b in ev_c]) * 1e-3
+    vb, cb = algorithmic_bytes(w, acc, args.mode)
+    L = w.layers
+    rows_per_step = w.batch * w.rows * L
+    gbps = (vb + cb) * L * args.steps / wall / 1e9
+    kernels = {"verify": {"avg_us": float(tv.mean() * 1e6), "bytes": vb, "gbps": float(vb / tv.mean() / 1e9)},
+               "commit_all_layers": {"avg_us": float(tc.mean() * 1e6), "bytes": cb * L,
+                                     "gbps": float(cb * L / tc.mean() / 1e9)}}
+    dom = "commit_all_layers" if tc.mean() >= tv.mean() * L else "verify"
+    line = {
+        "metric": METRIC, "value": rows_per_step * args.steps / wall, "unit": "rows/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "rows": w.rows, "layers": L,
+                   "key_heads": w.shape.num_k_heads, "value_heads": w.shape.num_v_heads,
+                   "head_dim": w.shape.d_k, "conv_width": w.shape.conv_width, "storage": w.shape.dtype,
+                   "state": "f32", "pool_slots": w.num_slots, "commit_mode": args.mode,
+                   "commit_launch": args.stack_commit, "accept_mean": float(np.mean(acc))},
+        "gbps": gbps, "hbm_frac": gbps / HBM_PEAK_GBPS, "kernels": kernels,
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["gbps"], "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": kernels[dom]["gbps"] / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic(w.name, args.mode, dom)},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -141,6 +228,8 @@ def main():
     ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--stack-commit", default="per-layer", choices=["fused", "per-layer"],
+                    help="multi-layer workloads: commit all layers in one launch or one per layer")
     ap.add_argument("--accept", default="given", choices=["given", "greedy"],
                     help="given: the commit reads the workload's drawn accept lengths; greedy: each "
                          "step runs device-side greedy acceptance on draft/target tokens that realise "
@@ -167,9 +256,9 @@ def main():
     from linear_attention_verify_amd import workloads as wl
 
     w = wl.WORKLOADS[args.workload]
-    if w.layers != 1:
-        raise SystemExit("bench workloads are single-layer configurations")
     torch.cuda.init()
+    if w.layers != 1:
+        return run_stack(args, w)
     if args.calibrate_copy:
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)

@@ -144,6 +144,29 @@ gdn_status gdn_spec_commit(const gdn_layer_desc *desc, const gdn_pool *pool,
                            size_t scratch_bytes, int32_t *err_flag, void *stream);
 
 /*
+ * Commit every GDN layer of a hybrid stack in one launch. Layer l's pool is
+ * pools[l] and scratch[l] is the scratch its last gdn_spec_verify used; all
+ * layers were verified with the same desc, batch, rows, mode and slot_ids,
+ * and share slot_ids and accept_len (FreeToken PR #844, Design: the commit
+ * restores the GDN state and every other slot state with one upload of the
+ * slot and count indices). The result is that of gdn_spec_commit on each
+ * layer in turn, bit for bit.
+ *
+ *  pools    host array of `layers` pools (device pointers inside; each may
+ *           have its own num_slots)
+ *  scratch  host array of `layers` device scratch pointers, each at least
+ *           scratch_bytes >= gdn_spec_scratch_bytes(desc, batch, rows, mode)
+ *  layers   1..64
+ * Errors as gdn_spec_commit; any bad layer refuses the whole call before a
+ * launch.
+ */
+gdn_status gdn_spec_commit_layers(const gdn_layer_desc *desc, const gdn_pool *pools,
+                                  void *const *scratch, int32_t layers, const int32_t *slot_ids,
+                                  const int32_t *accept_len, int32_t batch, int32_t rows,
+                                  gdn_commit_mode mode, size_t scratch_bytes, int32_t *err_flag,
+                                  void *stream);
+
+/*
  * Greedy acceptance on the device, producing the accept_len that
  * gdn_spec_commit reads. Verify row 0 of request b holds the pending token and
  * row t (1 <= t < rows) the draft token draft[b][t-1]; target[b][t] is the

@@ -28,8 +28,8 @@ GDN_ACT_NONE = 1
 
 MODES = {"replay": GDN_COMMIT_REPLAY, "snapshot": GDN_COMMIT_SNAPSHOT}
 
-EXPORTS = ("gdn_spec_scratch_bytes", "gdn_spec_verify", "gdn_spec_commit", "gdn_spec_accept_greedy",
-           "gdn_strerror")
+EXPORTS = ("gdn_spec_scratch_bytes", "gdn_spec_verify", "gdn_spec_commit", "gdn_spec_commit_layers",
+           "gdn_spec_accept_greedy", "gdn_strerror")
 
 
 class GdnLayerDesc(ctypes.Structure):
@@ -82,6 +82,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                                     vp, sz, vp, vp, vp]
     lib.gdn_spec_commit.restype = ctypes.c_int
     lib.gdn_spec_commit.argtypes = [pdesc, ppool, vp, vp, i32, i32, ctypes.c_int, vp, sz, vp, vp]
+    lib.gdn_spec_commit_layers.restype = ctypes.c_int
+    lib.gdn_spec_commit_layers.argtypes = [pdesc, ppool, ctypes.POINTER(vp), i32, vp, vp, i32, i32,
+                                           ctypes.c_int, sz, vp, vp]
     lib.gdn_spec_accept_greedy.restype = ctypes.c_int
     lib.gdn_spec_accept_greedy.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp]
     lib.gdn_strerror.restype = ctypes.c_char_p
@@ -168,6 +171,32 @@ def gdn_spec_commit(desc, ssm, conv, slot_ids, accept_len, rows, mode, scratch, 
         _mode(mode), _ptr(scratch), _nbytes(scratch), _ptr(err_flag), _stream(stream))
     if st != GDN_OK:
         raise GdnError(st, "gdn_spec_commit")
+
+
+class PreparedCommitLayers:
+    """gdn_spec_commit_layers over fixed per-layer (ssm, conv, scratch) device
+    tensors, ctypes arguments built once."""
+
+    def __init__(self, desc, layers, slot_ids, accept_len, rows, mode, err_flag=None, stream=None):
+        self.lib = load_library()
+        self._keep = (layers, slot_ids, accept_len, err_flag)
+        self.desc = desc
+        L = len(layers)
+        self.pools = (GdnPool * L)(*[make_pool(ssm, conv) for ssm, conv, _ in layers])
+        self.scratch = (ctypes.c_void_p * L)(*[_ptr(sc) for _, _, sc in layers])
+        nbytes = min(_nbytes(sc) for _, _, sc in layers)
+        self.args = (ctypes.byref(self.desc), self.pools, self.scratch, L, _ptr(slot_ids), _ptr(accept_len),
+                     int(slot_ids.shape[0]), rows, _mode(mode), nbytes, _ptr(err_flag), _stream(stream))
+
+    def __call__(self):
+        st = self.lib.gdn_spec_commit_layers(*self.args)
+        if st != GDN_OK:
+            raise GdnError(st, "gdn_spec_commit_layers")
+
+
+def gdn_spec_commit_layers(desc, layers, slot_ids, accept_len, rows, mode, err_flag=None, stream=None):
+    """Commit every layer in one launch; layers = [(ssm, conv, scratch), ...] device tensors."""
+    PreparedCommitLayers(desc, layers, slot_ids, accept_len, rows, mode, err_flag, stream)()
 
 
 def gdn_spec_accept_greedy(draft, target, slot_ids, rows, accept_len, next_token=None, stream=None,

@@ -1009,7 +1009,7 @@ template <typename T> struct CommitParams {
 template <int D> __host__ __device__ constexpr int commit_parts() { return D * D * 4 > 16384 ? D * D * 4 / 16384 : 1; }
 
 template <int D, typename T, bool SNAP>
-__global__ __launch_bounds__(kThreads) void gdn_commit_kernel(const CommitParams<T> p)
+__device__ __forceinline__ void commit_body(const CommitParams<T> &p)
 {
     constexpr int NPART = commit_parts<D>();
     constexpr int JW = D / NPART;          // key rows of this part
@@ -1167,6 +1167,45 @@ __global__ __launch_bounds__(kThreads) void gdn_commit_kernel(const CommitParams
     }
 }
 
+template <int D, typename T, bool SNAP>
+__global__ __launch_bounds__(kThreads) void gdn_commit_kernel(const CommitParams<T> p)
+{
+    commit_body<D, T, SNAP>(p);
+}
+
+// A hybrid stack commits every GDN layer in one launch: grid row y is layer
+// y, whose pool and scratch pointers arrive as kernel arguments (so a
+// captured launch keeps them); slot ids and accept lengths are shared.
+constexpr int kMaxLayers = 64;
+
+struct StackLayer {
+    float *ssm;
+    void *conv;
+    const char *scratch;
+    int P;
+};
+
+struct CommitStack {
+    StackLayer l[kMaxLayers];
+    size_t xs, es, ks, as, snap;   // scratch part offsets, the same in every layer
+};
+
+template <int D, typename T, bool SNAP>
+__global__ __launch_bounds__(kThreads) void gdn_commit_stack_kernel(const CommitParams<T> p0, const CommitStack st)
+{
+    CommitParams<T> p = p0;
+    const StackLayer &l = st.l[blockIdx.y];
+    p.ssm = l.ssm;
+    p.conv = static_cast<T *>(l.conv);
+    p.P = l.P;
+    p.xs = reinterpret_cast<const T *>(l.scratch + st.xs);
+    p.es = reinterpret_cast<const float *>(l.scratch + st.es);
+    p.ks = reinterpret_cast<const float *>(l.scratch + st.ks);
+    p.as = reinterpret_cast<const float *>(l.scratch + st.as);
+    p.snap = SNAP ? reinterpret_cast<const float *>(l.scratch + st.snap) : nullptr;
+    commit_body<D, T, SNAP>(p);
+}
+
 // ---- greedy acceptance --------------------------------------------------------
 
 // One thread per request: the first row whose draft differs from the target's
@@ -1306,21 +1345,26 @@ hipError_t verify_typed(const Checked &c, const gdn_layer_desc *d, const gdn_poo
 }
 
 template <int D, typename T, bool SNAP>
-hipError_t launch_commit(const CommitParams<T> &cp, int blocks, hipStream_t st)
+hipError_t launch_commit(const CommitParams<T> &cp, const CommitStack *stack, int layers, int blocks,
+                         hipStream_t st)
 {
     const int groups = (blocks + kXcds - 1) / kXcds;
-    hipLaunchKernelGGL((gdn_commit_kernel<D, T, SNAP>), dim3(groups * kXcds * commit_parts<D>()), dim3(kThreads), 0,
-                       st, cp);
+    const dim3 grid(groups * kXcds * commit_parts<D>(), layers);
+    if (stack)
+        hipLaunchKernelGGL((gdn_commit_stack_kernel<D, T, SNAP>), grid, dim3(kThreads), 0, st, cp, *stack);
+    else
+        hipLaunchKernelGGL((gdn_commit_kernel<D, T, SNAP>), grid, dim3(kThreads), 0, st, cp);
     return hipGetLastError();
 }
 
 template <typename T, bool SNAP>
-hipError_t commit_dim(int D, const CommitParams<T> &cp, int blocks, hipStream_t st)
+hipError_t commit_dim(int D, const CommitParams<T> &cp, const CommitStack *stack, int layers, int blocks,
+                      hipStream_t st)
 {
     switch (D) {
-    case 32: return launch_commit<32, T, SNAP>(cp, blocks, st);
-    case 64: return launch_commit<64, T, SNAP>(cp, blocks, st);
-    case 128: return launch_commit<128, T, SNAP>(cp, blocks, st);
+    case 32: return launch_commit<32, T, SNAP>(cp, stack, layers, blocks, st);
+    case 64: return launch_commit<64, T, SNAP>(cp, stack, layers, blocks, st);
+    case 128: return launch_commit<128, T, SNAP>(cp, stack, layers, blocks, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -1328,7 +1372,8 @@ hipError_t commit_dim(int D, const CommitParams<T> &cp, int blocks, hipStream_t 
 template <typename T>
 hipError_t commit_typed(const Checked &c, const gdn_pool *pool, const int32_t *slot_ids,
                         const int32_t *accept, int batch, int rows, bool snapshot,
-                        const void *scratch, const ScratchLayout &L, int32_t *err, hipStream_t st)
+                        const void *scratch, const ScratchLayout &L, int32_t *err, hipStream_t st,
+                        const CommitStack *stack = nullptr, int layers = 1)
 {
     CommitParams<T> cp;
     const char *base = static_cast<const char *>(scratch);
@@ -1349,8 +1394,8 @@ hipError_t commit_typed(const Checked &c, const gdn_pool *pool, const int32_t *s
     cp.R = rows;
     cp.B = batch;
     const int blocks = batch * c.HV;
-    return snapshot ? commit_dim<T, true>(c.D, cp, blocks, st)
-                    : commit_dim<T, false>(c.D, cp, blocks, st);
+    return snapshot ? commit_dim<T, true>(c.D, cp, stack, layers, blocks, st)
+                    : commit_dim<T, false>(c.D, cp, stack, layers, blocks, st);
 }
 
 gdn_status check_common(const gdn_layer_desc *desc, const gdn_pool *pool, int32_t batch,
@@ -1439,6 +1484,45 @@ gdn_status gdn_spec_commit(const gdn_layer_desc *desc, const gdn_pool *pool,
     hipError_t e = desc->dtype == GDN_F32
         ? commit_typed<float>(c, pool, slot_ids, accept_len, batch, rows, snap, scratch, L, err_flag, st)
         : commit_typed<bf16_t>(c, pool, slot_ids, accept_len, batch, rows, snap, scratch, L, err_flag, st);
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+gdn_status gdn_spec_commit_layers(const gdn_layer_desc *desc, const gdn_pool *pools,
+                                  void *const *scratch, int32_t layers, const int32_t *slot_ids,
+                                  const int32_t *accept_len, int32_t batch, int32_t rows,
+                                  gdn_commit_mode mode, size_t scratch_bytes, int32_t *err_flag,
+                                  void *stream)
+{
+    if (!pools || !scratch || layers < 1 || layers > kMaxLayers)
+        return GDN_ERR_INVALID_ARG;
+    Checked c;
+    ScratchLayout L;
+    for (int l = 0; l < layers; ++l) {
+        const gdn_status s = check_common(desc, &pools[l], batch, rows, mode, scratch[l], scratch_bytes, &c, &L);
+        if (s != GDN_OK)
+            return s;
+    }
+    if (batch == 0)
+        return GDN_OK;
+    if (!slot_ids || !accept_len)
+        return GDN_ERR_INVALID_ARG;
+    CommitStack stack = {};
+    for (int l = 0; l < layers; ++l)
+        stack.l[l] = StackLayer{pools[l].ssm, pools[l].conv, static_cast<const char *>(scratch[l]),
+                                pools[l].num_slots};
+    stack.xs = L.xs;
+    stack.es = L.es;
+    stack.ks = L.ks;
+    stack.as = L.as;
+    stack.snap = L.snap;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const bool snap = mode == GDN_COMMIT_SNAPSHOT;
+    // layer 0's pointers fill the shared parameters; each grid row swaps in its own
+    hipError_t e = desc->dtype == GDN_F32
+        ? commit_typed<float>(c, &pools[0], slot_ids, accept_len, batch, rows, snap, scratch[0], L, err_flag, st,
+                              &stack, layers)
+        : commit_typed<bf16_t>(c, &pools[0], slot_ids, accept_len, batch, rows, snap, scratch[0], L, err_flag, st,
+                               &stack, layers);
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 

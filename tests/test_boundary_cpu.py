@@ -126,6 +126,29 @@ def test_bad_arguments_are_refused(lib):
     assert _status_commit(lib, d, p, rows=10) == inv
 
 
+def _status_commit_layers(lib, desc, pools, scratch, layers, batch=2, rows=3, nbytes=1 << 30):
+    import ctypes as ct
+    P = (bd.GdnPool * max(len(pools), 1))(*pools) if pools is not None else None
+    S = (ct.c_void_p * max(len(scratch), 1))(*scratch) if scratch is not None else None
+    return lib.gdn_spec_commit_layers(ct.byref(desc), P, S, layers, 4096, 4096, batch, rows, 0, nbytes,
+                                      None, None)
+
+
+def test_commit_layers_arguments_are_refused(lib):
+    d, p = good_desc(), good_pool()
+    inv = bd.GDN_ERR_INVALID_ARG
+    assert _status_commit_layers(lib, d, [p], [4096], 0) == inv            # no layers
+    assert _status_commit_layers(lib, d, [p] * 65, [4096] * 65, 65) == inv  # above 64
+    assert _status_commit_layers(lib, d, None, [4096], 1) == inv
+    assert _status_commit_layers(lib, d, [p], None, 1) == inv
+    assert _status_commit_layers(lib, d, [p, bd.GdnPool(4096, 4100, 8)], [4096, 4096], 2) == inv
+    assert _status_commit_layers(lib, d, [p, p], [4096, 4104], 2) == inv    # misaligned scratch
+    assert _status_commit_layers(lib, d, [p, p], [4096, None], 2) == inv
+    need = bd.gdn_spec_scratch_bytes(d, 2, 3, "replay")
+    assert _status_commit_layers(lib, d, [p, p], [4096, 4096], 2, nbytes=need - 1) == bd.GDN_ERR_SCRATCH_TOO_SMALL
+    assert _status_commit_layers(lib, d, [p, p], [4096, 4096], 2, batch=0) == bd.GDN_OK
+
+
 def test_accept_greedy_arguments_are_refused(lib):
     inv = bd.GDN_ERR_INVALID_ARG
     f = lib.gdn_spec_accept_greedy
