@@ -111,8 +111,9 @@ gdn_status gdn_spec_scratch_bytes(const gdn_layer_desc *desc, int32_t batch, int
 
 /*
  * Verify `rows` rows (1..9) of `batch` requests; the pool is only read.
- *  conv_w    dtype [C][W]
- *  x         dtype [batch][rows][C]      pre-conv inputs of the verify rows
+ *  conv_w    dtype [C][W], 16-byte aligned
+ *  x         dtype [batch][rows][C]      pre-conv inputs of the verify rows,
+ *                                        16-byte aligned
  *  alpha     dtype [batch][rows][HV]     decay gate a_t
  *  beta      dtype [batch][rows][HV]     write strength b_t
  *  slot_ids  int32 [batch]               slot of each request, -1 = padding;

@@ -679,9 +679,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     constexpr int CK = 4;                    // K-steps per chunk
     constexpr int NCHUNK = D / 4 / CK;       // 8 chunks per wave
     constexpr int CW = 3 * NR * NR + NR + NC;  // per-wave coefficients: Am, Lb, Bm, gam, inv
+    // bf16 inputs are staged: rows [history (W-1) | verify rows] of the
+    // workgroup's 512 channels (q 128 | k 128 | v 256), in 16-byte units
+    constexpr bool STAGED = sizeof(T) == 2;
+    constexpr int NROWS = kWidth - 1 + NR;
+    constexpr int UPR = 64;                                 // units per row
+    constexpr int NU = (NROWS * UPR + kThreads - 1) / kThreads;
+    constexpr int PFLOATS = 4 * 64 * PS > NROWS * 256 ? 4 * 64 * PS : NROWS * 256;
 
     __shared__ __align__(16) float Mt[D * MS];      // [j][c]: raw k_c[j] (c < NR), q_{c-NR}[j]; 0 beyond NC
-    __shared__ __align__(16) float P[4 * 64 * PS];  // per wave [i][c]: Gram table, then (S_0 M^)[i][c], then e_t
+    __shared__ __align__(16) float P[PFLOATS];       // staged inputs; then per wave [i][c]: (S_0 M^)[i][c], then e_t
     __shared__ float cf[4 * CW];
     __shared__ float gp[4][NR * NC + NR];           // wave w's share: (M^T M)[u][c], u < NR; then |q_t|^2
     __shared__ float al[2][NR], be[2][NR];
@@ -716,8 +723,35 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const bool isq = tid < D;
     const int chA = isq ? kh * D + jc : HK * D + kh * D + jc;
     const int chV = 2 * HK * D + h0 * D + tid;
-    const ChanIn<NR, T> cinA = load_channel<NR>(p, slot, b, chA);
-    const ChanIn<NR, T> cinV = load_channel<NR>(p, slot, b, chV);
+    // staged units: unit u is row u / UPR; units 0..15 q, 16..31 k, 32..63 v
+    // channels of that row; unit k of a row starts at local channel 8k
+    auto unit_channel = [&](int k) {
+        return k < 16 ? kh * D + 8 * k : (k < 32 ? HK * D + kh * D + 8 * (k - 16) : 2 * HK * D + h0 * D + 8 * (k - 32));
+    };
+    static_assert(NU <= 3, "three staged units per thread at most");
+    uint4 su0 = {}, su1 = {}, su2 = {};   // separate registers: an array here ends up in scratch
+    uint2 wA = {}, wV = {};
+    ChanIn<NR, T> cinA, cinV;
+    if constexpr (STAGED) {
+        const T *hbase = p.conv + (size_t)slot * (kWidth - 1) * p.C;
+        const T *xbase = p.x + (size_t)b * NR * p.C;
+        auto load_unit = [&](int q) {
+            const int u = min(q * kThreads + tid, NROWS * UPR - 1);
+            const int r = u / UPR, c = unit_channel(u % UPR);
+            const T *src = r < kWidth - 1 ? hbase + (size_t)r * p.C + c : xbase + (size_t)(r - (kWidth - 1)) * p.C + c;
+            return *reinterpret_cast<const uint4 *>(src);
+        };
+        su0 = load_unit(0);
+        if constexpr (NU > 1)
+            su1 = load_unit(1);
+        if constexpr (NU > 2)
+            su2 = load_unit(2);
+        wA = *reinterpret_cast<const uint2 *>(p.conv_w + (size_t)chA * kWidth);
+        wV = *reinterpret_cast<const uint2 *>(p.conv_w + (size_t)chV * kWidth);
+    } else {
+        cinA = load_channel<NR>(p, slot, b, chA);
+        cinV = load_channel<NR>(p, slot, b, chV);
+    }
 
     const int kg = lane >> 4;
     const int m = lane & 15;
@@ -734,6 +768,45 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         be[ghh][gtt] = to_f32(gb);
         p.as[((size_t)b * HV + h0 + ghh) * NR + gtt] = to_f32(ga);
     }
+    const bool owner = (h0 % G) == 0;
+    if constexpr (STAGED) {
+        // to LDS, and the verify rows' units straight to the raw-row stash
+        uint4 *Xs = reinterpret_cast<uint4 *>(P);
+        auto stage_unit = [&](int q, uint4 val) {
+            const int u = q * kThreads + tid;
+            if (u < NROWS * UPR) {
+                const int r = u / UPR, k = u % UPR;
+                Xs[u] = val;
+                if (r >= kWidth - 1 && (k >= 32 || owner))
+                    *reinterpret_cast<uint4 *>(p.xs + ((size_t)b * NR + r - (kWidth - 1)) * p.C + unit_channel(k)) = val;
+            }
+        };
+        stage_unit(0, su0);
+        if constexpr (NU > 1)
+            stage_unit(1, su1);
+        if constexpr (NU > 2)
+            stage_unit(2, su2);
+        lds_barrier();
+        const T *Xt = reinterpret_cast<const T *>(P);
+        auto tap = [](uint2 w, int k) {
+            return T{(uint16_t)(((k < 2 ? w.x : w.y) >> (16 * (k & 1))) & 0xffffu)};
+        };
+#pragma unroll
+        for (int k = 0; k < kWidth; ++k) {
+            cinA.w[k] = tap(wA, k);
+            cinV.w[k] = tap(wV, k);
+        }
+#pragma unroll
+        for (int r = 0; r < kWidth - 1; ++r) {
+            cinA.hist[r] = Xt[r * 512 + tid];
+            cinV.hist[r] = Xt[r * 512 + 256 + tid];
+        }
+#pragma unroll
+        for (int t = 0; t < NR; ++t) {
+            cinA.x[t] = Xt[(kWidth - 1 + t) * 512 + tid];
+            cinV.x[t] = Xt[(kWidth - 1 + t) * 512 + 256 + tid];
+        }
+    }
     float v[NR];   // value channel tid = row rb + lane of head h0 + hh
     {
         float y[NR];
@@ -748,14 +821,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         }
         conv_rows(cinV, p.act, v);
     }
-    // raw row inputs for the commit's conv history; with more than two value
-    // heads per key head the first pair stores the key head's q/k channels
-    const bool owner = (h0 % G) == 0;
+    // raw row inputs for the commit's conv history (staged inputs were stored
+    // above); with more than two value heads per key head the first pair
+    // stores the key head's q/k channels
+    if constexpr (!STAGED) {
 #pragma unroll
-    for (int t = 0; t < NR; ++t) {
-        if (owner)
-            p.xs[((size_t)b * NR + t) * p.C + chA] = cinA.x[t];
-        p.xs[((size_t)b * NR + t) * p.C + chV] = cinV.x[t];
+        for (int t = 0; t < NR; ++t) {
+            if (owner)
+                p.xs[((size_t)b * NR + t) * p.C + chA] = cinA.x[t];
+            p.xs[((size_t)b * NR + t) * p.C + chV] = cinV.x[t];
+        }
     }
     __builtin_amdgcn_sched_barrier(0);
     load_chunk(c1, rs, soff, 1);
@@ -1453,7 +1528,7 @@ gdn_status gdn_spec_verify(const gdn_layer_desc *desc, const gdn_pool *pool, con
         return s;
     if (batch == 0)
         return GDN_OK;
-    if (!conv_w || !x || !alpha || !beta || !slot_ids || !out)
+    if (!conv_w || !x || !alpha || !beta || !slot_ids || !out || !aligned16(conv_w) || !aligned16(x))
         return GDN_ERR_INVALID_ARG;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool snap = mode == GDN_COMMIT_SNAPSHOT;

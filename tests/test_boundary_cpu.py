@@ -61,11 +61,11 @@ def test_scratch_bytes(lib, name, mode):
 
 
 def _status_verify(lib, desc, pool, batch=2, rows=3, mode=0, scratch=4096, nbytes=1 << 30,
-                   ptr=4096, slot=4096):
+                   ptr=4096, slot=4096, conv_w=None, x=None):
     return lib.gdn_spec_verify(ctypes.byref(desc) if desc is not None else None,
                                ctypes.byref(pool) if pool is not None else None,
-                               ptr, ptr, ptr, ptr, slot, batch, rows, mode, scratch, nbytes, ptr,
-                               None, None)
+                               ptr if conv_w is None else conv_w, ptr if x is None else x, ptr, ptr, slot,
+                               batch, rows, mode, scratch, nbytes, ptr, None, None)
 
 
 def _status_commit(lib, desc, pool, batch=2, rows=3, mode=0, scratch=4096, nbytes=1 << 30,
@@ -122,6 +122,8 @@ def test_bad_arguments_are_refused(lib):
     assert _status_verify(lib, d, p, scratch=4104) == inv                # misaligned scratch
     assert _status_verify(lib, d, p, slot=None) == inv
     assert _status_verify(lib, d, p, ptr=None) == inv
+    assert _status_verify(lib, d, p, x=4104) == inv                      # x not 16-byte aligned
+    assert _status_verify(lib, d, p, conv_w=4100) == inv                 # conv_w not 16-byte aligned
     assert _status_commit(lib, d, p, ptr=None) == inv
     assert _status_commit(lib, d, p, rows=10) == inv
 
