@@ -189,7 +189,7 @@ __host__ __device__ inline size_t align_up(size_t v) { return (v + kAlign - 1) /
 //   es   [B][R][HV][D]      fp32 correction vector e_t of each row and value head
 //   ks   [B][HK][R][D]      fp32 normalised k_t of each row and key head
 //   as   [B][HV][R]         fp32 decay gate a_t
-//   snap [B][R][HV][D][D]   fp32 S_t after each row (snapshot mode only), same
+//   snap [B][HV][R][D][D]   fp32 S_t after each row (snapshot mode only), same
 //                           per-head layout as the pool
 __host__ inline ScratchLayout scratch_layout(int HK, int HV, int D, int C, size_t esize, int B,
                                               int R, bool snapshot)
@@ -551,7 +551,7 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_kernel(const VerifyParams
         for (int t = 0; t < NR; ++t) {
             const float a = cf[t];
             const float4 ev = *reinterpret_cast<const float4 *>(&vb[t * D + 4 * rq]);
-            float *dst = p.snap + (((size_t)b * NR + t) * HV + h) * D * D;
+            float *dst = p.snap + (((size_t)b * HV + h) * NR + t) * D * D;
 #pragma unroll
             for (int jj = 0; jj < JPER; ++jj) {
                 const int j = jj * GJ + g;
@@ -1033,12 +1033,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     if (SNAP) {
         wave_lds_sync();
         // S_t for every row, by the same update the replay commit applies,
-        // chunk by chunk from a second read of S_0
-        float *snap_h = p.snap + ((size_t)b * NR * HV + h0 + hh) * D * D;
-#pragma unroll 1
-        for (int c = 0; c < NCHUNK; ++c) {
-            load_chunk(c0, rs, soff, c);
-#pragma unroll 1
+        // chunk by chunk from a second read of S_0; the next chunk loads
+        // while this one's snapshots are stored
+        float *snap_h = p.snap + ((size_t)b * HV + h0 + hh) * NR * D * D;   // a head's S_1..S_R are contiguous
+        auto snap_chunk = [&](f32x4 (&sc)[CK], int c) {
+#pragma unroll
             for (int t = 0; t < NR; ++t) {
                 const float a = alw[t];
                 const float it = invw[t];
@@ -1046,17 +1045,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 #pragma unroll
                 for (int v4 = 0; v4 < 4; ++v4)
                     ev[v4] = Pw[(4 * m + v4) * PS + t];
-                float *dst = snap_h + (size_t)t * HV * D * D;
+                float *dst = snap_h + (size_t)t * D * D;
 #pragma unroll
                 for (int k = 0; k < CK; ++k) {
                     const int j = 4 * (c * CK + k) + kg;
                     const float kk = Mt[j * MS + t] * it;
 #pragma unroll
                     for (int v4 = 0; v4 < 4; ++v4)
-                        c0[k][v4] = row_update(c0[k][v4], a, ev[v4], kk);
-                    stream_store(dst + (size_t)j * D + rb + 4 * m, c0[k]);
+                        sc[k][v4] = row_update(sc[k][v4], a, ev[v4], kk);
+                    stream_store(dst + (size_t)j * D + rb + 4 * m, sc[k]);
                 }
             }
+        };
+        static_assert(NCHUNK % 2 == 0, "chunks go in pairs");
+        load_chunk(c0, rs, soff, 0);
+        load_chunk(c1, rs, soff, 1);
+#pragma unroll 1
+        for (int c = 0; c < NCHUNK; c += 2) {
+            snap_chunk(c0, c);
+            if (c + 2 < NCHUNK)
+                load_chunk(c0, rs, soff, c + 2);
+            snap_chunk(c1, c + 1);
+            if (c + 3 < NCHUNK)
+                load_chunk(c1, rs, soff, c + 3);
         }
     }
 }
@@ -1168,7 +1179,7 @@ __device__ __forceinline__ void commit_body(const CommitParams<T> &p)
     float *Sd = p.ssm + ((size_t)slot * HV + h) * D * D + (size_t)j0 * D;
 
     if (SNAP) {
-        const float *src = p.snap + (((size_t)b * R + (n - 1)) * HV + h) * D * D + (size_t)j0 * D;
+        const float *src = p.snap + (((size_t)b * HV + h) * R + (n - 1)) * D * D + (size_t)j0 * D;
         constexpr int NV = JW * D / 4 / kThreads;
         float4 v[NV];
 #pragma unroll
