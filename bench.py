@@ -42,10 +42,10 @@ KERNEL_SOURCE = os.path.join(ROOT, "linear_attention_verify_amd", "csrc", "gdn_s
 # in the same run. They hold only for the kernel code they were taken on
 # (kernel_source_digest); for any other code the bench reports null.
 MEASURED_TRAFFIC = {
-    "source_sha256": "f5c03dc1dad85178c219aa1d730fa58a046f3b60d72d87bcb190df16921cb15c",
+    "source_sha256": "cfe77834bc0b797a5e25318790d866a8ea05da229ec7c65f7607b5349cbf3c75",
     "bytes": {   # (workload, mode, kernel) -> bytes per launch
-        ("saturated-b64", "replay", "verify"): 176116002,
-        ("saturated-b64", "replay", "commit"): 282707518,
+        ("saturated-b64", "replay", "verify"): 176115945,
+        ("saturated-b64", "replay", "commit"): 282700828,
     },
 }
 
@@ -173,24 +173,25 @@ def run_stack(args, w):
         step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # per-kernel durations in a second pass with HIP events on the launch stream
+    # per-phase durations in a second pass with HIP events on the launch stream:
+    # around each step's L verifies, and around its commits
     ev_v, ev_c = [], []
     for _ in range(args.steps):
-        for p in prepared:
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream); p.verify(); b.record(stream)
-            ev_v.append((a, b))
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
         a.record(stream)
+        for p in prepared:
+            p.verify()
+        b.record(stream)
         if args.stack_commit == "fused":
             fused()
         else:
             for p in prepared:
                 p.commit()
-        b.record(stream)
-        ev_c.append((a, b))
+        c.record(stream)
+        ev_v.append((a, b))
+        ev_c.append((b, c))
     torch.cuda.synchronize()
-    tv = np.array([a.elapsed_time(b) for a, b in ev_v]) * 1e-3
+    tv = np.array([a.elapsed_time(b) for a, b in ev_v]) * 1e-3 / w.layers
     tc = np.array([a.elapsed_time(b) for a, b in ev_c]) * 1e-3
     vb, cb = algorithmic_bytes(w, acc, args.mode)
     L = w.layers
@@ -300,49 +301,46 @@ def main():
                    for a in accepts]
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=cap):
-            for p, a in zip(on_cap, acc_cap):
+            for p in on_cap:
                 p.verify()
+            for a in acc_cap:
                 if a is not None:
                     a()
             for p in on_cap:
                 p.commit()
         torch.cuda.synchronize()
 
-    def run(nsteps, events=None):
-        if graph is not None and events is None:
+    def run(nsteps, marks=None):
+        """nsteps steps in groups of M copies: the group's verifies, then its
+        acceptances (if any), then its commits. With `marks`, HIP events on the
+        launch stream bracket each of the three phases of every group."""
+        if graph is not None and marks is None:
             for _ in range(nsteps // M):
                 graph.replay()
             return
         s = 0
         while s < nsteps:
             group = list(range(s, min(s + M, nsteps)))
+            ev = []
+
+            def mark():
+                if marks is not None:
+                    e = torch.cuda.Event(enable_timing=True)
+                    e.record(stream)
+                    ev.append(e)
+            mark()
             for k in group:
-                p = prepared[k % M]
-                if events is not None:
-                    events["v"].append((torch.cuda.Event(enable_timing=True),
-                                        torch.cuda.Event(enable_timing=True)))
-                    events["v"][-1][0].record(stream)
-                p.verify()
-                if events is not None:
-                    events["v"][-1][1].record(stream)
-                a = accepts[k % M]
-                if a is not None:
-                    if events is not None:
-                        events["a"].append((torch.cuda.Event(enable_timing=True),
-                                            torch.cuda.Event(enable_timing=True)))
-                        events["a"][-1][0].record(stream)
-                    a()
-                    if events is not None:
-                        events["a"][-1][1].record(stream)
+                prepared[k % M].verify()
+            mark()
             for k in group:
-                p = prepared[k % M]
-                if events is not None:
-                    events["c"].append((torch.cuda.Event(enable_timing=True),
-                                        torch.cuda.Event(enable_timing=True)))
-                    events["c"][-1][0].record(stream)
-                p.commit()
-                if events is not None:
-                    events["c"][-1][1].record(stream)
+                if accepts[k % M] is not None:
+                    accepts[k % M]()
+            mark()
+            for k in group:
+                prepared[k % M].commit()
+            mark()
+            if marks is not None:
+                marks.append((len(group), ev))
             s += len(group)
 
     run(args.warmup)
@@ -358,12 +356,15 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    # same K steps again with per-kernel HIP events on the launch stream
-    events = {"v": [], "c": [], "a": []}
-    run(args.steps, events)
+    # the same K steps again, eagerly, with HIP events on the launch stream around
+    # each phase of each group: a kernel's average duration is its phase time
+    # over the launches in it (back-to-back launches, as in the timed region)
+    marks = []
+    run(args.steps, marks)
     torch.cuda.synchronize()
-    tv = np.array([a.elapsed_time(b) for a, b in events["v"]]) * 1e-3
-    tc = np.array([a.elapsed_time(b) for a, b in events["c"]]) * 1e-3
+    launches = sum(n for n, _ in marks)
+    phase = [sum(ev[i].elapsed_time(ev[i + 1]) for _, ev in marks) * 1e-3 / launches for i in range(3)]
+    tv, ta, tc = (np.array(x) for x in phase)
 
     vbytes, cbytes = algorithmic_bytes(w, base.accept_np, args.mode)
     rows_per_step = w.batch * w.rows
@@ -375,9 +376,8 @@ def main():
         "commit": {"avg_us": float(tc.mean() * 1e6), "bytes": cbytes,
                    "gbps": float(cbytes / tc.mean() / 1e9)},
     }
-    if events["a"]:
-        ta = np.array([a.elapsed_time(b) for a, b in events["a"]]) * 1e-3
-        kernels["accept_greedy"] = {"avg_us": float(ta.mean() * 1e6)}
+    if args.accept == "greedy":
+        kernels["accept_greedy"] = {"avg_us": float(ta * 1e6)}
     dom = "verify" if tv.mean() >= tc.mean() else "commit"
     ach = kernels[dom]["gbps"]
     line = {

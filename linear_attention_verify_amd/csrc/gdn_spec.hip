@@ -1088,11 +1088,12 @@ template <typename T> struct CommitParams {
     int HK, HV, C, P, R, B;
 };
 
-// Workgroups per head: each streams one part of at most 16 KiB of the
-// head's state (key rows j0 .. j0 + D/parts - 1, contiguous in the pool), in
-// four 16-byte accesses per lane. Small read-modify-write pieces keep enough
-// workgroups in flight to cover HBM latency with loads and stores interleaved.
-template <int D> __host__ __device__ constexpr int commit_parts() { return D * D * 4 > 16384 ? D * D * 4 / 16384 : 1; }
+// Workgroups per head: each streams one part of at most 8 KiB of the head's
+// state (key rows j0 .. j0 + D/parts - 1, contiguous in the pool), in two
+// 16-byte accesses per lane. Small read-modify-write pieces keep enough
+// workgroups in flight to cover HBM latency with loads and stores interleaved
+// (8 KiB measured faster than 4, 16, 32 or 64 KiB parts).
+template <int D> __host__ __device__ constexpr int commit_parts() { return D * D * 4 > 8192 ? D * D * 4 / 8192 : 1; }
 
 template <int D, typename T, bool SNAP>
 __device__ __forceinline__ void commit_body(const CommitParams<T> &p)
