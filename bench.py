@@ -222,8 +222,8 @@ def run_stack(args, w):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=40)
-    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="saturated-b64")
     ap.add_argument("--mode", default="replay", choices=["replay", "snapshot"])
     ap.add_argument("--copies", type=int, default=4)

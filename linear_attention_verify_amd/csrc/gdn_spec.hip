@@ -684,7 +684,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     constexpr bool STAGED = sizeof(T) == 2;
     constexpr int NROWS = kWidth - 1 + NR;
     constexpr int UPR = 64;                                 // units per row
-    constexpr int NU = (NROWS * UPR + kThreads - 1) / kThreads;
+    constexpr int NXU = (NR * UPR + kThreads - 1) / kThreads;   // verify-row units per thread
     constexpr int PFLOATS = 4 * 64 * PS > NROWS * 256 ? 4 * 64 * PS : NROWS * 256;
 
     __shared__ __align__(16) float Mt[D * MS];      // [j][c]: raw k_c[j] (c < NR), q_{c-NR}[j]; 0 beyond NC
@@ -702,19 +702,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const int b = blockIdx.x / npair;
     const int h0 = 2 * (blockIdx.x % npair);
     const int kh = h0 / G;
-    const int slot = p.slot_ids[b];
-
-    if (slot < 0 || slot >= p.P) {
-        if (slot != -1 && tid == 0 && p.err)
-            atomicOr(p.err, 1);
-        zero_outputs(p, b, h0, NR, D);
-        zero_outputs(p, b, h0 + 1, NR, D);
-        return;
-    }
+    const int slot_in = p.slot_ids[b];   // its latency overlaps the slot-free loads below
 
     // Small loads first, branch-free, so they retire ahead of the state
-    // stream. Threads < 128 take q channel `tid`, threads 128.. k channel
-    // tid-128; thread tid takes value channel tid of the pair (head h0 + tid/128).
+    // stream; those that need no slot (gates, verify rows, taps) go before the
+    // slot id is waited for. Threads < 128 take q channel `tid`, threads 128..
+    // k channel tid-128; thread tid takes value channel tid of the pair (head
+    // h0 + tid/128).
     const int gidx = min(tid, 2 * NR - 1);
     const int ghh = gidx / NR, gtt = gidx % NR;
     const size_t gi = ((size_t)b * NR + gtt) * HV + h0 + ghh;
@@ -728,29 +722,42 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     auto unit_channel = [&](int k) {
         return k < 16 ? kh * D + 8 * k : (k < 32 ? HK * D + kh * D + 8 * (k - 16) : 2 * HK * D + h0 * D + 8 * (k - 32));
     };
-    static_assert(NU <= 3, "three staged units per thread at most");
-    uint4 su0 = {}, su1 = {}, su2 = {};   // separate registers: an array here ends up in scratch
+    static_assert(NXU <= 3 && (kWidth - 1) * UPR <= kThreads, "staged units per thread");
+    uint4 xu0 = {}, xu1 = {}, xu2 = {}, hu = {};   // separate registers: an array here ends up in scratch
     uint2 wA = {}, wV = {};
     ChanIn<NR, T> cinA, cinV;
     if constexpr (STAGED) {
-        const T *hbase = p.conv + (size_t)slot * (kWidth - 1) * p.C;
         const T *xbase = p.x + (size_t)b * NR * p.C;
-        auto load_unit = [&](int q) {
-            const int u = min(q * kThreads + tid, NROWS * UPR - 1);
-            const int r = u / UPR, c = unit_channel(u % UPR);
-            const T *src = r < kWidth - 1 ? hbase + (size_t)r * p.C + c : xbase + (size_t)(r - (kWidth - 1)) * p.C + c;
-            return *reinterpret_cast<const uint4 *>(src);
+        auto load_xunit = [&](int q) {
+            const int u = min(q * kThreads + tid, NR * UPR - 1);
+            return *reinterpret_cast<const uint4 *>(xbase + (size_t)(u / UPR) * p.C + unit_channel(u % UPR));
         };
-        su0 = load_unit(0);
-        if constexpr (NU > 1)
-            su1 = load_unit(1);
-        if constexpr (NU > 2)
-            su2 = load_unit(2);
+        xu0 = load_xunit(0);
+        if constexpr (NXU > 1)
+            xu1 = load_xunit(1);
+        if constexpr (NXU > 2)
+            xu2 = load_xunit(2);
         wA = *reinterpret_cast<const uint2 *>(p.conv_w + (size_t)chA * kWidth);
         wV = *reinterpret_cast<const uint2 *>(p.conv_w + (size_t)chV * kWidth);
+    }
+    // then the loads that need the slot: a bad slot id reads slot 0's history
+    // (any address inside the pool) and the workgroup leaves before the state
+    const bool bad = slot_in < 0 || slot_in >= p.P;
+    const int slot = bad ? 0 : slot_in;
+    if constexpr (STAGED) {
+        const int u = min(tid, (kWidth - 1) * UPR - 1);
+        hu = *reinterpret_cast<const uint4 *>(p.conv + ((size_t)slot * (kWidth - 1) + u / UPR) * p.C +
+                                              unit_channel(u % UPR));
     } else {
         cinA = load_channel<NR>(p, slot, b, chA);
         cinV = load_channel<NR>(p, slot, b, chV);
+    }
+    if (bad) {
+        if (slot_in != -1 && tid == 0 && p.err)
+            atomicOr(p.err, 1);
+        zero_outputs(p, b, h0, NR, D);
+        zero_outputs(p, b, h0 + 1, NR, D);
+        return;
     }
 
     const int kg = lane >> 4;
@@ -771,21 +778,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const bool owner = (h0 % G) == 0;
     if constexpr (STAGED) {
         // to LDS, and the verify rows' units straight to the raw-row stash
+        // LDS rows: history 0..W-2, then the verify rows
         uint4 *Xs = reinterpret_cast<uint4 *>(P);
-        auto stage_unit = [&](int q, uint4 val) {
+        if (tid < (kWidth - 1) * UPR)
+            Xs[tid] = hu;
+        auto stage_xunit = [&](int q, uint4 val) {
             const int u = q * kThreads + tid;
-            if (u < NROWS * UPR) {
+            if (u < NR * UPR) {
                 const int r = u / UPR, k = u % UPR;
-                Xs[u] = val;
-                if (r >= kWidth - 1 && (k >= 32 || owner))
-                    *reinterpret_cast<uint4 *>(p.xs + ((size_t)b * NR + r - (kWidth - 1)) * p.C + unit_channel(k)) = val;
+                Xs[(kWidth - 1) * UPR + u] = val;
+                if (k >= 32 || owner)
+                    *reinterpret_cast<uint4 *>(p.xs + ((size_t)b * NR + r) * p.C + unit_channel(k)) = val;
             }
         };
-        stage_unit(0, su0);
-        if constexpr (NU > 1)
-            stage_unit(1, su1);
-        if constexpr (NU > 2)
-            stage_unit(2, su2);
+        stage_xunit(0, xu0);
+        if constexpr (NXU > 1)
+            stage_xunit(1, xu1);
+        if constexpr (NXU > 2)
+            stage_xunit(2, xu2);
         lds_barrier();
         const T *Xt = reinterpret_cast<const T *>(P);
         auto tap = [](uint2 w, int k) {
@@ -1037,7 +1047,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         // while this one's snapshots are stored
         float *snap_h = p.snap + ((size_t)b * HV + h0 + hh) * NR * D * D;   // a head's S_1..S_R are contiguous
         auto snap_chunk = [&](f32x4 (&sc)[CK], int c) {
-#pragma unroll
+#pragma unroll 1
             for (int t = 0; t < NR; ++t) {
                 const float a = alw[t];
                 const float it = invw[t];
