@@ -29,7 +29,7 @@ GDN_ACT_NONE = 1
 MODES = {"replay": GDN_COMMIT_REPLAY, "snapshot": GDN_COMMIT_SNAPSHOT}
 
 EXPORTS = ("gdn_spec_scratch_bytes", "gdn_spec_verify", "gdn_spec_commit", "gdn_spec_commit_layers",
-           "gdn_spec_accept_greedy", "gdn_strerror")
+           "gdn_spec_accept_greedy", "gdn_strerror", "gdn_spec_attn_scratch_bytes", "gdn_spec_attn_verify")
 
 
 class GdnLayerDesc(ctypes.Structure):
@@ -51,6 +51,16 @@ class GdnPool(ctypes.Structure):
         ("ssm", ctypes.c_void_p),
         ("conv", ctypes.c_void_p),
         ("num_slots", ctypes.c_int32),
+    ]
+
+
+class GdnAttnDesc(ctypes.Structure):
+    _fields_ = [
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("scale", ctypes.c_float),
     ]
 
 
@@ -87,6 +97,11 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                                            ctypes.c_int, sz, vp, vp]
     lib.gdn_spec_accept_greedy.restype = ctypes.c_int
     lib.gdn_spec_accept_greedy.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp]
+    pattn = ctypes.POINTER(GdnAttnDesc)
+    lib.gdn_spec_attn_scratch_bytes.restype = ctypes.c_int
+    lib.gdn_spec_attn_scratch_bytes.argtypes = [pattn, i32, i32, i32, ctypes.POINTER(sz)]
+    lib.gdn_spec_attn_verify.restype = ctypes.c_int
+    lib.gdn_spec_attn_verify.argtypes = [pattn, vp, vp, vp, i32, vp, i32, vp, i32, i32, vp, sz, vp, vp, vp]
     lib.gdn_strerror.restype = ctypes.c_char_p
     lib.gdn_strerror.argtypes = [ctypes.c_int]
     if path is None:
@@ -253,3 +268,44 @@ class PreparedAccept:
         st = self.lib.gdn_spec_accept_greedy(*self.args)
         if st != GDN_OK:
             raise GdnError(st, "gdn_spec_accept_greedy")
+
+
+def attn_desc(shape) -> GdnAttnDesc:
+    """Descriptor from any object with the AttnShape fields."""
+    return GdnAttnDesc(shape.num_q_heads, shape.num_kv_heads, shape.head_dim, shape.page_size,
+                       float(shape.scale))
+
+
+def gdn_spec_attn_scratch_bytes(desc: GdnAttnDesc, batch: int, rows: int, max_blocks: int) -> int:
+    out = ctypes.c_size_t(0)
+    st = load_library().gdn_spec_attn_scratch_bytes(ctypes.byref(desc), batch, rows, max_blocks,
+                                                    ctypes.byref(out))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_spec_attn_scratch_bytes")
+    return out.value
+
+
+class PreparedAttn:
+    """gdn_spec_attn_verify on fixed device tensors, ctypes arguments built once.
+    q [B][R][Hq][D], caches [pages][page_size][Hkv][D] (bf16), block_table
+    [B][max_blocks] and seq_lens [B] (int32), out like q."""
+
+    def __init__(self, desc, q, k_cache, v_cache, block_table, seq_lens, scratch, out, err_flag=None,
+                 stream=None):
+        self.lib = load_library()
+        self._keep = (q, k_cache, v_cache, block_table, seq_lens, scratch, out, err_flag)
+        self.desc = desc
+        B, R = int(q.shape[0]), int(q.shape[1])
+        self.args = (ctypes.byref(self.desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), int(k_cache.shape[0]),
+                     _ptr(block_table), int(block_table.shape[1]), _ptr(seq_lens), B, R, _ptr(scratch),
+                     _nbytes(scratch), _ptr(out), _ptr(err_flag), _stream(stream))
+
+    def __call__(self):
+        st = self.lib.gdn_spec_attn_verify(*self.args)
+        if st != GDN_OK:
+            raise GdnError(st, "gdn_spec_attn_verify")
+
+
+def gdn_spec_attn_verify(desc, q, k_cache, v_cache, block_table, seq_lens, scratch, out, err_flag=None,
+                         stream=None):
+    PreparedAttn(desc, q, k_cache, v_cache, block_table, seq_lens, scratch, out, err_flag, stream)()

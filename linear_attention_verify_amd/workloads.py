@@ -200,3 +200,69 @@ def small_workload(shape: LayerShape, batch: int, rows: int, num_slots: int, see
 
 def with_shape(w: Workload, **shape_changes) -> Workload:
     return replace(w, shape=replace(w.shape, **shape_changes))
+
+
+# ---- verification attention (the hybrid model's full-attention layers) ----
+
+@dataclass(frozen=True)
+class AttnShape:
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    page_size: int = 64
+    scale: float | None = None    # None: 1 / sqrt(head_dim)
+
+    def __post_init__(self):
+        if self.scale is None:
+            object.__setattr__(self, "scale", 1.0 / float(np.sqrt(self.head_dim)))
+
+
+@dataclass(frozen=True)
+class AttnWorkload:
+    name: str
+    shape: AttnShape
+    batch: int
+    rows: int
+    min_len: int          # seq_len drawn uniformly in [min_len, max_len] (verify rows included)
+    max_len: int
+    seed: int = 0
+    padding: tuple = ()   # requests left as padding (seq_len 0)
+
+    @property
+    def max_blocks(self) -> int:
+        return -(-self.max_len // self.shape.page_size)
+
+
+ATTN_WORKLOADS = {
+    # Qwen3-Next-like full-attention layer: 16 query / 2 KV heads of 256
+    "attn-b64": AttnWorkload("attn-b64", AttnShape(16, 2, 256, 64), batch=64, rows=9,
+                             min_len=1024, max_len=8192, seed=11),
+    "attn-single": AttnWorkload("attn-single", AttnShape(16, 2, 256, 64), batch=1, rows=3,
+                                min_len=2048, max_len=2048, seed=12),
+}
+
+
+def draw_attention(w: AttnWorkload):
+    """seq_lens [B], block_table [B][max_blocks] (distinct pages per request, in
+    random order, unused entries -1), and as bf16 bits: q [B][R][Hq][D] and the
+    k/v caches [pages][page_size][Hkv][D], every value ~ N(0,1)."""
+    s = w.shape
+    rng = np.random.default_rng([w.seed, 31])
+    B, R, D = w.batch, w.rows, s.head_dim
+    seq = rng.integers(max(w.min_len, R), w.max_len + 1, size=B).astype(np.int32)
+    for b in w.padding:
+        seq[b] = 0
+    mb = w.max_blocks
+    need = -(-seq // s.page_size)
+    pages = int(need.sum()) + 3
+    perm = rng.permutation(pages).astype(np.int32)
+    table = np.full((B, mb), -1, np.int32)
+    off = 0
+    for b in range(B):
+        table[b, :need[b]] = perm[off:off + need[b]]
+        off += need[b]
+    f32 = np.float32
+    q = to_storage(rng.standard_normal((B, R, s.num_q_heads, D), dtype=f32), "bf16")
+    kc = to_storage(rng.standard_normal((pages, s.page_size, s.num_kv_heads, D), dtype=f32), "bf16")
+    vc = to_storage(rng.standard_normal((pages, s.page_size, s.num_kv_heads, D), dtype=f32), "bf16")
+    return {"seq_lens": seq, "block_table": table, "q": q, "k_cache": kc, "v_cache": vc}

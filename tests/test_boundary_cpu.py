@@ -24,8 +24,12 @@ def lib():
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(gdn_\w+)\s*\(", text, re.M)))
+    names = set()
+    for h in sorted(os.listdir(os.path.dirname(HEADER))):
+        if h.endswith(".h"):
+            text = open(os.path.join(os.path.dirname(HEADER), h)).read()
+            names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(gdn_\w+)\s*\(", text, re.M))
+    return sorted(names)
 
 
 def test_header_declares_the_boundary():
@@ -192,3 +196,44 @@ def test_product_code_never_touches_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle", text, re.M), f
                 assert "gdn_oracle" not in text, f
+
+
+def _attn_desc(**kw):
+    d = bd.GdnAttnDesc(8, 2, 128, 32, 0.088)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("num_q_heads", 0, bd.GDN_ERR_INVALID_ARG),
+    ("num_q_heads", 7, bd.GDN_ERR_INVALID_ARG),       # not a multiple of the KV heads
+    ("head_dim", 64, bd.GDN_ERR_UNSUPPORTED),
+    ("page_size", 16, bd.GDN_ERR_UNSUPPORTED),        # not a multiple of 32
+    ("num_kv_heads", 0, bd.GDN_ERR_INVALID_ARG),
+])
+def test_attention_descriptor_is_refused(lib, field, value, status):
+    import ctypes as ct
+    out = ct.c_size_t(0)
+    assert lib.gdn_spec_attn_scratch_bytes(ct.byref(_attn_desc(**{field: value})), 2, 3, 4, ct.byref(out)) == status
+
+
+def test_attention_arguments_are_refused(lib):
+    import ctypes as ct
+    d = _attn_desc()
+    inv = bd.GDN_ERR_INVALID_ARG
+    out = ct.c_size_t(0)
+    assert lib.gdn_spec_attn_scratch_bytes(ct.byref(d), 2, 10, 4, ct.byref(out)) == inv       # rows > 9
+    assert lib.gdn_spec_attn_scratch_bytes(ct.byref(_attn_desc(num_q_heads=64, num_kv_heads=1)), 2, 3, 4,
+                                           ct.byref(out)) == bd.GDN_ERR_UNSUPPORTED           # 192 queries
+    need = bd.gdn_spec_attn_scratch_bytes(d, 2, 3, 4)
+    f = lambda **kw: lib.gdn_spec_attn_verify(
+        ct.byref(d), kw.get("q", 4096), 4096, 4096, kw.get("pages", 8), 4096, kw.get("mb", 4), 4096,
+        kw.get("batch", 2), 3, kw.get("scratch", 4096), kw.get("nbytes", need), 4096, None, None)
+    assert f(q=None) == inv
+    assert f(q=4104) == inv                 # misaligned
+    assert f(pages=0) == inv
+    assert f(mb=0) == inv
+    assert f(scratch=None) == inv
+    assert f(nbytes=need - 1) == bd.GDN_ERR_SCRATCH_TOO_SMALL
+    assert f(batch=0, q=None, scratch=None) == bd.GDN_OK

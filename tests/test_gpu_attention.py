@@ -1,0 +1,122 @@
+"""Verification attention on the device against the oracle, element by
+element: ragged lengths across pages and splits, every verify row count,
+query-head groups, both head dims, padding, and the error flags."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+from oracle import attention  # noqa: E402
+from linear_attention_verify_amd import binding as bd  # noqa: E402
+from linear_attention_verify_amd import workloads as wl  # noqa: E402
+
+DEV = "cuda"
+ATOL, RTOL = 3e-3, 1e-2
+
+
+def _bits_to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def _run(w, d, table=None, seq=None):
+    s = w.shape
+    desc = bd.attn_desc(s)
+    table = d["block_table"] if table is None else table
+    seq = d["seq_lens"] if seq is None else seq
+    q = _bits_to_dev(d["q"])
+    kc = _bits_to_dev(d["k_cache"])
+    vc = _bits_to_dev(d["v_cache"])
+    bt = torch.from_numpy(np.ascontiguousarray(table, np.int32)).to(DEV)
+    sl = torch.from_numpy(np.ascontiguousarray(seq, np.int32)).to(DEV)
+    nbytes = bd.gdn_spec_attn_scratch_bytes(desc, w.batch, w.rows, table.shape[1])
+    scratch = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=DEV)
+    out = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    bd.gdn_spec_attn_verify(desc, q, kc, vc, bt, sl, scratch, out, err)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), int(err.item())
+
+
+def _oracle(w, d, seq=None):
+    f = lambda a: wl.bf16_bits_to_f32(a)
+    seq = d["seq_lens"] if seq is None else seq
+    return attention.verify_attention(f(d["q"]), f(d["k_cache"]), f(d["v_cache"]), d["block_table"],
+                                      seq, w.shape.page_size, w.shape.scale)
+
+
+CASES = [
+    # d, Hq, Hkv, page, rows, batch, min_len, max_len
+    (128, 4, 2, 32, 3, 3, 3, 200),
+    (128, 8, 1, 64, 1, 2, 1, 700),
+    (256, 16, 2, 64, 9, 3, 9, 1500),
+    (256, 16, 2, 32, 4, 4, 33, 300),
+    (128, 2, 2, 32, 9, 2, 9, 2100),
+    (256, 32, 2, 64, 4, 2, 64, 900),    # 64 queries per KV head: one full group of query tiles
+    (128, 16, 1, 32, 8, 2, 100, 500),   # 128 queries, the most one KV head takes: two groups
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=["d%d-hq%d-hkv%d-p%d-r%d" % c[:5] for c in CASES])
+def test_matches_oracle(case):
+    d_, hq, hkv, page, rows, batch, lo, hi = case
+    w = wl.AttnWorkload("t", wl.AttnShape(hq, hkv, d_, page), batch=batch, rows=rows, min_len=lo,
+                        max_len=hi, seed=sum(case), padding=(1,) if batch > 2 else ())
+    d = wl.draw_attention(w)
+    print("attention", case, "seq", d["seq_lens"].tolist(), flush=True)
+    got, err = _run(w, d)
+    assert err == 0
+    want = _oracle(w, d)
+    np.testing.assert_allclose(got, want, atol=ATOL, rtol=RTOL)
+    if batch > 2:
+        assert not np.any(got[1])
+
+
+def test_lengths_at_every_edge():
+    """seq_len = rows (no committed context), page and split boundaries on both sides."""
+    w = wl.AttnWorkload("edges", wl.AttnShape(8, 2, 128, 32), batch=9, rows=4, min_len=4, max_len=1100, seed=5)
+    d = wl.draw_attention(w)
+    seq = np.array([4, 31, 32, 33, 255, 256, 257, 1023, 1100], np.int32)
+    # the draw gave each request pages for its own length: rebuild the table for these lengths
+    need = -(-seq // 32)
+    pages = d["k_cache"].shape[0]
+    assert need.sum() <= pages
+    table = np.full((9, w.max_blocks), -1, np.int32)
+    perm = np.random.default_rng(0).permutation(pages)
+    off = 0
+    for b in range(9):
+        table[b, :need[b]] = perm[off:off + need[b]]
+        off += need[b]
+    d = dict(d, seq_lens=seq, block_table=table)
+    got, err = _run(w, d)
+    assert err == 0
+    np.testing.assert_allclose(got, _oracle(w, d), atol=ATOL, rtol=RTOL)
+
+
+def test_bad_pages_and_lengths_are_flagged():
+    w = wl.AttnWorkload("bad", wl.AttnShape(4, 2, 128, 32), batch=4, rows=3, min_len=40, max_len=90, seed=6)
+    d = wl.draw_attention(w)
+    table = d["block_table"].copy()
+    table[1, 0] = d["k_cache"].shape[0] + 5     # page outside the cache
+    seq = d["seq_lens"].copy()
+    seq[2] = 2                                   # below rows
+    got, err = _run(w, d, table=table, seq=seq)
+    assert err == 1 | 4
+    assert not np.any(got[1]) and not np.any(got[2])
+    ok = [0, 3]
+    want = _oracle(w, dict(d, seq_lens=seq), seq=np.where(np.isin(np.arange(4), ok), seq, 0))
+    np.testing.assert_allclose(got[ok], want[ok], atol=ATOL, rtol=RTOL)
+
+
+def test_full_size_batch_on_sampled_requests():
+    """The 64-request, 9-row workload at its real lengths; the oracle checks a
+    sample of requests (all rows and heads of each)."""
+    w = wl.ATTN_WORKLOADS["attn-b64"]
+    d = wl.draw_attention(w)
+    got, err = _run(w, d)
+    assert err == 0
+    sample = [0, 17, 42, 63]
+    sub = dict(d, q=d["q"][sample], block_table=d["block_table"][sample], seq_lens=d["seq_lens"][sample])
+    ws = wl.AttnWorkload(w.name, w.shape, batch=len(sample), rows=w.rows, min_len=w.min_len, max_len=w.max_len)
+    np.testing.assert_allclose(got[sample], _oracle(ws, sub), atol=ATOL, rtol=RTOL)
