@@ -678,7 +678,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     constexpr int PS = NC + 1;               // product-table row stride (odd)
     constexpr int CK = 4;                    // K-steps per chunk
     constexpr int NCHUNK = D / 4 / CK;       // 8 chunks per wave
-    constexpr int CW = 3 * NR * NR + NR + NC;  // per-wave coefficients: Am, Lb, Bm, gam, inv
+    constexpr int NT = NR * (NR + 1) / 2;      // pairs (t, u), u <= t
+    static_assert(NT <= 64, "one coefficient pair per lane");
     // bf16 inputs are staged: rows [history (W-1) | verify rows] of the
     // workgroup's 512 channels (q 128 | k 128 | v 256), in 16-byte units
     constexpr bool STAGED = sizeof(T) == 2;
@@ -689,13 +690,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 
     __shared__ __align__(16) float Mt[D * MS];      // [j][c]: raw k_c[j] (c < NR), q_{c-NR}[j]; 0 beyond NC
     __shared__ __align__(16) float P[PFLOATS];       // staged inputs; then per wave [i][c]: (S_0 M^)[i][c], then e_t
-    __shared__ float cf[4 * CW];
+    __shared__ float invs[4][NC];                   // per wave: 1 / |column c of M|
+    __shared__ float4 cpark[4][64];                 // per wave: each lane's coefficients during the stream
     __shared__ float gp[4][NR * NC + NR];           // wave w's share: (M^T M)[u][c], u < NR; then |q_t|^2
     __shared__ float al[2][NR], be[2][NR];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: state resources stay in SGPRs
     const int HV = p.HV, HK = p.HK;
     const int G = HV / HK;
     const int npair = HV / 2;
@@ -768,6 +770,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const uint32_t soff = (kg * D + rb + 4 * m) * 4;  // lane byte offset within each K-step block
     f32x4 c0[CK], c1[CK], c2[CK];
     load_chunk(c0, rs, soff, 0);
+    load_chunk(c1, rs, soff, 1);
     __builtin_amdgcn_sched_barrier(0);
 
     if (tid < 2 * NR) {
@@ -843,15 +846,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         }
     }
     __builtin_amdgcn_sched_barrier(0);
-    load_chunk(c1, rs, soff, 1);
     load_chunk(c2, rs, soff, 2);
     __builtin_amdgcn_sched_barrier(0);
     lds_barrier();   // the column table and the gates are complete
 
     float *Pw = P + wave * 64 * PS;
-    float *cw = cf + wave * CW;
-    float *Amw = cw, *Lbw = cw + NR * NR, *Bmw = cw + 2 * NR * NR, *gamw = cw + 3 * NR * NR;
-    float *invw = gamw + NR;
+    float *invw = invs[wave];
     const float *alw = al[hh], *bew = be[hh];
 
     // M^T M, each wave a quarter of the key indices; then every wave adds the
@@ -892,57 +892,40 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     }
     lds_barrier();   // from here on each wave finishes its rows alone
     auto gram = [&](int idx) { return (gp[0][idx] + gp[1][idx]) + (gp[2][idx] + gp[3][idx]); };
-    if (lane < NC) {
-        const float nn = lane < NR ? gram(lane * NC + lane) : gram(NR * NC + lane - NR);
-        invw[lane] = 1.0f / sqrtf(nn + p.eps);
-    }
-    wave_lds_sync();
+    auto inv_norm = [&](int c) {
+        const float nn = c < NR ? gram(c * NC + c) : gram(NR * NC + c - NR);
+        return 1.0f / sqrtf(nn + p.eps);
+    };
+    if (lane < NC)
+        invw[lane] = inv_norm(lane);
 
-    // this head's scalar coefficients from the normalised Gram entries; the
-    // decay products multiply a_{u+1} .. a_t in order (factors outside are 1)
+    // This head's scalar coefficients, one pair per lane and kept in
+    // registers (the solve broadcasts them with readlane). Lane i < NT holds
+    // the pair (t, u), u <= t, of the row-by-row enumeration:
+    //   cA = b_t g(t,u) k_u.k_t (u < t; 0 when u = t), cB = g(t,u) k_u.q_t;
+    // lane t < NR holds cG = g(t,-1) and cb = b_t. The decay products
+    // multiply a_{u+1} .. a_t in order (factors outside are 1).
+    float cA, cB, cG, cb;
     {
-        float a[NR];
+        int t, u;
+        tri_decode(min(lane, NT - 1), t, u);
+        float gtu = 1.0f;
+#pragma unroll
+        for (int q = 1; q < NR; ++q)
+            gtu *= (q > u && q <= t) ? alw[q] : 1.0f;
+        const float iu = inv_norm(u);
+        cA = (u < t) ? bew[t] * (gtu * (gram(u * NC + t) * iu * inv_norm(t))) : 0.0f;
+        cB = gtu * (gram(u * NC + NR + t) * iu * inv_norm(NR + t));
+        const int tt = min(lane, NR - 1);
+        float gt = 1.0f;
 #pragma unroll
         for (int q = 0; q < NR; ++q)
-            a[q] = alw[q];
-        for (int idx = lane; idx < NR * NR + NR; idx += 64) {
-            if (idx < NR * NR) {
-                const int t = idx / NR, u = idx % NR;
-                float gtu = 1.0f;
-#pragma unroll
-                for (int q = 1; q < NR; ++q)
-                    gtu *= (q > u && q <= t) ? a[q] : 1.0f;
-                const float iu = invw[u];
-                Amw[idx] = (u < t) ? bew[t] * (gtu * (gram(u * NC + t) * iu * invw[t])) : 0.0f;
-                Bmw[idx] = (u <= t) ? gtu * (gram(u * NC + NR + t) * iu * invw[NR + t]) : 0.0f;
-            } else {
-                const int t = idx - NR * NR;
-                float gt = 1.0f;
-#pragma unroll
-                for (int q = 0; q < NR; ++q)
-                    gt *= q <= t ? a[q] : 1.0f;
-                gamw[t] = gt;
-            }
-        }
+            gt *= q <= tt ? alw[q] : 1.0f;
+        cG = gt;
+        cb = bew[tt];
     }
-    wave_lds_sync();
-
-    // column j of L^{-1} diag(b) by forward substitution (lane j)
-    if (lane < NR) {
-        const int j = lane;
-        float x[NR];
-#pragma unroll
-        for (int t = 0; t < NR; ++t) {
-            float s = 0.0f;
-#pragma unroll
-            for (int u = 0; u < t; ++u)
-                s = __builtin_fmaf(Amw[t * NR + u], x[u], s);
-            x[t] = t < j ? 0.0f : (t == j ? bew[j] : -s);
-        }
-#pragma unroll
-        for (int t = 0; t < NR; ++t)
-            Lbw[t * NR + j] = x[t];
-    }
+    // parked in LDS while the state streams (registers are the limit there)
+    cpark[wave][lane] = float4{cA, cB, cG, cb};
 
     f32x4 acc[4];
     float pv[4][2];
@@ -1000,27 +983,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     }
     wave_lds_sync();
 
-    // row rb + lane: e = L^{-1} diag(b) (v - g S_0 k^), o = scale (g S_0 q^ + B e)
+    // row rb + lane, by forward substitution with the broadcast coefficients:
+    // e_t = b_t (v_t - g(t,-1) (S_0 k^_t)) - sum_{u<t} cA(t,u) e_u,
+    // o_t = scale (g(t,-1) (S_0 q^_t) + sum_{u<=t} cB(t,u) e_u)
     {
         float *Pr = Pw + lane * PS;
-        float r[NR], e[NR];
-#pragma unroll
-        for (int u = 0; u < NR; ++u)
-            r[u] = __builtin_fmaf(-gamw[u], Pr[u], v[u]);
+        const float4 cc = cpark[wave][lane];
+        cA = cc.x;
+        cB = cc.y;
+        cG = cc.z;
+        cb = cc.w;
+        float e[NR];
 #pragma unroll
         for (int t = 0; t < NR; ++t) {
-            float s = 0.0f;
+            const float r = __builtin_fmaf(-lane_value(cG, t), Pr[t], v[t]);
+            float s = lane_value(cb, t) * r;
 #pragma unroll
-            for (int u = 0; u <= t; ++u)
-                s = __builtin_fmaf(Lbw[t * NR + u], r[u], s);
+            for (int u = 0; u < t; ++u)
+                s = __builtin_fmaf(-lane_value(cA, t * (t + 1) / 2 + u), e[u], s);
             e[t] = s;
         }
 #pragma unroll
         for (int t = 0; t < NR; ++t) {
-            float s = gamw[t] * Pr[NR + t];
+            float s = lane_value(cG, t) * Pr[NR + t];
 #pragma unroll
             for (int u = 0; u <= t; ++u)
-                s = __builtin_fmaf(Bmw[t * NR + u], e[u], s);
+                s = __builtin_fmaf(lane_value(cB, t * (t + 1) / 2 + u), e[u], s);
             const size_t oi = (((size_t)b * NR + t) * HV + h0 + hh) * D + rb + lane;
             p.out[oi] = from_f32<T>(p.scale * s);
             p.es[oi] = e[t];
