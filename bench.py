@@ -131,6 +131,125 @@ def cpu_baseline(w, budget_s=12.0):
                       % (reps, w.name, w.batch, w.rows)}
 
 
+ATTN_METRIC = "verification attention rows/s and achieved HBM GB/s (% of MI355X peak)"
+
+
+def attention_bytes(w, seq_lens):
+    """Algorithmic bytes of one verification-attention call: every key and value
+    of each request's seq_len positions (Hkv heads of D bf16 values each) read
+    once, the queries read and the outputs written once. The split partial
+    results are scratch traffic of this implementation and are not counted."""
+    s = w.shape
+    kv = sum(2 * int(L) * s.num_kv_heads * s.head_dim * 2 for L in seq_lens)
+    qo = 2 * w.batch * w.rows * s.num_q_heads * s.head_dim * 2
+    return kv + qo
+
+
+def attention_cpu_baseline(w, d, budget_s=12.0):
+    """The attention oracle (NumPy fp64, as it stands) on a sample of requests."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import attention
+    from linear_attention_verify_amd import workloads as wl
+
+    f = wl.bf16_bits_to_f32
+    k, v = f(d["k_cache"]), f(d["v_cache"])
+    n = min(4, w.batch)
+    q = f(d["q"][:n])
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        attention.verify_attention(q, k, v, d["block_table"][:n], d["seq_lens"][:n], w.shape.page_size,
+                                   w.shape.scale)
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": reps * n * w.rows / dt, "unit": "rows/s", "cores": threads, "kind": "oracle",
+            "sample": "%d passes over requests 0..%d of the %s batch (%d rows each, seq_len %s), fp64"
+                      % (reps, n - 1, w.name, w.rows, d["seq_lens"][:n].tolist())}
+
+
+def run_attention(args, w):
+    """Verification attention over the paged KV cache: a step is one
+    gdn_spec_attn_verify call (split kernel + combine kernel) over the batch.
+    Steps alternate between two copies of the cache so that no call finds the
+    previous call's keys and values in the 256 MB memory-side cache."""
+    import numpy as np
+    import torch
+
+    from linear_attention_verify_amd import binding as bd
+    from linear_attention_verify_amd import workloads as wl
+
+    if args.graph or args.accept != "given" or args.calibrate_copy or args.mode != "replay":
+        raise SystemExit("--graph, --accept, --calibrate-copy and --mode apply to GDN workloads")
+    d = wl.draw_attention(w)
+    s = w.shape
+    dev = "cuda"
+
+    def bits(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    desc = bd.attn_desc(s)
+    q = bits(d["q"])
+    bt = torch.from_numpy(d["block_table"]).to(dev)
+    sl = torch.from_numpy(d["seq_lens"]).to(dev)
+    nbytes = bd.gdn_spec_attn_scratch_bytes(desc, w.batch, w.rows, bt.shape[1])
+    stream = torch.cuda.current_stream()
+    M = 2
+    calls, keep = [], []
+    for _ in range(M):
+        kc, vc = bits(d["k_cache"]), bits(d["v_cache"])
+        scratch = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+        out = torch.empty_like(q)
+        err = torch.zeros(1, dtype=torch.int32, device=dev)
+        calls.append(bd.PreparedAttn(desc, q, kc, vc, bt, sl, scratch, out, err, stream))
+        keep.append(err)
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        calls[i % M]()
+    torch.cuda.synchronize()
+    if any(int(e.item()) for e in keep):
+        raise SystemExit("device error flags set")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        calls[i % M]()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # per-call durations: HIP events on the launch stream around each call
+    ev = []
+    for i in range(args.steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        calls[i % M]()
+        b.record(stream)
+        ev.append((a, b))
+    torch.cuda.synchronize()
+    tcall = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
+    nb = attention_bytes(w, d["seq_lens"])
+    rows = w.batch * w.rows
+    ach = nb / tcall / 1e9
+    line = {
+        "metric": ATTN_METRIC, "value": rows * args.steps / wall, "unit": "rows/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "rows": w.rows, "q_heads": s.num_q_heads,
+                   "kv_heads": s.num_kv_heads, "head_dim": s.head_dim, "page_size": s.page_size,
+                   "seq_len_mean": float(np.mean(d["seq_lens"])), "seq_len_range": [w.min_len, w.max_len],
+                   "rotating_copies": M},
+        "gbps": nb * args.steps / wall / 1e9, "hbm_frac": nb * args.steps / wall / 1e9 / HBM_PEAK_GBPS,
+        "kernels": {"attn_verify": {"avg_us": tcall * 1e6, "bytes": nb, "gbps": ach}},
+        "roofline": {"bound": "hbm", "kernel": "attn_verify (split + combine)", "achieved": ach,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS, "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = attention_cpu_baseline(w, d, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
 def run_stack(args, w):
     """A hybrid stack slice: every step verifies the batch through each of the
     w.layers GDN layers (one pool per layer) and then commits all layers, one
@@ -256,8 +375,10 @@ def main():
     from linear_attention_verify_amd import binding as bd
     from linear_attention_verify_amd import workloads as wl
 
-    w = wl.WORKLOADS[args.workload]
     torch.cuda.init()
+    if args.workload in wl.ATTN_WORKLOADS:
+        return run_attention(args, wl.ATTN_WORKLOADS[args.workload])
+    w = wl.WORKLOADS[args.workload]
     if w.layers != 1:
         return run_stack(args, w)
     if args.calibrate_copy:

@@ -2,25 +2,33 @@
 // MI355X (gfx950): the C ABI of include/spec_attention.h.
 //
 // The k+1 verify rows of a request and the Hq/Hkv query heads that share a
-// KV head form a block of R*G queries; every key and value of that KV head is
-// read once per block (lmdeploy PR #5006, What's included, Verification path:
-// verification attention over paged KV with a cross-workgroup reduce).
+// KV head form a block of R*G queries (at most 128: eight tiles of 16); every
+// key and value of that KV head is read from HBM once for the whole block
+// (lmdeploy PR #5006, What's included, Verification path: verification
+// attention over paged KV with a cross-workgroup reduce).
 //
-// Split kernel: one workgroup per (request, KV head, key split, group of 4
-// query tiles); wave w takes 16 queries. Splits are long enough for about
-// 2048 workgroups per launch, in multiples of 256 positions. Per tile of 32
-// keys:
-//   S^T = K Q^T on v_mfma_f32_16x16x32_bf16: the key rows are the A operand
-//   (16 bytes of one key per lane, straight from the page), the wave's
-//   queries the B operand (held in registers). Lane (kg, n) ends with the
-//   scores of keys 4kg..4kg+3 (and 16 + the same) for query n.
-//   Online softmax per query: the max and sum over a query's 32 keys are
-//   within the lane and across lanes n, n^16, n^32, n^48.
-//   O += P V on the same instruction: the lane's 8 probabilities, in that key
-//   order, are exactly its A operand; V is the B operand, read from a
-//   transposed copy of the tile in LDS whose key order matches.
-// Combine kernel: per (request, KV head) the splits' partial results merge
-// with their running maxima into o.
+// Split kernel. The batch's key tiles (32 positions, inside one page) are
+// laid end to end over all (request, KV head) pairs and cut into equal
+// ranges, one per workgroup of a fixed grid, so every workgroup streams the
+// same number of bytes whatever the mix of sequence lengths. A workgroup
+// walks the pairs its range touches; for each piece it keeps one wave per
+// query tile (16 queries) and stages each key tile through LDS once:
+//   K rows in their cache layout, read as the A operand of
+//     S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (the queries, held in
+//     registers, are the B operand). Lane (kg, n) ends with the scores of
+//     keys 4kg..4kg+3 and 16+4kg..16+4kg+3 for query n.
+//   online softmax per query: its 32 scores sit in lanes n, n^16, n^32, n^48.
+//   O += P V on the same instruction: the lane's 8 probabilities are its A
+//     operand as they stand; the V operand (8 keys of one head-dim column)
+//     comes from V rows in LDS through ds_read_b64_tr_b16, whose 16-lane
+//     transpose hands lane n the column it needs, so V is never rearranged.
+// Tiles are double-buffered: the next tile's loads are in flight while the
+// current one is consumed, one workgroup barrier per tile.
+// Each piece leaves a partial result (its running max, sum and unnormalised
+// output per query) in a record; cutting at both range and pair boundaries
+// numbers the records range + pair, so no index table is needed.
+// Combine kernel. Per (pair, query tile) the pair's records merge, weighted
+// by their running maxima, into o.
 
 #include <hip/hip_runtime.h>
 
@@ -33,14 +41,32 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreadsA = 256;   // 4 waves, one query tile each
-constexpr int kTilesPerGroup = 4;
-constexpr int kKeyTile = 32;
-constexpr int kSplitUnit = 256;  // split lengths are multiples of this
-constexpr int kTargetGroups = 2048;  // workgroups a launch aims for
+constexpr int kKeyTile = 32;      // positions per tile; page sizes are multiples of it
 constexpr int kMaxRowsA = 9;
+constexpr int kMaxQTiles = 8;     // at most 128 queries per KV head
+constexpr int kSplitGroups = 256; // split-kernel workgroups on a large batch: one per compute unit
+constexpr int kThreadsS = 512;    // split kernel: eight waves, one per query tile, all loading tiles
 constexpr float kNeg = -1.0e30f;  // masked score: finite, so a fully masked row stays NaN-free
+
+// LDS tile geometry. K rows keep 16-byte alignment for the A-operand reads,
+// padded so the 16 rows a read instruction touches fall in distinct banks;
+// V rows are padded by 8 bytes, which spreads the transposing reads (16
+// keys x 4 column groups per instruction) evenly over the banks.
+template <int D> struct Tile {
+    static constexpr int KS = D * 2 + 16;                // K row stride, bytes
+    static constexpr int VS = D * 2 + 8;                 // V row stride, bytes
+    static constexpr int KB = kKeyTile * KS;
+    static constexpr int VB = kKeyTile * VS;
+    static constexpr int BUF = KB + VB;                  // one K + V tile
+    static constexpr int UPR = D / 8;                    // 16-byte units per row
+    static constexpr int UNITS = 2 * kKeyTile * UPR;     // units of a K + V tile
+    static constexpr int NU = UNITS / kThreadsS;         // units per thread
+    static constexpr int PD = D == 256 ? 3 : 4;          // tiles whose loads are in flight
+    static_assert(UNITS % kThreadsS == 0, "tile units spread evenly");
+    static_assert(KB % 16 == 0 && BUF % 16 == 0, "tile buffers stay 16-byte aligned");
+};
 
 struct AttnParams {
     const uint16_t *q;
@@ -48,13 +74,10 @@ struct AttnParams {
     const uint16_t *vc;
     const int32_t *bt;
     const int32_t *seq;
-    float *opart;     // [B*Hkv][S][QG*64][D]
-    float *mpart;     // [B*Hkv][S][QG*64]
-    float *lpart;     // [B*Hkv][S][QG*64]
-    int32_t *flags;   // [B*Hkv][S][QG]: a page id was out of range
+    float *rec;       // records: [NW + B*Hkv][RECF] (O [QP][D], m [QP], l [QP], flag)
     uint16_t *out;
     int32_t *err;
-    int B, R, Hq, Hkv, G, PS, NP, MB, S, QG, KC;   // KC: positions per split
+    int B, R, Hq, Hkv, G, PS, NP, MB, NQ, QT, NW, RECF;
     float scale;
 };
 
@@ -67,231 +90,413 @@ __device__ __forceinline__ uint16_t bf16_bits(float v)
     return (uint16_t)(u >> 16);
 }
 
+// Lengths and block-table entries are read-only for the whole launch: read
+// through the constant address space, a uniform index becomes a scalar load,
+// whose wait does not hold back the tile loads in flight.
+typedef const __attribute__((address_space(4))) int32_t cint32;
+
+__device__ __forceinline__ int seq_len(int b, const AttnParams &p) { return ((cint32 *)p.seq)[b]; }
+
+__device__ __forceinline__ int table_entry(size_t i, const AttnParams &p) { return ((cint32 *)p.bt)[i]; }
+
 __device__ __forceinline__ bool request_refused(int L, const AttnParams &p)
 {
     return L < 0 || (L != 0 && (L < p.R || L > p.MB * p.PS));
 }
 
-// LDS position of key k (0..31) of a tile: keys 4c..4c+3 and 16+4c..16+4c+3
-// sit together at 8c..8c+7, the order in which lane group c holds their
-// probabilities.
-__device__ __forceinline__ int key_slot(int k)
+// Key tiles of pair pr = (request pr / Hkv, KV head pr % Hkv); padding and
+// refused requests have none.
+__device__ __forceinline__ int pair_tiles(int pr, const AttnParams &p)
 {
-    return 8 * ((k & 15) >> 2) + 4 * (k >> 4) + (k & 3);
+    const int L = seq_len(pr / p.Hkv, p);
+    return (L <= 0 || request_refused(L, p)) ? 0 : (L + kKeyTile - 1) / kKeyTile;
+}
+
+// Inclusive prefix sum over the workgroup (blockDim.x a multiple of 64, at
+// most 512); `total` gets the sum over all threads.
+__device__ int block_scan(int x, int *wsum, int &total)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o)
+            x += y;
+    }
+    if (lane == 63)
+        wsum[wave] = x;
+    __syncthreads();
+    int before = 0;
+    total = 0;
+    for (int i = 0; i < nw; ++i) {
+        const int v = wsum[i];
+        before += i < wave ? v : 0;
+        total += v;
+    }
+    __syncthreads();
+    return x + before;
+}
+
+// Total key tiles T of the batch, and the tiles before pair `want`; or, if
+// want < 0, the pair holding tile lo = w ceil(T / NW), the first of range w,
+// and the tiles before it (pair -1 when the range is empty).
+struct Located {
+    int T, pair, start;
+};
+
+__device__ Located locate(const AttnParams &p, int want, int w, int *wsum, int *loc)
+{
+    const int np = p.B * p.Hkv;
+    const int tid = threadIdx.x, nthr = blockDim.x;
+    int T = 0;
+    for (int c0 = 0; c0 < np; c0 += nthr) {
+        const int x = c0 + tid < np ? pair_tiles(c0 + tid, p) : 0;
+        int tot;
+        block_scan(x, wsum, tot);
+        T += tot;
+    }
+    const int lo = want >= 0 ? 0 : w * ((T + p.NW - 1) / p.NW);
+    T = __builtin_amdgcn_readfirstlane(T);
+    Located r{T, -1, 0};
+    if (want >= 0 ? want >= np : lo >= T)
+        return r;
+    if (tid == 0)
+        loc[0] = -1;
+    __syncthreads();
+    int base = 0;
+    for (int c0 = 0; c0 < np; c0 += nthr) {
+        const int pr = c0 + tid;
+        const int x = pr < np ? pair_tiles(pr, p) : 0;
+        int tot;
+        const int incl = block_scan(x, wsum, tot) + base;
+        const bool hit = want >= 0 ? pr == want : (x > 0 && incl > lo && incl - x <= lo);
+        if (pr < np && hit) {
+            loc[0] = pr;
+            loc[1] = incl - x;
+        }
+        base += tot;
+        __syncthreads();
+        if (loc[0] >= 0)
+            break;
+    }
+    // the same for every thread: kept in scalar registers, so the loads that
+    // depend on it (lengths, block-table entries) are scalar loads
+    r.pair = __builtin_amdgcn_readfirstlane(loc[0]);
+    r.start = __builtin_amdgcn_readfirstlane(loc[1]);
+    __syncthreads();
+    return r;
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreadsA) __attribute__((amdgpu_waves_per_eu(2))) void gdn_attn_split_kernel(const AttnParams p)
+__device__ __forceinline__ void load_tile(const AttnParams &p, int b, int g, int L, int i, uint4 (&pre)[Tile<D>::NU],
+                                          int &bad)
 {
-    constexpr int DS = D / 32;   // K-steps of Q K^T
-    constexpr int DT = D / 16;   // output tiles of P V
-    constexpr int NVU = kKeyTile * D / 8 / kThreadsA;   // 16-byte V units per thread per tile
-    static_assert(NVU * kThreadsA * 8 == kKeyTile * D, "V tile splits evenly");
-
-    __shared__ __align__(16) uint16_t vt[D * kKeyTile];   // [d][slot]: V^T of the tile
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int kg = lane >> 4, n = lane & 15;
-    const int qg = blockIdx.x % p.QG;
-    const int rest = blockIdx.x / p.QG;
-    const int s = rest % p.S;
-    const int bg = rest / p.S;
-    const int g = bg % p.Hkv, b = bg / p.Hkv;
-    const int L = p.seq[b];
-    const int k0 = s * p.KC;
-
-    if (request_refused(L, p) || L == 0 || k0 >= L) {
-        if (request_refused(L, p) && s == 0 && qg == 0 && tid == 0 && p.err)
-            atomicOr(p.err, 4);
-        return;   // the combine counts the splits that ran from seq_len alone
+    using TL = Tile<D>;
+    const int p0 = i * kKeyTile;   // a multiple of 32: the tile lies in one page
+    int page = table_entry((size_t)b * p.MB + p0 / p.PS, p);
+    if (page < 0 || page >= p.NP) {
+        bad = 1;
+        page = 0;
     }
-    const int k1 = min(k0 + p.KC, L);
-    const int ntile = (k1 - k0 + kKeyTile - 1) / kKeyTile;
+    const size_t row0 = (size_t)page * p.PS + p0 % p.PS;
+#pragma unroll
+    for (int k = 0; k < TL::NU; ++k) {
+        const int u = threadIdx.x + k * kThreadsS;
+        {
+            const int isv = u >= TL::UNITS / 2;
+            const int rem = u - isv * (TL::UNITS / 2);
+            const int key = rem / TL::UPR, du = rem % TL::UPR;
+            const uint16_t *src = (isv ? p.vc : p.kc) + ((row0 + key) * p.Hkv + g) * D + 8 * du;
+            pre[k] = *reinterpret_cast<const uint4 *>(src);
+        }
+    }
+}
 
-    // this wave's queries: column n of query tile 4 qg + wave
-    const int nq = p.R * p.G;
-    const int qi = 16 * (kTilesPerGroup * qg + wave) + n;
-    const bool qok = qi < nq;
-    const bool active = 16 * (kTilesPerGroup * qg + wave) < nq;   // wave has any query
-    const int qc = qok ? qi : 0;
-    const int t = qc / p.G, h = g * p.G + qc % p.G;
-    const int last = qok ? L - p.R + t : -1;   // the last position this query sees
+// Keys past the sequence are stored as zeros: their slots may hold anything,
+// and 0 * NaN would reach o through P V. (Applied here, not at the load, so
+// that nothing waits for the loads before the tile is needed.)
+template <int D>
+__device__ __forceinline__ void store_tile(char *buf, const uint4 (&pre)[Tile<D>::NU], int p0, int L)
+{
+    using TL = Tile<D>;
+#pragma unroll
+    for (int k = 0; k < TL::NU; ++k) {
+        const int u = threadIdx.x + k * kThreadsS;
+        {
+            const int isv = u >= TL::UNITS / 2;
+            const int rem = u - isv * (TL::UNITS / 2);
+            const int key = rem / TL::UPR, du = rem % TL::UPR;
+            const uint4 val = p0 + key < L ? pre[k] : uint4{0u, 0u, 0u, 0u};
+            if (!isv) {
+                *reinterpret_cast<uint4 *>(buf + key * TL::KS + 16 * du) = val;
+            } else {
+                uint2 *dst = reinterpret_cast<uint2 *>(buf + TL::KB + key * TL::VS + 16 * du);
+                dst[0] = uint2{val.x, val.y};
+                dst[1] = uint2{val.z, val.w};
+            }
+        }
+    }
+}
 
-    bf16x8 qv[DS];
-    {
-        const uint16_t *qrow = p.q + (((size_t)b * p.R + t) * p.Hq + h) * D + 8 * kg;
+// One key tile against this wave's 16 queries: scores, online softmax, and
+// the tile's P V added into o. `buf` holds the tile's K and V rows, `p0` is
+// its first position, `last` the last position the lane's query n sees.
+template <int D>
+__device__ __forceinline__ void attend(const char *buf, int p0, int last, float scale, int kg, int n,
+                                       const bf16x8 (&qv)[D / 32], f32x4 (&o)[D / 16], float &mrun, float &lrun)
+{
+    using TL = Tile<D>;
+    constexpr int DS = D / 32;
+    constexpr int DT = D / 16;
+    f32x4 sacc[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+        sacc[st] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        const char *krow = buf + (16 * st + n) * TL::KS + 16 * kg;
 #pragma unroll
         for (int ks = 0; ks < DS; ++ks)
-            qv[ks] = *reinterpret_cast<const bf16x8 *>(qrow + 32 * ks);
+            sacc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8 *>(krow + 64 * ks),
+                                                               qv[ks], sacc[st], 0, 0, 0);
     }
-    f32x4 o[DT];
+    // lane (kg, n): sacc[st][v] is the score of position p0 + 16 st + 4 kg + v, query n
+    float sv[8];
+    float tmax = kNeg;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-        o[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    float mrun = kNeg, lrun = 0.0f;
-    int badpage = 0;
-
-    for (int it = 0; it < ntile; ++it) {
-        const int p0 = k0 + it * kKeyTile;   // a multiple of 32: the tile lies in one page
-        int page = p.bt[(size_t)b * p.MB + p0 / p.PS];
-        if (page < 0 || page >= p.NP) {
-            badpage = 1;
-            page = 0;
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int pos = p0 + 16 * st + 4 * kg + v;
+            const float x = pos <= last ? sacc[st][v] * scale : kNeg;
+            sv[4 * st + v] = x;
+            tmax = fmaxf(tmax, x);
         }
-        const size_t row0 = (size_t)page * p.PS + p0 % p.PS;   // cache row of position p0
-
-        // V units of the tile, loaded first so they arrive under Q K^T
-        uint4 vu[NVU];
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float mnew = fmaxf(mrun, tmax);
+    const float alpha = __expf(mrun - mnew);
+    float psum = 0.0f;
+    bf16x8 pa;
 #pragma unroll
-        for (int i = 0; i < NVU; ++i) {
-            const int u = i * kThreadsA + tid;
-            const int k = u % kKeyTile, d0 = 8 * (u / kKeyTile);
-            vu[i] = *reinterpret_cast<const uint4 *>(p.vc + ((row0 + k) * p.Hkv + g) * D + d0);
-        }
-
-        float pv[8];
-        if (active) {
-            f32x4 sacc[2];
-#pragma unroll
-            for (int st = 0; st < 2; ++st) {
-                sacc[st] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-                const uint16_t *krow = p.kc + ((row0 + 16 * st + n) * p.Hkv + g) * D + 8 * kg;
-#pragma unroll
-                for (int ks = 0; ks < DS; ++ks)
-                    sacc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        *reinterpret_cast<const bf16x8 *>(krow + 32 * ks), qv[ks], sacc[st], 0, 0, 0);
-            }
-            // lane (kg, n): sacc[st][v] is the score of position p0 + 16 st + 4 kg + v, query n
-            float sv[8];
-            float tmax = kNeg;
-#pragma unroll
-            for (int st = 0; st < 2; ++st)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int pos = p0 + 16 * st + 4 * kg + v;
-                    const float x = pos <= last ? sacc[st][v] * p.scale : kNeg;
-                    sv[4 * st + v] = x;
-                    tmax = fmaxf(tmax, x);
-                }
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-            const float mnew = fmaxf(mrun, tmax);
-            const float alpha = __expf(mrun - mnew);
-            float psum = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                pv[i] = __expf(sv[i] - mnew);
-                psum += pv[i];
-            }
-            psum += __shfl_xor(psum, 16, 64);
-            psum += __shfl_xor(psum, 32, 64);
-            lrun = lrun * alpha + psum;
-            mrun = mnew;
-            // o[dt][v] belongs to query 4 kg + v, whose factor lane 4 kg + v holds
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const float a = __shfl(alpha, 4 * kg + v, 64);
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt)
-                    o[dt][v] *= a;
-            }
-        }
-
-        __syncthreads();   // the previous tile's V is no longer read
-#pragma unroll
-        for (int i = 0; i < NVU; ++i) {
-            const int u = i * kThreadsA + tid;
-            const int k = u % kKeyTile, d0 = 8 * (u / kKeyTile);
-            const int slot = key_slot(k);
-            const uint32_t w[4] = {vu[i].x, vu[i].y, vu[i].z, vu[i].w};
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                vt[(d0 + j) * kKeyTile + slot] = (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
-        }
-        __syncthreads();
-
-        if (active) {
-            bf16x8 pa;
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                pa[i] = __builtin_bit_cast(__bf16, bf16_bits(pv[i]));
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const bf16x8 vb = *reinterpret_cast<const bf16x8 *>(&vt[(16 * dt + n) * kKeyTile + 8 * kg]);
-                o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[dt], 0, 0, 0);
-            }
-        }
+    for (int j = 0; j < 8; ++j) {
+        const float pj = __expf(sv[j] - mnew);
+        psum += pj;
+        pa[j] = __builtin_bit_cast(__bf16, bf16_bits(pj));
     }
-
-    // partial results: lane (kg, n) holds o of queries 4 kg + v, dims 16 dt + n
-    const int QP = p.QG * 64;
-    const size_t part = (size_t)bg * p.S + s;
-    if (active) {
-        const int qbase = 16 * (kTilesPerGroup * qg + wave);
-        float *op = p.opart + (part * QP + qbase) * D;
+    psum += __shfl_xor(psum, 16, 64);
+    psum += __shfl_xor(psum, 32, 64);
+    lrun = lrun * alpha + psum;
+    mrun = mnew;
+    // o[dt][v] belongs to query 4 kg + v, whose factor lane 4 kg + v holds
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const float f = __shfl(alpha, 4 * kg + v, 64);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-                op[(size_t)(4 * kg + v) * D + 16 * dt + n] = o[dt][v];
-        if (kg == 0) {
-            p.mpart[part * QP + qbase + n] = mrun;
-            p.lpart[part * QP + qbase + n] = lrun;
-        }
+            o[dt][v] *= f;
     }
-    if (tid == 0)
-        p.flags[part * p.QG + qg] = badpage;
+    // V operand of column tile dt: lane r of group kg names a row (key
+    // 4 kg + r/4, columns 16 dt + 4 (r%4) ..) and the transpose gives lane n
+    // keys 4 kg .. 4 kg + 3 of column 16 dt + n; the second read does keys
+    // 16 + 4 kg ..: the key order of the probabilities in pa
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const char *vrow = buf + TL::KB + (4 * kg + (n >> 2)) * TL::VS + 8 * (n & 3);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+        const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vrow + 32 * dt));
+        const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vrow + 16 * TL::VS + 32 * dt));
+        const bf16x8 vb = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[dt], 0, 0, 0);
+    }
 }
 
-// One workgroup per (request, KV head): o = sum_s e^{m_s - M} O_s / sum_s e^{m_s - M} l_s.
 template <int D>
-__global__ __launch_bounds__(kThreadsA) void gdn_attn_combine_kernel(const AttnParams p)
+__global__ __launch_bounds__(kThreadsS) __attribute__((amdgpu_waves_per_eu(2))) void gdn_attn_split_kernel(const AttnParams p)
 {
-    const int bg = blockIdx.x;
-    const int g = bg % p.Hkv, b = bg / p.Hkv;
-    const int L = p.seq[b];
-    const int nq = p.R * p.G;
-    const int QP = p.QG * 64;
-    bool zero = L == 0 || request_refused(L, p);
-    const int ns = zero ? 0 : (L + p.KC - 1) / p.KC;
+    using TL = Tile<D>;
+    constexpr int DS = D / 32;   // K-steps of Q K^T
+    constexpr int DT = D / 16;   // output column tiles of P V
+
+    __shared__ __align__(16) char smem[2 * TL::BUF];
+    __shared__ int wsum[8];
+    __shared__ int loc[2];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kg = lane >> 4, n = lane & 15;
+    const int np = p.B * p.Hkv;
+    const int w = blockIdx.x;
+
+    // this workgroup's range of the batch's key tiles, and the pair it starts in
+    const Located first = locate(p, -1, w, wsum, loc);
+    if (first.pair < 0)
+        return;
+    const int total = first.T;
+    const int per = (total + p.NW - 1) / p.NW;
+    const int lo = w * per;
+    const int hi = min(total, lo + per);
+
+    const bool computes = wave < p.QT;   // one wave per query tile; the others only load
+    int pr = first.pair, S = first.start;
+    while (S < hi && pr < np) {
+        const int nt = pair_tiles(pr, p);
+        const int a = max(lo, S) - S, e = min(hi, S + nt) - S;   // this piece: tiles a .. e-1 of the pair
+        if (a < e) {
+            const int b = pr / p.Hkv, g = pr % p.Hkv;
+            const int L = seq_len(b, p);
+            // this wave's queries: query qi = 16 wave + n is verify row qi / G of
+            // query head g G + qi % G, which sees positions 0 .. L - R + row
+            const int qi = 16 * wave + n;
+            const bool qok = computes && qi < p.NQ;
+            const int qc = qok ? qi : 0;
+            const int t = qc / p.G, h = g * p.G + qc % p.G;
+            const int last = qok ? L - p.R + t : -1;
+            bf16x8 qv[DS];
+            {
+                const uint16_t *qrow = p.q + (((size_t)b * p.R + t) * p.Hq + h) * D + 8 * kg;
+#pragma unroll
+                for (int ks = 0; ks < DS; ++ks)
+                    qv[ks] = *reinterpret_cast<const bf16x8 *>(qrow + 32 * ks);
+            }
+            f32x4 o[DT];
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+                o[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            float mrun = kNeg, lrun = 0.0f;
+            int bad = 0;
+
+            // Tile j of the piece (tile a + j of the pair) is consumed from LDS
+            // buffer j & 1. Its loads went out PD tiles earlier, into register
+            // set j % PD, which is stored to its buffer one tile ahead. Every
+            // step issues the same loads and stores whatever the piece's
+            // length (tile indices past the piece are clamped to its last
+            // tile, and the steps past its end skip only the arithmetic), so
+            // each wait for a register set covers just that set's loads.
+            const int ntp = e - a;
+            const int nsteps = (ntp + TL::PD - 1) / TL::PD * TL::PD;
+            auto tile_at = [&](int j) { return a + min(j, ntp - 1); };
+            uint4 pre[TL::PD][TL::NU];
+#pragma unroll
+            for (int s = 0; s < TL::PD; ++s)
+                load_tile<D>(p, b, g, L, tile_at(s), pre[s], bad);
+            store_tile<D>(smem, pre[0], a * kKeyTile, L);
+            __syncthreads();
+            for (int j0 = 0; j0 < nsteps; j0 += TL::PD) {
+#pragma unroll
+                for (int s = 0; s < TL::PD; ++s) {
+                    const int j = j0 + s;
+                    load_tile<D>(p, b, g, L, tile_at(j + TL::PD), pre[s], bad);
+                    if (computes && j < ntp)
+                        attend<D>(smem + (j & 1) * TL::BUF, (a + j) * kKeyTile, last, p.scale, kg, n, qv, o, mrun,
+                                  lrun);
+                    store_tile<D>(smem + ((j + 1) & 1) * TL::BUF, pre[(s + 1) % TL::PD], tile_at(j + 1) * kKeyTile, L);
+                    __syncthreads();
+                }
+            }
+
+            // the piece's record: lane (kg, n) holds o of queries 16 wave + 4 kg + v, columns 16 dt + n
+            float *rec = p.rec + (size_t)(w + pr) * p.RECF;
+            const int QP = p.QT * 16;
+            if (computes) {
+                const int qb = 16 * wave;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        rec[(size_t)(qb + 4 * kg + v) * D + 16 * dt + n] = o[dt][v];
+                if (kg == 0) {
+                    rec[(size_t)QP * D + qb + n] = mrun;
+                    rec[(size_t)QP * D + QP + qb + n] = lrun;
+                }
+            }
+            const int anybad = __syncthreads_or(bad);
+            if (tid == 0)
+                rec[(size_t)QP * (D + 2)] = anybad ? 1.0f : 0.0f;
+        }
+        S += nt;
+        ++pr;
+    }
+}
+
+// One workgroup per (pair, query tile): o = sum_r e^{m_r - M} O_r / sum_r e^{m_r - M} l_r
+// over the pair's records r. The per-query maxima and sums come first; then
+// each thread takes one output column for 16 / (256 / D) queries, whose loads
+// from every record are independent of each other.
+template <int D>
+__global__ __launch_bounds__(256) void gdn_attn_combine_kernel(const AttnParams p)
+{
+    constexpr int QG = 16 / (256 / D);   // queries per thread
+    __shared__ int wsum[8];
+    __shared__ int loc[2];
+    __shared__ float Ms[16], Ls[16];
+    const int tid = threadIdx.x;
+    const int pr = blockIdx.x, qt = blockIdx.y;
+    const int b = pr / p.Hkv, g = pr % p.Hkv;
+    const int L = seq_len(b, p);
+    const int QP = p.QT * 16;
+
+    const Located at = locate(p, pr, 0, wsum, loc);
+    const int nt = pair_tiles(pr, p);
+    bool zero = nt == 0;
+    if (request_refused(L, p) && g == 0 && qt == 0 && tid == 0 && p.err)
+        atomicOr(p.err, 4);
+    int w0 = 0, w1 = -1;
     if (!zero) {
-        int bad = 0;
-        for (int i = 0; i < ns * p.QG; ++i)
-            bad |= p.flags[(size_t)bg * p.S * p.QG + i];
+        const int per = (at.T + p.NW - 1) / p.NW;
+        w0 = at.start / per;
+        w1 = (at.start + nt - 1) / per;
+        bool bad = false;
+        for (int w = w0; w <= w1; ++w)
+            bad |= p.rec[(size_t)(w + pr) * p.RECF + (size_t)QP * (D + 2)] != 0.0f;
         if (bad) {
             zero = true;
-            if (threadIdx.x == 0 && p.err)
+            if (g == 0 && qt == 0 && tid == 0 && p.err)
                 atomicOr(p.err, 1);
         }
     }
-    for (int idx = threadIdx.x; idx < nq * D; idx += kThreadsA) {
-        const int qi = idx / D, d = idx % D;
-        const int t = qi / p.G, h = g * p.G + qi % p.G;
-        float r = 0.0f;
-        if (!zero) {
-            float M = kNeg;
-            for (int s = 0; s < ns; ++s)
-                M = fmaxf(M, p.mpart[((size_t)bg * p.S + s) * QP + qi]);
-            float num = 0.0f, den = 0.0f;
-            for (int s = 0; s < ns; ++s) {
-                const size_t part = (size_t)bg * p.S + s;
-                const float w = __expf(p.mpart[part * QP + qi] - M);
-                num += w * p.opart[(part * QP + qi) * D + d];
-                den += w * p.lpart[part * QP + qi];
-            }
-            r = num / den;
+    if (!zero && tid < 16) {
+        const int qi = 16 * qt + tid;
+        float M = kNeg;
+        for (int w = w0; w <= w1; ++w)
+            M = fmaxf(M, p.rec[(size_t)(w + pr) * p.RECF + (size_t)QP * D + qi]);
+        float den = 0.0f;
+        for (int w = w0; w <= w1; ++w) {
+            const float *rec = p.rec + (size_t)(w + pr) * p.RECF + (size_t)QP * D;
+            den += __expf(rec[qi] - M) * rec[QP + qi];
         }
-        p.out[(((size_t)b * p.R + t) * p.Hq + h) * D + d] = bf16_bits(r);
+        Ms[tid] = M;
+        Ls[tid] = 1.0f / den;
+    }
+    __syncthreads();
+    const int d = tid % D, q0 = (tid / D) * QG;
+    float acc[QG];
+#pragma unroll
+    for (int k = 0; k < QG; ++k)
+        acc[k] = 0.0f;
+    if (!zero) {
+        for (int w = w0; w <= w1; ++w) {
+            const float *rec = p.rec + (size_t)(w + pr) * p.RECF;
+#pragma unroll
+            for (int k = 0; k < QG; ++k) {
+                const int qi = 16 * qt + q0 + k;
+                acc[k] += __expf(rec[(size_t)QP * D + qi] - Ms[q0 + k]) * rec[(size_t)qi * D + d];
+            }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < QG; ++k) {
+        const int qi = 16 * qt + q0 + k;
+        if (qi < p.NQ) {
+            const int t = qi / p.G, h = g * p.G + qi % p.G;
+            p.out[(((size_t)b * p.R + t) * p.Hq + h) * D + d] = bf16_bits(zero ? 0.0f : acc[k] * Ls[q0 + k]);
+        }
     }
 }
 
 struct AttnLayout {
-    size_t opart, mpart, lpart, flags, total;
-    int S, QG, KC;
+    size_t total;
+    int QT, NW, RECF;
 };
-
-size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
 gdn_status attn_layout(const gdn_attn_desc *d, int batch, int rows, int max_blocks, AttnLayout *l)
 {
@@ -301,33 +506,21 @@ gdn_status attn_layout(const gdn_attn_desc *d, int batch, int rows, int max_bloc
         d->page_size < 1)
         return GDN_ERR_INVALID_ARG;
     if ((d->head_dim != 128 && d->head_dim != 256) || d->page_size % kKeyTile != 0 ||
-        (d->num_q_heads / d->num_kv_heads) * rows > 128)
+        (d->num_q_heads / d->num_kv_heads) * rows > 16 * kMaxQTiles)
         return GDN_ERR_UNSUPPORTED;
     const size_t maxpos = (size_t)max_blocks * d->page_size;
     if (maxpos > (size_t)1 << 30)
         return GDN_ERR_UNSUPPORTED;
+    // every tile index of the batch fits an int
+    const size_t pairs = (size_t)batch * d->num_kv_heads;
+    const size_t max_tiles = pairs * ((maxpos + kKeyTile - 1) / kKeyTile);
+    if (max_tiles > 0x7fffffffu || pairs > 0x7fffffffu)
+        return GDN_ERR_UNSUPPORTED;
     const int nq = (d->num_q_heads / d->num_kv_heads) * rows;
-    l->QG = (nq + 16 * kTilesPerGroup - 1) / (16 * kTilesPerGroup);
-    // enough splits to fill the chip, in whole units: long splits for a
-    // large batch keep the partial results small
-    const size_t units = (maxpos + kSplitUnit - 1) / kSplitUnit;
-    const size_t per_split_groups = (size_t)(batch > 0 ? batch : 1) * d->num_kv_heads * l->QG;
-    size_t want = (kTargetGroups + per_split_groups - 1) / per_split_groups;
-    want = want < 1 ? 1 : (want > units ? units : want);
-    l->KC = (int)((units + want - 1) / want) * kSplitUnit;
-    l->S = (int)((maxpos + l->KC - 1) / l->KC);
-    const size_t parts = (size_t)batch * d->num_kv_heads * l->S;
-    const size_t QP = (size_t)l->QG * 64;
-    size_t off = 0;
-    l->opart = off;
-    off = align256(off + parts * QP * d->head_dim * sizeof(float));
-    l->mpart = off;
-    off = align256(off + parts * QP * sizeof(float));
-    l->lpart = off;
-    off = align256(off + parts * QP * sizeof(float));
-    l->flags = off;
-    off = align256(off + parts * l->QG * sizeof(int32_t));
-    l->total = off;
+    l->QT = (nq + 15) / 16;
+    l->NW = (int)(max_tiles < (size_t)kSplitGroups ? (max_tiles > 0 ? max_tiles : 1) : kSplitGroups);
+    l->RECF = l->QT * 16 * (d->head_dim + 2) + 4;
+    l->total = ((size_t)l->NW + pairs) * (size_t)l->RECF * sizeof(float);
     return GDN_OK;
 }
 
@@ -367,19 +560,13 @@ gdn_status gdn_spec_attn_verify(const gdn_attn_desc *desc, const void *q, const 
         return GDN_ERR_INVALID_ARG;
     if (scratch_bytes < l.total)
         return GDN_ERR_SCRATCH_TOO_SMALL;
-    if ((size_t)batch * desc->num_kv_heads * l.S * l.QG > 0x7fffffffu)
-        return GDN_ERR_UNSUPPORTED;
-    char *base = static_cast<char *>(scratch);
     AttnParams p;
     p.q = static_cast<const uint16_t *>(q);
     p.kc = static_cast<const uint16_t *>(k_cache);
     p.vc = static_cast<const uint16_t *>(v_cache);
     p.bt = block_table;
     p.seq = seq_lens;
-    p.opart = reinterpret_cast<float *>(base + l.opart);
-    p.mpart = reinterpret_cast<float *>(base + l.mpart);
-    p.lpart = reinterpret_cast<float *>(base + l.lpart);
-    p.flags = reinterpret_cast<int32_t *>(base + l.flags);
+    p.rec = static_cast<float *>(scratch);
     p.out = static_cast<uint16_t *>(out);
     p.err = err_flag;
     p.B = batch;
@@ -390,19 +577,20 @@ gdn_status gdn_spec_attn_verify(const gdn_attn_desc *desc, const void *q, const 
     p.PS = desc->page_size;
     p.NP = num_pages;
     p.MB = max_blocks;
-    p.S = l.S;
-    p.QG = l.QG;
-    p.KC = l.KC;
+    p.NQ = p.G * rows;
+    p.QT = l.QT;
+    p.NW = l.NW;
+    p.RECF = l.RECF;
     p.scale = desc->scale;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const dim3 split_grid((unsigned)(batch * p.Hkv * l.S * l.QG));
-    const dim3 combine_grid((unsigned)(batch * p.Hkv));
+    const dim3 split_grid((unsigned)l.NW);
+    const dim3 combine_grid((unsigned)(batch * p.Hkv), (unsigned)l.QT);
     if (desc->head_dim == 128) {
-        hipLaunchKernelGGL(gdn_attn_split_kernel<128>, split_grid, dim3(kThreadsA), 0, st, p);
-        hipLaunchKernelGGL(gdn_attn_combine_kernel<128>, combine_grid, dim3(kThreadsA), 0, st, p);
+        hipLaunchKernelGGL(gdn_attn_split_kernel<128>, split_grid, dim3(kThreadsS), 0, st, p);
+        hipLaunchKernelGGL(gdn_attn_combine_kernel<128>, combine_grid, dim3(256), 0, st, p);
     } else {
-        hipLaunchKernelGGL(gdn_attn_split_kernel<256>, split_grid, dim3(kThreadsA), 0, st, p);
-        hipLaunchKernelGGL(gdn_attn_combine_kernel<256>, combine_grid, dim3(kThreadsA), 0, st, p);
+        hipLaunchKernelGGL(gdn_attn_split_kernel<256>, split_grid, dim3(kThreadsS), 0, st, p);
+        hipLaunchKernelGGL(gdn_attn_combine_kernel<256>, combine_grid, dim3(256), 0, st, p);
     }
     return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
