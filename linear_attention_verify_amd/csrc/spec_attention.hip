@@ -50,22 +50,21 @@ constexpr int kSplitGroups = 256; // split-kernel workgroups on a large batch: o
 constexpr int kThreadsS = 512;    // split kernel: eight waves, one per query tile, all loading tiles
 constexpr float kNeg = -1.0e30f;  // masked score: finite, so a fully masked row stays NaN-free
 
-// LDS tile geometry. K rows keep 16-byte alignment for the A-operand reads,
-// padded so the 16 rows a read instruction touches fall in distinct banks;
-// V rows are padded by 8 bytes, which spreads the transposing reads (16
-// keys x 4 column groups per instruction) evenly over the banks.
+// LDS tile geometry: K rows, then V rows, each 2D bytes with no padding.
+// The 16-byte units of row r are stored XOR-swizzled, unit c at position
+// c ^ (r & 15): the 16 rows one operand read touches (16 keys of K for the
+// A operand; 16 keys x 4 column groups of V for the transposing reads) then
+// fall on distinct banks, and every write of a row stays one contiguous run.
 template <int D> struct Tile {
-    static constexpr int KS = D * 2 + 16;                // K row stride, bytes
-    static constexpr int VS = D * 2 + 8;                 // V row stride, bytes
-    static constexpr int KB = kKeyTile * KS;
-    static constexpr int VB = kKeyTile * VS;
-    static constexpr int BUF = KB + VB;                  // one K + V tile
+    static constexpr int RS = D * 2;                     // row stride, bytes
+    static constexpr int KB = kKeyTile * RS;
+    static constexpr int BUF = 2 * KB;                   // one K + V tile
     static constexpr int UPR = D / 8;                    // 16-byte units per row
     static constexpr int UNITS = 2 * kKeyTile * UPR;     // units of a K + V tile
     static constexpr int NU = UNITS / kThreadsS;         // units per thread
     static constexpr int PD = D == 256 ? 3 : 4;          // tiles whose loads are in flight
     static_assert(UNITS % kThreadsS == 0, "tile units spread evenly");
-    static_assert(KB % 16 == 0 && BUF % 16 == 0, "tile buffers stay 16-byte aligned");
+    static_assert(D / 8 >= 16, "the swizzle permutes units within a row");
 };
 
 struct AttnParams {
@@ -199,43 +198,61 @@ __device__ __forceinline__ void load_tile(const AttnParams &p, int b, int g, int
         page = 0;
     }
     const size_t row0 = (size_t)page * p.PS + p0 % p.PS;
+    const uint16_t *kb = p.kc + (row0 * p.Hkv + g) * D, *vb = p.vc + (row0 * p.Hkv + g) * D;
 #pragma unroll
     for (int k = 0; k < TL::NU; ++k) {
-        const int u = threadIdx.x + k * kThreadsS;
-        {
-            const int isv = u >= TL::UNITS / 2;
-            const int rem = u - isv * (TL::UNITS / 2);
-            const int key = rem / TL::UPR, du = rem % TL::UPR;
-            const uint16_t *src = (isv ? p.vc : p.kc) + ((row0 + key) * p.Hkv + g) * D + 8 * du;
-            pre[k] = *reinterpret_cast<const uint4 *>(src);
-        }
+        const int u = threadIdx.x + k * kThreadsS;   // K units, then V units (a uniform split per k)
+        const int row = u / TL::UPR, du = u % TL::UPR;
+        const int key = row % kKeyTile;
+        const uint16_t *src = (row < kKeyTile ? kb : vb) + (size_t)key * p.Hkv * D + 8 * du;
+        pre[k] = *reinterpret_cast<const uint4 *>(src);
     }
 }
 
 // Keys past the sequence are stored as zeros: their slots may hold anything,
 // and 0 * NaN would reach o through P V. (Applied here, not at the load, so
-// that nothing waits for the loads before the tile is needed.)
+// that nothing waits for the loads before the tile is needed; only the tile
+// that holds position L - 1 can reach past it.)
 template <int D>
 __device__ __forceinline__ void store_tile(char *buf, const uint4 (&pre)[Tile<D>::NU], int p0, int L)
 {
     using TL = Tile<D>;
+    const bool tail = p0 + kKeyTile > L;
 #pragma unroll
     for (int k = 0; k < TL::NU; ++k) {
-        const int u = threadIdx.x + k * kThreadsS;
-        {
-            const int isv = u >= TL::UNITS / 2;
-            const int rem = u - isv * (TL::UNITS / 2);
-            const int key = rem / TL::UPR, du = rem % TL::UPR;
-            const uint4 val = p0 + key < L ? pre[k] : uint4{0u, 0u, 0u, 0u};
-            if (!isv) {
-                *reinterpret_cast<uint4 *>(buf + key * TL::KS + 16 * du) = val;
-            } else {
-                uint2 *dst = reinterpret_cast<uint2 *>(buf + TL::KB + key * TL::VS + 16 * du);
-                dst[0] = uint2{val.x, val.y};
-                dst[1] = uint2{val.z, val.w};
-            }
-        }
+        const int u = threadIdx.x + k * kThreadsS;   // K units, then V units
+        const int row = u / TL::UPR, du = u % TL::UPR;   // row: key (K) or 32 + key (V)
+        const int key = row % kKeyTile;
+        uint4 val = pre[k];
+        if (tail && p0 + key >= L)
+            val = uint4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<uint4 *>(buf + row * TL::RS + 16 * (du ^ (key & 15))) = val;
     }
+}
+
+// Reductions over the four lanes n, n^16, n^32, n^48 that hold one query's
+// scores. v_permlane16_swap / v_permlane32_swap (with the value as both
+// operands) leave x[l] and x[l^16] (or x[l^32]) in the two results, in lane
+// order, on every lane: no LDS round trip as a shuffle would take.
+__device__ __forceinline__ float max_xor16(float x)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // One key tile against this wave's 16 queries: scores, online softmax, and
@@ -252,11 +269,12 @@ __device__ __forceinline__ void attend(const char *buf, int p0, int last, float 
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
         sacc[st] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        const char *krow = buf + (16 * st + n) * TL::KS + 16 * kg;
+        // key 16 st + n, units 4 ks + kg (at position (4 ks + kg) ^ n)
+        const char *krow = buf + (16 * st + n) * TL::RS;
 #pragma unroll
         for (int ks = 0; ks < DS; ++ks)
-            sacc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8 *>(krow + 64 * ks),
-                                                               qv[ks], sacc[st], 0, 0, 0);
+            sacc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                *reinterpret_cast<const bf16x8 *>(krow + 16 * ((4 * ks + kg) ^ n)), qv[ks], sacc[st], 0, 0, 0);
     }
     // lane (kg, n): sacc[st][v] is the score of position p0 + 16 st + 4 kg + v, query n
     float sv[8];
@@ -270,8 +288,7 @@ __device__ __forceinline__ void attend(const char *buf, int p0, int last, float 
             sv[4 * st + v] = x;
             tmax = fmaxf(tmax, x);
         }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    tmax = max_xor32(max_xor16(tmax));
     const float mnew = fmaxf(mrun, tmax);
     const float alpha = __expf(mrun - mnew);
     float psum = 0.0f;
@@ -282,30 +299,35 @@ __device__ __forceinline__ void attend(const char *buf, int p0, int last, float 
         psum += pj;
         pa[j] = __builtin_bit_cast(__bf16, bf16_bits(pj));
     }
-    psum += __shfl_xor(psum, 16, 64);
-    psum += __shfl_xor(psum, 32, 64);
+    psum = sum_xor32(sum_xor16(psum));
     lrun = lrun * alpha + psum;
     mrun = mnew;
-    // o[dt][v] belongs to query 4 kg + v, whose factor lane 4 kg + v holds
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        const float f = __shfl(alpha, 4 * kg + v, 64);
+    // o holds O^T: o[dt][v] is column 16 dt + 4 kg + v of query n, this lane's
+    // own; once the maxima settle every factor is exactly 1 and the rescale
+    // is skipped
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
-            o[dt][v] *= f;
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                o[dt][v] *= alpha;
     }
-    // V operand of column tile dt: lane r of group kg names a row (key
-    // 4 kg + r/4, columns 16 dt + 4 (r%4) ..) and the transpose gives lane n
-    // keys 4 kg .. 4 kg + 3 of column 16 dt + n; the second read does keys
-    // 16 + 4 kg ..: the key order of the probabilities in pa
+    // O^T += V^T P^T. V operand (A) of column tile dt: lane r of group kg
+    // names a row (key 4 kg + r/4, columns 16 dt + 4 (r%4) ..) and the
+    // transpose gives lane n keys 4 kg .. 4 kg + 3 of column 16 dt + n; the
+    // second read does keys 16 + 4 kg ..: the key order of the probabilities
+    // in pa, which are the B operand as they stand
+    // (row 4 kg + r/4 has swizzle 4 kg + r/4; 16 rows further the same)
     typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-    const char *vrow = buf + TL::KB + (4 * kg + (n >> 2)) * TL::VS + 8 * (n & 3);
+    const int vr = 4 * kg + (n >> 2);
+    const char *vrow = buf + TL::KB + vr * TL::RS + 8 * (n & 1);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-        const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vrow + 32 * dt));
-        const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vrow + 16 * TL::VS + 32 * dt));
+        const int unit = (2 * dt + ((n >> 1) & 1)) ^ vr;
+        const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vrow + 16 * unit));
+        const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vrow + 16 * TL::RS + 16 * unit));
         const bf16x8 vb = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[dt], 0, 0, 0);
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, pa, o[dt], 0, 0, 0);
     }
 }
 
@@ -394,16 +416,14 @@ __global__ __launch_bounds__(kThreadsS) __attribute__((amdgpu_waves_per_eu(2))) 
                 }
             }
 
-            // the piece's record: lane (kg, n) holds o of queries 16 wave + 4 kg + v, columns 16 dt + n
+            // the piece's record: lane (kg, n) holds columns 16 dt + 4 kg .. + 3 of query 16 wave + n
             float *rec = p.rec + (size_t)(w + pr) * p.RECF;
             const int QP = p.QT * 16;
             if (computes) {
                 const int qb = 16 * wave;
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        rec[(size_t)(qb + 4 * kg + v) * D + 16 * dt + n] = o[dt][v];
+                    *reinterpret_cast<f32x4 *>(&rec[(size_t)(qb + n) * D + 16 * dt + 4 * kg]) = o[dt];
                 if (kg == 0) {
                     rec[(size_t)QP * D + qb + n] = mrun;
                     rec[(size_t)QP * D + QP + qb + n] = lrun;
