@@ -35,19 +35,22 @@ METRIC = "GDN verify+commit rows/s and achieved HBM GB/s (% of MI355X peak)"
 HBM_PEAK_GBPS = 8000.0
 COPY_BYTES = 256 << 20
 KERNEL_SOURCE = os.path.join(ROOT, "linear_attention_verify_amd", "csrc", "gdn_spec.hip")
+ATTN_SOURCE = os.path.join(ROOT, "linear_attention_verify_amd", "csrc", "spec_attention.hip")
 
 # HBM bytes per launch read from rocprofv3 counters: FETCH_SIZE and WRITE_SIZE
 # (KiB per dispatch, one run each) of every launch of the kernel, averaged,
 # each scaled by known bytes / counter bytes of a plain 256 MiB device copy
 # in the same run. They hold only for the kernel code they were taken on
-# (kernel_source_digest); for any other code the bench reports null.
-MEASURED_TRAFFIC = {
-    "source_sha256": "cfe77834bc0b797a5e25318790d866a8ea05da229ec7c65f7607b5349cbf3c75",
-    "bytes": {   # (workload, mode, kernel) -> bytes per launch
-        ("saturated-b64", "replay", "verify"): 176115945,
-        ("saturated-b64", "replay", "commit"): 282700828,
-    },
-}
+# (kernel_source_digest of the source file); for any other code the bench
+# reports null.
+MEASURED_TRAFFIC = [
+    {"source": KERNEL_SOURCE,
+     "source_sha256": "f178ff24483e32ab99e93c91519fa6b87507c50a5725e979c28710268e173713",
+     "bytes": {   # (workload, mode, kernel) -> bytes per launch
+         ("saturated-b64", "replay", "verify"): 176091558,
+         ("saturated-b64", "replay", "commit"): 282700274,
+     }},
+]
 
 
 def kernel_source_digest(path=KERNEL_SOURCE):
@@ -63,9 +66,23 @@ def kernel_source_digest(path=KERNEL_SOURCE):
 
 
 def measured_traffic(workload, mode, kernel):
-    if kernel_source_digest() != MEASURED_TRAFFIC["source_sha256"]:
-        return None
-    return MEASURED_TRAFFIC["bytes"].get((workload, mode, kernel))
+    for entry in MEASURED_TRAFFIC:
+        key = (workload, mode, kernel)
+        if key in entry["bytes"] and kernel_source_digest(entry["source"]) == entry["source_sha256"]:
+            return entry["bytes"][key]
+    return None
+
+
+def calibration_copy():
+    """A plain 256 MiB device copy: the reference dispatch that scales the
+    rocprofv3 FETCH_SIZE / WRITE_SIZE readings to bytes."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
 
 
 def algorithmic_bytes(w, accept, mode="replay"):
@@ -183,8 +200,10 @@ def run_attention(args, w):
     from linear_attention_verify_amd import binding as bd
     from linear_attention_verify_amd import workloads as wl
 
-    if args.graph or args.accept != "given" or args.calibrate_copy or args.mode != "replay":
-        raise SystemExit("--graph, --accept, --calibrate-copy and --mode apply to GDN workloads")
+    if args.graph or args.accept != "given" or args.mode != "replay":
+        raise SystemExit("--graph, --accept and --mode apply to GDN workloads")
+    if args.calibrate_copy:
+        calibration_copy()
     d = wl.draw_attention(w)
     s = w.shape
     dev = "cuda"
@@ -243,7 +262,8 @@ def run_attention(args, w):
         "gbps": nb * args.steps / wall / 1e9, "hbm_frac": nb * args.steps / wall / 1e9 / HBM_PEAK_GBPS,
         "kernels": {"attn_verify": {"avg_us": tcall * 1e6, "bytes": nb, "gbps": ach}},
         "roofline": {"bound": "hbm", "kernel": "attn_verify (split + combine)", "achieved": ach,
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS, "traffic": None},
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic(w.name, "-", "attn_verify")},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = attention_cpu_baseline(w, d, args.cpu_seconds)
@@ -382,13 +402,7 @@ def main():
     if w.layers != 1:
         return run_stack(args, w)
     if args.calibrate_copy:
-        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        for _ in range(2):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        calibration_copy()
     M = max(1, args.copies)
     base = gh.make_case(w, mode=args.mode)
     cases = [base]
