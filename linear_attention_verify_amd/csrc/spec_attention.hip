@@ -49,22 +49,25 @@ constexpr int kMaxQTiles = 8;     // at most 128 queries per KV head
 constexpr int kSplitGroups = 256; // split-kernel workgroups on a large batch: one per compute unit
 constexpr int kThreadsS = 512;    // split kernel: eight waves, one per query tile, all loading tiles
 constexpr float kNeg = -1.0e30f;  // masked score: finite, so a fully masked row stays NaN-free
+constexpr float kSlack = 8.0f;    // how far a score may pass the running softmax reference
 
-// LDS tile geometry: K rows, then V rows, each 2D bytes with no padding.
-// The 16-byte units of row r are stored XOR-swizzled, unit c at position
-// c ^ (r & 15): the 16 rows one operand read touches (16 keys of K for the
-// A operand; 16 keys x 4 column groups of V for the transposing reads) then
-// fall on distinct banks, and every write of a row stays one contiguous run.
+// LDS tile geometry: K rows, then V rows, 2D bytes each plus 128 spare.
+// Row r starts its units (r & 7) positions in: the 16 rows one operand read
+// touches (16 keys of K for the A operand; 16 keys x 4 column groups of V
+// for the transposing reads) then fall evenly on the banks, every write of
+// a row stays one contiguous run, and a lane's addresses for successive
+// column or K steps differ by constants (instruction offsets, no per-step
+// address arithmetic).
 template <int D> struct Tile {
-    static constexpr int RS = D * 2;                     // row stride, bytes
+    static constexpr int RS = D * 2 + 128;               // row stride, bytes
     static constexpr int KB = kKeyTile * RS;
     static constexpr int BUF = 2 * KB;                   // one K + V tile
     static constexpr int UPR = D / 8;                    // 16-byte units per row
     static constexpr int UNITS = 2 * kKeyTile * UPR;     // units of a K + V tile
     static constexpr int NU = UNITS / kThreadsS;         // units per thread
-    static constexpr int PD = D == 256 ? 3 : 4;          // tiles whose loads are in flight
+    static constexpr int PD = D == 256 ? 2 : 4;          // tiles whose loads are in flight
     static_assert(UNITS % kThreadsS == 0, "tile units spread evenly");
-    static_assert(D / 8 >= 16, "the swizzle permutes units within a row");
+    static_assert(RS % 16 == 0, "rows stay 16-byte aligned");
 };
 
 struct AttnParams {
@@ -226,7 +229,7 @@ __device__ __forceinline__ void store_tile(char *buf, const uint4 (&pre)[Tile<D>
         uint4 val = pre[k];
         if (tail && p0 + key >= L)
             val = uint4{0u, 0u, 0u, 0u};
-        *reinterpret_cast<uint4 *>(buf + row * TL::RS + 16 * (du ^ (key & 15))) = val;
+        *reinterpret_cast<uint4 *>(buf + row * TL::RS + 16 * (du + (key & 7))) = val;
     }
 }
 
@@ -269,12 +272,12 @@ __device__ __forceinline__ void attend(const char *buf, int p0, int last, float 
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
         sacc[st] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        // key 16 st + n, units 4 ks + kg (at position (4 ks + kg) ^ n)
-        const char *krow = buf + (16 * st + n) * TL::RS;
+        // key 16 st + n, unit 4 ks + kg (at position 4 ks + kg + (n & 7))
+        const char *krow = buf + (16 * st + n) * TL::RS + 16 * (kg + (n & 7));
 #pragma unroll
         for (int ks = 0; ks < DS; ++ks)
-            sacc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                *reinterpret_cast<const bf16x8 *>(krow + 16 * ((4 * ks + kg) ^ n)), qv[ks], sacc[st], 0, 0, 0);
+            sacc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8 *>(krow + 64 * ks),
+                                                               qv[ks], sacc[st], 0, 0, 0);
     }
     // lane (kg, n): sacc[st][v] is the score of position p0 + 16 st + 4 kg + v, query n
     float sv[8];
@@ -289,7 +292,11 @@ __device__ __forceinline__ void attend(const char *buf, int p0, int last, float 
             tmax = fmaxf(tmax, x);
         }
     tmax = max_xor32(max_xor16(tmax));
-    const float mnew = fmaxf(mrun, tmax);
+    // The running reference mrun moves only when a score passes it by more
+    // than kSlack: softmax does not depend on the reference, and probabilities
+    // up to e^kSlack are exact in fp32 and as relative in bf16 as any other,
+    // so the rescale of o is rare once the first tile has set mrun.
+    const float mnew = tmax > mrun + kSlack ? tmax : mrun;
     const float alpha = __expf(mrun - mnew);
     float psum = 0.0f;
     bf16x8 pa;
@@ -297,14 +304,12 @@ __device__ __forceinline__ void attend(const char *buf, int p0, int last, float 
     for (int j = 0; j < 8; ++j) {
         const float pj = __expf(sv[j] - mnew);
         psum += pj;
-        pa[j] = __builtin_bit_cast(__bf16, bf16_bits(pj));
+        pa[j] = (__bf16)pj;   // nearest, ties to even (v_cvt_pk_bf16_f32)
     }
     psum = sum_xor32(sum_xor16(psum));
     lrun = lrun * alpha + psum;
     mrun = mnew;
-    // o holds O^T: o[dt][v] is column 16 dt + 4 kg + v of query n, this lane's
-    // own; once the maxima settle every factor is exactly 1 and the rescale
-    // is skipped
+    // o holds O^T: o[dt][v] is column 16 dt + 4 kg + v of query n, this lane's own
     if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
@@ -317,15 +322,14 @@ __device__ __forceinline__ void attend(const char *buf, int p0, int last, float 
     // transpose gives lane n keys 4 kg .. 4 kg + 3 of column 16 dt + n; the
     // second read does keys 16 + 4 kg ..: the key order of the probabilities
     // in pa, which are the B operand as they stand
-    // (row 4 kg + r/4 has swizzle 4 kg + r/4; 16 rows further the same)
+    // (rows 4 kg + r/4 and 16 rows further start their units equally far in)
     typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
     const int vr = 4 * kg + (n >> 2);
-    const char *vrow = buf + TL::KB + vr * TL::RS + 8 * (n & 1);
+    const char *vrow = buf + TL::KB + vr * TL::RS + 16 * (vr & 7) + 8 * (n & 3);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-        const int unit = (2 * dt + ((n >> 1) & 1)) ^ vr;
-        const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vrow + 16 * unit));
-        const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vrow + 16 * TL::RS + 16 * unit));
+        const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vrow + 32 * dt));
+        const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vrow + 16 * TL::RS + 32 * dt));
         const bf16x8 vb = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
         o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, pa, o[dt], 0, 0, 0);
     }
@@ -495,12 +499,19 @@ __global__ __launch_bounds__(256) void gdn_attn_combine_kernel(const AttnParams 
         acc[k] = 0.0f;
     if (!zero) {
         for (int w = w0; w <= w1; ++w) {
+            // all of the record's loads first, then the arithmetic
             const float *rec = p.rec + (size_t)(w + pr) * p.RECF;
+            float ov[QG], mv[QG];
 #pragma unroll
             for (int k = 0; k < QG; ++k) {
                 const int qi = 16 * qt + q0 + k;
-                acc[k] += __expf(rec[(size_t)QP * D + qi] - Ms[q0 + k]) * rec[(size_t)qi * D + d];
+                ov[k] = rec[(size_t)qi * D + d];
+                mv[k] = rec[(size_t)QP * D + qi];
             }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int k = 0; k < QG; ++k)
+                acc[k] += __expf(mv[k] - Ms[q0 + k]) * ov[k];
         }
     }
 #pragma unroll
