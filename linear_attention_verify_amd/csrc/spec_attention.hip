@@ -47,6 +47,7 @@ constexpr int kKeyTile = 32;      // positions per tile; page sizes are multiple
 constexpr int kMaxRowsA = 9;
 constexpr int kMaxQTiles = 8;     // at most 128 queries per KV head
 constexpr int kSplitGroups = 256; // split-kernel workgroups on a large batch: one per compute unit
+constexpr int kMinGroupTiles = 8; // a small batch gets fewer workgroups, each at least this many tiles
 constexpr int kThreadsS = 512;    // split kernel: eight waves, one per query tile, all loading tiles
 constexpr float kNeg = -1.0e30f;  // masked score: finite, so a fully masked row stays NaN-free
 constexpr float kSlack = 8.0f;    // how far a score may pass the running softmax reference
@@ -549,7 +550,8 @@ gdn_status attn_layout(const gdn_attn_desc *d, int batch, int rows, int max_bloc
         return GDN_ERR_UNSUPPORTED;
     const int nq = (d->num_q_heads / d->num_kv_heads) * rows;
     l->QT = (nq + 15) / 16;
-    l->NW = (int)(max_tiles < (size_t)kSplitGroups ? (max_tiles > 0 ? max_tiles : 1) : kSplitGroups);
+    const size_t groups = (max_tiles + kMinGroupTiles - 1) / kMinGroupTiles;
+    l->NW = (int)(groups < (size_t)kSplitGroups ? (groups > 0 ? groups : 1) : kSplitGroups);
     l->RECF = l->QT * 16 * (d->head_dim + 2) + 4;
     l->total = ((size_t)l->NW + pairs) * (size_t)l->RECF * sizeof(float);
     return GDN_OK;
