@@ -120,3 +120,42 @@ def test_full_size_batch_on_sampled_requests():
     sub = dict(d, q=d["q"][sample], block_table=d["block_table"][sample], seq_lens=d["seq_lens"][sample])
     ws = wl.AttnWorkload(w.name, w.shape, batch=len(sample), rows=w.rows, min_len=w.min_len, max_len=w.max_len)
     np.testing.assert_allclose(got[sample], _oracle(ws, sub), atol=ATOL, rtol=RTOL)
+
+
+def test_single_request_full_oracle():
+    """The single-request workload (one request, 3 verify rows, 2048 positions)
+    checked in full: few workgroups, each a run of tiles of one pair."""
+    w = wl.ATTN_WORKLOADS["attn-single"]
+    d = wl.draw_attention(w)
+    got, err = _run(w, d)
+    assert err == 0
+    np.testing.assert_allclose(got, _oracle(w, d), atol=ATOL, rtol=RTOL)
+
+
+def test_long_sequence_merges_many_records():
+    """One request of 8192 positions: each (request, KV head) pair is cut over
+    many workgroups, so the combine merges dozens of partial records."""
+    w = wl.AttnWorkload("long", wl.AttnShape(16, 2, 256, 64), batch=1, rows=9, min_len=8192, max_len=8192, seed=21)
+    d = wl.draw_attention(w)
+    got, err = _run(w, d)
+    assert err == 0
+    np.testing.assert_allclose(got, _oracle(w, d), atol=ATOL, rtol=RTOL)
+
+
+def test_slots_past_the_sequence_may_hold_nan():
+    """Cache slots past a request's length (in its last page) hold NaN: they
+    are masked out and must not reach the output through P V."""
+    w = wl.AttnWorkload("nan-tail", wl.AttnShape(8, 2, 128, 64), batch=3, rows=4, min_len=70, max_len=250, seed=8)
+    d = wl.draw_attention(w)
+    kc, vc = d["k_cache"].copy(), d["v_cache"].copy()
+    nan_bits = np.uint16(0x7FC1)
+    for b in range(w.batch):
+        L = int(d["seq_lens"][b])
+        last_page = d["block_table"][b, (L - 1) // 64]
+        kc[last_page, L % 64 or 64:] = nan_bits
+        vc[last_page, L % 64 or 64:] = nan_bits
+    d2 = dict(d, k_cache=kc, v_cache=vc)
+    got, err = _run(w, d2)
+    assert err == 0
+    assert np.isfinite(got).all()
+    np.testing.assert_allclose(got, _oracle(w, d), atol=ATOL, rtol=RTOL)
