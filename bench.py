@@ -50,6 +50,11 @@ MEASURED_TRAFFIC = [
          ("saturated-b64", "replay", "verify"): 176091558,
          ("saturated-b64", "replay", "commit"): 282700274,
      }},
+    {"source": ATTN_SOURCE,
+     "source_sha256": "6bab8e10717244244a4f3e452d5965de79e3afbfd7f2f127b137d0e270689b94",
+     "bytes": {   # one call: split kernel + combine kernel
+         ("attn-b64", "-", "attn_verify"): 685011236,
+     }},
 ]
 
 
