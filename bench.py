@@ -7,11 +7,12 @@ Qwen3-Next-shaped layer (16 key / 32 value heads, d = 128, conv width 4 over
 8192 channels, bf16 inputs, fp32 state), a 256-slot pool and geometric(0.3)
 accept lengths capped at 9.
 
-Steps rotate over several independent copies of the workload (as the layers of
-a hybrid stack would), verifying a group of copies and then committing them,
-so no kernel finds its state still in the 256 MB Infinity Cache from the
-previous kernel on the same copy. All inputs are resident in HBM before the
-timed region.
+Steps rotate over 16 independent copies of the workload (as the layers of a
+hybrid stack would), verifying a group of copies and then committing them, as
+a model verifies every layer before it commits any. Between two uses of a
+copy the other copies move several GB, so nothing of it (state, inputs, or
+the stash the commit reads back) is still in the 256 MB Infinity Cache: every
+kernel runs cold. All inputs are resident in HBM before the timed region.
 
 Prints one JSON line. value = verify rows per second (batch x rows per step);
 gbps = algorithmic HBM bytes per second: per request, verify reads the state,
@@ -370,7 +371,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="saturated-b64")
     ap.add_argument("--mode", default="replay", choices=["replay", "snapshot"])
-    ap.add_argument("--copies", type=int, default=4)
+    ap.add_argument("--copies", type=int, default=16,
+                    help="independent copies of the workload the steps rotate over; with 16, a "
+                         "copy's inputs, state and scratch have left every cache when it comes round")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--stack-commit", default="per-layer", choices=["fused", "per-layer"],
