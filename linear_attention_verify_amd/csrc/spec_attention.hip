@@ -78,6 +78,7 @@ struct AttnParams {
     const int32_t *bt;
     const int32_t *seq;
     float *rec;       // records: [NW + B*Hkv][RECF] (O [QP][D], m [QP], l [QP], flag)
+    int32_t *starts;  // [B*Hkv + 1]: key tiles before each pair, then the total (from the split kernel)
     uint16_t *out;
     int32_t *err;
     int B, R, Hq, Hkv, G, PS, NP, MB, NQ, QT, NW, RECF;
@@ -356,6 +357,21 @@ __global__ __launch_bounds__(kThreadsS) __attribute__((amdgpu_waves_per_eu(2))) 
 
     // this workgroup's range of the batch's key tiles, and the pair it starts in
     const Located first = locate(p, -1, w, wsum, loc);
+    if (w == 0) {
+        // the pairs' starting tiles and the total, for the combine kernel
+        int base = 0;
+        for (int c0 = 0; c0 < np; c0 += blockDim.x) {
+            const int pr = c0 + tid;
+            const int x = pr < np ? pair_tiles(pr, p) : 0;
+            int tot;
+            const int incl = block_scan(x, wsum, tot) + base;
+            if (pr < np)
+                p.starts[pr] = incl - x;
+            base += tot;
+        }
+        if (tid == 0)
+            p.starts[np] = base;
+    }
     if (first.pair < 0)
         return;
     const int total = first.T;
@@ -451,8 +467,6 @@ template <int D>
 __global__ __launch_bounds__(256) void gdn_attn_combine_kernel(const AttnParams p)
 {
     constexpr int QG = 16 / (256 / D);   // queries per thread
-    __shared__ int wsum[8];
-    __shared__ int loc[2];
     __shared__ float Ms[16], Ls[16];
     const int tid = threadIdx.x;
     const int pr = blockIdx.x, qt = blockIdx.y;
@@ -460,16 +474,16 @@ __global__ __launch_bounds__(256) void gdn_attn_combine_kernel(const AttnParams 
     const int L = seq_len(b, p);
     const int QP = p.QT * 16;
 
-    const Located at = locate(p, pr, 0, wsum, loc);
+    const int total = p.starts[p.B * p.Hkv], start = p.starts[pr];
     const int nt = pair_tiles(pr, p);
     bool zero = nt == 0;
     if (request_refused(L, p) && g == 0 && qt == 0 && tid == 0 && p.err)
         atomicOr(p.err, 4);
     int w0 = 0, w1 = -1;
     if (!zero) {
-        const int per = (at.T + p.NW - 1) / p.NW;
-        w0 = at.start / per;
-        w1 = (at.start + nt - 1) / per;
+        const int per = (total + p.NW - 1) / p.NW;
+        w0 = start / per;
+        w1 = (start + nt - 1) / per;
         bool bad = false;
         for (int w = w0; w <= w1; ++w)
             bad |= p.rec[(size_t)(w + pr) * p.RECF + (size_t)QP * (D + 2)] != 0.0f;
@@ -526,7 +540,7 @@ __global__ __launch_bounds__(256) void gdn_attn_combine_kernel(const AttnParams 
 }
 
 struct AttnLayout {
-    size_t total;
+    size_t starts, total;
     int QT, NW, RECF;
 };
 
@@ -553,7 +567,8 @@ gdn_status attn_layout(const gdn_attn_desc *d, int batch, int rows, int max_bloc
     const size_t groups = (max_tiles + kMinGroupTiles - 1) / kMinGroupTiles;
     l->NW = (int)(groups < (size_t)kSplitGroups ? (groups > 0 ? groups : 1) : kSplitGroups);
     l->RECF = l->QT * 16 * (d->head_dim + 2) + 4;
-    l->total = ((size_t)l->NW + pairs) * (size_t)l->RECF * sizeof(float);
+    l->starts = ((size_t)l->NW + pairs) * (size_t)l->RECF * sizeof(float);
+    l->total = l->starts + (pairs + 1) * sizeof(int32_t);
     return GDN_OK;
 }
 
@@ -600,6 +615,7 @@ gdn_status gdn_spec_attn_verify(const gdn_attn_desc *desc, const void *q, const 
     p.bt = block_table;
     p.seq = seq_lens;
     p.rec = static_cast<float *>(scratch);
+    p.starts = reinterpret_cast<int32_t *>(static_cast<char *>(scratch) + l.starts);
     p.out = static_cast<uint16_t *>(out);
     p.err = err_flag;
     p.B = batch;
