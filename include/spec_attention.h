@@ -58,7 +58,8 @@ gdn_status gdn_spec_attn_scratch_bytes(const gdn_attn_desc *desc, int32_t batch,
  *  seq_lens     int32 [batch]: positions in the cache including the verify
  *               rows, in [rows, max_blocks * page_size]; 0 = padding
  *  scratch      scratch_bytes >= gdn_spec_attn_scratch_bytes(), 16-byte aligned
- *  out          bf16 [batch][rows][Hq][D] (zeros for padding and refused requests)
+ *  out          bf16 [batch][rows][Hq][D], 16-byte aligned (zeros for padding and
+ *               refused requests)
  *  err_flag     int32, nullable: bit 0 is OR-ed in when a page id is outside
  *               [0, num_pages), bit 2 when a seq_len is outside the range
  *               above; that request's output is zero.

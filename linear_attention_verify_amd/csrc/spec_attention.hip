@@ -460,81 +460,94 @@ __global__ __launch_bounds__(kThreadsS) __attribute__((amdgpu_waves_per_eu(2))) 
 }
 
 // One workgroup per (pair, query tile): o = sum_r e^{m_r - M} O_r / sum_r e^{m_r - M} l_r
-// over the pair's records r. The per-query maxima and sums come first; then
-// each thread takes one output column for 16 / (256 / D) queries, whose loads
-// from every record are independent of each other.
+// over the pair's records r. Thread (query tid / 16, columns D/16 (tid % 16)
+// on) merges its query's slice of each record. The records come in chunks of
+// kChunk: every load of a chunk is issued before any arithmetic and the
+// chunks merge online, so a pair spread over a few records costs one round
+// trip to memory once its range is known.
+constexpr int kChunk = 4;
+
 template <int D>
 __global__ __launch_bounds__(256) void gdn_attn_combine_kernel(const AttnParams p)
 {
-    constexpr int QG = 16 / (256 / D);   // queries per thread
-    __shared__ float Ms[16], Ls[16];
+    constexpr int CV = D / 64;   // float4 column groups per thread
     const int tid = threadIdx.x;
     const int pr = blockIdx.x, qt = blockIdx.y;
+    const int np = p.B * p.Hkv;
     const int b = pr / p.Hkv, g = pr % p.Hkv;
     const int L = seq_len(b, p);
     const int QP = p.QT * 16;
 
-    const int total = p.starts[p.B * p.Hkv], start = p.starts[pr];
+    const int total = ((cint32 *)p.starts)[np], start = ((cint32 *)p.starts)[pr];
     const int nt = pair_tiles(pr, p);
-    bool zero = nt == 0;
     if (request_refused(L, p) && g == 0 && qt == 0 && tid == 0 && p.err)
         atomicOr(p.err, 4);
-    int w0 = 0, w1 = -1;
-    if (!zero) {
+    const int qi = 16 * qt + (tid >> 4);
+    const int c0 = (D / 16) * (tid & 15);
+    f32x4 acc[CV];
+#pragma unroll
+    for (int j = 0; j < CV; ++j)
+        acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    float mrun = kNeg, den = 0.0f;
+    bool bad = false;
+    if (nt > 0) {
         const int per = (total + p.NW - 1) / p.NW;
-        w0 = start / per;
-        w1 = (start + nt - 1) / per;
-        bool bad = false;
-        for (int w = w0; w <= w1; ++w)
-            bad |= p.rec[(size_t)(w + pr) * p.RECF + (size_t)QP * (D + 2)] != 0.0f;
-        if (bad) {
-            zero = true;
-            if (g == 0 && qt == 0 && tid == 0 && p.err)
-                atomicOr(p.err, 1);
-        }
-    }
-    if (!zero && tid < 16) {
-        const int qi = 16 * qt + tid;
-        float M = kNeg;
-        for (int w = w0; w <= w1; ++w)
-            M = fmaxf(M, p.rec[(size_t)(w + pr) * p.RECF + (size_t)QP * D + qi]);
-        float den = 0.0f;
-        for (int w = w0; w <= w1; ++w) {
-            const float *rec = p.rec + (size_t)(w + pr) * p.RECF + (size_t)QP * D;
-            den += __expf(rec[qi] - M) * rec[QP + qi];
-        }
-        Ms[tid] = M;
-        Ls[tid] = 1.0f / den;
-    }
-    __syncthreads();
-    const int d = tid % D, q0 = (tid / D) * QG;
-    float acc[QG];
+        const int w0 = start / per, w1 = (start + nt - 1) / per;
+        for (int c = w0; c <= w1; c += kChunk) {
+            f32x4 ov[kChunk][CV];
+            float mv[kChunk], lv[kChunk], fl[kChunk];
 #pragma unroll
-    for (int k = 0; k < QG; ++k)
-        acc[k] = 0.0f;
-    if (!zero) {
-        for (int w = w0; w <= w1; ++w) {
-            // all of the record's loads first, then the arithmetic
-            const float *rec = p.rec + (size_t)(w + pr) * p.RECF;
-            float ov[QG], mv[QG];
+            for (int r = 0; r < kChunk; ++r) {
+                const float *rec = p.rec + (size_t)(min(c + r, w1) + pr) * p.RECF;   // past w1: w1 again, unused
 #pragma unroll
-            for (int k = 0; k < QG; ++k) {
-                const int qi = 16 * qt + q0 + k;
-                ov[k] = rec[(size_t)qi * D + d];
-                mv[k] = rec[(size_t)QP * D + qi];
+                for (int j = 0; j < CV; ++j)
+                    ov[r][j] = *reinterpret_cast<const f32x4 *>(&rec[(size_t)qi * D + c0 + 4 * j]);
+                mv[r] = rec[(size_t)QP * D + qi];
+                lv[r] = rec[(size_t)QP * D + QP + qi];
+                fl[r] = rec[(size_t)QP * (D + 2)];
             }
             __builtin_amdgcn_sched_barrier(0);
+            float m = mrun;
 #pragma unroll
-            for (int k = 0; k < QG; ++k)
-                acc[k] += __expf(mv[k] - Ms[q0 + k]) * ov[k];
+            for (int r = 0; r < kChunk; ++r) {
+                bad |= c + r <= w1 && fl[r] != 0.0f;
+                m = c + r <= w1 ? fmaxf(m, mv[r]) : m;
+            }
+            const float alpha = __expf(mrun - m);
+            den *= alpha;
+#pragma unroll
+            for (int j = 0; j < CV; ++j)
+                acc[j] *= alpha;
+#pragma unroll
+            for (int r = 0; r < kChunk; ++r) {
+                const float wr = c + r <= w1 ? __expf(mv[r] - m) : 0.0f;
+                den = fmaf(wr, lv[r], den);
+#pragma unroll
+                for (int j = 0; j < CV; ++j)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        acc[j][v] = fmaf(wr, ov[r][j][v], acc[j][v]);
+            }
+            mrun = m;
         }
+        if (bad && g == 0 && qt == 0 && tid == 0 && p.err)
+            atomicOr(p.err, 1);
     }
+    if (qi < p.NQ) {
+        const bool zero = nt == 0 || bad;
+        const float inv = zero ? 0.0f : 1.0f / den;
+        const int t = qi / p.G, h = g * p.G + qi % p.G;
+        uint16_t *dst = p.out + (((size_t)b * p.R + t) * p.Hq + h) * D + c0;
 #pragma unroll
-    for (int k = 0; k < QG; ++k) {
-        const int qi = 16 * qt + q0 + k;
-        if (qi < p.NQ) {
-            const int t = qi / p.G, h = g * p.G + qi % p.G;
-            p.out[(((size_t)b * p.R + t) * p.Hq + h) * D + d] = bf16_bits(zero ? 0.0f : acc[k] * Ls[q0 + k]);
+        for (int j = 0; j < CV; j += 2) {
+            uint32_t w[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const float x0 = zero ? 0.0f : acc[j + v / 2][2 * (v % 2)] * inv;
+                const float x1 = zero ? 0.0f : acc[j + v / 2][2 * (v % 2) + 1] * inv;
+                w[v] = (uint32_t)bf16_bits(x0) | ((uint32_t)bf16_bits(x1) << 16);
+            }
+            *reinterpret_cast<uint4 *>(dst + 4 * j) = uint4{w[0], w[1], w[2], w[3]};
         }
     }
 }
@@ -604,7 +617,8 @@ gdn_status gdn_spec_attn_verify(const gdn_attn_desc *desc, const void *q, const 
     if (batch == 0)
         return GDN_OK;
     if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !scratch || !out || num_pages < 1 ||
-        !aligned16a(q) || !aligned16a(k_cache) || !aligned16a(v_cache) || !aligned16a(scratch))
+        !aligned16a(q) || !aligned16a(k_cache) || !aligned16a(v_cache) || !aligned16a(scratch) ||
+        !aligned16a(out))
         return GDN_ERR_INVALID_ARG;
     if (scratch_bytes < l.total)
         return GDN_ERR_SCRATCH_TOO_SMALL;

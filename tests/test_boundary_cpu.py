@@ -229,9 +229,11 @@ def test_attention_arguments_are_refused(lib):
     need = bd.gdn_spec_attn_scratch_bytes(d, 2, 3, 4)
     f = lambda **kw: lib.gdn_spec_attn_verify(
         ct.byref(d), kw.get("q", 4096), 4096, 4096, kw.get("pages", 8), 4096, kw.get("mb", 4), 4096,
-        kw.get("batch", 2), 3, kw.get("scratch", 4096), kw.get("nbytes", need), 4096, None, None)
+        kw.get("batch", 2), 3, kw.get("scratch", 4096), kw.get("nbytes", need), kw.get("out", 4096), None, None)
     assert f(q=None) == inv
     assert f(q=4104) == inv                 # misaligned
+    assert f(out=4104) == inv
+    assert f(out=None) == inv
     assert f(pages=0) == inv
     assert f(mb=0) == inv
     assert f(scratch=None) == inv
