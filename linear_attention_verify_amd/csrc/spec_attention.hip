@@ -42,6 +42,7 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kKeyTile = 32;      // positions per tile; page sizes are multiples of it
 constexpr int kMaxRowsA = 9;
@@ -51,6 +52,7 @@ constexpr int kMinGroupTiles = 8; // a small batch gets fewer workgroups, each a
 constexpr int kThreadsS = 512;    // split kernel: eight waves, one per query tile, all loading tiles
 constexpr float kNeg = -1.0e30f;  // masked score: finite, so a fully masked row stays NaN-free
 constexpr float kSlack = 8.0f;    // how far a score may pass the running softmax reference
+constexpr int kVmcnt0 = 0x0F70;   // s_waitcnt operand: vector memory count 0, the other counters untouched
 
 // LDS tile geometry: K rows, then V rows, 2D bytes each plus 128 spare.
 // Row r starts its units (r & 7) positions in: the 16 rows one operand read
@@ -141,47 +143,64 @@ __device__ int block_scan(int x, int *wsum, int &total)
     return x + before;
 }
 
-// Total key tiles T of the batch, and the tiles before pair `want`; or, if
-// want < 0, the pair holding tile lo = w ceil(T / NW), the first of range w,
-// and the tiles before it (pair -1 when the range is empty).
+// Total key tiles T of the batch, the pair holding tile lo = w ceil(T / NW)
+// (the first of range w) and the tiles before it; pair -1 when the range is
+// empty. Workgroup 0 also writes each pair's first tile, then T, to starts[]
+// for the combine kernel.
 struct Located {
     int T, pair, start;
 };
 
-__device__ Located locate(const AttnParams &p, int want, int w, int *wsum, int *loc)
+__device__ Located locate(const AttnParams &p, int w, int *wsum, int *loc)
 {
     const int np = p.B * p.Hkv;
     const int tid = threadIdx.x, nthr = blockDim.x;
-    int T = 0;
-    for (int c0 = 0; c0 < np; c0 += nthr) {
-        const int x = c0 + tid < np ? pair_tiles(c0 + tid, p) : 0;
-        int tot;
-        block_scan(x, wsum, tot);
-        T += tot;
-    }
-    const int lo = want >= 0 ? 0 : w * ((T + p.NW - 1) / p.NW);
-    T = __builtin_amdgcn_readfirstlane(T);
-    Located r{T, -1, 0};
-    if (want >= 0 ? want >= np : lo >= T)
-        return r;
     if (tid == 0)
         loc[0] = -1;
-    __syncthreads();
-    int base = 0;
+    int T = 0, x0 = 0, incl0 = 0;
     for (int c0 = 0; c0 < np; c0 += nthr) {
         const int pr = c0 + tid;
         const int x = pr < np ? pair_tiles(pr, p) : 0;
         int tot;
-        const int incl = block_scan(x, wsum, tot) + base;
-        const bool hit = want >= 0 ? pr == want : (x > 0 && incl > lo && incl - x <= lo);
-        if (pr < np && hit) {
-            loc[0] = pr;
-            loc[1] = incl - x;
+        const int incl = block_scan(x, wsum, tot) + T;
+        if (w == 0 && pr < np)
+            p.starts[pr] = incl - x;
+        if (c0 == 0) {
+            x0 = x;
+            incl0 = incl;
         }
-        base += tot;
+        T += tot;
+    }
+    if (w == 0 && tid == 0)
+        p.starts[np] = T;
+    T = __builtin_amdgcn_readfirstlane(T);
+    const int lo = w * ((T + p.NW - 1) / p.NW);
+    Located r{T, -1, 0};
+    if (lo >= T)
+        return r;
+    if (np <= nthr) {
+        // the one scan already placed every pair
+        if (tid < np && x0 > 0 && incl0 > lo && incl0 - x0 <= lo) {
+            loc[0] = tid;
+            loc[1] = incl0 - x0;
+        }
         __syncthreads();
-        if (loc[0] >= 0)
-            break;
+    } else {
+        int base = 0;
+        for (int c0 = 0; c0 < np; c0 += nthr) {
+            const int pr = c0 + tid;
+            const int x = pr < np ? pair_tiles(pr, p) : 0;
+            int tot;
+            const int incl = block_scan(x, wsum, tot) + base;
+            if (pr < np && x > 0 && incl > lo && incl - x <= lo) {
+                loc[0] = pr;
+                loc[1] = incl - x;
+            }
+            base += tot;
+            __syncthreads();
+            if (loc[0] >= 0)
+                break;
+        }
     }
     // the same for every thread: kept in scalar registers, so the loads that
     // depend on it (lengths, block-table entries) are scalar loads
@@ -191,26 +210,51 @@ __device__ Located locate(const AttnParams &p, int want, int w, int *wsum, int *
     return r;
 }
 
+// A walk along the batch's run of key tiles: the pair holding the current
+// tile, the tiles before that pair, its tile count, request, KV head and
+// length. Every field is the same for the whole workgroup.
+struct Cursor {
+    int pr, S, nt, b, g, L;
+};
+
+__device__ __forceinline__ Cursor cursor_at(int pr, int S, const AttnParams &p)
+{
+    Cursor c;
+    c.pr = pr;
+    c.S = S;
+    c.b = pr / p.Hkv;
+    c.g = pr - c.b * p.Hkv;
+    c.L = seq_len(c.b, p);
+    c.nt = (c.L <= 0 || request_refused(c.L, p)) ? 0 : (c.L + kKeyTile - 1) / kKeyTile;
+    return c;
+}
+
+// Moves c on to the pair holding tile i (i below the batch's total).
+__device__ __forceinline__ void advance(Cursor &c, int i, const AttnParams &p)
+{
+    while (i >= c.S + c.nt)
+        c = cursor_at(c.pr + 1, c.S + c.nt, p);
+}
+
 template <int D>
-__device__ __forceinline__ void load_tile(const AttnParams &p, int b, int g, int L, int i, uint4 (&pre)[Tile<D>::NU],
-                                          int &bad)
+__device__ __forceinline__ void load_tile(const AttnParams &p, const Cursor &c, int i, uint4 (&pre)[Tile<D>::NU])
 {
     using TL = Tile<D>;
-    const int p0 = i * kKeyTile;   // a multiple of 32: the tile lies in one page
-    int page = table_entry((size_t)b * p.MB + p0 / p.PS, p);
-    if (page < 0 || page >= p.NP) {
-        bad = 1;
-        page = 0;
-    }
+    const int p0 = (i - c.S) * kKeyTile;   // a multiple of 32: the tile lies in one page
+    int page = table_entry((size_t)c.b * p.MB + p0 / p.PS, p);
+    if (page < 0 || page >= p.NP)
+        page = 0;   // flagged where the tile is consumed
     const size_t row0 = (size_t)page * p.PS + p0 % p.PS;
-    const uint16_t *kb = p.kc + (row0 * p.Hkv + g) * D, *vb = p.vc + (row0 * p.Hkv + g) * D;
+    const uint16_t *kb = p.kc + (row0 * p.Hkv + c.g) * D, *vb = p.vc + (row0 * p.Hkv + c.g) * D;
 #pragma unroll
     for (int k = 0; k < TL::NU; ++k) {
         const int u = threadIdx.x + k * kThreadsS;   // K units, then V units (a uniform split per k)
         const int row = u / TL::UPR, du = u % TL::UPR;
         const int key = row % kKeyTile;
         const uint16_t *src = (row < kKeyTile ? kb : vb) + (size_t)key * p.Hkv * D + 8 * du;
-        pre[k] = *reinterpret_cast<const uint4 *>(src);
+        // read once per call: streamed past the caches
+        const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src));
+        pre[k] = uint4{x[0], x[1], x[2], x[3]};
     }
 }
 
@@ -352,110 +396,126 @@ __global__ __launch_bounds__(kThreadsS) __attribute__((amdgpu_waves_per_eu(2))) 
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int kg = lane >> 4, n = lane & 15;
-    const int np = p.B * p.Hkv;
     const int w = blockIdx.x;
 
-    // this workgroup's range of the batch's key tiles, and the pair it starts in
-    const Located first = locate(p, -1, w, wsum, loc);
-    if (w == 0) {
-        // the pairs' starting tiles and the total, for the combine kernel
-        int base = 0;
-        for (int c0 = 0; c0 < np; c0 += blockDim.x) {
-            const int pr = c0 + tid;
-            const int x = pr < np ? pair_tiles(pr, p) : 0;
-            int tot;
-            const int incl = block_scan(x, wsum, tot) + base;
-            if (pr < np)
-                p.starts[pr] = incl - x;
-            base += tot;
-        }
-        if (tid == 0)
-            p.starts[np] = base;
-    }
+    // this workgroup's range lo .. hi-1 of the batch's key tiles
+    const Located first = locate(p, w, wsum, loc);
     if (first.pair < 0)
         return;
-    const int total = first.T;
-    const int per = (total + p.NW - 1) / p.NW;
-    const int lo = w * per;
-    const int hi = min(total, lo + per);
+    const int per = (first.T + p.NW - 1) / p.NW;
+    const int lo = w * per, hi = min(first.T, lo + per);
+    const int ntot = hi - lo;
 
+    // this wave's queries: query qi = 16 wave + n is verify row qi / G of
+    // query head g G + qi % G, which sees positions 0 .. L - R + row
     const bool computes = wave < p.QT;   // one wave per query tile; the others only load
-    int pr = first.pair, S = first.start;
-    while (S < hi && pr < np) {
-        const int nt = pair_tiles(pr, p);
-        const int a = max(lo, S) - S, e = min(hi, S + nt) - S;   // this piece: tiles a .. e-1 of the pair
-        if (a < e) {
-            const int b = pr / p.Hkv, g = pr % p.Hkv;
-            const int L = seq_len(b, p);
-            // this wave's queries: query qi = 16 wave + n is verify row qi / G of
-            // query head g G + qi % G, which sees positions 0 .. L - R + row
-            const int qi = 16 * wave + n;
-            const bool qok = computes && qi < p.NQ;
-            const int qc = qok ? qi : 0;
-            const int t = qc / p.G, h = g * p.G + qc % p.G;
-            const int last = qok ? L - p.R + t : -1;
-            bf16x8 qv[DS];
+    const int qi = 16 * wave + n;
+    const bool qok = computes && qi < p.NQ;
+    const int qc = qok ? qi : 0;
+    const int qrow = qc / p.G, qhead = qc % p.G;
+    auto load_q = [&](const Cursor &c, bf16x8 (&qv)[DS]) {
+        const uint16_t *src = p.q + (((size_t)c.b * p.R + qrow) * p.Hq + c.g * p.G + qhead) * D + 8 * kg;
+#pragma unroll
+        for (int ks = 0; ks < DS; ++ks)
+            qv[ks] = *reinterpret_cast<const bf16x8 *>(src + 32 * ks);
+    };
+
+    // The range is one stream of tiles, whatever pairs it crosses: the
+    // loads run PD tiles ahead of the arithmetic and LDS stores one tile
+    // ahead, each with its own cursor, so the pipeline never drains at a
+    // pair boundary. The compute cursor cc ends a piece (its record) at the
+    // pair's last tile or the range's.
+    const Cursor c0 = cursor_at(first.pair, first.start, p);
+    Cursor cl = c0, cs = c0, cc = c0;   // loads, LDS stores, arithmetic
+    bf16x8 qv[DS];
+    if (computes)
+        load_q(cc, qv);
+    int last = qok ? cc.L - p.R + qrow : -1;
+    f32x4 o[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+        o[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    float mrun = kNeg, lrun = 0.0f;
+    bool bad = false;
+    const int QP = p.QT * 16;
+
+    // Tile j of the range is consumed from LDS buffer j & 1. Its loads went
+    // out PD tiles earlier, into register set j % PD, which is stored to its
+    // buffer one tile ahead. Every step issues the same loads and stores
+    // (tile indices past the range are clamped to its last tile, and the
+    // steps past its end skip only the arithmetic), so each wait for a
+    // register set covers just that set's loads.
+    auto tile_at = [&](int j) { return lo + min(j, ntot - 1); };
+    uint4 pre[TL::PD][TL::NU];
+#pragma unroll
+    for (int s = 0; s < TL::PD; ++s) {
+        const int i = tile_at(s);
+        advance(cl, i, p);
+        load_tile<D>(p, cl, i, pre[s]);
+    }
+    store_tile<D>(smem, pre[0], (lo - cs.S) * kKeyTile, cs.L);
+    __syncthreads();
+    const int nsteps = (ntot + TL::PD - 1) / TL::PD * TL::PD;
+    for (int j0 = 0; j0 < nsteps; j0 += TL::PD) {
+#pragma unroll
+        for (int s = 0; s < TL::PD; ++s) {
+            const int j = j0 + s;
             {
-                const uint16_t *qrow = p.q + (((size_t)b * p.R + t) * p.Hq + h) * D + 8 * kg;
-#pragma unroll
-                for (int ks = 0; ks < DS; ++ks)
-                    qv[ks] = *reinterpret_cast<const bf16x8 *>(qrow + 32 * ks);
+                const int i = tile_at(j + TL::PD);
+                advance(cl, i, p);
+                load_tile<D>(p, cl, i, pre[s]);
             }
-            f32x4 o[DT];
+            if (j < ntot) {
+                const int i = lo + j, t = i - cc.S;
+                if (computes)
+                    attend<D>(smem + (j & 1) * TL::BUF, t * kKeyTile, last, p.scale, kg, n, qv, o, mrun, lrun);
+                const int page = table_entry((size_t)cc.b * p.MB + t * kKeyTile / p.PS, p);
+                bad |= page < 0 || page >= p.NP;
+                if (i == cc.S + cc.nt - 1 || i == hi - 1) {
+                    // the piece of pair cc in this range ends: its record, in
+                    // which lane (kg, n) holds columns 16 dt + 4 kg .. + 3 of query 16 wave + n
+                    float *rec = p.rec + (size_t)(w + cc.pr) * p.RECF;
+                    if (computes) {
+                        const int qb = 16 * wave;
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-                o[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            float mrun = kNeg, lrun = 0.0f;
-            int bad = 0;
-
-            // Tile j of the piece (tile a + j of the pair) is consumed from LDS
-            // buffer j & 1. Its loads went out PD tiles earlier, into register
-            // set j % PD, which is stored to its buffer one tile ahead. Every
-            // step issues the same loads and stores whatever the piece's
-            // length (tile indices past the piece are clamped to its last
-            // tile, and the steps past its end skip only the arithmetic), so
-            // each wait for a register set covers just that set's loads.
-            const int ntp = e - a;
-            const int nsteps = (ntp + TL::PD - 1) / TL::PD * TL::PD;
-            auto tile_at = [&](int j) { return a + min(j, ntp - 1); };
-            uint4 pre[TL::PD][TL::NU];
+                        for (int dt = 0; dt < DT; ++dt)
+                            *reinterpret_cast<f32x4 *>(&rec[(size_t)(qb + n) * D + 16 * dt + 4 * kg]) = o[dt];
+                        if (kg == 0) {
+                            rec[(size_t)QP * D + qb + n] = mrun;
+                            rec[(size_t)QP * D + QP + qb + n] = lrun;
+                        }
+                    }
+                    if (tid == 0)
+                        rec[(size_t)QP * (D + 2)] = bad ? 1.0f : 0.0f;
+                    if (i < hi - 1) {
+                        // on to the next pair: its queries (the first tile of the
+                        // new piece waits for them, and so for the tile loads in
+                        // flight: one memory latency per switch)
+                        advance(cc, i + 1, p);
+                        last = qok ? cc.L - p.R + qrow : -1;
+                        if (computes)
+                            load_q(cc, qv);
+                        // wait for them here, on this path only: otherwise the
+                        // queries would count as possibly in flight at every
+                        // step, and each step's products would first wait for
+                        // the previous step's tile loads
+                        __builtin_amdgcn_s_waitcnt(kVmcnt0);
 #pragma unroll
-            for (int s = 0; s < TL::PD; ++s)
-                load_tile<D>(p, b, g, L, tile_at(s), pre[s], bad);
-            store_tile<D>(smem, pre[0], a * kKeyTile, L);
+                        for (int dt = 0; dt < DT; ++dt)
+                            o[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                        mrun = kNeg;
+                        lrun = 0.0f;
+                        bad = false;
+                    }
+                }
+            }
+            {
+                const int i = tile_at(j + 1);
+                advance(cs, i, p);
+                store_tile<D>(smem + ((j + 1) & 1) * TL::BUF, pre[(s + 1) % TL::PD], (i - cs.S) * kKeyTile, cs.L);
+            }
             __syncthreads();
-            for (int j0 = 0; j0 < nsteps; j0 += TL::PD) {
-#pragma unroll
-                for (int s = 0; s < TL::PD; ++s) {
-                    const int j = j0 + s;
-                    load_tile<D>(p, b, g, L, tile_at(j + TL::PD), pre[s], bad);
-                    if (computes && j < ntp)
-                        attend<D>(smem + (j & 1) * TL::BUF, (a + j) * kKeyTile, last, p.scale, kg, n, qv, o, mrun,
-                                  lrun);
-                    store_tile<D>(smem + ((j + 1) & 1) * TL::BUF, pre[(s + 1) % TL::PD], tile_at(j + 1) * kKeyTile, L);
-                    __syncthreads();
-                }
-            }
-
-            // the piece's record: lane (kg, n) holds columns 16 dt + 4 kg .. + 3 of query 16 wave + n
-            float *rec = p.rec + (size_t)(w + pr) * p.RECF;
-            const int QP = p.QT * 16;
-            if (computes) {
-                const int qb = 16 * wave;
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt)
-                    *reinterpret_cast<f32x4 *>(&rec[(size_t)(qb + n) * D + 16 * dt + 4 * kg]) = o[dt];
-                if (kg == 0) {
-                    rec[(size_t)QP * D + qb + n] = mrun;
-                    rec[(size_t)QP * D + QP + qb + n] = lrun;
-                }
-            }
-            const int anybad = __syncthreads_or(bad);
-            if (tid == 0)
-                rec[(size_t)QP * (D + 2)] = anybad ? 1.0f : 0.0f;
         }
-        S += nt;
-        ++pr;
     }
 }
 
