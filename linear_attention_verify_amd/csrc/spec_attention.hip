@@ -51,7 +51,8 @@ constexpr int kSplitGroups = 256; // split-kernel workgroups on a large batch: o
 constexpr int kMinGroupTiles = 8; // a small batch gets fewer workgroups, each at least this many tiles
 constexpr int kThreadsS = 512;    // split kernel: eight waves, one per query tile, all loading tiles
 constexpr float kNeg = -1.0e30f;  // masked score: finite, so a fully masked row stays NaN-free
-constexpr float kSlack = 8.0f;    // how far a score may pass the running softmax reference
+constexpr float kSlack = 8.0f;    // how far (log2 units) a score may pass the running softmax reference
+constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kVmcnt0 = 0x0F70;   // s_waitcnt operand: vector memory count 0, the other counters untouched
 
 // LDS tile geometry: K rows, then V rows, 2D bytes each plus 128 spare.
@@ -79,11 +80,11 @@ struct AttnParams {
     const uint16_t *vc;
     const int32_t *bt;
     const int32_t *seq;
-    float *rec;       // records: [NW + B*Hkv][RECF] (O [QP][D], m [QP], l [QP], flag)
+    float *rec;       // records: [NW + B*Hkv][RECF] (O [QP][D], m [QP] in log2 units, l [QP], flag)
     int32_t *starts;  // [B*Hkv + 1]: key tiles before each pair, then the total (from the split kernel)
     uint16_t *out;
     int32_t *err;
-    int B, R, Hq, Hkv, G, PS, NP, MB, NQ, QT, NW, RECF;
+    int B, R, Hq, Hkv, G, PS, NP, MB, NQ, QT, NW, RECF, TPP;   // TPP: key tiles per page
     float scale;
 };
 
@@ -210,48 +211,117 @@ __device__ Located locate(const AttnParams &p, int w, int *wsum, int *loc)
     return r;
 }
 
-// A walk along the batch's run of key tiles: the pair holding the current
-// tile, the tiles before that pair, its tile count, request, KV head and
-// length. Every field is the same for the whole workgroup.
+// A walk along the batch's run of key tiles, at most one tile per step: the
+// pair holding the current tile (its request, KV head, length and tile
+// count) and the tile's index t within the pair. Every field is the same for
+// the whole workgroup, so it lives in scalar registers.
 struct Cursor {
-    int pr, S, nt, b, g, L;
+    int pr, b, g, L, nt, t;
 };
 
-__device__ __forceinline__ Cursor cursor_at(int pr, int S, const AttnParams &p)
+__device__ __forceinline__ void set_pair(Cursor &c, int pr, const AttnParams &p)
 {
-    Cursor c;
     c.pr = pr;
-    c.S = S;
     c.b = pr / p.Hkv;
     c.g = pr - c.b * p.Hkv;
     c.L = seq_len(c.b, p);
     c.nt = (c.L <= 0 || request_refused(c.L, p)) ? 0 : (c.L + kKeyTile - 1) / kKeyTile;
-    return c;
 }
 
-// Moves c on to the pair holding tile i (i below the batch's total).
-__device__ __forceinline__ void advance(Cursor &c, int i, const AttnParams &p)
+// To tile 0 of the next pair that has tiles (the caller knows one remains).
+__device__ __forceinline__ void next_pair(Cursor &c, const AttnParams &p)
 {
-    while (i >= c.S + c.nt)
-        c = cursor_at(c.pr + 1, c.S + c.nt, p);
+    do
+        set_pair(c, c.pr + 1, p);
+    while (c.nt == 0);
+    c.t = 0;
+}
+
+__device__ __forceinline__ void step(Cursor &c, const AttnParams &p)
+{
+    if (++c.t == c.nt)
+        next_pair(c, p);
+}
+
+// The load side's walk also follows the pages: the block of the request
+// that holds the tile, the tile's place in its page, and the addresses of
+// the tile's first key in the K and V caches for KV head g. The block
+// table is read once per page. A page id outside the pool is read as page 0
+// and flagged in `bad`, which goes into the piece's record when the walk
+// leaves the pair.
+struct PageWalk {
+    Cursor c;
+    int blk, tip;
+    const char *kt, *vt;
+    bool bad;
+};
+
+template <int D>
+__device__ __forceinline__ void set_page(PageWalk &pw, const AttnParams &p)
+{
+    int page = table_entry((size_t)pw.c.b * p.MB + pw.blk, p);
+    if (page < 0 || page >= p.NP) {
+        pw.bad = true;
+        page = 0;
+    }
+    const size_t off = (((size_t)page * p.PS + pw.tip * kKeyTile) * p.Hkv + pw.c.g) * D;
+    pw.kt = reinterpret_cast<const char *>(p.kc + off);
+    pw.vt = reinterpret_cast<const char *>(p.vc + off);
 }
 
 template <int D>
-__device__ __forceinline__ void load_tile(const AttnParams &p, const Cursor &c, int i, uint4 (&pre)[Tile<D>::NU])
+__device__ __forceinline__ void record_flag(const PageWalk &pw, const AttnParams &p, int w)
+{
+    if (threadIdx.x == 0)
+        p.rec[(size_t)(w + pw.c.pr) * p.RECF + (size_t)p.QT * 16 * (D + 2)] = pw.bad ? 1.0f : 0.0f;
+}
+
+template <int D>
+__device__ __forceinline__ void step_pages(PageWalk &pw, const AttnParams &p, int w)
+{
+    if (pw.c.t + 1 == pw.c.nt) {
+        record_flag<D>(pw, p, w);   // leaving the pair
+        next_pair(pw.c, p);
+        pw.blk = 0;
+        pw.tip = 0;
+        pw.bad = false;
+        set_page<D>(pw, p);
+    } else {
+        ++pw.c.t;
+        if (++pw.tip == p.TPP) {
+            pw.tip = 0;
+            ++pw.blk;
+            set_page<D>(pw, p);
+        } else {
+            const size_t rows = (size_t)kKeyTile * p.Hkv * D * 2;   // the page's next 32 positions
+            pw.kt += rows;
+            pw.vt += rows;
+        }
+    }
+}
+
+// This thread's units of a K + V tile, k < NU/2 in K and the rest the same
+// units of V: byte offsets from the tile's first key (fixed for the launch).
+template <int D>
+__device__ __forceinline__ void unit_offsets(const AttnParams &p, uint32_t (&off)[Tile<D>::NU / 2])
 {
     using TL = Tile<D>;
-    const int p0 = (i - c.S) * kKeyTile;   // a multiple of 32: the tile lies in one page
-    int page = table_entry((size_t)c.b * p.MB + p0 / p.PS, p);
-    if (page < 0 || page >= p.NP)
-        page = 0;   // flagged where the tile is consumed
-    const size_t row0 = (size_t)page * p.PS + p0 % p.PS;
-    const uint16_t *kb = p.kc + (row0 * p.Hkv + c.g) * D, *vb = p.vc + (row0 * p.Hkv + c.g) * D;
+#pragma unroll
+    for (int k = 0; k < TL::NU / 2; ++k) {
+        const int u = threadIdx.x + k * kThreadsS;
+        const int key = u / TL::UPR, du = u % TL::UPR;
+        off[k] = (uint32_t)(key * p.Hkv * D * 2 + 16 * du);
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void load_tile(const PageWalk &pw, const uint32_t (&off)[Tile<D>::NU / 2],
+                                          uint4 (&pre)[Tile<D>::NU])
+{
+    using TL = Tile<D>;
 #pragma unroll
     for (int k = 0; k < TL::NU; ++k) {
-        const int u = threadIdx.x + k * kThreadsS;   // K units, then V units (a uniform split per k)
-        const int row = u / TL::UPR, du = u % TL::UPR;
-        const int key = row % kKeyTile;
-        const uint16_t *src = (row < kKeyTile ? kb : vb) + (size_t)key * p.Hkv * D + 8 * du;
+        const char *src = (k < TL::NU / 2 ? pw.kt : pw.vt) + off[k % (TL::NU / 2)];
         // read once per call: streamed past the caches
         const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src));
         pre[k] = uint4{x[0], x[1], x[2], x[3]};
@@ -306,9 +376,11 @@ __device__ __forceinline__ float sum_xor32(float x)
 
 // One key tile against this wave's 16 queries: scores, online softmax, and
 // the tile's P V added into o. `buf` holds the tile's K and V rows, `p0` is
-// its first position, `last` the last position the lane's query n sees.
+// its first position, `last` the last position the lane's query n sees, and
+// `full` says every query of the workgroup sees the whole tile. The softmax
+// runs in base 2: c2 = scale log2(e), and mrun is in units of log2.
 template <int D>
-__device__ __forceinline__ void attend(const char *buf, int p0, int last, float scale, int kg, int n,
+__device__ __forceinline__ void attend(const char *buf, int p0, int last, bool full, float c2, int kg, int n,
                                        const bf16x8 (&qv)[D / 32], f32x4 (&o)[D / 16], float &mrun, float &lrun)
 {
     using TL = Tile<D>;
@@ -325,30 +397,39 @@ __device__ __forceinline__ void attend(const char *buf, int p0, int last, float 
             sacc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8 *>(krow + 64 * ks),
                                                                qv[ks], sacc[st], 0, 0, 0);
     }
-    // lane (kg, n): sacc[st][v] is the score of position p0 + 16 st + 4 kg + v, query n
+    // lane (kg, n): sacc[st][v] is the (unscaled) score of position
+    // p0 + 16 st + 4 kg + v, query n
     float sv[8];
-    float tmax = kNeg;
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int pos = p0 + 16 * st + 4 * kg + v;
-            const float x = pos <= last ? sacc[st][v] * scale : kNeg;
-            sv[4 * st + v] = x;
-            tmax = fmaxf(tmax, x);
-        }
-    tmax = max_xor32(max_xor16(tmax));
+        for (int v = 0; v < 4; ++v)
+            sv[4 * st + v] = sacc[st][v];
+    if (!full) {
+        // only a pair's last tile or two hold positions that some verify row does not see
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                if (p0 + 16 * st + 4 * kg + v > last)
+                    sv[4 * st + v] = kNeg;
+    }
+    float tmax = sv[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j)
+        tmax = fmaxf(tmax, sv[j]);
+    tmax = max_xor32(max_xor16(tmax)) * c2;   // scale > 0: the maximum commutes with it
     // The running reference mrun moves only when a score passes it by more
     // than kSlack: softmax does not depend on the reference, and probabilities
-    // up to e^kSlack are exact in fp32 and as relative in bf16 as any other,
+    // up to 2^kSlack are exact in fp32 and as relative in bf16 as any other,
     // so the rescale of o is rare once the first tile has set mrun.
     const float mnew = tmax > mrun + kSlack ? tmax : mrun;
-    const float alpha = __expf(mrun - mnew);
+    const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
     float psum = 0.0f;
     bf16x8 pa;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        const float pj = __expf(sv[j] - mnew);
+        const float pj = __builtin_amdgcn_exp2f(fmaf(sv[j], c2, -mnew));
         psum += pj;
         pa[j] = (__bf16)pj;   // nearest, ties to even (v_cvt_pk_bf16_f32)
     }
@@ -425,8 +506,18 @@ __global__ __launch_bounds__(kThreadsS) __attribute__((amdgpu_waves_per_eu(2))) 
     // ahead, each with its own cursor, so the pipeline never drains at a
     // pair boundary. The compute cursor cc ends a piece (its record) at the
     // pair's last tile or the range's.
-    const Cursor c0 = cursor_at(first.pair, first.start, p);
-    Cursor cl = c0, cs = c0, cc = c0;   // loads, LDS stores, arithmetic
+    Cursor c0;
+    set_pair(c0, first.pair, p);
+    c0.t = lo - first.start;
+    Cursor cs = c0, cc = c0;   // LDS stores, arithmetic
+    PageWalk pw;               // loads
+    pw.c = c0;
+    pw.blk = c0.t / p.TPP;
+    pw.tip = c0.t - pw.blk * p.TPP;
+    pw.bad = false;
+    set_page<D>(pw, p);
+    uint32_t off[TL::NU / 2];
+    unit_offsets<D>(p, off);
     bf16x8 qv[DS];
     if (computes)
         load_q(cc, qv);
@@ -436,8 +527,8 @@ __global__ __launch_bounds__(kThreadsS) __attribute__((amdgpu_waves_per_eu(2))) 
     for (int dt = 0; dt < DT; ++dt)
         o[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     float mrun = kNeg, lrun = 0.0f;
-    bool bad = false;
     const int QP = p.QT * 16;
+    const float c2 = p.scale * kLog2e;
 
     // Tile j of the range is consumed from LDS buffer j & 1. Its loads went
     // out PD tiles earlier, into register set j % PD, which is stored to its
@@ -445,33 +536,29 @@ __global__ __launch_bounds__(kThreadsS) __attribute__((amdgpu_waves_per_eu(2))) 
     // (tile indices past the range are clamped to its last tile, and the
     // steps past its end skip only the arithmetic), so each wait for a
     // register set covers just that set's loads.
-    auto tile_at = [&](int j) { return lo + min(j, ntot - 1); };
+    // (Each cursor moves on one tile per step while its tile is inside the range.)
     uint4 pre[TL::PD][TL::NU];
 #pragma unroll
     for (int s = 0; s < TL::PD; ++s) {
-        const int i = tile_at(s);
-        advance(cl, i, p);
-        load_tile<D>(p, cl, i, pre[s]);
+        if (s > 0 && s < ntot)
+            step_pages<D>(pw, p, w);
+        load_tile<D>(pw, off, pre[s]);
     }
-    store_tile<D>(smem, pre[0], (lo - cs.S) * kKeyTile, cs.L);
+    store_tile<D>(smem, pre[0], cs.t * kKeyTile, cs.L);
     __syncthreads();
     const int nsteps = (ntot + TL::PD - 1) / TL::PD * TL::PD;
     for (int j0 = 0; j0 < nsteps; j0 += TL::PD) {
 #pragma unroll
         for (int s = 0; s < TL::PD; ++s) {
             const int j = j0 + s;
-            {
-                const int i = tile_at(j + TL::PD);
-                advance(cl, i, p);
-                load_tile<D>(p, cl, i, pre[s]);
-            }
+            if (j + TL::PD < ntot)
+                step_pages<D>(pw, p, w);
+            load_tile<D>(pw, off, pre[s]);
             if (j < ntot) {
-                const int i = lo + j, t = i - cc.S;
                 if (computes)
-                    attend<D>(smem + (j & 1) * TL::BUF, t * kKeyTile, last, p.scale, kg, n, qv, o, mrun, lrun);
-                const int page = table_entry((size_t)cc.b * p.MB + t * kKeyTile / p.PS, p);
-                bad |= page < 0 || page >= p.NP;
-                if (i == cc.S + cc.nt - 1 || i == hi - 1) {
+                    attend<D>(smem + (j & 1) * TL::BUF, cc.t * kKeyTile, last,
+                              cc.t * kKeyTile + kKeyTile - 1 <= cc.L - p.R, c2, kg, n, qv, o, mrun, lrun);
+                if (cc.t == cc.nt - 1 || j == ntot - 1) {
                     // the piece of pair cc in this range ends: its record, in
                     // which lane (kg, n) holds columns 16 dt + 4 kg .. + 3 of query 16 wave + n
                     float *rec = p.rec + (size_t)(w + cc.pr) * p.RECF;
@@ -485,13 +572,11 @@ __global__ __launch_bounds__(kThreadsS) __attribute__((amdgpu_waves_per_eu(2))) 
                             rec[(size_t)QP * D + QP + qb + n] = lrun;
                         }
                     }
-                    if (tid == 0)
-                        rec[(size_t)QP * (D + 2)] = bad ? 1.0f : 0.0f;
-                    if (i < hi - 1) {
+                    if (j < ntot - 1) {
                         // on to the next pair: its queries (the first tile of the
                         // new piece waits for them, and so for the tile loads in
                         // flight: one memory latency per switch)
-                        advance(cc, i + 1, p);
+                        next_pair(cc, p);
                         last = qok ? cc.L - p.R + qrow : -1;
                         if (computes)
                             load_q(cc, qv);
@@ -505,22 +590,22 @@ __global__ __launch_bounds__(kThreadsS) __attribute__((amdgpu_waves_per_eu(2))) 
                             o[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
                         mrun = kNeg;
                         lrun = 0.0f;
-                        bad = false;
                     }
+                } else {
+                    ++cc.t;
                 }
             }
-            {
-                const int i = tile_at(j + 1);
-                advance(cs, i, p);
-                store_tile<D>(smem + ((j + 1) & 1) * TL::BUF, pre[(s + 1) % TL::PD], (i - cs.S) * kKeyTile, cs.L);
-            }
+            if (j + 1 < ntot)
+                step(cs, p);
+            store_tile<D>(smem + ((j + 1) & 1) * TL::BUF, pre[(s + 1) % TL::PD], cs.t * kKeyTile, cs.L);
             __syncthreads();
         }
     }
+    record_flag<D>(pw, p, w);   // the range's last piece
 }
 
-// One workgroup per (pair, query tile): o = sum_r e^{m_r - M} O_r / sum_r e^{m_r - M} l_r
-// over the pair's records r. Thread (query tid / 16, columns D/16 (tid % 16)
+// One workgroup per (pair, query tile): o = sum_r 2^{m_r - M} O_r / sum_r 2^{m_r - M} l_r
+// over the pair's records r (maxima in units of log2). Thread (query tid / 16, columns D/16 (tid % 16)
 // on) merges its query's slice of each record. The records come in chunks of
 // kChunk: every load of a chunk is issued before any arithmetic and the
 // chunks merge online, so a pair spread over a few records costs one round
@@ -573,14 +658,14 @@ __global__ __launch_bounds__(256) void gdn_attn_combine_kernel(const AttnParams 
                 bad |= c + r <= w1 && fl[r] != 0.0f;
                 m = c + r <= w1 ? fmaxf(m, mv[r]) : m;
             }
-            const float alpha = __expf(mrun - m);
+            const float alpha = __builtin_amdgcn_exp2f(mrun - m);
             den *= alpha;
 #pragma unroll
             for (int j = 0; j < CV; ++j)
                 acc[j] *= alpha;
 #pragma unroll
             for (int r = 0; r < kChunk; ++r) {
-                const float wr = c + r <= w1 ? __expf(mv[r] - m) : 0.0f;
+                const float wr = c + r <= w1 ? __builtin_amdgcn_exp2f(mv[r] - m) : 0.0f;
                 den = fmaf(wr, lv[r], den);
 #pragma unroll
                 for (int j = 0; j < CV; ++j)
@@ -698,6 +783,7 @@ gdn_status gdn_spec_attn_verify(const gdn_attn_desc *desc, const void *q, const 
     p.Hkv = desc->num_kv_heads;
     p.G = desc->num_q_heads / desc->num_kv_heads;
     p.PS = desc->page_size;
+    p.TPP = desc->page_size / kKeyTile;
     p.NP = num_pages;
     p.MB = max_blocks;
     p.NQ = p.G * rows;
