@@ -38,7 +38,7 @@ extern "C" {
 
 typedef struct {
     int32_t num_q_heads;    /* Hq */
-    int32_t num_kv_heads;   /* Hkv, dividing Hq; (Hq/Hkv) * rows <= 128 */
+    int32_t num_kv_heads;   /* Hkv, dividing Hq, at most 1024; (Hq/Hkv) * rows <= 128 */
     int32_t head_dim;       /* D: 128 or 256 */
     int32_t page_size;      /* positions per page: a multiple of 32 */
     float scale;            /* score scale, usually 1/sqrt(D) */

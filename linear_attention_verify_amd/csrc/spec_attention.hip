@@ -47,6 +47,7 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kKeyTile = 32;      // positions per tile; page sizes are multiples of it
 constexpr int kMaxRowsA = 9;
 constexpr int kMaxQTiles = 8;     // at most 128 queries per KV head
+constexpr int kMaxKvHeads = 1024; // a tile's per-thread byte offsets stay 32-bit
 constexpr int kSplitGroups = 256; // split-kernel workgroups on a large batch: one per compute unit
 constexpr int kMinGroupTiles = 8; // a small batch gets fewer workgroups, each at least this many tiles
 constexpr int kThreadsS = 512;    // split kernel: eight waves, one per query tile, all loading tiles
@@ -310,18 +311,26 @@ __device__ __forceinline__ void unit_offsets(const AttnParams &p, uint32_t (&off
     for (int k = 0; k < TL::NU / 2; ++k) {
         const int u = threadIdx.x + k * kThreadsS;
         const int key = u / TL::UPR, du = u % TL::UPR;
-        off[k] = (uint32_t)(key * p.Hkv * D * 2 + 16 * du);
+        off[k] = (uint32_t)key * (uint32_t)p.Hkv * (uint32_t)(D * 2) + 16u * (uint32_t)du;
     }
 }
 
+// A step past the end of the range loads nothing it needs; it still issues
+// its loads (so every step counts the same loads), from `spare`, 8 KiB of
+// this workgroup's own scratch that stays in the cache, rather than reading
+// the last tile from memory again.
+constexpr uint32_t kSpareMask = 0x1FF0;
+static_assert(16 * (128 + 2) * 4 >= kSpareMask + 16, "a record (one query tile, D >= 128) covers the spare reads");
+
 template <int D>
-__device__ __forceinline__ void load_tile(const PageWalk &pw, const uint32_t (&off)[Tile<D>::NU / 2],
-                                          uint4 (&pre)[Tile<D>::NU])
+__device__ __forceinline__ void load_tile(const PageWalk &pw, const uint32_t (&off)[Tile<D>::NU / 2], bool past,
+                                          const char *spare, uint4 (&pre)[Tile<D>::NU])
 {
     using TL = Tile<D>;
 #pragma unroll
     for (int k = 0; k < TL::NU; ++k) {
-        const char *src = (k < TL::NU / 2 ? pw.kt : pw.vt) + off[k % (TL::NU / 2)];
+        const uint32_t o = off[k % (TL::NU / 2)];
+        const char *src = past ? spare + (o & kSpareMask) : (k < TL::NU / 2 ? pw.kt : pw.vt) + o;
         // read once per call: streamed past the caches
         const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src));
         pre[k] = uint4{x[0], x[1], x[2], x[3]};
@@ -538,11 +547,13 @@ __global__ __launch_bounds__(kThreadsS) __attribute__((amdgpu_waves_per_eu(2))) 
     // register set covers just that set's loads.
     // (Each cursor moves on one tile per step while its tile is inside the range.)
     uint4 pre[TL::PD][TL::NU];
+    // (scratch record w: at least 8 KiB, see attn_layout)
+    const char *spare = reinterpret_cast<const char *>(p.rec + (size_t)w * p.RECF);
 #pragma unroll
     for (int s = 0; s < TL::PD; ++s) {
         if (s > 0 && s < ntot)
             step_pages<D>(pw, p, w);
-        load_tile<D>(pw, off, pre[s]);
+        load_tile<D>(pw, off, s >= ntot, spare, pre[s]);
     }
     store_tile<D>(smem, pre[0], cs.t * kKeyTile, cs.L);
     __syncthreads();
@@ -553,7 +564,7 @@ __global__ __launch_bounds__(kThreadsS) __attribute__((amdgpu_waves_per_eu(2))) 
             const int j = j0 + s;
             if (j + TL::PD < ntot)
                 step_pages<D>(pw, p, w);
-            load_tile<D>(pw, off, pre[s]);
+            load_tile<D>(pw, off, j + TL::PD >= ntot, spare, pre[s]);
             if (j < ntot) {
                 if (computes)
                     attend<D>(smem + (j & 1) * TL::BUF, cc.t * kKeyTile, last,
@@ -605,94 +616,111 @@ __global__ __launch_bounds__(kThreadsS) __attribute__((amdgpu_waves_per_eu(2))) 
 }
 
 // One workgroup per (pair, query tile): o = sum_r 2^{m_r - M} O_r / sum_r 2^{m_r - M} l_r
-// over the pair's records r (maxima in units of log2). Thread (query tid / 16, columns D/16 (tid % 16)
-// on) merges its query's slice of each record. The records come in chunks of
-// kChunk: every load of a chunk is issued before any arithmetic and the
-// chunks merge online, so a pair spread over a few records costs one round
-// trip to memory once its range is known.
-constexpr int kChunk = 4;
+// over the pair's records r (maxima in units of log2). Each load instruction
+// of a wave reads whole record rows (lane l: columns 4 l .. 4 l + 3 of a row
+// of D floats); wave v of eight takes queries 2 v and 2 v + 1 of the tile.
+// The records come in chunks of kChunk: every load of a chunk is issued
+// before any arithmetic and the chunks merge online, so a pair spread over
+// up to kChunk records costs one round trip to memory once its range is
+// known.
+constexpr int kChunk = 8;
+constexpr int kThreadsC = 512;
 
 template <int D>
-__global__ __launch_bounds__(256) void gdn_attn_combine_kernel(const AttnParams p)
+__global__ __launch_bounds__(kThreadsC) void gdn_attn_combine_kernel(const AttnParams p)
 {
-    constexpr int CV = D / 64;   // float4 column groups per thread
-    const int tid = threadIdx.x;
+    constexpr int LPR = D / 4;            // lanes per row
+    constexpr int RPI = 64 / LPR;         // rows per load instruction
+    constexpr int QPT = 2 / RPI;          // queries per thread
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int pr = blockIdx.x, qt = blockIdx.y;
     const int np = p.B * p.Hkv;
     const int b = pr / p.Hkv, g = pr % p.Hkv;
     const int L = seq_len(b, p);
     const int QP = p.QT * 16;
+    typedef const __attribute__((address_space(4))) float cfloat;
 
     const int total = ((cint32 *)p.starts)[np], start = ((cint32 *)p.starts)[pr];
     const int nt = pair_tiles(pr, p);
     if (request_refused(L, p) && g == 0 && qt == 0 && tid == 0 && p.err)
         atomicOr(p.err, 4);
-    const int qi = 16 * qt + (tid >> 4);
-    const int c0 = (D / 16) * (tid & 15);
-    f32x4 acc[CV];
+    const int c0 = 4 * (lane % LPR);
+    const int q0 = 16 * qt + 2 * wave + lane / LPR;   // this thread's queries: q0 + RPI k
+    f32x4 acc[QPT];
+    float mrun[QPT], den[QPT];
 #pragma unroll
-    for (int j = 0; j < CV; ++j)
-        acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    float mrun = kNeg, den = 0.0f;
+    for (int k = 0; k < QPT; ++k) {
+        acc[k] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        mrun[k] = kNeg;
+        den[k] = 0.0f;
+    }
     bool bad = false;
     if (nt > 0) {
         const int per = (total + p.NW - 1) / p.NW;
         const int w0 = start / per, w1 = (start + nt - 1) / per;
         for (int c = w0; c <= w1; c += kChunk) {
-            f32x4 ov[kChunk][CV];
-            float mv[kChunk], lv[kChunk], fl[kChunk];
+            f32x4 ov[kChunk][QPT];
+            float mv[kChunk][QPT], lv[kChunk][QPT], fl[kChunk];
 #pragma unroll
             for (int r = 0; r < kChunk; ++r) {
                 const float *rec = p.rec + (size_t)(min(c + r, w1) + pr) * p.RECF;   // past w1: w1 again, unused
 #pragma unroll
-                for (int j = 0; j < CV; ++j)
-                    ov[r][j] = *reinterpret_cast<const f32x4 *>(&rec[(size_t)qi * D + c0 + 4 * j]);
-                mv[r] = rec[(size_t)QP * D + qi];
-                lv[r] = rec[(size_t)QP * D + QP + qi];
-                fl[r] = rec[(size_t)QP * (D + 2)];
+                for (int k = 0; k < QPT; ++k) {
+                    const int qi = q0 + RPI * k;
+                    ov[r][k] = *reinterpret_cast<const f32x4 *>(&rec[(size_t)qi * D + c0]);
+                    if (RPI == 1) {
+                        // the wave's queries are uniform: scalar loads, no vector registers
+                        mv[r][k] = ((const cfloat *)rec)[(size_t)QP * D + qi];
+                        lv[r][k] = ((const cfloat *)rec)[(size_t)QP * D + QP + qi];
+                    } else {
+                        mv[r][k] = rec[(size_t)QP * D + qi];
+                        lv[r][k] = rec[(size_t)QP * D + QP + qi];
+                    }
+                }
+                fl[r] = ((const cfloat *)rec)[(size_t)QP * (D + 2)];
             }
             __builtin_amdgcn_sched_barrier(0);
-            float m = mrun;
 #pragma unroll
-            for (int r = 0; r < kChunk; ++r) {
+            for (int r = 0; r < kChunk; ++r)
                 bad |= c + r <= w1 && fl[r] != 0.0f;
-                m = c + r <= w1 ? fmaxf(m, mv[r]) : m;
-            }
-            const float alpha = __builtin_amdgcn_exp2f(mrun - m);
-            den *= alpha;
 #pragma unroll
-            for (int j = 0; j < CV; ++j)
-                acc[j] *= alpha;
+            for (int k = 0; k < QPT; ++k) {
+                float m = mrun[k];
 #pragma unroll
-            for (int r = 0; r < kChunk; ++r) {
-                const float wr = c + r <= w1 ? __builtin_amdgcn_exp2f(mv[r] - m) : 0.0f;
-                den = fmaf(wr, lv[r], den);
+                for (int r = 0; r < kChunk; ++r)
+                    m = c + r <= w1 ? fmaxf(m, mv[r][k]) : m;
+                const float alpha = __builtin_amdgcn_exp2f(mrun[k] - m);
+                float dsum = den[k] * alpha;
+                f32x4 a = acc[k] * alpha;
 #pragma unroll
-                for (int j = 0; j < CV; ++j)
+                for (int r = 0; r < kChunk; ++r) {
+                    const float wr = c + r <= w1 ? __builtin_amdgcn_exp2f(mv[r][k] - m) : 0.0f;
+                    dsum = fmaf(wr, lv[r][k], dsum);
 #pragma unroll
                     for (int v = 0; v < 4; ++v)
-                        acc[j][v] = fmaf(wr, ov[r][j][v], acc[j][v]);
+                        a[v] = fmaf(wr, ov[r][k][v], a[v]);
+                }
+                mrun[k] = m;
+                den[k] = dsum;
+                acc[k] = a;
             }
-            mrun = m;
         }
         if (bad && g == 0 && qt == 0 && tid == 0 && p.err)
             atomicOr(p.err, 1);
     }
-    if (qi < p.NQ) {
-        const bool zero = nt == 0 || bad;
-        const float inv = zero ? 0.0f : 1.0f / den;
-        const int t = qi / p.G, h = g * p.G + qi % p.G;
-        uint16_t *dst = p.out + (((size_t)b * p.R + t) * p.Hq + h) * D + c0;
+    const bool zero = nt == 0 || bad;
 #pragma unroll
-        for (int j = 0; j < CV; j += 2) {
-            uint32_t w[4];
+    for (int k = 0; k < QPT; ++k) {
+        const int qi = q0 + RPI * k;
+        if (qi < p.NQ) {
+            const float inv = zero ? 0.0f : 1.0f / den[k];
+            const int t = qi / p.G, h = g * p.G + qi % p.G;
+            uint32_t wd[2];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const float x0 = zero ? 0.0f : acc[j + v / 2][2 * (v % 2)] * inv;
-                const float x1 = zero ? 0.0f : acc[j + v / 2][2 * (v % 2) + 1] * inv;
-                w[v] = (uint32_t)bf16_bits(x0) | ((uint32_t)bf16_bits(x1) << 16);
-            }
-            *reinterpret_cast<uint4 *>(dst + 4 * j) = uint4{w[0], w[1], w[2], w[3]};
+            for (int v = 0; v < 2; ++v)
+                wd[v] = (uint32_t)bf16_bits(zero ? 0.0f : acc[k][2 * v] * inv) |
+                        ((uint32_t)bf16_bits(zero ? 0.0f : acc[k][2 * v + 1] * inv) << 16);
+            *reinterpret_cast<uint2 *>(p.out + (((size_t)b * p.R + t) * p.Hq + h) * D + c0) = uint2{wd[0], wd[1]};
         }
     }
 }
@@ -709,7 +737,7 @@ gdn_status attn_layout(const gdn_attn_desc *d, int batch, int rows, int max_bloc
     if (d->num_q_heads < 1 || d->num_kv_heads < 1 || d->num_q_heads % d->num_kv_heads != 0 ||
         d->page_size < 1)
         return GDN_ERR_INVALID_ARG;
-    if ((d->head_dim != 128 && d->head_dim != 256) || d->page_size % kKeyTile != 0 ||
+    if ((d->head_dim != 128 && d->head_dim != 256) || d->page_size % kKeyTile != 0 || d->num_kv_heads > kMaxKvHeads ||
         (d->num_q_heads / d->num_kv_heads) * rows > 16 * kMaxQTiles)
         return GDN_ERR_UNSUPPORTED;
     const size_t maxpos = (size_t)max_blocks * d->page_size;
@@ -796,10 +824,10 @@ gdn_status gdn_spec_attn_verify(const gdn_attn_desc *desc, const void *q, const 
     const dim3 combine_grid((unsigned)(batch * p.Hkv), (unsigned)l.QT);
     if (desc->head_dim == 128) {
         hipLaunchKernelGGL(gdn_attn_split_kernel<128>, split_grid, dim3(kThreadsS), 0, st, p);
-        hipLaunchKernelGGL(gdn_attn_combine_kernel<128>, combine_grid, dim3(256), 0, st, p);
+        hipLaunchKernelGGL(gdn_attn_combine_kernel<128>, combine_grid, dim3(kThreadsC), 0, st, p);
     } else {
         hipLaunchKernelGGL(gdn_attn_split_kernel<256>, split_grid, dim3(kThreadsS), 0, st, p);
-        hipLaunchKernelGGL(gdn_attn_combine_kernel<256>, combine_grid, dim3(256), 0, st, p);
+        hipLaunchKernelGGL(gdn_attn_combine_kernel<256>, combine_grid, dim3(kThreadsC), 0, st, p);
     }
     return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }

@@ -226,6 +226,8 @@ def test_attention_arguments_are_refused(lib):
     assert lib.gdn_spec_attn_scratch_bytes(ct.byref(d), 2, 10, 4, ct.byref(out)) == inv       # rows > 9
     assert lib.gdn_spec_attn_scratch_bytes(ct.byref(_attn_desc(num_q_heads=64, num_kv_heads=1)), 2, 3, 4,
                                            ct.byref(out)) == bd.GDN_ERR_UNSUPPORTED           # 192 queries
+    assert lib.gdn_spec_attn_scratch_bytes(ct.byref(_attn_desc(num_q_heads=2048, num_kv_heads=2048)), 2, 3, 4,
+                                           ct.byref(out)) == bd.GDN_ERR_UNSUPPORTED           # past 1024 KV heads
     need = bd.gdn_spec_attn_scratch_bytes(d, 2, 3, 4)
     f = lambda **kw: lib.gdn_spec_attn_verify(
         ct.byref(d), kw.get("q", 4096), 4096, 4096, kw.get("pages", 8), 4096, kw.get("mb", 4), 4096,
