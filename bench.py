@@ -52,9 +52,9 @@ MEASURED_TRAFFIC = [
          ("saturated-b64", "replay", "commit"): 282700274,
      }},
     {"source": ATTN_SOURCE,
-     "source_sha256": "6bab8e10717244244a4f3e452d5965de79e3afbfd7f2f127b137d0e270689b94",
+     "source_sha256": "af9b5963b14220db8291c10f3859d108f4bc3fca9b1efca90e1770e789f70f80",
      "bytes": {   # one call: split kernel + combine kernel
-         ("attn-b64", "-", "attn_verify"): 685011236,
+         ("attn-b64", "-", "attn_verify"): 687602971,
      }},
 ]
 
