@@ -41,7 +41,7 @@ typedef struct {
     int32_t num_kv_heads;   /* Hkv, dividing Hq, at most 1024; (Hq/Hkv) * rows <= 128 */
     int32_t head_dim;       /* D: 128 or 256 */
     int32_t page_size;      /* positions per page: a multiple of 32 */
-    float scale;            /* score scale, usually 1/sqrt(D) */
+    float scale;            /* score scale, finite and > 0; usually 1/sqrt(D) */
 } gdn_attn_desc;
 
 /* Scratch bytes gdn_spec_attn_verify needs for this batch: the per-split

@@ -51,7 +51,7 @@ constexpr int kMaxKvHeads = 1024; // a tile's per-thread byte offsets stay 32-bi
 constexpr int kSplitGroups = 256; // split-kernel workgroups on a large batch: one per compute unit
 constexpr int kMinGroupTiles = 8; // a small batch gets fewer workgroups, each at least this many tiles
 constexpr int kThreadsS = 512;    // split kernel: eight waves, one per query tile, all loading tiles
-constexpr float kNeg = -1.0e30f;  // masked score: finite, so a fully masked row stays NaN-free
+constexpr float kNeg = -1.0e30f;  // starting softmax reference: below any score, and finite
 constexpr float kSlack = 8.0f;    // how far (log2 units) a score may pass the running softmax reference
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kVmcnt0 = 0x0F70;   // s_waitcnt operand: vector memory count 0, the other counters untouched
@@ -415,13 +415,18 @@ __device__ __forceinline__ void attend(const char *buf, int p0, int last, bool f
         for (int v = 0; v < 4; ++v)
             sv[4 * st + v] = sacc[st][v];
     if (!full) {
-        // only a pair's last tile or two hold positions that some verify row does not see
+        // only a pair's last tile or two hold positions that some verify row
+        // does not see. Masked scores are -inf: if a row sees none of the
+        // tile, its maximum stays -inf, the reference does not move, and every
+        // probability is exp2(-inf) = 0, so a piece the row cannot see leaves
+        // l = 0, o = 0 (a finite masked score would become the reference and
+        // its scaled rounding error could reach exp2 as a huge argument)
 #pragma unroll
         for (int st = 0; st < 2; ++st)
 #pragma unroll
             for (int v = 0; v < 4; ++v)
                 if (p0 + 16 * st + 4 * kg + v > last)
-                    sv[4 * st + v] = kNeg;
+                    sv[4 * st + v] = -__builtin_inff();
     }
     float tmax = sv[0];
 #pragma unroll
@@ -735,7 +740,7 @@ gdn_status attn_layout(const gdn_attn_desc *d, int batch, int rows, int max_bloc
     if (!d || batch < 0 || rows < 1 || rows > kMaxRowsA || max_blocks < 1)
         return GDN_ERR_INVALID_ARG;
     if (d->num_q_heads < 1 || d->num_kv_heads < 1 || d->num_q_heads % d->num_kv_heads != 0 ||
-        d->page_size < 1)
+        d->page_size < 1 || !(d->scale > 0.0f && d->scale <= 3.0e38f))
         return GDN_ERR_INVALID_ARG;
     if ((d->head_dim != 128 && d->head_dim != 256) || d->page_size % kKeyTile != 0 || d->num_kv_heads > kMaxKvHeads ||
         (d->num_q_heads / d->num_kv_heads) * rows > 16 * kMaxQTiles)

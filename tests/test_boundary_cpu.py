@@ -211,6 +211,10 @@ def _attn_desc(**kw):
     ("head_dim", 64, bd.GDN_ERR_UNSUPPORTED),
     ("page_size", 16, bd.GDN_ERR_UNSUPPORTED),        # not a multiple of 32
     ("num_kv_heads", 0, bd.GDN_ERR_INVALID_ARG),
+    ("scale", 0.0, bd.GDN_ERR_INVALID_ARG),
+    ("scale", -0.5, bd.GDN_ERR_INVALID_ARG),
+    ("scale", float("inf"), bd.GDN_ERR_INVALID_ARG),
+    ("scale", float("nan"), bd.GDN_ERR_INVALID_ARG),
 ])
 def test_attention_descriptor_is_refused(lib, field, value, status):
     import ctypes as ct

@@ -55,6 +55,9 @@ CASES = [
     (128, 2, 2, 32, 9, 2, 9, 2100),
     (256, 32, 2, 64, 4, 2, 64, 900),    # 64 queries per KV head: one full group of query tiles
     (128, 16, 1, 32, 8, 2, 100, 500),   # 128 queries, the most one KV head takes: two groups
+    (128, 8, 2, 128, 5, 3, 5, 900),     # pages of four key tiles
+    (256, 16, 2, 256, 9, 2, 9, 1600),   # pages of eight key tiles
+    (128, 4, 1, 96, 3, 3, 3, 700),      # a page size that is not a power of two (three key tiles)
 ]
 
 
@@ -94,6 +97,26 @@ def test_lengths_at_every_edge():
     np.testing.assert_allclose(got, _oracle(w, d), atol=ATOL, rtol=RTOL)
 
 
+def test_pieces_that_some_rows_cannot_see():
+    """A piece of the split whose positions all lie past what some verify
+    row sees (a pair's short last tile, cut off by itself) must add nothing
+    to that row. Lengths 40 and 161 with 9 rows and 13 blocks of 32 give
+    seven workgroups of three tiles, and three such pieces."""
+    w = wl.AttnWorkload("unseen", wl.AttnShape(8, 2, 128, 32), batch=2, rows=9, min_len=9, max_len=416, seed=13)
+    d = wl.draw_attention(w)
+    seq = np.array([40, 161], np.int32)
+    need = -(-seq // 32)
+    table = np.full((2, w.max_blocks), -1, np.int32)
+    perm = np.random.default_rng(1).permutation(d["k_cache"].shape[0])
+    table[0, :need[0]] = perm[:need[0]]
+    table[1, :need[1]] = perm[need[0]:need[0] + need[1]]
+    d = dict(d, seq_lens=seq, block_table=table)
+    got, err = _run(w, d)
+    assert err == 0
+    assert not np.isnan(got).any()
+    np.testing.assert_allclose(got, _oracle(w, d), atol=ATOL, rtol=RTOL)
+
+
 def test_bad_pages_and_lengths_are_flagged():
     w = wl.AttnWorkload("bad", wl.AttnShape(4, 2, 128, 32), batch=4, rows=3, min_len=40, max_len=90, seed=6)
     d = wl.draw_attention(w)
@@ -109,6 +132,23 @@ def test_bad_pages_and_lengths_are_flagged():
     np.testing.assert_allclose(got[ok], want[ok], atol=ATOL, rtol=RTOL)
 
 
+def test_bad_page_inside_a_request_is_flagged():
+    """A page id outside the pool in the middle of a request (its third
+    block): that request is zero on both KV heads and flagged, the others
+    are exact."""
+    w = wl.AttnWorkload("bad-mid", wl.AttnShape(8, 2, 128, 64), batch=3, rows=4, min_len=300, max_len=600, seed=9)
+    d = wl.draw_attention(w)
+    table = d["block_table"].copy()
+    table[1, 2] = -3
+    print("bad page inside request 1, seq", d["seq_lens"].tolist(), flush=True)
+    got, err = _run(w, d, table=table)
+    assert err == 1
+    assert not np.any(got[1])
+    ok = [0, 2]
+    want = _oracle(w, d, seq=np.where(np.isin(np.arange(3), ok), d["seq_lens"], 0))
+    np.testing.assert_allclose(got[ok], want[ok], atol=ATOL, rtol=RTOL)
+
+
 def test_full_size_batch_on_sampled_requests():
     """The 64-request, 9-row workload at its real lengths; the oracle checks a
     sample of requests (all rows and heads of each)."""
@@ -120,6 +160,16 @@ def test_full_size_batch_on_sampled_requests():
     sub = dict(d, q=d["q"][sample], block_table=d["block_table"][sample], seq_lens=d["seq_lens"][sample])
     ws = wl.AttnWorkload(w.name, w.shape, batch=len(sample), rows=w.rows, min_len=w.min_len, max_len=w.max_len)
     np.testing.assert_allclose(got[sample], _oracle(ws, sub), atol=ATOL, rtol=RTOL)
+    # every request: o is a convex combination of the value rows it sees, so
+    # each column lies between their least and greatest entry (up to bf16)
+    assert np.isfinite(got).all()
+    s_, G = w.shape, w.shape.num_q_heads // w.shape.num_kv_heads
+    for b, L in enumerate(d["seq_lens"]):
+        pos = np.arange(L)
+        V = wl.bf16_bits_to_f32(d["v_cache"][d["block_table"][b][pos // s_.page_size], pos % s_.page_size])
+        lo, hi = V.min(axis=0), V.max(axis=0)                   # [Hkv][D], over all positions
+        o = got[b].reshape(w.rows, s_.num_kv_heads, G, s_.head_dim)
+        assert (o >= lo[None, :, None, :] - 0.02).all() and (o <= hi[None, :, None, :] + 0.02).all(), b
 
 
 def test_single_request_full_oracle():
