@@ -52,9 +52,9 @@ MEASURED_TRAFFIC = [
          ("saturated-b64", "replay", "commit"): 282700274,
      }},
     {"source": ATTN_SOURCE,
-     "source_sha256": "af9b5963b14220db8291c10f3859d108f4bc3fca9b1efca90e1770e789f70f80",
+     "source_sha256": "156e94fc44e37f142cca0ca2e1351b38f4381899104ad1acd82d888d59640bef",
      "bytes": {   # one call: split kernel + combine kernel
-         ("attn-b64", "-", "attn_verify"): 687602971,
+         ("attn-b64", "-", "attn_verify"): 687598629,
      }},
 ]
 
