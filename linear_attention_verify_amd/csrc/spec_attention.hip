@@ -576,9 +576,10 @@ __global__ __launch_bounds__(kThreadsS) __attribute__((amdgpu_waves_per_eu(2))) 
                               cc.t * kKeyTile + kKeyTile - 1 <= cc.L - p.R, c2, kg, n, qv, o, mrun, lrun);
                 if (cc.t == cc.nt - 1 || j == ntot - 1) {
                     // the piece of pair cc in this range ends: its record, in
-                    // which lane (kg, n) holds columns 16 dt + 4 kg .. + 3 of query 16 wave + n
+                    // which lane (kg, n) holds columns 16 dt + 4 kg .. + 3 of query
+                    // 16 wave + n (rows of the query slots past NQ are not written)
                     float *rec = p.rec + (size_t)(w + cc.pr) * p.RECF;
-                    if (computes) {
+                    if (qok) {
                         const int qb = 16 * wave;
 #pragma unroll
                         for (int dt = 0; dt < DT; ++dt)
@@ -672,7 +673,9 @@ __global__ __launch_bounds__(kThreadsC) void gdn_attn_combine_kernel(const AttnP
 #pragma unroll
                 for (int k = 0; k < QPT; ++k) {
                     const int qi = q0 + RPI * k;
-                    ov[r][k] = *reinterpret_cast<const f32x4 *>(&rec[(size_t)qi * D + c0]);
+                    // (a query slot past NQ has no row: its result is never stored)
+                    ov[r][k] = qi < p.NQ ? *reinterpret_cast<const f32x4 *>(&rec[(size_t)qi * D + c0])
+                                         : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
                     if (RPI == 1) {
                         // the wave's queries are uniform: scalar loads, no vector registers
                         mv[r][k] = ((const cfloat *)rec)[(size_t)QP * D + qi];
