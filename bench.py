@@ -52,9 +52,9 @@ MEASURED_TRAFFIC = [
          ("saturated-b64", "replay", "commit"): 282700274,
      }},
     {"source": ATTN_SOURCE,
-     "source_sha256": "156e94fc44e37f142cca0ca2e1351b38f4381899104ad1acd82d888d59640bef",
+     "source_sha256": "ad021266b0aa8d96ca11e709c23abd1cf8611b5560fc08eac32e6ce9fa58e534",
      "bytes": {   # one call: split kernel + combine kernel
-         ("attn-b64", "-", "attn_verify"): 687598629,
+         ("attn-b64", "-", "attn_verify"): 681299700,
      }},
 ]
 
