@@ -10,23 +10,26 @@
 // Split kernel. The batch's key tiles (32 positions, inside one page) are
 // laid end to end over all (request, KV head) pairs and cut into equal
 // ranges, one per workgroup of a fixed grid, so every workgroup streams the
-// same number of bytes whatever the mix of sequence lengths. A workgroup
-// walks the pairs its range touches; for each piece it keeps one wave per
-// query tile (16 queries) and stages each key tile through LDS once:
-//   K rows in their cache layout, read as the A operand of
-//     S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (the queries, held in
-//     registers, are the B operand). Lane (kg, n) ends with the scores of
-//     keys 4kg..4kg+3 and 16+4kg..16+4kg+3 for query n.
-//   online softmax per query: its 32 scores sit in lanes n, n^16, n^32, n^48.
-//   O += P V on the same instruction: the lane's 8 probabilities are its A
-//     operand as they stand; the V operand (8 keys of one head-dim column)
-//     comes from V rows in LDS through ds_read_b64_tr_b16, whose 16-lane
-//     transpose hands lane n the column it needs, so V is never rearranged.
-// Tiles are double-buffered: the next tile's loads are in flight while the
-// current one is consumed, one workgroup barrier per tile.
-// Each piece leaves a partial result (its running max, sum and unnormalised
-// output per query) in a record; cutting at both range and pair boundaries
-// numbers the records range + pair, so no index table is needed.
+// same number of bytes whatever the mix of sequence lengths. A workgroup's
+// range is one stream of tiles, whatever pairs it crosses: cursors for the
+// loads (two tiles ahead, nontemporal, following the block table page by
+// page), the LDS stores (one tile ahead) and the arithmetic each move one
+// tile per step, with one workgroup barrier per tile. One wave per query
+// tile (16 queries) does the arithmetic on each tile staged in LDS:
+//   S^T = K Q^T on v_mfma_f32_16x16x32_bf16, K rows in their cache layout
+//     as the A operand, the queries (in registers) as B. Lane (kg, n) ends
+//     with the scores of keys 4kg..4kg+3 and 16+4kg..16+4kg+3 for query n.
+//   online softmax per query in base 2: its 32 scores sit in lanes n, n^16,
+//     n^32, n^48.
+//   O^T += V^T P^T on the same instruction: the lane's 8 probabilities are
+//     the B operand as they stand; the V operand (8 keys of one head-dim
+//     column) comes from V rows in LDS through ds_read_b64_tr_b16, whose
+//     16-lane transpose hands lane n the column it needs, so V is never
+//     rearranged.
+// Each (range, pair) piece leaves a partial result (its running max, sum and
+// unnormalised output per query) in a record; cutting at both range and
+// pair boundaries numbers the records range + pair, so no index table is
+// needed.
 // Combine kernel. Per (pair, query tile) the pair's records merge, weighted
 // by their running maxima, into o.
 
@@ -547,12 +550,12 @@ __global__ __launch_bounds__(kThreadsS) __attribute__((amdgpu_waves_per_eu(2))) 
     // Tile j of the range is consumed from LDS buffer j & 1. Its loads went
     // out PD tiles earlier, into register set j % PD, which is stored to its
     // buffer one tile ahead. Every step issues the same loads and stores
-    // (tile indices past the range are clamped to its last tile, and the
-    // steps past its end skip only the arithmetic), so each wait for a
-    // register set covers just that set's loads.
-    // (Each cursor moves on one tile per step while its tile is inside the range.)
+    // (past the range the loads read `spare` and the stores go to a buffer
+    // no step consumes; the steps past its end skip only the arithmetic), so
+    // each wait for a register set covers just that set's loads. Each cursor
+    // moves on one tile per step while its tile is inside the range.
     uint4 pre[TL::PD][TL::NU];
-    // (scratch record w: at least 8 KiB, see attn_layout)
+    // record w of the scratch: at least 8 KiB (one query tile, D >= 128)
     const char *spare = reinterpret_cast<const char *>(p.rec + (size_t)w * p.RECF);
 #pragma unroll
     for (int s = 0; s < TL::PD; ++s) {
