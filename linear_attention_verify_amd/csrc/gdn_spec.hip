@@ -913,9 +913,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 #pragma unroll
         for (int q = 1; q < NR; ++q)
             gtu *= (q > u && q <= t) ? alw[q] : 1.0f;
-        const float iu = inv_norm(u);
-        cA = (u < t) ? bew[t] * (gtu * (gram(u * NC + t) * iu * inv_norm(t))) : 0.0f;
-        cB = gtu * (gram(u * NC + NR + t) * iu * inv_norm(NR + t));
+        // the norms this wave just stored (the same bits inv_norm gives; a
+        // wave's LDS accesses stay in order, so no sync is needed)
+        const float iu = invw[u];
+        cA = (u < t) ? bew[t] * (gtu * (gram(u * NC + t) * iu * invw[t])) : 0.0f;
+        cB = gtu * (gram(u * NC + NR + t) * iu * invw[NR + t]);
         const int tt = min(lane, NR - 1);
         float gt = 1.0f;
 #pragma unroll
