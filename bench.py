@@ -46,10 +46,10 @@ ATTN_SOURCE = os.path.join(ROOT, "linear_attention_verify_amd", "csrc", "spec_at
 # reports null.
 MEASURED_TRAFFIC = [
     {"source": KERNEL_SOURCE,
-     "source_sha256": "f178ff24483e32ab99e93c91519fa6b87507c50a5725e979c28710268e173713",
+     "source_sha256": "a1fafa7881d47b9d9fadeca8be396761abef21dcbee917a15fb034bb7aff727d",
      "bytes": {   # (workload, mode, kernel) -> bytes per launch
-         ("saturated-b64", "replay", "verify"): 176091558,
-         ("saturated-b64", "replay", "commit"): 282700274,
+         ("saturated-b64", "replay", "verify"): 176078658,
+         ("saturated-b64", "replay", "commit"): 282700443,
      }},
     {"source": ATTN_SOURCE,
      "source_sha256": "ad021266b0aa8d96ca11e709c23abd1cf8611b5560fc08eac32e6ce9fa58e534",
