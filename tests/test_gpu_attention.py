@@ -58,6 +58,8 @@ CASES = [
     (128, 8, 2, 128, 5, 3, 5, 900),     # pages of four key tiles
     (256, 16, 2, 256, 9, 2, 9, 1600),   # pages of eight key tiles
     (128, 4, 1, 96, 3, 3, 3, 700),      # a page size that is not a power of two (three key tiles)
+    (128, 4, 4, 32, 1, 3, 1, 300),      # one query per KV head: one query tile, one computing wave
+    (256, 16, 8, 64, 3, 2, 3, 900),     # eight KV heads
 ]
 
 
