@@ -21,7 +21,7 @@ is synthetic:
 """
 from __future__ import annotations
 
-from dataclasses import dataclass, replace
+from dataclasses import dataclass
 
 import numpy as np
 
@@ -50,10 +50,6 @@ class LayerShape:
     @property
     def elem_bytes(self) -> int:
         return 4 if self.dtype == "f32" else 2
-
-    @property
-    def np_storage(self):
-        return np.float32 if self.dtype == "f32" else np.uint16
 
 
 @dataclass(frozen=True)
@@ -196,10 +192,6 @@ def small_workload(shape: LayerShape, batch: int, rows: int, num_slots: int, see
                    name: str = "custom", **kw) -> Workload:
     return Workload(name=name, shape=shape, batch=batch, rows=rows, num_slots=num_slots,
                     seed=seed, **kw)
-
-
-def with_shape(w: Workload, **shape_changes) -> Workload:
-    return replace(w, shape=replace(w.shape, **shape_changes))
 
 
 # ---- verification attention (the hybrid model's full-attention layers) ----
