@@ -52,9 +52,9 @@ MEASURED_TRAFFIC = [
          ("saturated-b64", "replay", "commit"): 282700443,
      }},
     {"source": ATTN_SOURCE,
-     "source_sha256": "ad021266b0aa8d96ca11e709c23abd1cf8611b5560fc08eac32e6ce9fa58e534",
+     "source_sha256": "fea23cda85474a1911ac64c84d0a72c07fb0b452f40e9d09e97bd7684f15892b",
      "bytes": {   # one call: split kernel + combine kernel
-         ("attn-b64", "-", "attn_verify"): 681299700,
+         ("attn-b64", "-", "attn_verify"): 681315402,
      }},
 ]
 

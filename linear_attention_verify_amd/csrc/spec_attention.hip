@@ -52,7 +52,7 @@ constexpr int kMaxRowsA = 9;
 constexpr int kMaxQTiles = 8;     // at most 128 queries per KV head
 constexpr int kMaxKvHeads = 1024; // a tile's per-thread byte offsets stay 32-bit
 constexpr int kSplitGroups = 256; // split-kernel workgroups on a large batch: one per compute unit
-constexpr int kMinGroupTiles = 8; // a small batch gets fewer workgroups, each at least this many tiles
+constexpr int kMinGroupTiles = 4; // a small batch gets fewer workgroups, each at least this many tiles
 constexpr int kThreadsS = 512;    // split kernel: eight waves, one per query tile, all loading tiles
 constexpr float kNeg = -1.0e30f;  // starting softmax reference: below any score, and finite
 constexpr float kSlack = 8.0f;    // how far (log2 units) a score may pass the running softmax reference
