@@ -117,6 +117,27 @@ __device__ __forceinline__ void stream_store(float *ptr, float4 v)
     stream_store(ptr, f32x4{v.x, v.y, v.z, v.w});
 }
 
+// The verify's outputs and the stash it leaves for the commit are written
+// once and read by later kernels only. Written back (plain stores), they are
+// still dirty in L2 when the last wave ends, and the release at the end of
+// the kernel flushes them while the rest of the chip idles: about 4 us of
+// the saturated batch's 28 MB. Nontemporal stores drain them as they go.
+template <typename X> __device__ __forceinline__ void out_store(X *ptr, X v)
+{
+    __builtin_nontemporal_store(v, ptr);
+}
+
+__device__ __forceinline__ void out_store(bf16_t *ptr, bf16_t v)
+{
+    __builtin_nontemporal_store(v.bits, &ptr->bits);
+}
+
+__device__ __forceinline__ void out_store(uint4 *ptr, uint4 v)
+{
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4 *>(ptr));
+}
+
 // Barrier that orders LDS only: global loads already in flight (the state
 // prefetch) are not drained by it.
 __device__ __forceinline__ void lds_barrier()
@@ -290,7 +311,7 @@ __device__ __forceinline__ void zero_outputs(const VerifyParams<T> &p, int b, in
 {
     for (int idx = threadIdx.x; idx < NR * D; idx += kThreads) {
         const int t = idx / D, i = idx % D;
-        p.out[(((size_t)b * NR + t) * p.HV + h) * D + i] = from_f32<T>(0.0f);
+        out_store(&p.out[(((size_t)b * NR + t) * p.HV + h) * D + i], from_f32<T>(0.0f));
     }
 }
 
@@ -314,8 +335,8 @@ __device__ __forceinline__ void solve_row(const VerifyParams<T> &p, const float 
         for (int u = 0; u <= t; ++u)
             o = __builtin_fmaf(cB[t * NR + u], e[u], o);
         const size_t oi = (((size_t)b * NR + t) * p.HV + h) * D + i;
-        p.out[oi] = from_f32<T>(p.scale * o);
-        p.es[oi] = e[t];
+        out_store(&p.out[oi], from_f32<T>(p.scale * o));
+        out_store(&p.es[oi], e[t]);
         __builtin_amdgcn_sched_barrier(0);  // one row at a time: bounds the hoisted coefficient reads
     }
 }
@@ -506,18 +527,18 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_kernel(const VerifyParams
 #pragma unroll
     for (int t = 0; t < NR; ++t) {
         if (nch == 1 || (nch == 2 && owner)) {
-            p.xs[((size_t)b * NR + t) * p.C + chan0] = cin0.x[t];
+            out_store(&p.xs[((size_t)b * NR + t) * p.C + chan0], cin0.x[t]);
             if (nch == 2)
-                p.xs[((size_t)b * NR + t) * p.C + chan1] = cin1.x[t];
+                out_store(&p.xs[((size_t)b * NR + t) * p.C + chan1], cin1.x[t]);
         }
     }
     if (owner) {
         float *ks = p.ks + ((size_t)b * HK + kh) * NR * D;
         for (int idx = tid; idx < NR * D; idx += kThreads)
-            ks[idx] = Mt[(idx % D) * MS + idx / D];
+            out_store(&ks[idx], Mt[(idx % D) * MS + idx / D]);
     }
     if (tid < NR)
-        p.as[((size_t)b * HV + h) * NR + tid] = al[tid];
+        out_store(&p.as[((size_t)b * HV + h) * NR + tid], al[tid]);
     lds_barrier();
 
     // per state row i: correction vectors and outputs
@@ -776,7 +797,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     if (tid < 2 * NR) {
         al[ghh][gtt] = to_f32(ga);
         be[ghh][gtt] = to_f32(gb);
-        p.as[((size_t)b * HV + h0 + ghh) * NR + gtt] = to_f32(ga);
+        out_store(&p.as[((size_t)b * HV + h0 + ghh) * NR + gtt], to_f32(ga));
     }
     const bool owner = (h0 % G) == 0;
     if constexpr (STAGED) {
@@ -791,7 +812,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
                 const int r = u / UPR, k = u % UPR;
                 Xs[(kWidth - 1) * UPR + u] = val;
                 if (k >= 32 || owner)
-                    *reinterpret_cast<uint4 *>(p.xs + ((size_t)b * NR + r) * p.C + unit_channel(k)) = val;
+                    out_store(reinterpret_cast<uint4 *>(p.xs + ((size_t)b * NR + r) * p.C + unit_channel(k)), val);
             }
         };
         stage_xunit(0, xu0);
@@ -841,8 +862,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 #pragma unroll
         for (int t = 0; t < NR; ++t) {
             if (owner)
-                p.xs[((size_t)b * NR + t) * p.C + chA] = cinA.x[t];
-            p.xs[((size_t)b * NR + t) * p.C + chV] = cinV.x[t];
+                out_store(&p.xs[((size_t)b * NR + t) * p.C + chA], cinA.x[t]);
+            out_store(&p.xs[((size_t)b * NR + t) * p.C + chV], cinV.x[t]);
         }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -1012,8 +1033,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
             for (int u = 0; u <= t; ++u)
                 s = __builtin_fmaf(lane_value(cB, t * (t + 1) / 2 + u), e[u], s);
             const size_t oi = (((size_t)b * NR + t) * HV + h0 + hh) * D + rb + lane;
-            p.out[oi] = from_f32<T>(p.scale * s);
-            p.es[oi] = e[t];
+            out_store(&p.out[oi], from_f32<T>(p.scale * s));
+            out_store(&p.es[oi], e[t]);
         }
         if (SNAP) {
             // this row of the product table is read only by this lane: reuse it for e_t
@@ -1027,7 +1048,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     if (owner) {
         float *ks = p.ks + ((size_t)b * HK + kh) * NR * D;
         for (int idx = tid; idx < NR * D; idx += kThreads)
-            ks[idx] = Mt[(idx % D) * MS + idx / D] * invw[idx / D];
+            out_store(&ks[idx], Mt[(idx % D) * MS + idx / D] * invw[idx / D]);
     }
 
     if (SNAP) {
