@@ -46,10 +46,10 @@ ATTN_SOURCE = os.path.join(ROOT, "linear_attention_verify_amd", "csrc", "spec_at
 # reports null.
 MEASURED_TRAFFIC = [
     {"source": KERNEL_SOURCE,
-     "source_sha256": "a1fafa7881d47b9d9fadeca8be396761abef21dcbee917a15fb034bb7aff727d",
+     "source_sha256": "f0436b5cecf214df6802988cbdc20b3b72b7597e3ed04699adba958ace1e0189",
      "bytes": {   # (workload, mode, kernel) -> bytes per launch
-         ("saturated-b64", "replay", "verify"): 176078658,
-         ("saturated-b64", "replay", "commit"): 282700443,
+         ("saturated-b64", "replay", "verify"): 176085313,
+         ("saturated-b64", "replay", "commit"): 282700576,
      }},
     {"source": ATTN_SOURCE,
      "source_sha256": "fea23cda85474a1911ac64c84d0a72c07fb0b452f40e9d09e97bd7684f15892b",
