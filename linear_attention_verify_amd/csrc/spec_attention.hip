@@ -731,7 +731,12 @@ __global__ __launch_bounds__(kThreadsC) void gdn_attn_combine_kernel(const AttnP
             for (int v = 0; v < 2; ++v)
                 wd[v] = (uint32_t)bf16_bits(zero ? 0.0f : acc[k][2 * v] * inv) |
                         ((uint32_t)bf16_bits(zero ? 0.0f : acc[k][2 * v + 1] * inv) << 16);
-            *reinterpret_cast<uint2 *>(p.out + (((size_t)b * p.R + t) * p.Hq + h) * D + c0) = uint2{wd[0], wd[1]};
+            // nontemporal: written back as it goes, not by the release at the
+            // kernel's end (the partial records above stay write-back: this
+            // kernel reads them right after the split kernel wrote them)
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            __builtin_nontemporal_store(u32x2{wd[0], wd[1]},
+                                        reinterpret_cast<u32x2 *>(p.out + (((size_t)b * p.R + t) * p.Hq + h) * D + c0));
         }
     }
 }
