@@ -52,9 +52,9 @@ MEASURED_TRAFFIC = [
          ("saturated-b64", "replay", "commit"): 282700576,
      }},
     {"source": ATTN_SOURCE,
-     "source_sha256": "fea23cda85474a1911ac64c84d0a72c07fb0b452f40e9d09e97bd7684f15892b",
+     "source_sha256": "48053594bb5c23d84287f0f2482f4eed15c191f19f7704bebaaaec6088e44d2a",
      "bytes": {   # one call: split kernel + combine kernel
-         ("attn-b64", "-", "attn_verify"): 681315402,
+         ("attn-b64", "-", "attn_verify"): 681306111,
      }},
 ]
 
