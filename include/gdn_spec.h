@@ -5,9 +5,9 @@
  * The step: for every request, the target model scores k+1 verify rows (the
  * pending token and k draft tokens, k <= 8) through each GatedDeltaNet layer,
  * then keeps the first n of them (FreeToken PR #844 "MTP drafts for the
- * Qwen3.5 family and Flash-Next", Summary and Design; the accept length n is
- * the number of committed tokens per request per verify step, at most k+1,
- * same page, End-to-end). Per layer this library does:
+ * Qwen3.5 family and Flash-Next", Summary and Design). n, the accept length,
+ * counts the rows a request keeps from one verify, so it never exceeds k+1
+ * (same page, End-to-end). Per layer this library does:
  *
  *   gdn_spec_verify  the spec-decode causal conv over [history | rows], SiLU,
  *                    per-key-head L2 norm of q and k, and the gated delta rule

@@ -123,14 +123,102 @@ def _mode(mode) -> int:
 
 
 def _ptr(t):
-    """Device pointer of a torch tensor (None -> NULL; ints pass through)."""
+    """Device pointer of a torch tensor (None -> NULL). Callers check the
+    tensor with _check first."""
     if t is None:
         return None
-    if isinstance(t, int):
-        return t
     if not t.is_contiguous():
         raise ValueError("tensor must be contiguous")
     return t.data_ptr()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _storage_dtype(desc):
+    torch = _torch()
+    return torch.float32 if int(desc.dtype) == GDN_F32 else torch.bfloat16
+
+
+def _check(t, name, dtype, shape=None, device=None, optional=False, min_numel=None):
+    """Refuses, before any pointer reaches the library, a tensor the C ABI
+    would misread: not a torch tensor on a GPU, on another device than the
+    call's other buffers, of another dtype, not contiguous, or of another
+    shape (an exact tuple; None entries match any extent) or too small.
+    The library cannot see buffer sizes, so these checks are what stands
+    between a wrong tensor and an out-of-bounds access on the device."""
+    torch = _torch()
+    if t is None:
+        if optional:
+            return
+        raise ValueError("%s is required" % name)
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch tensor, got %s" % (name, type(t).__name__))
+    if t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if shape is not None:
+        got = tuple(t.shape)
+        if len(got) != len(shape) or any(w is not None and g != w for g, w in zip(got, shape)):
+            raise ValueError("%s has shape %s, expected %s" % (name, got, tuple("*" if w is None else w for w in shape)))
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError("%s holds %d elements, at least %d needed" % (name, t.numel(), min_numel))
+    if not t.is_cuda:
+        raise ValueError("%s must be in GPU memory (got device %s)" % (name, t.device))
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, the call's other buffers on %s" % (name, t.device, device))
+
+
+def _layer_dims(desc):
+    HK, HV, dk, dv, W = (int(desc.num_k_heads), int(desc.num_v_heads), int(desc.d_k), int(desc.d_v),
+                         int(desc.conv_width))
+    return HK, HV, dk, dv, W, 2 * HK * dk + HV * dv
+
+
+def _check_pool(desc, ssm, conv):
+    """The pool tensors of one layer; returns (device, num_slots)."""
+    torch = _torch()
+    HK, HV, dk, dv, W, C = _layer_dims(desc)
+    _check(ssm, "ssm", torch.float32, (None, HV, dk, dv))
+    P = int(ssm.shape[0])
+    _check(conv, "conv", _storage_dtype(desc), (P, W - 1, C), device=ssm.device)
+    return ssm.device, P
+
+
+def _check_slot_table(slot_ids, device, batch=None):
+    torch = _torch()
+    _check(slot_ids, "slot_ids", torch.int32, (None,) if batch is None else (batch,), device=device)
+    return int(slot_ids.shape[0])
+
+
+def check_slot_ids_host(slot_ids, num_slots):
+    """Opt-in check of a host copy of a slot table: every id is -1 (padding)
+    or in [0, num_slots), and no two requests share a slot. Two requests on
+    one slot would have two sets of workgroups committing into the same
+    state, with no defined result. The library cannot see this without a
+    device-to-host read, so the check runs on a table the caller still holds
+    on the host (a list, a numpy array or a CPU tensor). Raises ValueError."""
+    import numpy as np
+    if hasattr(slot_ids, "detach"):
+        if slot_ids.is_cuda:
+            raise ValueError("check_slot_ids_host takes the host copy of the slot table")
+        slot_ids = slot_ids.detach().numpy()
+    a = np.asarray(slot_ids)
+    if a.ndim != 1 or not np.issubdtype(a.dtype, np.integer):
+        raise ValueError("slot table must be a 1-D integer array")
+    bad = (a < -1) | (a >= num_slots)
+    if bad.any():
+        i = int(np.flatnonzero(bad)[0])
+        raise ValueError("slot id %d of request %d is outside [-1, %d)" % (int(a[i]), i, num_slots))
+    live = a[a >= 0]
+    uniq, counts = np.unique(live, return_counts=True)
+    if (counts > 1).any():
+        s = int(uniq[np.flatnonzero(counts > 1)[0]])
+        reqs = np.flatnonzero(a == s).tolist()
+        raise ValueError("slot %d is shared by requests %s" % (s, reqs))
 
 
 def _stream(stream):
@@ -156,43 +244,87 @@ def gdn_spec_scratch_bytes(desc: GdnLayerDesc, batch: int, rows: int, mode="repl
 
 
 def make_pool(ssm, conv) -> GdnPool:
-    return GdnPool(_ptr(ssm), _ptr(conv), int(ssm.shape[0]) if hasattr(ssm, "shape") else 0)
+    return GdnPool(_ptr(ssm), _ptr(conv), int(ssm.shape[0]))
 
 
 def _nbytes(t):
     return t.numel() * t.element_size()
 
 
+def _check_verify_args(desc, ssm, conv, conv_w, x, alpha, beta, slot_ids, rows, scratch, out, err_flag):
+    """Every tensor of a verify call against the header's layouts; returns the batch."""
+    torch = _torch()
+    dev, _ = _check_pool(desc, ssm, conv)
+    HK, HV, dk, dv, W, C = _layer_dims(desc)
+    B = _check_slot_table(slot_ids, dev)
+    st = _storage_dtype(desc)
+    if B > 0:
+        _check(conv_w, "conv_w", st, (C, W), device=dev)
+        _check(x, "x", st, (B, rows, C), device=dev)
+        _check(alpha, "alpha", st, (B, rows, HV), device=dev)
+        _check(beta, "beta", st, (B, rows, HV), device=dev)
+        _check(out, "out", st, (B, rows, HV, dv), device=dev)
+        _check(scratch, "scratch", torch.uint8, device=dev)
+    _check(err_flag, "err_flag", torch.int32, device=dev, optional=True, min_numel=1)
+    return B
+
+
+def _check_commit_args(desc, ssm, conv, slot_ids, accept_len, scratch, err_flag):
+    torch = _torch()
+    dev, _ = _check_pool(desc, ssm, conv)
+    B = _check_slot_table(slot_ids, dev)
+    if B > 0:
+        _check(accept_len, "accept_len", torch.int32, (B,), device=dev)
+        _check(scratch, "scratch", torch.uint8, device=dev)
+    _check(err_flag, "err_flag", torch.int32, device=dev, optional=True, min_numel=1)
+    return B
+
+
 def gdn_spec_verify(desc, ssm, conv, conv_w, x, alpha, beta, slot_ids, rows, mode, scratch, out,
-                    err_flag=None, stream=None, batch=None):
-    """Verify `rows` rows of every request; tensors are device tensors in the header's layouts."""
+                    err_flag=None, stream=None, host_slot_ids=None):
+    """Verify `rows` rows of every request; tensors are device tensors in the
+    header's layouts (checked here). With `host_slot_ids` (the caller's host
+    copy of slot_ids), the slot table is also checked for range and for
+    requests sharing a slot."""
+    B = _check_verify_args(desc, ssm, conv, conv_w, x, alpha, beta, slot_ids, rows, scratch, out, err_flag)
+    if host_slot_ids is not None:
+        check_slot_ids_host(host_slot_ids, int(ssm.shape[0]))
     pool = make_pool(ssm, conv)
-    B = int(slot_ids.shape[0]) if batch is None else batch
     st = load_library().gdn_spec_verify(
         ctypes.byref(desc), ctypes.byref(pool), _ptr(conv_w), _ptr(x), _ptr(alpha), _ptr(beta),
-        _ptr(slot_ids), B, rows, _mode(mode), _ptr(scratch), _nbytes(scratch), _ptr(out),
+        _ptr(slot_ids), B, rows, _mode(mode), _ptr(scratch), _nbytes(scratch) if B else 0, _ptr(out),
         _ptr(err_flag), _stream(stream))
     if st != GDN_OK:
         raise GdnError(st, "gdn_spec_verify")
 
 
 def gdn_spec_commit(desc, ssm, conv, slot_ids, accept_len, rows, mode, scratch, err_flag=None,
-                    stream=None, batch=None):
-    """Commit accept_len[b] rows of each request verified on this scratch."""
+                    stream=None, host_slot_ids=None):
+    """Commit accept_len[b] rows of each request verified on this scratch
+    (tensors checked as for gdn_spec_verify)."""
+    B = _check_commit_args(desc, ssm, conv, slot_ids, accept_len, scratch, err_flag)
+    if host_slot_ids is not None:
+        check_slot_ids_host(host_slot_ids, int(ssm.shape[0]))
     pool = make_pool(ssm, conv)
-    B = int(slot_ids.shape[0]) if batch is None else batch
     st = load_library().gdn_spec_commit(
         ctypes.byref(desc), ctypes.byref(pool), _ptr(slot_ids), _ptr(accept_len), B, rows,
-        _mode(mode), _ptr(scratch), _nbytes(scratch), _ptr(err_flag), _stream(stream))
+        _mode(mode), _ptr(scratch), _nbytes(scratch) if B else 0, _ptr(err_flag), _stream(stream))
     if st != GDN_OK:
         raise GdnError(st, "gdn_spec_commit")
 
 
 class PreparedCommitLayers:
     """gdn_spec_commit_layers over fixed per-layer (ssm, conv, scratch) device
-    tensors, ctypes arguments built once."""
+    tensors, checked and turned into ctypes arguments once."""
 
-    def __init__(self, desc, layers, slot_ids, accept_len, rows, mode, err_flag=None, stream=None):
+    def __init__(self, desc, layers, slot_ids, accept_len, rows, mode, err_flag=None, stream=None,
+                 host_slot_ids=None):
+        if not layers:
+            raise ValueError("no layers")
+        for ssm, conv, sc in layers:
+            B = _check_commit_args(desc, ssm, conv, slot_ids, accept_len, sc, err_flag)
+            if host_slot_ids is not None:
+                check_slot_ids_host(host_slot_ids, int(ssm.shape[0]))
         self.lib = load_library()
         self._keep = (layers, slot_ids, accept_len, err_flag)
         self.desc = desc
@@ -201,7 +333,7 @@ class PreparedCommitLayers:
         self.scratch = (ctypes.c_void_p * L)(*[_ptr(sc) for _, _, sc in layers])
         nbytes = min(_nbytes(sc) for _, _, sc in layers)
         self.args = (ctypes.byref(self.desc), self.pools, self.scratch, L, _ptr(slot_ids), _ptr(accept_len),
-                     int(slot_ids.shape[0]), rows, _mode(mode), nbytes, _ptr(err_flag), _stream(stream))
+                     B, rows, _mode(mode), nbytes, _ptr(err_flag), _stream(stream))
 
     def __call__(self):
         st = self.lib.gdn_spec_commit_layers(*self.args)
@@ -209,15 +341,27 @@ class PreparedCommitLayers:
             raise GdnError(st, "gdn_spec_commit_layers")
 
 
-def gdn_spec_commit_layers(desc, layers, slot_ids, accept_len, rows, mode, err_flag=None, stream=None):
+def gdn_spec_commit_layers(desc, layers, slot_ids, accept_len, rows, mode, err_flag=None, stream=None,
+                           host_slot_ids=None):
     """Commit every layer in one launch; layers = [(ssm, conv, scratch), ...] device tensors."""
-    PreparedCommitLayers(desc, layers, slot_ids, accept_len, rows, mode, err_flag, stream)()
+    PreparedCommitLayers(desc, layers, slot_ids, accept_len, rows, mode, err_flag, stream, host_slot_ids)()
 
 
-def gdn_spec_accept_greedy(draft, target, slot_ids, rows, accept_len, next_token=None, stream=None,
-                           batch=None):
+def _check_accept_args(draft, target, slot_ids, rows, accept_len, next_token):
+    torch = _torch()
+    _check(target, "target", torch.int32, (None, rows))
+    dev = target.device
+    B = int(target.shape[0])
+    _check(draft, "draft", torch.int32, (B, rows - 1), device=dev, optional=rows == 1)
+    _check(slot_ids, "slot_ids", torch.int32, (B,), device=dev, optional=True)
+    _check(accept_len, "accept_len", torch.int32, (B,), device=dev)
+    _check(next_token, "next_token", torch.int32, (B,), device=dev, optional=True)
+    return B
+
+
+def gdn_spec_accept_greedy(draft, target, slot_ids, rows, accept_len, next_token=None, stream=None):
     """accept_len (and next_token) from the draft and target greedy tokens, on the device."""
-    B = int(target.shape[0]) if batch is None else batch
+    B = _check_accept_args(draft, target, slot_ids, rows, accept_len, next_token)
     st = load_library().gdn_spec_accept_greedy(_ptr(draft), _ptr(target), _ptr(slot_ids), B, rows,
                                                _ptr(accept_len), _ptr(next_token), _stream(stream))
     if st != GDN_OK:
@@ -225,16 +369,17 @@ def gdn_spec_accept_greedy(draft, target, slot_ids, rows, accept_len, next_token
 
 
 class Prepared:
-    """Verify and commit on fixed device tensors with the ctypes arguments built
-    once, so that issuing a launch costs one foreign call."""
+    """Verify and commit on fixed device tensors, checked and turned into
+    ctypes arguments once, so that issuing a launch costs one foreign call."""
 
     def __init__(self, desc, ssm, conv, conv_w, x, alpha, beta, slot_ids, accept_len, rows, mode,
                  scratch, out, err_flag=None, stream=None):
+        B = _check_verify_args(desc, ssm, conv, conv_w, x, alpha, beta, slot_ids, rows, scratch, out, err_flag)
+        _check_commit_args(desc, ssm, conv, slot_ids, accept_len, scratch, err_flag)
         self.lib = load_library()
         self._keep = (ssm, conv, conv_w, x, alpha, beta, slot_ids, accept_len, scratch, out, err_flag)
         self.desc = desc
         self.pool = make_pool(ssm, conv)
-        B = int(slot_ids.shape[0])
         st = _stream(stream)
         m = _mode(mode)
         self.vargs = (ctypes.byref(self.desc), ctypes.byref(self.pool), _ptr(conv_w), _ptr(x),
@@ -256,12 +401,14 @@ class Prepared:
 
 
 class PreparedAccept:
-    """gdn_spec_accept_greedy on fixed device tensors, ctypes arguments built once."""
+    """gdn_spec_accept_greedy on fixed device tensors, checked and turned into
+    ctypes arguments once."""
 
     def __init__(self, draft, target, slot_ids, rows, accept_len, next_token=None, stream=None):
+        B = _check_accept_args(draft, target, slot_ids, rows, accept_len, next_token)
         self.lib = load_library()
         self._keep = (draft, target, slot_ids, accept_len, next_token)
-        self.args = (_ptr(draft), _ptr(target), _ptr(slot_ids), int(target.shape[0]), rows,
+        self.args = (_ptr(draft), _ptr(target), _ptr(slot_ids), B, rows,
                      _ptr(accept_len), _ptr(next_token), _stream(stream))
 
     def __call__(self):
@@ -285,17 +432,33 @@ def gdn_spec_attn_scratch_bytes(desc: GdnAttnDesc, batch: int, rows: int, max_bl
     return out.value
 
 
+def _check_attn_args(desc, q, k_cache, v_cache, block_table, seq_lens, scratch, out, err_flag):
+    torch = _torch()
+    Hq, Hkv, D, page = int(desc.num_q_heads), int(desc.num_kv_heads), int(desc.head_dim), int(desc.page_size)
+    _check(q, "q", torch.bfloat16, (None, None, Hq, D))
+    dev = q.device
+    B, R = int(q.shape[0]), int(q.shape[1])
+    _check(k_cache, "k_cache", torch.bfloat16, (None, page, Hkv, D), device=dev)
+    _check(v_cache, "v_cache", torch.bfloat16, tuple(k_cache.shape), device=dev)
+    _check(block_table, "block_table", torch.int32, (B, None), device=dev)
+    _check(seq_lens, "seq_lens", torch.int32, (B,), device=dev)
+    _check(out, "out", torch.bfloat16, (B, R, Hq, D), device=dev)
+    _check(scratch, "scratch", torch.uint8, device=dev)
+    _check(err_flag, "err_flag", torch.int32, device=dev, optional=True, min_numel=1)
+    return B, R
+
+
 class PreparedAttn:
-    """gdn_spec_attn_verify on fixed device tensors, ctypes arguments built once.
-    q [B][R][Hq][D], caches [pages][page_size][Hkv][D] (bf16), block_table
-    [B][max_blocks] and seq_lens [B] (int32), out like q."""
+    """gdn_spec_attn_verify on fixed device tensors, checked and turned into
+    ctypes arguments once. q [B][R][Hq][D], caches [pages][page_size][Hkv][D]
+    (bf16), block_table [B][max_blocks] and seq_lens [B] (int32), out like q."""
 
     def __init__(self, desc, q, k_cache, v_cache, block_table, seq_lens, scratch, out, err_flag=None,
                  stream=None):
+        B, R = _check_attn_args(desc, q, k_cache, v_cache, block_table, seq_lens, scratch, out, err_flag)
         self.lib = load_library()
         self._keep = (q, k_cache, v_cache, block_table, seq_lens, scratch, out, err_flag)
         self.desc = desc
-        B, R = int(q.shape[0]), int(q.shape[1])
         self.args = (ctypes.byref(self.desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), int(k_cache.shape[0]),
                      _ptr(block_table), int(block_table.shape[1]), _ptr(seq_lens), B, R, _ptr(scratch),
                      _nbytes(scratch), _ptr(out), _ptr(err_flag), _stream(stream))

@@ -18,12 +18,13 @@
  *    Here a verify copies the slot's state, runs the rows on the copy and
  *    returns the outputs; a commit runs the first n rows on the slot itself.
  *
- *  - The conv of a verify runs the decode taps over every verify row on the
- *    staged window [live history | verify conv inputs], and the commit leaves
- *    the history as it stands after the accepted rows (FreeToken PR #844,
- *    Design, "Flash-Next target verify", the PLE verify conv paragraph; the
- *    causal_conv1d_spec kernel of LightLLM PR #1330, Summary, does the same
- *    for the GDN layer).
+ *  - The verify's conv applies the same width-W taps a decode step uses to
+ *    each of its rows in turn, reading a window that joins the slot's stored
+ *    history to the new rows' conv inputs; the commit then stores the
+ *    history that results once only the accepted rows have been taken in
+ *    (FreeToken PR #844, Design, "Flash-Next target verify", the paragraph
+ *    on the PLE verify conv; the causal_conv1d_spec kernel named by LightLLM
+ *    PR #1330, Summary, plays the same part for the GDN layer).
  *
  *  - The layer itself is the gated delta rule over L2-normalised q and k
  *    (LightLLM PR #1330, Summary, names the Gated Delta Net / qwen3next
