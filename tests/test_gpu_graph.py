@@ -11,7 +11,7 @@ to its captured sizes (LightLLM PR #1330, Summary: padding of the captured
 decode batch).
 
 Every replay is checked against the eager result, with eager work and
-synchronisation between the replays.
+synchronisation between the replays, and against the CPU oracle.
 """
 import numpy as np
 import pytest
@@ -21,7 +21,14 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 import gpu_harness as gh  # noqa: E402
+import oracle  # noqa: E402
+import parity as par  # noqa: E402
 from linear_attention_verify_amd import workloads as wl  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.Oracle()
 
 
 def _bits(t):
@@ -54,10 +61,11 @@ def _capture(c):
 
 @pytest.mark.parametrize("mode", ["replay", "snapshot"])
 @pytest.mark.parametrize("name", ["tiny-fp32", "low-concurrency"])
-def test_graph_replays_match_eager_bitwise(name, mode):
+def test_graph_replays_match_eager_bitwise(orc, name, mode):
     w = wl.WORKLOADS[name]
     print("graph %s %s" % (name, mode), flush=True)
     c = gh.make_case(w, mode=mode)
+    ref = par.oracle_step(orc, c)
     ssm0, conv0 = c.ssm.clone(), c.conv.clone()
     out_e, ssm_e, conv_e = _eager(c, ssm0, conv0)
     assert int(c.err.item()) == 0
@@ -75,12 +83,15 @@ def test_graph_replays_match_eager_bitwise(name, mode):
         assert torch.equal(_bits(c.out), _bits(out_e)), rep
         assert torch.equal(_bits(c.ssm), _bits(ssm_e)), rep
         assert torch.equal(_bits(c.conv), _bits(conv_e)), rep
+        par.assert_matches(c, ref)
+        par.check_untouched(c)
 
 
-def test_padded_graph_batch_matches_live_requests():
+def test_padded_graph_batch_matches_live_requests(orc):
     """Capture at batch 8; run 5 live requests with the last 3 slots -1. The
     live requests' outputs and committed states equal an eager batch of the 5
-    alone; padding rows come out zero and no other slot changes."""
+    alone and the oracle's; padding rows come out zero and no other slot
+    changes."""
     shape = wl.LayerShape(num_k_heads=2, num_v_heads=4, d_k=128, d_v=128, dtype="bf16")
     w8 = wl.small_workload(shape, batch=8, rows=4, num_slots=12, seed=401)
     sid8, acc8 = wl.draw_requests(w8)
@@ -94,6 +105,7 @@ def test_padded_graph_batch_matches_live_requests():
     c5 = gh.make_case(w5, slot_ids=sid8[:5], accept=acc8[:5], draw=d5)
     out5, ssm5, conv5 = _eager(c5, c5.ssm.clone(), c5.conv.clone())
 
+    ref = par.oracle_step(orc, c8, requests=np.arange(5))
     _restore(c8, ssm0, conv0)
     g = _capture(c8)
     for rep in range(2):
@@ -106,3 +118,5 @@ def test_padded_graph_batch_matches_live_requests():
         assert not bool(c8.out[5:].float().abs().sum()), rep
         assert torch.equal(_bits(c8.ssm), _bits(ssm5)), rep
         assert torch.equal(_bits(c8.conv), _bits(conv5)), rep
+        par.assert_matches(c8, ref)
+        par.check_untouched(c8)

@@ -1,7 +1,7 @@
 """One launch commits every layer of a stack: bit for bit the per-layer
-commits, in both modes, with padding and per-layer pools of different sizes
-(FreeToken PR #844, Design: one upload of the slot and count indices serves
-every state the commit restores)."""
+commits and within tolerance of the oracle, in both modes, with padding and
+per-layer pools of different sizes (FreeToken PR #844, Design: one upload of
+the slot and count indices serves every state the commit restores)."""
 import numpy as np
 import pytest
 
@@ -10,6 +10,8 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 import gpu_harness as gh  # noqa: E402
+import oracle  # noqa: E402
+import parity as par  # noqa: E402
 from linear_attention_verify_amd import binding as bd  # noqa: E402
 from linear_attention_verify_amd import workloads as wl  # noqa: E402
 
@@ -21,6 +23,7 @@ def _bits(t):
 @pytest.mark.parametrize("mode", ["replay", "snapshot"])
 @pytest.mark.parametrize("d,dtype", [(128, "bf16"), (32, "f32")])
 def test_stack_commit_matches_per_layer_commits(d, dtype, mode):
+    orc = oracle.Oracle()
     shape = wl.LayerShape(num_k_heads=2, num_v_heads=4, d_k=d, d_v=d, dtype=dtype)
     L = 3
     base = wl.small_workload(shape, batch=6, rows=5, num_slots=9, seed=700)
@@ -55,6 +58,8 @@ def test_stack_commit_matches_per_layer_commits(d, dtype, mode):
     for layer, (c, (ws, wc)) in enumerate(zip(cases, want)):
         assert torch.equal(_bits(c.ssm), _bits(ws)), layer
         assert torch.equal(_bits(c.conv), _bits(wc)), layer
+        par.assert_matches(c, par.oracle_step(orc, c))
+        par.check_untouched(c)
 
 
 def test_stack_commit_flags_bad_lengths_once_per_call():
