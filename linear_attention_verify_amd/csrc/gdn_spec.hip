@@ -1093,6 +1093,406 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     }
 }
 
+// ---- verify, d = 128, snapshot mode: the state held in registers ------------
+//
+// The arithmetic of gdn_verify_d128_kernel (bf16 inputs), plus the snapshots
+// S_t = a_t S_{t-1} + e_t k_t^T of every row. Those need S_0 once more after
+// the solve, when e_t is known. Here each wave keeps its whole 32 KiB share of
+// a unit's S_0 in registers (8 chunks of 4 K-steps, 128 VGPRs) from the
+// products through the snapshot stores, so S_0 is read from HBM once.
+//
+// With that many registers a compute unit holds one or two workgroups, too few
+// for a one-round grid, so the grid is fixed (one or two workgroups per
+// compute unit) and each workgroup walks a list of (request, pair of value
+// heads) units: w, w + grid, w + 2 grid, ... The next unit's inputs are
+// requested as soon as the current unit's conv has consumed its own, and all
+// 8 chunks of its state as soon as the current unit's snapshots are stored.
+//
+// A unit whose slot id is padding or outside the pool streams nothing: its
+// state resource has size 0, so its chunk loads return zeros without touching
+// memory, the pipeline keeps its shape, and its outputs are stored as zeros.
+//
+// (Replay mode keeps the one-round kernel: measured, walking units with this
+// register-resident stream was slower there, 55.0 against 32.2 us for 64
+// requests x 9 rows at one workgroup per compute unit, and 61 against 57 us for
+// 128 requests x 4 rows at two. The per-unit chain of barriers, LDS round
+// trips and broadcasts needs four resident workgroups to overlap.)
+
+constexpr int kComputeUnits = 256;   // MI355X
+
+// Resident workgroups per compute unit: two while the registers allow (up to
+// 256 per lane), one where more are needed (up to 512).
+template <int NR> __host__ __device__ constexpr int snapshot_groups_per_cu() { return (NR >= 3 && NR <= 6) ? 2 : 1; }
+
+__device__ __forceinline__ int load_uniform(const int32_t *ptr, int idx)
+{
+    // a scalar load: its wait does not drain the vector loads in flight
+    return ((const __attribute__((address_space(4))) int32_t *)ptr)[idx];
+}
+
+template <int NR>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(snapshot_groups_per_cu<NR>())))
+void gdn_verify_d128_snapshot_kernel(const VerifyParams<bf16_t> p, int units)
+{
+    using T = bf16_t;
+    constexpr int D = 128;
+    constexpr int NC = 2 * NR;
+    constexpr int NMF = NC < 16 ? NC : 16;
+    constexpr int NVL = NC - NMF;
+    static_assert(NVL == 0 || NVL == 2, "unsupported row count");
+    constexpr int MS = NVL ? 20 : 16;
+    constexpr int PS = NC + 1;
+    constexpr int CK = 4;
+    constexpr int NCHUNK = D / 4 / CK;
+    constexpr int NT = NR * (NR + 1) / 2;
+    static_assert(NT <= 64, "one coefficient pair per lane");
+    constexpr int NROWS = kWidth - 1 + NR;
+    constexpr int UPR = 64;
+    constexpr int NXU = (NR * UPR + kThreads - 1) / kThreads;
+    static_assert(NXU <= 3 && (kWidth - 1) * UPR <= kThreads, "staged units per thread");
+    constexpr int PFLOATS = 4 * 64 * PS > NROWS * 256 ? 4 * 64 * PS : NROWS * 256;
+
+    __shared__ __align__(16) float Mt[D * MS];
+    __shared__ __align__(16) float P[PFLOATS];
+    __shared__ float invs[4][NC];
+    __shared__ float4 cpark[4][64];
+    __shared__ float gp[4][NR * NC + NR];
+    __shared__ float al[2][NR], be[2][NR];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int HV = p.HV, HK = p.HK;
+    const int G = HV / HK;
+    const int npair = HV / 2;
+    const int kg = lane >> 4;
+    const int m = lane & 15;
+    const int hh = wave >> 1;
+    const int rb = 64 * (wave & 1);
+    const uint32_t soff = (kg * D + rb + 4 * m) * 4;
+    const int jc = tid & (D - 1);
+    const bool isq = tid < D;
+    const int gidx = min(tid, 2 * NR - 1);
+    const int ghh = gidx / NR, gtt = gidx % NR;
+
+    // staged units: unit k of a row starts at local channel 8k; units 0..15
+    // q, 16..31 k, 32..63 v channels of the pair
+    auto unit_channel = [&](int kh, int h0, int k) {
+        return k < 16 ? kh * D + 8 * k : (k < 32 ? HK * D + kh * D + 8 * (k - 16) : 2 * HK * D + h0 * D + 8 * (k - 32));
+    };
+
+    // one unit's inputs, held in registers from their request to the conv
+    int slot_in;
+    T ga, gb;
+    uint4 xu0 = {}, xu1 = {}, xu2 = {}, hu = {};
+    uint2 wA = {}, wV = {};
+    auto load_inputs = [&](int u) {
+        const int b = u / npair, h0 = 2 * (u % npair), kh = h0 / G;
+        slot_in = load_uniform(p.slot_ids, b);
+        const size_t gi = ((size_t)b * NR + gtt) * HV + h0 + ghh;
+        ga = p.alpha[gi];
+        gb = p.beta[gi];
+        const T *xbase = p.x + (size_t)b * NR * p.C;
+        auto xunit = [&](int q) {
+            const int uu = min(q * kThreads + tid, NR * UPR - 1);
+            return *reinterpret_cast<const uint4 *>(xbase + (size_t)(uu / UPR) * p.C + unit_channel(kh, h0, uu % UPR));
+        };
+        xu0 = xunit(0);
+        if constexpr (NXU > 1)
+            xu1 = xunit(1);
+        if constexpr (NXU > 2)
+            xu2 = xunit(2);
+        const int chA = isq ? kh * D + jc : HK * D + kh * D + jc;
+        const int chV = 2 * HK * D + h0 * D + tid;
+        wA = *reinterpret_cast<const uint2 *>(p.conv_w + (size_t)chA * kWidth);
+        wV = *reinterpret_cast<const uint2 *>(p.conv_w + (size_t)chV * kWidth);
+        // a slot id outside the pool reads slot 0's history (inside the pool)
+        const int sl = (slot_in < 0 || slot_in >= p.P) ? 0 : slot_in;
+        const int uh = min(tid, (kWidth - 1) * UPR - 1);
+        hu = *reinterpret_cast<const uint4 *>(p.conv + ((size_t)sl * (kWidth - 1) + uh / UPR) * p.C +
+                                              unit_channel(kh, h0, uh % UPR));
+    };
+    // this wave's head of unit u; an empty resource for a unit that streams nothing
+    auto state_rsrc = [&](int u, bool valid, int slot) {
+        const int h0 = 2 * (u % npair);
+        return valid ? make_rsrc(p.ssm + ((size_t)slot * HV + h0 + hh) * D * D, D * D * 4)
+                     : make_rsrc(p.ssm, 0);
+    };
+
+    int u = blockIdx.x;
+    if (u >= units)
+        return;
+    f32x4 S[NCHUNK][CK];
+    load_inputs(u);
+    bool valid = slot_in >= 0 && slot_in < p.P;
+    {
+        const __amdgpu_buffer_rsrc_t rs = state_rsrc(u, valid, slot_in);
+#pragma unroll
+        for (int c = 0; c < NCHUNK; ++c)
+            load_chunk(S[c], rs, soff, c);
+    }
+
+    while (true) {
+        const int b = u / npair, h0 = 2 * (u % npair), kh = h0 / G;
+        const bool owner = (h0 % G) == 0;
+        const int nxt = u + (int)gridDim.x;
+        const bool has_next = nxt < units;
+        if (!valid && slot_in != -1 && tid == 0 && p.err)
+            atomicOr(p.err, 1);
+
+        if (tid < 2 * NR) {
+            al[ghh][gtt] = to_f32(ga);
+            be[ghh][gtt] = to_f32(gb);
+            if (valid)
+                out_store(&p.as[((size_t)b * HV + h0 + ghh) * NR + gtt], to_f32(ga));
+        }
+        // inputs to LDS (history rows, then the verify rows), and the verify
+        // rows' units straight to the raw-row stash
+        uint4 *Xs = reinterpret_cast<uint4 *>(P);
+        if (tid < (kWidth - 1) * UPR)
+            Xs[tid] = hu;
+        auto stage_xunit = [&](int q, uint4 val) {
+            const int uu = q * kThreads + tid;
+            if (uu < NR * UPR) {
+                const int r = uu / UPR, k = uu % UPR;
+                Xs[(kWidth - 1) * UPR + uu] = val;
+                if (valid && (k >= 32 || owner))
+                    out_store(reinterpret_cast<uint4 *>(p.xs + ((size_t)b * NR + r) * p.C + unit_channel(kh, h0, k)), val);
+            }
+        };
+        stage_xunit(0, xu0);
+        if constexpr (NXU > 1)
+            stage_xunit(1, xu1);
+        if constexpr (NXU > 2)
+            stage_xunit(2, xu2);
+        lds_barrier();
+
+        float v[NR];   // value channel tid = row rb + lane of head h0 + hh
+        {
+            ChanIn<NR, T> cinA, cinV;
+            const T *Xt = reinterpret_cast<const T *>(P);
+            auto tap = [](uint2 w, int k) {
+                return T{(uint16_t)(((k < 2 ? w.x : w.y) >> (16 * (k & 1))) & 0xffffu)};
+            };
+#pragma unroll
+            for (int k = 0; k < kWidth; ++k) {
+                cinA.w[k] = tap(wA, k);
+                cinV.w[k] = tap(wV, k);
+            }
+#pragma unroll
+            for (int r = 0; r < kWidth - 1; ++r) {
+                cinA.hist[r] = Xt[r * 512 + tid];
+                cinV.hist[r] = Xt[r * 512 + 256 + tid];
+            }
+#pragma unroll
+            for (int t = 0; t < NR; ++t) {
+                cinA.x[t] = Xt[(kWidth - 1 + t) * 512 + tid];
+                cinV.x[t] = Xt[(kWidth - 1 + t) * 512 + 256 + tid];
+            }
+            float y[NR];
+            conv_rows(cinA, p.act, y);
+#pragma unroll
+            for (int t = 0; t < NR; ++t)
+                Mt[jc * MS + (isq ? NR + t : t)] = y[t];
+            if (isq) {
+#pragma unroll
+                for (int c = NC; c < MS; ++c)
+                    Mt[jc * MS + c] = 0.0f;
+            }
+            conv_rows(cinV, p.act, v);
+        }
+        // the next unit's inputs load while this one is finished
+        if (has_next)
+            load_inputs(nxt);
+        const bool nvalid = has_next && slot_in >= 0 && slot_in < p.P;
+        lds_barrier();   // the column table and the gates are complete
+
+        float *Pw = P + wave * 64 * PS;
+        float *invw = invs[wave];
+        const float *alw = al[hh], *bew = be[hh];
+        {
+            f32x4 accg = {0.0f, 0.0f, 0.0f, 0.0f};
+            float gv[2] = {0.0f, 0.0f}, dv[2] = {0.0f, 0.0f};
+            gram_share<NVL, MS>(wave, kg, m, Mt, accg, gv, dv);
+            float *g = gp[wave];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int uq = 4 * kg + q;
+                if (uq < NR && m < NMF)
+                    g[uq * NC + m] = accg[q];
+                if (uq == m && m >= NR && m < NMF)
+                    g[NR * NC + m - NR] = accg[q];
+            }
+            if (NVL) {
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    float x = gv[c], y = dv[c];
+                    x += __shfl_xor(x, 16, 64);
+                    x += __shfl_xor(x, 32, 64);
+                    y += __shfl_xor(y, 16, 64);
+                    y += __shfl_xor(y, 32, 64);
+                    gv[c] = x;
+                    dv[c] = y;
+                }
+                if (kg == 0 && m < NR) {
+                    g[m * NC + NMF] = gv[0];
+                    g[m * NC + NMF + 1] = gv[1];
+                }
+                if (lane == 0) {
+                    g[NR * NC + NMF - NR] = dv[0];
+                    g[NR * NC + NMF - NR + 1] = dv[1];
+                }
+            }
+        }
+        lds_barrier();   // from here on each wave finishes its rows alone
+        auto gram = [&](int idx) { return (gp[0][idx] + gp[1][idx]) + (gp[2][idx] + gp[3][idx]); };
+        if (lane < NC) {
+            const float nn = lane < NR ? gram(lane * NC + lane) : gram(NR * NC + lane - NR);
+            invw[lane] = 1.0f / sqrtf(nn + p.eps);
+        }
+        {
+            int t, uu;
+            tri_decode(min(lane, NT - 1), t, uu);
+            float gtu = 1.0f;
+#pragma unroll
+            for (int q = 1; q < NR; ++q)
+                gtu *= (q > uu && q <= t) ? alw[q] : 1.0f;
+            const float iu = invw[uu];
+            const float cA = (uu < t) ? bew[t] * (gtu * (gram(uu * NC + t) * iu * invw[t])) : 0.0f;
+            const float cB = gtu * (gram(uu * NC + NR + t) * iu * invw[NR + t]);
+            const int tt = min(lane, NR - 1);
+            float gt = 1.0f;
+#pragma unroll
+            for (int q = 0; q < NR; ++q)
+                gt *= q <= tt ? alw[q] : 1.0f;
+            cpark[wave][lane] = float4{cA, cB, gt, bew[tt]};
+        }
+
+        // products with the column table
+        const __amdgpu_buffer_rsrc_t nrs = state_rsrc(nxt, nvalid, slot_in);
+        f32x4 acc[4];
+        float pv[4][2];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            acc[q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            pv[q][0] = pv[q][1] = 0.0f;
+        }
+#pragma unroll
+        for (int c = 0; c < NCHUNK; ++c) {
+            mfma_chunk<CK, NVL, MS>(S[c], c, kg, m, Mt, acc, pv);
+            __builtin_amdgcn_sched_barrier(0);   // keeps each chunk's column-table reads next to its products
+        }
+
+        if (m < NMF) {
+            const float ic = invw[m];
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    Pw[(16 * kg + 4 * q + v4) * PS + m] = acc[v4][q] * ic;
+        }
+        if (NVL) {
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4)
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    float x = pv[v4][c];
+                    x += __shfl_xor(x, 16, 64);
+                    x += __shfl_xor(x, 32, 64);
+                    pv[v4][c] = x;
+                }
+            if (kg == 0) {
+                const float i0 = invw[NMF], i1 = invw[NMF + 1];
+#pragma unroll
+                for (int v4 = 0; v4 < 4; ++v4) {
+                    Pw[(4 * m + v4) * PS + NMF] = pv[v4][0] * i0;
+                    Pw[(4 * m + v4) * PS + NMF + 1] = pv[v4][1] * i1;
+                }
+            }
+        }
+        wave_lds_sync();
+
+        // row rb + lane by forward substitution with the broadcast coefficients
+        {
+            float *Pr = Pw + lane * PS;
+            const float4 cc = cpark[wave][lane];
+            float e[NR];
+            // one row at a time: each row's broadcasts are issued where they are used
+#pragma unroll
+            for (int t = 0; t < NR; ++t) {
+                const float r = __builtin_fmaf(-lane_value(cc.z, t), Pr[t], v[t]);
+                float s = lane_value(cc.w, t) * r;
+#pragma unroll
+                for (int uu = 0; uu < t; ++uu)
+                    s = __builtin_fmaf(-lane_value(cc.x, t * (t + 1) / 2 + uu), e[uu], s);
+                e[t] = s;
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int t = 0; t < NR; ++t) {
+                float s = lane_value(cc.z, t) * Pr[NR + t];
+#pragma unroll
+                for (int uu = 0; uu <= t; ++uu)
+                    s = __builtin_fmaf(lane_value(cc.y, t * (t + 1) / 2 + uu), e[uu], s);
+                const size_t oi = (((size_t)b * NR + t) * HV + h0 + hh) * D + rb + lane;
+                out_store(&p.out[oi], from_f32<T>(valid ? p.scale * s : 0.0f));
+                if (valid)
+                    out_store(&p.es[oi], e[t]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // this row of the product table is read only by this lane: reuse it for e_t
+#pragma unroll
+            for (int t = 0; t < NR; ++t)
+                Pr[t] = e[t];
+        }
+        if (owner && valid) {
+            float *ks = p.ks + ((size_t)b * HK + kh) * NR * D;
+            for (int idx = tid; idx < NR * D; idx += kThreads)
+                out_store(&ks[idx], Mt[(idx % D) * MS + idx / D] * invw[idx / D]);
+        }
+
+        {
+            wave_lds_sync();
+            if (valid) {
+                // S_t for every row, by the update the replay commit applies, from
+                // the S_0 still in registers; a head's S_1..S_R are contiguous
+                float *snap_h = p.snap + ((size_t)b * HV + h0 + hh) * NR * D * D;
+#pragma unroll 1
+                for (int t = 0; t < NR; ++t) {
+                    const float a = alw[t];
+                    const float it = invw[t];
+                    float ev[4];
+#pragma unroll
+                    for (int v4 = 0; v4 < 4; ++v4)
+                        ev[v4] = Pw[(4 * m + v4) * PS + t];
+                    float *dst = snap_h + (size_t)t * D * D;
+#pragma unroll
+                    for (int c = 0; c < NCHUNK; ++c)
+#pragma unroll
+                        for (int k = 0; k < CK; ++k) {
+                            const int j = 4 * (c * CK + k) + kg;
+                            const float kk = Mt[j * MS + t] * it;
+#pragma unroll
+                            for (int v4 = 0; v4 < 4; ++v4)
+                                S[c][k][v4] = row_update(S[c][k][v4], a, ev[v4], kk);
+                            stream_store(dst + (size_t)j * D + rb + 4 * m, S[c][k]);
+                        }
+                }
+            }
+            if (has_next) {
+#pragma unroll
+                for (int c = 0; c < NCHUNK; ++c)
+                    load_chunk(S[c], nrs, soff, c);
+            }
+        }
+        if (!has_next)
+            break;
+        u = nxt;
+        valid = nvalid;
+        lds_barrier();   // every wave is done with this unit's LDS
+    }
+}
+
 // ---- commit ----------------------------------------------------------------
 
 template <typename T> struct CommitParams {
@@ -1382,8 +1782,16 @@ template <int D, int NR, typename T, bool SNAP>
 hipError_t launch_verify(const VerifyParams<T> &vp, const VerifyLaunch &l)
 {
     if (D == 128 && (l.HV / l.HK) % 2 == 0) {
-        hipLaunchKernelGGL((gdn_verify_d128_kernel<NR, T, SNAP>), dim3(l.batch * (l.HV / 2)), dim3(kThreads),
-                           0, l.st, vp);
+        if constexpr (sizeof(T) == 2 && SNAP) {
+            const int units = l.batch * (l.HV / 2);
+            const int cap = kComputeUnits * snapshot_groups_per_cu<NR>();
+            const int grid = units < cap ? units : cap;
+            hipLaunchKernelGGL((gdn_verify_d128_snapshot_kernel<NR>), dim3(grid), dim3(kThreads), 0, l.st, vp,
+                               units);
+        } else {
+            hipLaunchKernelGGL((gdn_verify_d128_kernel<NR, T, SNAP>), dim3(l.batch * (l.HV / 2)), dim3(kThreads),
+                               0, l.st, vp);
+        }
     } else {
         hipLaunchKernelGGL((gdn_verify_kernel<D, NR, T, SNAP>), dim3(l.batch * l.HV), dim3(kThreads),
                            0, l.st, vp);
