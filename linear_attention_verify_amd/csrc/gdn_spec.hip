@@ -1455,7 +1455,10 @@ void gdn_verify_d128_snapshot_kernel(const VerifyParams<bf16_t> p, int units)
             wave_lds_sync();
             if (valid) {
                 // S_t for every row, by the update the replay commit applies, from
-                // the S_0 still in registers; a head's S_1..S_R are contiguous
+                // the S_0 still in registers; a head's S_1..S_R are contiguous.
+                // Plain stores: for this volume (R states per request) they
+                // measured faster than nontemporal ones (270 against 285 us for
+                // 64 requests x 9 rows)
                 float *snap_h = p.snap + ((size_t)b * HV + h0 + hh) * NR * D * D;
 #pragma unroll 1
                 for (int t = 0; t < NR; ++t) {
@@ -1475,7 +1478,7 @@ void gdn_verify_d128_snapshot_kernel(const VerifyParams<bf16_t> p, int units)
 #pragma unroll
                             for (int v4 = 0; v4 < 4; ++v4)
                                 S[c][k][v4] = row_update(S[c][k][v4], a, ev[v4], kk);
-                            stream_store(dst + (size_t)j * D + rb + 4 * m, S[c][k]);
+                            *reinterpret_cast<f32x4 *>(dst + (size_t)j * D + rb + 4 * m) = S[c][k];
                         }
                 }
             }
