@@ -507,12 +507,10 @@ def main():
             s += len(group)
 
     run(args.warmup)
-    torch.cuda.synchronize()
-    errs = [int(c.err.item()) for c in cases]
-    if any(errs):
-        raise SystemExit("device error flags set: %s" % errs)
 
-    # timed region: exactly K steps, wall clock bracketed by synchronisation
+    # timed region: exactly K steps, wall clock bracketed by synchronisation.
+    # The device error flags are read after the timed passes (they are
+    # sticky), so that no host reads sit between the warmup and the region.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     run(args.steps)
@@ -528,6 +526,9 @@ def main():
     launches = sum(n for n, _ in marks)
     phase = [sum(ev[i].elapsed_time(ev[i + 1]) for _, ev in marks) * 1e-3 / launches for i in range(3)]
     tv, ta, tc = (np.array(x) for x in phase)
+    errs = torch.stack([c.err for c in cases]).cpu().numpy().ravel().tolist()
+    if any(errs):
+        raise SystemExit("device error flags set: %s" % errs)
 
     vbytes, cbytes = algorithmic_bytes(w, base.accept_np, args.mode)
     rows_per_step = w.batch * w.rows

@@ -1093,6 +1093,339 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     }
 }
 
+// ---- verify, d = 128, small batches: a unit split over four workgroups --------
+//
+// With fewer (request, pair of value heads) units than compute units, one
+// workgroup per unit leaves most of the chip idle and each
+// workgroup streams 128 KiB in a long dependent chain. Here a workgroup takes
+// one 64-row block of one value head (a quarter of a unit), and its four waves
+// split the block's 128 key indices: wave w streams K-steps 8w..8w+7 (8 KiB,
+// both chunks requested at the start) into partial products of all 64 rows,
+// which are summed through LDS before wave 0 solves the 64 rows. Each
+// workgroup repeats the unit's conv of the key head and its Gram matrix: more
+// arithmetic, no more HBM traffic (the repeated input loads hit the caches).
+// In snapshot mode each wave then applies every row's update to its two
+// chunks, still in registers, and stores its part of S_1..S_R. Both modes
+// form the products in the same order, so they agree bit for bit.
+template <int NR, bool SNAP>
+__global__ __launch_bounds__(kThreads) void gdn_verify_d128_split_kernel(const VerifyParams<bf16_t> p)
+{
+    using T = bf16_t;
+    constexpr int D = 128;
+    constexpr int NC = 2 * NR;
+    constexpr int NMF = NC < 16 ? NC : 16;
+    constexpr int NVL = NC - NMF;
+    static_assert(NVL == 0 || NVL == 2, "unsupported row count");
+    constexpr int MS = NVL ? 20 : 16;
+    constexpr int PS = NC + 1;
+    constexpr int CK = 4;
+    constexpr int NT = NR * (NR + 1) / 2;
+    static_assert(NT <= 64, "one coefficient pair per lane");
+    constexpr int NROWS = kWidth - 1 + NR;
+    constexpr int UPR = 40;   // 16-byte units per staged row: q 16 | k 16 | v 8 (64 channels)
+    constexpr int NU = NROWS * UPR;
+    constexpr int NUT = (NU + kThreads - 1) / kThreads;   // staged units per thread
+    static_assert(NUT <= 2, "staged units per thread");
+    constexpr int XFLOATS = NROWS * UPR * 4;               // staged rows, as floats
+    constexpr int RFLOATS = 4 * 64 * PS;                    // per-wave partial products
+    constexpr int PFLOATS = XFLOATS > RFLOATS ? XFLOATS : RFLOATS;
+
+    __shared__ __align__(16) float Mt[D * MS];
+    __shared__ __align__(16) float P[PFLOATS];   // staged inputs; then the four waves' partial products
+    __shared__ float invs[NC];
+    __shared__ float gp[4][NR * NC + NR];
+    __shared__ float al[NR], be[NR];
+    __shared__ float eb[SNAP ? NR * 64 : 1];   // e_t of the block's rows, for the snapshots
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int HV = p.HV, HK = p.HK;
+    const int G = HV / HK;
+    const int npair = HV / 2;
+    const int b = blockIdx.x / (npair * 4);
+    const int rem = blockIdx.x % (npair * 4);
+    const int h0 = 2 * (rem / 4);
+    const int blk = rem % 4;
+    const int h = h0 + (blk >> 1);       // this workgroup's value head
+    const int rb = 64 * (blk & 1);       // and its 64-row block
+    const int kh = h0 / G;
+    const bool owner = (h0 % G) == 0;    // the key head's first pair stores its q/k inputs
+    const int slot_in = p.slot_ids[b];
+
+    // staged unit k of a row: q units 0..15, k units 16..31, then the block's
+    // value channels rb..rb+63 of head h; unit k starts at local channel 8k
+    auto unit_channel = [&](int k) {
+        return k < 16 ? kh * D + 8 * k : (k < 32 ? HK * D + kh * D + 8 * (k - 16) : 2 * HK * D + h * D + rb + 8 * (k - 32));
+    };
+    const int gt_ = min(tid, NR - 1);
+    const size_t gi = ((size_t)b * NR + gt_) * HV + h;
+    const T ga = p.alpha[gi], gb = p.beta[gi];
+    const int jc = tid & (D - 1);
+    const bool isq = tid < D;
+    const int chA = isq ? kh * D + jc : HK * D + kh * D + jc;
+    const int chV = 2 * HK * D + h * D + rb + min(tid, 63);
+    const uint2 wA = *reinterpret_cast<const uint2 *>(p.conv_w + (size_t)chA * kWidth);
+    const uint2 wV = *reinterpret_cast<const uint2 *>(p.conv_w + (size_t)chV * kWidth);
+    const bool bad = slot_in < 0 || slot_in >= p.P;
+    const int slot = bad ? 0 : slot_in;
+    // staged rows: history (from the pool) then the verify rows
+    uint4 su[NUT];
+#pragma unroll
+    for (int q = 0; q < NUT; ++q) {
+        const int uu = min(q * kThreads + tid, NU - 1);
+        const int r = uu / UPR, k = uu % UPR;
+        const T *row = r < kWidth - 1 ? p.conv + ((size_t)slot * (kWidth - 1) + r) * p.C
+                                      : p.x + ((size_t)b * NR + (r - (kWidth - 1))) * p.C;
+        su[q] = *reinterpret_cast<const uint4 *>(row + unit_channel(k));
+    }
+    if (bad) {
+        if (slot_in != -1 && tid == 0 && blk == 0 && p.err)
+            atomicOr(p.err, 1);
+        for (int idx = tid; idx < NR * 64; idx += kThreads) {
+            const int t = idx / 64, i = idx % 64;
+            out_store(&p.out[(((size_t)b * NR + t) * HV + h) * D + rb + i], from_f32<T>(0.0f));
+        }
+        return;
+    }
+
+    // this wave's two chunks: K-steps 8w .. 8w + 7 of the block
+    const int kg = lane >> 4;
+    const int m = lane & 15;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.ssm + ((size_t)slot * HV + h) * D * D, D * D * 4);
+    const uint32_t soff = (kg * D + rb + 4 * m) * 4;
+    f32x4 c0[CK], c1[CK];
+    load_chunk(c0, rs, soff, 2 * wave);
+    load_chunk(c1, rs, soff, 2 * wave + 1);
+    __builtin_amdgcn_sched_barrier(0);
+
+    if (tid < NR) {
+        al[tid] = to_f32(ga);
+        be[tid] = to_f32(gb);
+        if (rb == 0)
+            out_store(&p.as[((size_t)b * HV + h) * NR + tid], to_f32(ga));
+    }
+    uint4 *Xs = reinterpret_cast<uint4 *>(P);
+#pragma unroll
+    for (int q = 0; q < NUT; ++q) {
+        const int uu = q * kThreads + tid;
+        if (uu < NU) {
+            Xs[uu] = su[q];
+            const int r = uu / UPR, k = uu % UPR;
+            // verify rows to the raw-row stash: the block's value channels, and
+            // the key head's q/k channels from the first block of its first pair
+            if (r >= kWidth - 1 && (k >= 32 || (owner && blk == 0)))
+                out_store(reinterpret_cast<uint4 *>(p.xs + ((size_t)b * NR + r - (kWidth - 1)) * p.C + unit_channel(k)), su[q]);
+        }
+    }
+    lds_barrier();
+    float v[NR];   // value channel rb + tid of head h (threads < 64)
+    {
+        ChanIn<NR, T> cinA, cinV;
+        const T *Xt = reinterpret_cast<const T *>(P);
+        auto tap = [](uint2 w, int k) {
+            return T{(uint16_t)(((k < 2 ? w.x : w.y) >> (16 * (k & 1))) & 0xffffu)};
+        };
+#pragma unroll
+        for (int k = 0; k < kWidth; ++k) {
+            cinA.w[k] = tap(wA, k);
+            cinV.w[k] = tap(wV, k);
+        }
+        const int cv = 256 + min(tid, 63);   // local channel of the value input
+#pragma unroll
+        for (int r = 0; r < kWidth - 1; ++r) {
+            cinA.hist[r] = Xt[r * UPR * 8 + tid];
+            cinV.hist[r] = Xt[r * UPR * 8 + cv];
+        }
+#pragma unroll
+        for (int t = 0; t < NR; ++t) {
+            cinA.x[t] = Xt[(kWidth - 1 + t) * UPR * 8 + tid];
+            cinV.x[t] = Xt[(kWidth - 1 + t) * UPR * 8 + cv];
+        }
+        float y[NR];
+        conv_rows(cinA, p.act, y);
+#pragma unroll
+        for (int t = 0; t < NR; ++t)
+            Mt[jc * MS + (isq ? NR + t : t)] = y[t];
+        if (isq) {
+#pragma unroll
+            for (int c = NC; c < MS; ++c)
+                Mt[jc * MS + c] = 0.0f;
+        }
+        conv_rows(cinV, p.act, v);
+    }
+    lds_barrier();   // the column table and the gates are complete
+
+    // M^T M, each wave a quarter of the key indices (as in the one-round kernel)
+    {
+        f32x4 accg = {0.0f, 0.0f, 0.0f, 0.0f};
+        float gv[2] = {0.0f, 0.0f}, dv[2] = {0.0f, 0.0f};
+        gram_share<NVL, MS>(wave, kg, m, Mt, accg, gv, dv);
+        float *g = gp[wave];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int uq = 4 * kg + q;
+            if (uq < NR && m < NMF)
+                g[uq * NC + m] = accg[q];
+            if (uq == m && m >= NR && m < NMF)
+                g[NR * NC + m - NR] = accg[q];
+        }
+        if (NVL) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                float x = gv[c], y = dv[c];
+                x += __shfl_xor(x, 16, 64);
+                x += __shfl_xor(x, 32, 64);
+                y += __shfl_xor(y, 16, 64);
+                y += __shfl_xor(y, 32, 64);
+                gv[c] = x;
+                dv[c] = y;
+            }
+            if (kg == 0 && m < NR) {
+                g[m * NC + NMF] = gv[0];
+                g[m * NC + NMF + 1] = gv[1];
+            }
+            if (lane == 0) {
+                g[NR * NC + NMF - NR] = dv[0];
+                g[NR * NC + NMF - NR + 1] = dv[1];
+            }
+        }
+    }
+
+    // partial products of this wave's K-steps: all 64 rows, every column
+    f32x4 acc[4];
+    float pv[4][2];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        acc[q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        pv[q][0] = pv[q][1] = 0.0f;
+    }
+    mfma_chunk<CK, NVL, MS>(c0, 2 * wave, kg, m, Mt, acc, pv);
+    mfma_chunk<CK, NVL, MS>(c1, 2 * wave + 1, kg, m, Mt, acc, pv);
+    lds_barrier();   // the Gram shares are in; the staged inputs are no longer read
+    float *Pw = P + wave * 64 * PS;
+    if (m < NMF) {
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                Pw[(16 * kg + 4 * q + v4) * PS + m] = acc[v4][q];
+    }
+    if (NVL) {
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4)
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                float x = pv[v4][c];
+                x += __shfl_xor(x, 16, 64);
+                x += __shfl_xor(x, 32, 64);
+                pv[v4][c] = x;
+            }
+        if (kg == 0) {
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4) {
+                Pw[(4 * m + v4) * PS + NMF] = pv[v4][0];
+                Pw[(4 * m + v4) * PS + NMF + 1] = pv[v4][1];
+            }
+        }
+    }
+    auto gram = [&](int idx) { return (gp[0][idx] + gp[1][idx]) + (gp[2][idx] + gp[3][idx]); };
+    if (tid < NC) {
+        const float nn = tid < NR ? gram(tid * NC + tid) : gram(NR * NC + tid - NR);
+        invs[tid] = 1.0f / sqrtf(nn + p.eps);
+    }
+    lds_barrier();   // partial products and norms are complete
+
+    if (wave == 0) {
+        // coefficients, one pair (t, u) per lane, as in the one-round kernel
+        float cA, cB, cG, cb;
+        {
+            int t, uu;
+            tri_decode(min(lane, NT - 1), t, uu);
+            float gtu = 1.0f;
+#pragma unroll
+            for (int q = 1; q < NR; ++q)
+                gtu *= (q > uu && q <= t) ? al[q] : 1.0f;
+            const float iu = invs[uu];
+            cA = (uu < t) ? be[t] * (gtu * (gram(uu * NC + t) * iu * invs[t])) : 0.0f;
+            cB = gtu * (gram(uu * NC + NR + t) * iu * invs[NR + t]);
+            const int tt = min(lane, NR - 1);
+            float g = 1.0f;
+#pragma unroll
+            for (int q = 0; q < NR; ++q)
+                g *= q <= tt ? al[q] : 1.0f;
+            cG = g;
+            cb = be[tt];
+        }
+        // row rb + lane: the four waves' partial products, scaled by the norms
+        float pr[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            float s = 0.0f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+                s += P[(w * 64 + lane) * PS + c];
+            pr[c] = s * invs[c];
+        }
+        float e[NR];
+#pragma unroll
+        for (int t = 0; t < NR; ++t) {
+            const float r = __builtin_fmaf(-lane_value(cG, t), pr[t], v[t]);
+            float s = lane_value(cb, t) * r;
+#pragma unroll
+            for (int uu = 0; uu < t; ++uu)
+                s = __builtin_fmaf(-lane_value(cA, t * (t + 1) / 2 + uu), e[uu], s);
+            e[t] = s;
+        }
+#pragma unroll
+        for (int t = 0; t < NR; ++t) {
+            float s = lane_value(cG, t) * pr[NR + t];
+#pragma unroll
+            for (int uu = 0; uu <= t; ++uu)
+                s = __builtin_fmaf(lane_value(cB, t * (t + 1) / 2 + uu), e[uu], s);
+            const size_t oi = (((size_t)b * NR + t) * HV + h) * D + rb + lane;
+            out_store(&p.out[oi], from_f32<T>(p.scale * s));
+            out_store(&p.es[oi], e[t]);
+            if (SNAP)
+                eb[t * 64 + lane] = e[t];
+        }
+    } else if (owner && blk == 0) {
+        // normalised keys for the commit (three waves of the key head's first block)
+        float *ks = p.ks + ((size_t)b * HK + kh) * NR * D;
+        for (int idx = tid - 64; idx < NR * D; idx += kThreads - 64)
+            out_store(&ks[idx], Mt[(idx % D) * MS + idx / D] * invs[idx / D]);
+    }
+    if (SNAP) {
+        lds_barrier();   // e_t of every row of the block
+        // S_t for every row by the update the replay commit applies: this
+        // wave's K-steps of the block, from the S_0 still in registers
+        float *snap_h = p.snap + ((size_t)b * HV + h) * NR * D * D;
+#pragma unroll 1
+        for (int t = 0; t < NR; ++t) {
+            const float a = al[t];
+            const float it = invs[t];
+            float ev[4];
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4)
+                ev[v4] = eb[t * 64 + 4 * m + v4];
+            float *dst = snap_h + (size_t)t * D * D;
+            auto snap_chunk = [&](f32x4 (&sc)[CK], int c) {
+#pragma unroll
+                for (int k = 0; k < CK; ++k) {
+                    const int j = 4 * (c * CK + k) + kg;
+                    const float kk = Mt[j * MS + t] * it;
+#pragma unroll
+                    for (int v4 = 0; v4 < 4; ++v4)
+                        sc[k][v4] = row_update(sc[k][v4], a, ev[v4], kk);
+                    *reinterpret_cast<f32x4 *>(dst + (size_t)j * D + rb + 4 * m) = sc[k];
+                }
+            };
+            snap_chunk(c0, 2 * wave);
+            snap_chunk(c1, 2 * wave + 1);
+        }
+    }
+}
+
 // ---- verify, d = 128, snapshot mode: the state held in registers ------------
 //
 // The arithmetic of gdn_verify_d128_kernel (bf16 inputs), plus the snapshots
@@ -1519,10 +1852,9 @@ template <typename T> struct CommitParams {
 // (8 KiB measured faster than 4, 16, 32 or 64 KiB parts).
 template <int D> __host__ __device__ constexpr int commit_parts() { return D * D * 4 > 8192 ? D * D * 4 / 8192 : 1; }
 
-template <int D, typename T, bool SNAP>
+template <int D, typename T, bool SNAP, int NPART>
 __device__ __forceinline__ void commit_body(const CommitParams<T> &p)
 {
-    constexpr int NPART = commit_parts<D>();
     constexpr int JW = D / NPART;          // key rows of this part
     constexpr int LPJ = D / 4;             // lanes per key row, 4 state rows each
     constexpr int GJ = kThreads / LPJ;     // key rows per pass
@@ -1678,10 +2010,10 @@ __device__ __forceinline__ void commit_body(const CommitParams<T> &p)
     }
 }
 
-template <int D, typename T, bool SNAP>
+template <int D, typename T, bool SNAP, int NPART>
 __global__ __launch_bounds__(kThreads) void gdn_commit_kernel(const CommitParams<T> p)
 {
-    commit_body<D, T, SNAP>(p);
+    commit_body<D, T, SNAP, NPART>(p);
 }
 
 // A hybrid stack commits every GDN layer in one launch: grid row y is layer
@@ -1701,7 +2033,7 @@ struct CommitStack {
     size_t xs, es, ks, as, snap;   // scratch part offsets, the same in every layer
 };
 
-template <int D, typename T, bool SNAP>
+template <int D, typename T, bool SNAP, int NPART>
 __global__ __launch_bounds__(kThreads) void gdn_commit_stack_kernel(const CommitParams<T> p0, const CommitStack st)
 {
     CommitParams<T> p = p0;
@@ -1714,7 +2046,7 @@ __global__ __launch_bounds__(kThreads) void gdn_commit_stack_kernel(const Commit
     p.ks = reinterpret_cast<const float *>(l.scratch + st.ks);
     p.as = reinterpret_cast<const float *>(l.scratch + st.as);
     p.snap = SNAP ? reinterpret_cast<const float *>(l.scratch + st.snap) : nullptr;
-    commit_body<D, T, SNAP>(p);
+    commit_body<D, T, SNAP, NPART>(p);
 }
 
 // ---- greedy acceptance --------------------------------------------------------
@@ -1785,16 +2117,28 @@ template <int D, int NR, typename T, bool SNAP>
 hipError_t launch_verify(const VerifyParams<T> &vp, const VerifyLaunch &l)
 {
     if (D == 128 && (l.HV / l.HK) % 2 == 0) {
-        if constexpr (sizeof(T) == 2 && SNAP) {
-            const int units = l.batch * (l.HV / 2);
-            const int cap = kComputeUnits * snapshot_groups_per_cu<NR>();
-            const int grid = units < cap ? units : cap;
-            hipLaunchKernelGGL((gdn_verify_d128_snapshot_kernel<NR>), dim3(grid), dim3(kThreads), 0, l.st, vp,
-                               units);
-        } else {
-            hipLaunchKernelGGL((gdn_verify_d128_kernel<NR, T, SNAP>), dim3(l.batch * (l.HV / 2)), dim3(kThreads),
-                               0, l.st, vp);
+        const int units = l.batch * (l.HV / 2);
+        bool done = false;
+        if constexpr (sizeof(T) == 2) {
+            // fewer units than compute units: split each over four workgroups
+            // (measured: 1 request, replay 7.3 -> 6.1 us; at 16 requests, one unit
+            // per compute unit, the split was slower in replay mode, 12.0 against
+            // 11.0 us). One threshold for both modes keeps their products in the
+            // same order, so replay and snapshot agree bit for bit
+            if (units < kComputeUnits) {
+                hipLaunchKernelGGL((gdn_verify_d128_split_kernel<NR, SNAP>), dim3(units * 4), dim3(kThreads), 0,
+                                   l.st, vp);
+                done = true;
+            } else if constexpr (SNAP) {
+                const int cap = kComputeUnits * snapshot_groups_per_cu<NR>();
+                const int grid = units < cap ? units : cap;
+                hipLaunchKernelGGL((gdn_verify_d128_snapshot_kernel<NR>), dim3(grid), dim3(kThreads), 0, l.st, vp,
+                                   units);
+                done = true;
+            }
         }
+        if (!done)
+            hipLaunchKernelGGL((gdn_verify_d128_kernel<NR, T, SNAP>), dim3(units), dim3(kThreads), 0, l.st, vp);
     } else {
         hipLaunchKernelGGL((gdn_verify_kernel<D, NR, T, SNAP>), dim3(l.batch * l.HV), dim3(kThreads),
                            0, l.st, vp);
@@ -1863,17 +2207,26 @@ hipError_t verify_typed(const Checked &c, const gdn_layer_desc *d, const gdn_poo
     return snapshot ? verify_dim<T, true>(c.D, rows, vp, l) : verify_dim<T, false>(c.D, rows, vp, l);
 }
 
+template <int D, typename T, bool SNAP, int NPART>
+hipError_t launch_commit_parts(const CommitParams<T> &cp, const CommitStack *stack, int layers, int blocks,
+                               hipStream_t st)
+{
+    const int groups = (blocks + kXcds - 1) / kXcds;
+    const dim3 grid(groups * kXcds * NPART, layers);
+    if (stack)
+        hipLaunchKernelGGL((gdn_commit_stack_kernel<D, T, SNAP, NPART>), grid, dim3(kThreads), 0, st, cp, *stack);
+    else
+        hipLaunchKernelGGL((gdn_commit_kernel<D, T, SNAP, NPART>), grid, dim3(kThreads), 0, st, cp);
+    return hipGetLastError();
+}
+
 template <int D, typename T, bool SNAP>
 hipError_t launch_commit(const CommitParams<T> &cp, const CommitStack *stack, int layers, int blocks,
                          hipStream_t st)
 {
-    const int groups = (blocks + kXcds - 1) / kXcds;
-    const dim3 grid(groups * kXcds * commit_parts<D>(), layers);
-    if (stack)
-        hipLaunchKernelGGL((gdn_commit_stack_kernel<D, T, SNAP>), grid, dim3(kThreads), 0, st, cp, *stack);
-    else
-        hipLaunchKernelGGL((gdn_commit_kernel<D, T, SNAP>), grid, dim3(kThreads), 0, st, cp);
-    return hipGetLastError();
+    // 8 KiB parts at every batch size: 16 KiB parts for 16 requests and 4 KiB
+    // parts for one request measured no faster
+    return launch_commit_parts<D, T, SNAP, commit_parts<D>()>(cp, stack, layers, blocks, st);
 }
 
 template <typename T, bool SNAP>

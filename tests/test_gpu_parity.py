@@ -153,6 +153,22 @@ def test_head_groups_at_d128(orc, hk, hv, dtype, rows, mode):
     check_untouched(c)
 
 
+@pytest.mark.parametrize("rows", [1, 2, 3, 5, 8, 9])
+def test_large_batch_kernel_at_every_row_count(orc, rows):
+    """512 (request, value-head pair) units at d = 128, bf16: the one-round
+    kernel (smaller batches take the split kernel), ragged accept lengths and
+    two padding requests; every request against the oracle."""
+    w = wl.small_workload(wl.QWEN3_NEXT_LAYER, batch=32, rows=rows, num_slots=80, seed=900 + rows)
+    slot_ids, _ = wl.draw_requests(w)
+    slot_ids[[5, 17]] = -1
+    accept = np.random.default_rng(rows).integers(0, rows + 1, size=32).astype(np.int32)
+    c = gh.make_case(w, slot_ids=slot_ids, accept=accept)
+    _log("one-round kernel rows=%d" % rows)
+    check_layer(orc, c)
+    check_untouched(c)
+    assert not bool(c.out[[5, 17]].float().abs().sum())
+
+
 @pytest.mark.parametrize("mode", ["replay", "snapshot"])
 @pytest.mark.parametrize("d,dtype", PAIRS)
 def test_identity_gate_leaves_the_state_bitwise(orc, d, dtype, mode):
@@ -201,7 +217,7 @@ def test_zero_and_eps_dominated_keys_and_queries(orc, d, dtype, mode):
     assert bool(o[:, :, 4:6].abs().sum()), "eps-dominated heads came out zero"
 
 
-@pytest.mark.parametrize("name", ["tiny-fp32", "low-concurrency"])
+@pytest.mark.parametrize("name", ["tiny-fp32", "single-stream", "low-concurrency", "saturated-b64"])
 def test_replay_and_snapshot_agree_bitwise(name):
     w = wl.WORKLOADS[name]
     cr = gh.make_case(w, mode="replay")
