@@ -71,6 +71,30 @@ gdn_status gdn_spec_attn_verify(const gdn_attn_desc *desc, const void *q, const 
                                 int32_t rows, void *scratch, size_t scratch_bytes, void *out,
                                 int32_t *err_flag, void *stream);
 
+/*
+ * gdn_spec_attn_verify with no scratch argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, serving loops and
+ * harnesses that forbid hipMalloc. It allocates nothing and calls no
+ * allocating routine. The partial results go to a file-scope device array of
+ * GDN_SPEC_ATTN_STATIC_SCRATCH_BYTES (64 MiB) that every GPU the library runs
+ * on holds until the process ends; its address is looked up on the first call
+ * on each device. Nothing in it needs to start at zero: each call writes every
+ * record it reads back.
+ *
+ * A call whose gdn_spec_attn_scratch_bytes() exceeds the array returns
+ * GDN_ERR_SCRATCH_TOO_SMALL before anything is launched; all other arguments,
+ * results and errors are those of gdn_spec_attn_verify. Every call on one GPU
+ * uses that GPU's array and leaves the last call's contents in it: calls that
+ * may overlap on one GPU (other streams, other host threads) race and must be
+ * ordered by the caller. GDN_ERR_HIP if the array's address cannot be found.
+ */
+#define GDN_SPEC_ATTN_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+
+gdn_status gdn_spec_attn_verify_static(const gdn_attn_desc *desc, const void *q, const void *k_cache,
+                                       const void *v_cache, int32_t num_pages, const int32_t *block_table,
+                                       int32_t max_blocks, const int32_t *seq_lens, int32_t batch,
+                                       int32_t rows, void *out, int32_t *err_flag, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

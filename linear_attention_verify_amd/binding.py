@@ -29,7 +29,11 @@ GDN_ACT_NONE = 1
 MODES = {"replay": GDN_COMMIT_REPLAY, "snapshot": GDN_COMMIT_SNAPSHOT}
 
 EXPORTS = ("gdn_spec_scratch_bytes", "gdn_spec_verify", "gdn_spec_commit", "gdn_spec_commit_layers",
-           "gdn_spec_accept_greedy", "gdn_strerror", "gdn_spec_attn_scratch_bytes", "gdn_spec_attn_verify")
+           "gdn_spec_accept_greedy", "gdn_strerror", "gdn_spec_attn_scratch_bytes", "gdn_spec_attn_verify",
+           "gdn_spec_attn_verify_static")
+
+# bytes of the device array behind gdn_spec_attn_verify_static (GDN_SPEC_ATTN_STATIC_SCRATCH_BYTES)
+ATTN_STATIC_SCRATCH_BYTES = 64 << 20
 
 
 class GdnLayerDesc(ctypes.Structure):
@@ -102,6 +106,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.gdn_spec_attn_scratch_bytes.argtypes = [pattn, i32, i32, i32, ctypes.POINTER(sz)]
     lib.gdn_spec_attn_verify.restype = ctypes.c_int
     lib.gdn_spec_attn_verify.argtypes = [pattn, vp, vp, vp, i32, vp, i32, vp, i32, i32, vp, sz, vp, vp, vp]
+    lib.gdn_spec_attn_verify_static.restype = ctypes.c_int
+    lib.gdn_spec_attn_verify_static.argtypes = [pattn, vp, vp, vp, i32, vp, i32, vp, i32, i32, vp, vp, vp]
     lib.gdn_strerror.restype = ctypes.c_char_p
     lib.gdn_strerror.argtypes = [ctypes.c_int]
     if path is None:
@@ -432,7 +438,7 @@ def gdn_spec_attn_scratch_bytes(desc: GdnAttnDesc, batch: int, rows: int, max_bl
     return out.value
 
 
-def _check_attn_args(desc, q, k_cache, v_cache, block_table, seq_lens, scratch, out, err_flag):
+def _check_attn_args(desc, q, k_cache, v_cache, block_table, seq_lens, scratch, out, err_flag, static=False):
     torch = _torch()
     Hq, Hkv, D, page = int(desc.num_q_heads), int(desc.num_kv_heads), int(desc.head_dim), int(desc.page_size)
     _check(q, "q", torch.bfloat16, (None, None, Hq, D))
@@ -443,7 +449,8 @@ def _check_attn_args(desc, q, k_cache, v_cache, block_table, seq_lens, scratch, 
     _check(block_table, "block_table", torch.int32, (B, None), device=dev)
     _check(seq_lens, "seq_lens", torch.int32, (B,), device=dev)
     _check(out, "out", torch.bfloat16, (B, R, Hq, D), device=dev)
-    _check(scratch, "scratch", torch.uint8, device=dev)
+    if not static:
+        _check(scratch, "scratch", torch.uint8, device=dev)
     _check(err_flag, "err_flag", torch.int32, device=dev, optional=True, min_numel=1)
     return B, R
 
@@ -472,3 +479,15 @@ class PreparedAttn:
 def gdn_spec_attn_verify(desc, q, k_cache, v_cache, block_table, seq_lens, scratch, out, err_flag=None,
                          stream=None):
     PreparedAttn(desc, q, k_cache, v_cache, block_table, seq_lens, scratch, out, err_flag, stream)()
+
+
+def gdn_spec_attn_verify_static(desc, q, k_cache, v_cache, block_table, seq_lens, out, err_flag=None,
+                                stream=None):
+    """gdn_spec_attn_verify on the library's own device array instead of a
+    scratch argument: no allocation anywhere (tensors checked as there)."""
+    B, R = _check_attn_args(desc, q, k_cache, v_cache, block_table, seq_lens, None, out, err_flag, static=True)
+    st = load_library().gdn_spec_attn_verify_static(
+        ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), int(k_cache.shape[0]), _ptr(block_table),
+        int(block_table.shape[1]), _ptr(seq_lens), B, R, _ptr(out), _ptr(err_flag), _stream(stream))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_spec_attn_verify_static")

@@ -35,10 +35,18 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
 #include <stddef.h>
 #include <stdint.h>
 
 #include "spec_attention.h"
+
+// Scratch of gdn_spec_attn_verify_static: the split records and pair starts
+// of one call, on every GPU the library runs on, for the life of the process.
+// Host code never uses this name as an address (on the host it is only a
+// stand-in for the symbol): the device address comes from
+// hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[GDN_SPEC_ATTN_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -776,6 +784,90 @@ gdn_status attn_layout(const gdn_attn_desc *d, int batch, int rows, int max_bloc
 
 bool aligned16a(const void *ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
+// Checks that need no scratch, then the launch of both kernels on `buf`.
+gdn_status attn_check(const gdn_attn_desc *desc, const void *q, const void *k_cache, const void *v_cache,
+                      int32_t num_pages, const int32_t *block_table, const int32_t *seq_lens, void *out)
+{
+    if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out || num_pages < 1 || !aligned16a(q) ||
+        !aligned16a(k_cache) || !aligned16a(v_cache) || !aligned16a(out))
+        return GDN_ERR_INVALID_ARG;
+    return GDN_OK;
+}
+
+gdn_status attn_launch(const gdn_attn_desc *desc, const AttnLayout &l, const void *q, const void *k_cache,
+                       const void *v_cache, int32_t num_pages, const int32_t *block_table, int32_t max_blocks,
+                       const int32_t *seq_lens, int32_t batch, int32_t rows, void *buf, void *out,
+                       int32_t *err_flag, hipStream_t st)
+{
+    AttnParams p;
+    p.q = static_cast<const uint16_t *>(q);
+    p.kc = static_cast<const uint16_t *>(k_cache);
+    p.vc = static_cast<const uint16_t *>(v_cache);
+    p.bt = block_table;
+    p.seq = seq_lens;
+    p.rec = static_cast<float *>(buf);
+    p.starts = reinterpret_cast<int32_t *>(static_cast<char *>(buf) + l.starts);
+    p.out = static_cast<uint16_t *>(out);
+    p.err = err_flag;
+    p.B = batch;
+    p.R = rows;
+    p.Hq = desc->num_q_heads;
+    p.Hkv = desc->num_kv_heads;
+    p.G = desc->num_q_heads / desc->num_kv_heads;
+    p.PS = desc->page_size;
+    p.TPP = desc->page_size / kKeyTile;
+    p.NP = num_pages;
+    p.MB = max_blocks;
+    p.NQ = p.G * rows;
+    p.QT = l.QT;
+    p.NW = l.NW;
+    p.RECF = l.RECF;
+    p.scale = desc->scale;
+    const dim3 split_grid((unsigned)l.NW);
+    const dim3 combine_grid((unsigned)(batch * p.Hkv), (unsigned)l.QT);
+    if (desc->head_dim == 128) {
+        hipLaunchKernelGGL(gdn_attn_split_kernel<128>, split_grid, dim3(kThreadsS), 0, st, p);
+        hipLaunchKernelGGL(gdn_attn_combine_kernel<128>, combine_grid, dim3(kThreadsC), 0, st, p);
+    } else {
+        hipLaunchKernelGGL(gdn_attn_split_kernel<256>, split_grid, dim3(kThreadsS), 0, st, p);
+        hipLaunchKernelGGL(gdn_attn_combine_kernel<256>, combine_grid, dim3(kThreadsC), 0, st, p);
+    }
+    return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+// Device address of `scratch` on the device of `st` (the current device for
+// the null stream), looked up on the first call on that device with the
+// device current, and kept for the life of the process.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+gdn_status static_scratch(hipStream_t st, void **ptr)
+{
+    int dev = 0;
+    if ((st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev)) != hipSuccess)
+        return GDN_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices)
+        return GDN_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess)
+            return GDN_ERR_HIP;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess)
+            return GDN_ERR_HIP;
+        void *addr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+        if (cur != dev)
+            (void)hipSetDevice(cur);
+        if (e != hipSuccess || !addr)
+            return GDN_ERR_HIP;
+        g_scratch_ptr[dev] = addr;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return GDN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -796,7 +888,7 @@ gdn_status gdn_spec_attn_scratch_bytes(const gdn_attn_desc *desc, int32_t batch,
 gdn_status gdn_spec_attn_verify(const gdn_attn_desc *desc, const void *q, const void *k_cache,
                                 const void *v_cache, int32_t num_pages, const int32_t *block_table,
                                 int32_t max_blocks, const int32_t *seq_lens, int32_t batch,
-                                int32_t rows, void *scratch, size_t scratch_bytes, void *out,
+                                int32_t rows, void *scratch_buf, size_t scratch_bytes, void *out,
                                 int32_t *err_flag, void *stream)
 {
     AttnLayout l;
@@ -805,47 +897,40 @@ gdn_status gdn_spec_attn_verify(const gdn_attn_desc *desc, const void *q, const 
         return s;
     if (batch == 0)
         return GDN_OK;
-    if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !scratch || !out || num_pages < 1 ||
-        !aligned16a(q) || !aligned16a(k_cache) || !aligned16a(v_cache) || !aligned16a(scratch) ||
-        !aligned16a(out))
+    s = attn_check(desc, q, k_cache, v_cache, num_pages, block_table, seq_lens, out);
+    if (s != GDN_OK)
+        return s;
+    if (!scratch_buf || !aligned16a(scratch_buf))
         return GDN_ERR_INVALID_ARG;
     if (scratch_bytes < l.total)
         return GDN_ERR_SCRATCH_TOO_SMALL;
-    AttnParams p;
-    p.q = static_cast<const uint16_t *>(q);
-    p.kc = static_cast<const uint16_t *>(k_cache);
-    p.vc = static_cast<const uint16_t *>(v_cache);
-    p.bt = block_table;
-    p.seq = seq_lens;
-    p.rec = static_cast<float *>(scratch);
-    p.starts = reinterpret_cast<int32_t *>(static_cast<char *>(scratch) + l.starts);
-    p.out = static_cast<uint16_t *>(out);
-    p.err = err_flag;
-    p.B = batch;
-    p.R = rows;
-    p.Hq = desc->num_q_heads;
-    p.Hkv = desc->num_kv_heads;
-    p.G = desc->num_q_heads / desc->num_kv_heads;
-    p.PS = desc->page_size;
-    p.TPP = desc->page_size / kKeyTile;
-    p.NP = num_pages;
-    p.MB = max_blocks;
-    p.NQ = p.G * rows;
-    p.QT = l.QT;
-    p.NW = l.NW;
-    p.RECF = l.RECF;
-    p.scale = desc->scale;
+    return attn_launch(desc, l, q, k_cache, v_cache, num_pages, block_table, max_blocks, seq_lens, batch, rows,
+                       scratch_buf, out, err_flag, static_cast<hipStream_t>(stream));
+}
+
+gdn_status gdn_spec_attn_verify_static(const gdn_attn_desc *desc, const void *q, const void *k_cache,
+                                       const void *v_cache, int32_t num_pages, const int32_t *block_table,
+                                       int32_t max_blocks, const int32_t *seq_lens, int32_t batch,
+                                       int32_t rows, void *out, int32_t *err_flag, void *stream)
+{
+    AttnLayout l;
+    gdn_status s = attn_layout(desc, batch, rows, max_blocks, &l);
+    if (s != GDN_OK)
+        return s;
+    if (batch == 0)
+        return GDN_OK;
+    s = attn_check(desc, q, k_cache, v_cache, num_pages, block_table, seq_lens, out);
+    if (s != GDN_OK)
+        return s;
+    if (l.total > GDN_SPEC_ATTN_STATIC_SCRATCH_BYTES)
+        return GDN_ERR_SCRATCH_TOO_SMALL;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const dim3 split_grid((unsigned)l.NW);
-    const dim3 combine_grid((unsigned)(batch * p.Hkv), (unsigned)l.QT);
-    if (desc->head_dim == 128) {
-        hipLaunchKernelGGL(gdn_attn_split_kernel<128>, split_grid, dim3(kThreadsS), 0, st, p);
-        hipLaunchKernelGGL(gdn_attn_combine_kernel<128>, combine_grid, dim3(kThreadsC), 0, st, p);
-    } else {
-        hipLaunchKernelGGL(gdn_attn_split_kernel<256>, split_grid, dim3(kThreadsS), 0, st, p);
-        hipLaunchKernelGGL(gdn_attn_combine_kernel<256>, combine_grid, dim3(kThreadsC), 0, st, p);
-    }
-    return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+    void *buf = nullptr;
+    s = static_scratch(st, &buf);
+    if (s != GDN_OK)
+        return s;
+    return attn_launch(desc, l, q, k_cache, v_cache, num_pages, block_table, max_blocks, seq_lens, batch, rows,
+                       buf, out, err_flag, st);
 }
 
 }  // extern "C"

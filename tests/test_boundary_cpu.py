@@ -245,3 +245,24 @@ def test_attention_arguments_are_refused(lib):
     assert f(scratch=None) == inv
     assert f(nbytes=need - 1) == bd.GDN_ERR_SCRATCH_TOO_SMALL
     assert f(batch=0, q=None, scratch=None) == bd.GDN_OK
+
+
+def test_static_attention_refuses_before_launching(lib):
+    """The allocation-free attention call checks its arguments, and that the
+    batch fits its device array, before any HIP call: a batch whose records
+    need more than the array returns GDN_ERR_SCRATCH_TOO_SMALL."""
+    import ctypes as ct
+    assert bd.ATTN_STATIC_SCRATCH_BYTES == 64 << 20
+    d = _attn_desc(num_q_heads=1024, num_kv_heads=1024, head_dim=256)
+    need = bd.gdn_spec_attn_scratch_bytes(d, 4, 3, 4)
+    assert need > bd.ATTN_STATIC_SCRATCH_BYTES
+    f = lambda desc, **kw: lib.gdn_spec_attn_verify_static(
+        ct.byref(desc), kw.get("q", 4096), 4096, 4096, 8, 4096, 4, 4096, kw.get("batch", 4), kw.get("rows", 3),
+        kw.get("out", 4096), None, None)
+    assert f(d) == bd.GDN_ERR_SCRATCH_TOO_SMALL
+    assert bd.gdn_spec_attn_scratch_bytes(d, 3, 3, 4) <= bd.ATTN_STATIC_SCRATCH_BYTES   # 3 requests fit
+    small = _attn_desc()
+    assert f(small, q=None) == bd.GDN_ERR_INVALID_ARG
+    assert f(small, out=4104) == bd.GDN_ERR_INVALID_ARG
+    assert f(small, rows=10) == bd.GDN_ERR_INVALID_ARG
+    assert f(small, batch=0, q=None, out=None) == bd.GDN_OK
