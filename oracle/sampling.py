@@ -38,13 +38,14 @@ from Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As
 Easy as 1, 2, 3", SC'11), keyed by the call's 64-bit seed:
   - G of row t, vocab entry v: counter (v >> 2, t, b, 0), word v & 3;
   - u_t: counter (0, t, b, 1), word 0;
-  - U = (word + 0.5) / 2^32, in (0, 1).
+  - U = (2 * (word >> 9) + 1) / 2^24: the top 23 bits as an odd fraction,
+    in (0, 1) and exact in fp32 as well as fp64.
 
 Reading where the pages are silent (parity unpinned: no page value fixes
 them): the penalties act on the logits before the temperature, the pending
-token counts towards every row's penalties, a zero draft probability accepts
-the draft, and padding requests (slot id -1) get accept_len 0 and next token
--1.
+token (when given) counts towards every row's penalties, a zero draft
+probability accepts the draft, and padding requests (slot id -1) get
+accept_len 0 and next token -1.
 """
 from __future__ import annotations
 
@@ -81,8 +82,9 @@ def _key(seed):
 
 
 def _unit(word):
-    """A 32-bit word as a uniform in (0, 1), in fp64."""
-    return (np.asarray(word, np.float64) + 0.5) / 4294967296.0
+    """A 32-bit word as a uniform in (0, 1): (2 * (word >> 9) + 1) / 2^24."""
+    w = np.asarray(word, np.uint64) >> np.uint64(9)
+    return (2.0 * w.astype(np.float64) + 1.0) / 16777216.0
 
 
 def gumbel_row(seed, b, t, vocab):
@@ -105,9 +107,10 @@ def penalized_logits(logits_row, counts, presence, frequency):
 
 
 def row_counts(prior, pending, draft, t, vocab):
-    """c_t: prior output counts plus the tokens of rows 0..t."""
+    """c_t: prior output counts plus the tokens of rows 0..t (the pending
+    token is left out when it is None)."""
     c = np.zeros(vocab, np.int64) if prior is None else np.asarray(prior, np.int64).copy()
-    toks = [int(pending)] + [int(x) for x in draft[:t]]
+    toks = ([] if pending is None else [int(pending)]) + [int(x) for x in draft[:t]]
     for tok in toks:
         c[tok] += 1
     return c
@@ -139,7 +142,7 @@ def speculative_sample(logits, draft, seed, temperature, draft_probs=None, pendi
         T = float(temperature[b])
         pres = 0.0 if presence is None else float(presence[b])
         freq = 0.0 if frequency is None else float(frequency[b])
-        pend = 0 if pending is None else int(pending[b])
+        pend = None if pending is None else int(pending[b])
         prior = None if prior_counts is None else prior_counts[b]
         use_pen = pres != 0.0 or freq != 0.0
         p_rows = []

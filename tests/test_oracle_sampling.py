@@ -133,8 +133,8 @@ MUTANTS = {
     "residual without the clamp": ("resid = np.maximum(p_rows[t] - q, 0.0)", "resid = np.abs(p_rows[t] - q)"),
     "residual is p": ("resid = np.maximum(p_rows[t] - q, 0.0)", "resid = p_rows[t].copy()"),
     "acceptance with p and q swapped": ("lhs, rhs = u * q[d], p_rows[t][d]", "lhs, rhs = u * p_rows[t][d], q[d]"),
-    "penalty counts stop a row early": ("toks = [int(pending)] + [int(x) for x in draft[:t]]",
-                                        "toks = [int(pending)] + [int(x) for x in draft[:max(t - 1, 0)]]"),
+    "penalty counts stop a row early": ("toks = ([] if pending is None else [int(pending)]) + [int(x) for x in draft[:t]]",
+                                        "toks = ([] if pending is None else [int(pending)]) + [int(x) for x in draft[:max(t - 1, 0)]]"),
     "presence weighted by the count": ("return np.asarray(logits_row, np.float64) - frequency * c - presence * (c > 0)",
                                        "return np.asarray(logits_row, np.float64) - frequency * c - presence * c"),
     "temperature applied twice": ("p_rows.append(softmax(row / T))", "p_rows.append(softmax(row / T / T))"),
