@@ -192,6 +192,67 @@ gdn_status gdn_spec_accept_greedy(const int32_t *draft, const int32_t *target,
                                   const int32_t *slot_ids, int32_t batch, int32_t rows,
                                   int32_t *accept_len, int32_t *next_token, void *stream);
 
+/*
+ * Speculative (rejection) sampling on the device: the accept_len that
+ * gdn_spec_commit reads, and the next pending token (FreeToken issue #828
+ * "Speculative decoding: MTP and DFlash", Plan: target-side verify with
+ * rejection sampling and per-row presence and frequency penalties; lmdeploy
+ * PR #5006, What's included, Verification path: speculative sampling).
+ *
+ * Row t of request b (0 <= t < rows) holds the pending token (t = 0) or draft
+ * d_t = draft[b][t-1]; its logits give the target distribution of the token
+ * after it,
+ *     p_t = softmax((l_t - frequency * c_t - presence * [c_t > 0]) / temperature),
+ * where c_t[v] = prior_counts[b][v] plus the number of rows 0..t whose token
+ * is v (the pending token counts only when given). For t = 0..rows-2, draft
+ * d_{t+1} is accepted when u_t * q_t(d_{t+1}) <= p_t(d_{t+1}), i.e. with
+ * probability min(1, p/q); q_t is draft_probs[b][t] or, without it, one on
+ * d_{t+1} (a greedy drafter). At the first rejection (row t) accept_len is
+ * t + 1 and the next token is drawn from max(0, p_t - q_t); with no rejection
+ * accept_len is rows and the next token is drawn from p_{rows-1}. The emitted
+ * tokens are then distributed as the target's own sampling.
+ *
+ * Draws are Gumbel-max, argmax_v (log w_v + G_v) with G = -log(-log U). The
+ * uniforms come from Philox4x32-10 (Salmon et al., SC'11) with key (seed low
+ * word, seed high word): G of row t at entry v from counter (v >> 2, t, b, 0),
+ * word v & 3; u_t from counter (0, t, b, 1), word 0; U = (2 (word >> 9) + 1)
+ * / 2^24. Pass a new seed for every call.
+ *
+ * Inputs (device memory; vocab V):
+ *  logits        [batch][rows][V], logits_dtype (GDN_F32 or GDN_BF16), finite
+ *  draft_probs   fp32 [batch][rows-1][V], nullable (greedy drafter)
+ *  draft         int32 [batch][rows-1] (nullable when rows == 1)
+ *  pending       int32 [batch], nullable: the token of row 0, for the counts
+ *  prior_counts  int32 [batch][V], nullable: occurrences in the earlier output
+ *  temperature   fp32 [batch], finite and > 0
+ *  presence, frequency  fp32 [batch], nullable (0)
+ *  slot_ids      int32 [batch], nullable: -1 marks padding (accept_len 0,
+ *                next_token -1)
+ * Outputs: accept_len, next_token int32 [batch]. A request with a temperature
+ * that is not finite and > 0, or a draft or pending token outside [0, V), gets
+ * accept_len 0 and next_token -1, and bit 3 is OR-ed into *err_flag.
+ * scratch: gdn_spec_sample_scratch_bytes() bytes, 16-byte aligned, used
+ * within the call only. Host checks return a status before any launch.
+ */
+typedef struct {
+    const void *logits;
+    const float *draft_probs;
+    const int32_t *draft;
+    const int32_t *pending;
+    const int32_t *prior_counts;
+    const float *temperature;
+    const float *presence;
+    const float *frequency;
+    const int32_t *slot_ids;
+} gdn_sample_inputs;
+
+gdn_status gdn_spec_sample_scratch_bytes(int32_t batch, int32_t rows, int32_t vocab, size_t *bytes);
+
+gdn_status gdn_spec_accept_sample(const gdn_sample_inputs *in, int32_t logits_dtype, int32_t batch,
+                                  int32_t rows, int32_t vocab, uint64_t seed, void *scratch,
+                                  size_t scratch_bytes, int32_t *accept_len, int32_t *next_token,
+                                  int32_t *err_flag, void *stream);
+
 /* Static description of a status code. */
 const char *gdn_strerror(gdn_status status);
 

@@ -30,7 +30,7 @@ MODES = {"replay": GDN_COMMIT_REPLAY, "snapshot": GDN_COMMIT_SNAPSHOT}
 
 EXPORTS = ("gdn_spec_scratch_bytes", "gdn_spec_verify", "gdn_spec_commit", "gdn_spec_commit_layers",
            "gdn_spec_accept_greedy", "gdn_strerror", "gdn_spec_attn_scratch_bytes", "gdn_spec_attn_verify",
-           "gdn_spec_attn_verify_static")
+           "gdn_spec_attn_verify_static", "gdn_spec_sample_scratch_bytes", "gdn_spec_accept_sample")
 
 # bytes of the device array behind gdn_spec_attn_verify_static (GDN_SPEC_ATTN_STATIC_SCRATCH_BYTES)
 ATTN_STATIC_SCRATCH_BYTES = 64 << 20
@@ -66,6 +66,12 @@ class GdnAttnDesc(ctypes.Structure):
         ("page_size", ctypes.c_int32),
         ("scale", ctypes.c_float),
     ]
+
+
+class GdnSampleInputs(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in (
+        "logits", "draft_probs", "draft", "pending", "prior_counts", "temperature", "presence", "frequency",
+        "slot_ids")]
 
 
 class GdnError(RuntimeError):
@@ -108,6 +114,11 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.gdn_spec_attn_verify.argtypes = [pattn, vp, vp, vp, i32, vp, i32, vp, i32, i32, vp, sz, vp, vp, vp]
     lib.gdn_spec_attn_verify_static.restype = ctypes.c_int
     lib.gdn_spec_attn_verify_static.argtypes = [pattn, vp, vp, vp, i32, vp, i32, vp, i32, i32, vp, vp, vp]
+    lib.gdn_spec_sample_scratch_bytes.restype = ctypes.c_int
+    lib.gdn_spec_sample_scratch_bytes.argtypes = [i32, i32, i32, ctypes.POINTER(sz)]
+    lib.gdn_spec_accept_sample.restype = ctypes.c_int
+    lib.gdn_spec_accept_sample.argtypes = [ctypes.POINTER(GdnSampleInputs), i32, i32, i32, i32, ctypes.c_uint64,
+                                           vp, sz, vp, vp, vp, vp]
     lib.gdn_strerror.restype = ctypes.c_char_p
     lib.gdn_strerror.argtypes = [ctypes.c_int]
     if path is None:
@@ -491,3 +502,61 @@ def gdn_spec_attn_verify_static(desc, q, k_cache, v_cache, block_table, seq_lens
         int(block_table.shape[1]), _ptr(seq_lens), B, R, _ptr(out), _ptr(err_flag), _stream(stream))
     if st != GDN_OK:
         raise GdnError(st, "gdn_spec_attn_verify_static")
+
+
+def gdn_spec_sample_scratch_bytes(batch: int, rows: int, vocab: int) -> int:
+    out = ctypes.c_size_t(0)
+    st = load_library().gdn_spec_sample_scratch_bytes(batch, rows, vocab, ctypes.byref(out))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_spec_sample_scratch_bytes")
+    return out.value
+
+
+class PreparedSample:
+    """gdn_spec_accept_sample on fixed device tensors, checked and turned into
+    ctypes arguments once; the seed is given per call. logits [B][R][V] fp32
+    or bf16, draft [B][R-1] int32, the optional inputs as in the header."""
+
+    def __init__(self, logits, draft, temperature, accept_len, next_token, scratch, draft_probs=None,
+                 pending=None, prior_counts=None, presence=None, frequency=None, slot_ids=None, err_flag=None,
+                 stream=None):
+        torch = _torch()
+        if logits is None or logits.dim() != 3:
+            raise ValueError("logits must be [batch][rows][vocab]")
+        if logits.dtype not in (torch.float32, torch.bfloat16):
+            raise ValueError("logits must be float32 or bfloat16, got %s" % logits.dtype)
+        B, R, V = (int(x) for x in logits.shape)
+        _check(logits, "logits", logits.dtype, (B, R, V))
+        dev = logits.device
+        _check(draft, "draft", torch.int32, (B, R - 1), device=dev, optional=R == 1)
+        _check(draft_probs, "draft_probs", torch.float32, (B, R - 1, V), device=dev, optional=True)
+        _check(pending, "pending", torch.int32, (B,), device=dev, optional=True)
+        _check(prior_counts, "prior_counts", torch.int32, (B, V), device=dev, optional=True)
+        _check(temperature, "temperature", torch.float32, (B,), device=dev)
+        _check(presence, "presence", torch.float32, (B,), device=dev, optional=True)
+        _check(frequency, "frequency", torch.float32, (B,), device=dev, optional=True)
+        _check(slot_ids, "slot_ids", torch.int32, (B,), device=dev, optional=True)
+        _check(accept_len, "accept_len", torch.int32, (B,), device=dev)
+        _check(next_token, "next_token", torch.int32, (B,), device=dev)
+        _check(scratch, "scratch", torch.uint8, device=dev, min_numel=gdn_spec_sample_scratch_bytes(B, R, V))
+        _check(err_flag, "err_flag", torch.int32, device=dev, optional=True, min_numel=1)
+        self.lib = load_library()
+        self._keep = (logits, draft, temperature, accept_len, next_token, scratch, draft_probs, pending,
+                      prior_counts, presence, frequency, slot_ids, err_flag)
+        self.inputs = GdnSampleInputs(_ptr(logits), _ptr(draft_probs), _ptr(draft), _ptr(pending),
+                                      _ptr(prior_counts), _ptr(temperature), _ptr(presence), _ptr(frequency),
+                                      _ptr(slot_ids))
+        self.head = (ctypes.byref(self.inputs), GDN_F32 if logits.dtype == torch.float32 else GDN_BF16, B, R, V)
+        self.tail = (_ptr(scratch), _nbytes(scratch), _ptr(accept_len), _ptr(next_token), _ptr(err_flag),
+                     _stream(stream))
+
+    def __call__(self, seed: int):
+        st = self.lib.gdn_spec_accept_sample(*self.head, ctypes.c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF),
+                                             *self.tail)
+        if st != GDN_OK:
+            raise GdnError(st, "gdn_spec_accept_sample")
+
+
+def gdn_spec_accept_sample(logits, draft, temperature, seed, accept_len, next_token, scratch, **optional):
+    """Speculative sampling on the device (see PreparedSample for the inputs)."""
+    PreparedSample(logits, draft, temperature, accept_len, next_token, scratch, **optional)(seed)

@@ -7,7 +7,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SOURCES = [os.path.join(PKG, "csrc", "gdn_spec.hip"), os.path.join(PKG, "csrc", "spec_attention.hip")]
+SOURCES = [os.path.join(PKG, "csrc", n) for n in ("gdn_spec.hip", "spec_attention.hip", "spec_sample.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libgdn_spec.so")
 ARCH = "gfx950"

@@ -266,3 +266,28 @@ def test_static_attention_refuses_before_launching(lib):
     assert f(small, out=4104) == bd.GDN_ERR_INVALID_ARG
     assert f(small, rows=10) == bd.GDN_ERR_INVALID_ARG
     assert f(small, batch=0, q=None, out=None) == bd.GDN_OK
+
+
+def test_sample_arguments_are_refused(lib):
+    import ctypes as ct
+    inv = bd.GDN_ERR_INVALID_ARG
+    out = ct.c_size_t(0)
+    assert lib.gdn_spec_sample_scratch_bytes(4, 10, 1000, ct.byref(out)) == inv     # rows > 9
+    assert lib.gdn_spec_sample_scratch_bytes(4, 3, 0, ct.byref(out)) == inv         # empty vocabulary
+    assert lib.gdn_spec_sample_scratch_bytes(-1, 3, 10, ct.byref(out)) == inv
+    need = bd.gdn_spec_sample_scratch_bytes(4, 3, 1000)
+    assert need > 0
+    good = bd.GdnSampleInputs(4096, None, 4096, None, None, 4096, None, None, None)
+
+    def f(inputs=good, dtype=bd.GDN_BF16, batch=4, rows=3, scratch=4096, nbytes=need, acc=4096, nxt=4096):
+        return lib.gdn_spec_accept_sample(ct.byref(inputs) if inputs is not None else None, dtype, batch, rows, 1000,
+                                          ct.c_uint64(1), scratch, nbytes, acc, nxt, None, None)
+    assert f(inputs=None) == inv
+    assert f(inputs=bd.GdnSampleInputs(None, None, 4096, None, None, 4096, None, None, None)) == inv   # no logits
+    assert f(inputs=bd.GdnSampleInputs(4096, None, None, None, None, 4096, None, None, None)) == inv   # no drafts
+    assert f(inputs=bd.GdnSampleInputs(4096, None, 4096, None, None, None, None, None, None)) == inv   # no temperature
+    assert f(dtype=7) == inv
+    assert f(acc=None) == inv
+    assert f(scratch=4104) == inv                                        # misaligned
+    assert f(nbytes=need - 1) == bd.GDN_ERR_SCRATCH_TOO_SMALL
+    assert f(batch=0, inputs=None, scratch=None, acc=None, nxt=None) == bd.GDN_OK
