@@ -296,6 +296,116 @@ def run_attention(args, w):
     print(json.dumps(line), flush=True)
 
 
+SAMPLE_METRIC = "speculative sampling rows/s and achieved HBM GB/s (% of MI355X peak)"
+
+
+def sample_bytes(w, d):
+    """Algorithmic bytes of one sampling call: every logit of every row read
+    once (each row's softmax needs its whole row), the prior counts once, and
+    the small per-request inputs and outputs."""
+    B, R, V = w.batch, w.rows, w.vocab
+    logits = B * R * V * 2
+    counts = B * V * 4 if "prior_counts" in d else 0
+    probs = B * (R - 1) * V * 4 if w.draft_probs else 0
+    small = B * (R - 1) * 4 + B * 4 * 6
+    return logits + counts + probs + small
+
+
+def sample_cpu_baseline(w, d, budget_s=12.0):
+    """The sampling oracle (NumPy fp64, as it stands) on a sample of requests."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import sampling
+    from linear_attention_verify_amd import workloads as wl
+
+    n = min(2, w.batch)
+    lg = wl.bf16_bits_to_f32(d["logits"][:n])
+    opt = {k: d[k][:n] for k in ("pending", "prior_counts", "presence", "frequency") if k in d}
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        sampling.speculative_sample(lg, d["draft"][:n], 1 + reps, d["temperature"][:n], **opt)
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": reps * n * w.rows / dt, "unit": "rows/s", "cores": threads, "kind": "oracle",
+            "sample": "%d passes over requests 0..%d of the %s batch (%d rows x %d vocabulary), fp64"
+                      % (reps, n - 1, w.name, w.rows, w.vocab)}
+
+
+def run_sample(args, w):
+    """Speculative sampling of the verify rows' logits: a step is one
+    gdn_spec_accept_sample call (stats, residual and final kernels) over the
+    batch, with a new seed per step. Steps alternate between two copies of the
+    logits so that no call finds the previous call's in the memory-side cache."""
+    import numpy as np
+    import torch
+
+    from linear_attention_verify_amd import binding as bd
+    from linear_attention_verify_amd import workloads as wl
+
+    if args.graph or args.accept != "given" or args.mode != "replay":
+        raise SystemExit("--graph, --accept and --mode apply to GDN workloads")
+    d = wl.draw_sample(w)
+    dev = "cuda"
+    t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    B, R, V = w.batch, w.rows, w.vocab
+    M = 2
+    calls, keep = [], []
+    for _ in range(M):
+        lg = torch.from_numpy(np.ascontiguousarray(d["logits"]).view(np.int16)).to(dev).view(torch.bfloat16)
+        acc = torch.empty(B, dtype=torch.int32, device=dev)
+        nxt = torch.empty(B, dtype=torch.int32, device=dev)
+        err = torch.zeros(1, dtype=torch.int32, device=dev)
+        scratch = torch.empty(bd.gdn_spec_sample_scratch_bytes(B, R, V), dtype=torch.uint8, device=dev)
+        calls.append(bd.PreparedSample(lg, t(d["draft"]), t(d["temperature"]), acc, nxt, scratch,
+                                       pending=t(d.get("pending")), prior_counts=t(d.get("prior_counts")),
+                                       presence=t(d.get("presence")), frequency=t(d.get("frequency")),
+                                       err_flag=err, stream=torch.cuda.current_stream()))
+        keep.append((acc, err))
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        calls[i % M](1000 + i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        calls[i % M](i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    a, b2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(args.steps):
+        calls[i % M](i)
+    b2.record(stream)
+    torch.cuda.synchronize()
+    tcall = a.elapsed_time(b2) * 1e-3 / args.steps
+    if any(int(e.item()) for _, e in keep):
+        raise SystemExit("device error flags set")
+    acc_mean = float(np.mean(keep[0][0].cpu().numpy()))
+    nb = sample_bytes(w, d)
+    ach = nb / tcall / 1e9
+    line = {
+        "metric": SAMPLE_METRIC, "value": B * R * args.steps / wall, "unit": "rows/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "rows": R, "vocab": V, "logits": "bf16",
+                   "drafter": "probabilities" if w.draft_probs else "greedy", "penalties": w.penalties,
+                   "accept_mean": acc_mean, "rotating_copies": M},
+        "gbps": nb * args.steps / wall / 1e9, "hbm_frac": nb * args.steps / wall / 1e9 / HBM_PEAK_GBPS,
+        "kernels": {"accept_sample": {"avg_us": tcall * 1e6, "bytes": nb, "gbps": ach}},
+        "roofline": {"bound": "hbm", "kernel": "accept_sample (stats + residual + final)", "achieved": ach,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic(w.name, "-", "accept_sample")},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = sample_cpu_baseline(w, d, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
 def run_stack(args, w):
     """A hybrid stack slice: every step verifies the batch through each of the
     w.layers GDN layers (one pool per layer) and then commits all layers, one
@@ -426,6 +536,8 @@ def main():
     torch.cuda.init()
     if args.workload in wl.ATTN_WORKLOADS:
         return run_attention(args, wl.ATTN_WORKLOADS[args.workload])
+    if args.workload in wl.SAMPLE_WORKLOADS:
+        return run_sample(args, wl.SAMPLE_WORKLOADS[args.workload])
     w = wl.WORKLOADS[args.workload]
     if w.layers != 1:
         return run_stack(args, w)

@@ -218,7 +218,7 @@ gdn_status gdn_spec_accept_greedy(const int32_t *draft, const int32_t *target,
  * word v & 3; u_t from counter (0, t, b, 1), word 0; U = (2 (word >> 9) + 1)
  * / 2^24. Pass a new seed for every call.
  *
- * Inputs (device memory; vocab V):
+ * Inputs (device memory; vocab V, at most 2^20):
  *  logits        [batch][rows][V], logits_dtype (GDN_F32 or GDN_BF16), finite
  *  draft_probs   fp32 [batch][rows-1][V], nullable (greedy drafter)
  *  draft         int32 [batch][rows-1] (nullable when rows == 1)

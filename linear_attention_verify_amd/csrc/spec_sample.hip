@@ -49,6 +49,7 @@ constexpr int kSampleThreads = 256;
 constexpr int kSampleChunk = 4096;                        // vocabulary entries per workgroup
 constexpr int kPerThread = kSampleChunk / kSampleThreads;  // 16: two units of 8
 constexpr int kMaxSampleRows = 9;
+constexpr int kMaxSplits = 256;                            // vocabulary up to 2^20 entries
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_huge_valf();
 
@@ -66,9 +67,9 @@ __device__ __forceinline__ U4 philox(U4 c, uint32_t k0, uint32_t k1)
             k0 += 0x9E3779B9u;
             k1 += 0xBB67AE85u;
         }
-        const uint32_t lo0 = 0xD2511F53u * c.x, hi0 = __umulhi(0xD2511F53u, c.x);
-        const uint32_t lo1 = 0xCD9E8D57u * c.z, hi1 = __umulhi(0xCD9E8D57u, c.z);
-        c = U4{hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0};
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c.x;   // one 32x32 -> 64-bit multiply each
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
+        c = U4{(uint32_t)(p1 >> 32) ^ c.y ^ k0, (uint32_t)p1, (uint32_t)(p0 >> 32) ^ c.w ^ k1, (uint32_t)p0};
     }
     return c;
 }
@@ -80,9 +81,12 @@ __device__ __forceinline__ float unit_uniform(uint32_t word)
 
 // Gumbel noise in base 2, up to a constant that no argmax sees:
 // -log2(-ln U) = -log2(-log2 U) - log2(ln 2).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }   // 2^x, v_exp_f32
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }    // log2 x, v_log_f32
+
 __device__ __forceinline__ float gumbel2(uint32_t word)
 {
-    return -__log2f(-__log2f(unit_uniform(word)));
+    return -fast_log2(-fast_log2(unit_uniform(word)));
 }
 
 // ---- inputs -----------------------------------------------------------------
@@ -185,7 +189,7 @@ __device__ __forceinline__ void combine_ms(float &m, float &s, float m2, float s
     const float mm = fmaxf(m, m2);
     if (mm == kNegInf)
         return;
-    s = s * exp2f(m - mm) + s2 * exp2f(m2 - mm);
+    s = s * fast_exp2(m - mm) + s2 * fast_exp2(m2 - mm);
     m = mm;
 }
 
@@ -239,15 +243,139 @@ __device__ __forceinline__ float temperature_scale(const SampleParams &p, int b)
     return (T > 0.0f && T <= 3.0e38f) ? kLog2e / T : 0.0f;   // invalid temperatures are flagged by the final kernel
 }
 
-// ---- stats kernel -----------------------------------------------------------
-
-template <typename L>
-__global__ __launch_bounds__(kSampleThreads) void gdn_sample_stats_kernel(const SampleParams p)
+// Prior counts of a unit's 8 entries (zero without penalties or counts).
+__device__ __forceinline__ void prior_unit(const SampleParams &p, int b, int v0, int V, bool pen, int (&c)[8])
 {
-    __shared__ float2 sh_ms[kMaxSampleRows][kSampleThreads / 64];
+    if (pen && p.prior && v0 + 8 <= V && (((size_t)b * V + v0) & 3) == 0) {
+        const int4 a = *reinterpret_cast<const int4 *>(p.prior + (size_t)b * V + v0);
+        const int4 d = *reinterpret_cast<const int4 *>(p.prior + (size_t)b * V + v0 + 4);
+        c[0] = a.x; c[1] = a.y; c[2] = a.z; c[3] = a.w; c[4] = d.x; c[5] = d.y; c[6] = d.z; c[7] = d.w;
+    } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            c[k] = (pen && p.prior && v0 + k < V) ? p.prior[(size_t)b * V + v0 + k] : 0;
+    }
+}
+
+// ---- stats kernel -----------------------------------------------------------
+//
+// Per thread, two units of 8 consecutive entries. For each unit all R rows
+// are loaded first (one 16-byte load per row), then row by row: with
+// penalties, the counts grow by the row's own token (c_t = c_{t-1} + [token
+// of row t == v], from the prior counts); the logits are scaled to base 2; and
+// the unit's maximum and sum of 2^(y - max) (one exp2 per entry) join the
+// thread's running pair for that row. R is a template parameter, so the row
+// loops are straight-line code.
+
+// FULL: all 8 entries inside the vocabulary and the rows 16-byte aligned, so
+// the loads are plain 16-byte loads and no entry needs a range check.
+template <bool FULL, typename L> __device__ __forceinline__ void load8(const L *row, int v0, int V, float (&x)[8])
+{
+    if constexpr (FULL) {
+        if constexpr (sizeof(L) == 4) {
+            const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row + v0));
+            const f32x4 c = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row + v0) + 1);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                x[k] = a[k];
+                x[4 + k] = c[k];
+            }
+        } else {
+            const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(row + v0));
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                x[2 * k] = __uint_as_float(a[k] << 16);
+                x[2 * k + 1] = __uint_as_float(a[k] & 0xffff0000u);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            x[k] = v0 + k < V ? load_logit(row, v0 + k) : 0.0f;
+    }
+}
+
+// The running pair (m, s) joined by a unit's (mu, su); mu is finite.
+__device__ __forceinline__ void join_finite(float &m, float &s, float mu, float su)
+{
+    const float mm = fmaxf(m, mu);
+    s = __builtin_fmaf(s, fast_exp2(m - mm), su * fast_exp2(mu - mm));
+    m = mm;
+}
+
+template <int R, typename L, bool PEN, bool FULL>
+__device__ __forceinline__ void stats_unit(const SampleParams &p, const L *lg, const Tokens &tk, int b, int v0,
+                                           float f, float r, float scale2, float (&m)[R], float (&s)[R], float &bk,
+                                           int &bi)
+{
+    const int V = p.V;
+    float x[R][8];
+#pragma unroll
+    for (int t = 0; t < R; ++t)
+        load8<FULL, L>(lg + (size_t)t * V, v0, V, x[t]);
+    int c[8];
+    if (PEN) {
+        if constexpr (FULL) {
+            if (p.prior) {
+                const int4 a = *reinterpret_cast<const int4 *>(p.prior + (size_t)b * V + v0);
+                const int4 d = *reinterpret_cast<const int4 *>(p.prior + (size_t)b * V + v0 + 4);
+                c[0] = a.x; c[1] = a.y; c[2] = a.z; c[3] = a.w; c[4] = d.x; c[5] = d.y; c[6] = d.z; c[7] = d.w;
+            } else {
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    c[k] = 0;
+            }
+        } else {
+            prior_unit(p, b, v0, V, true, c);
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < R; ++t) {
+        float y[8];
+        float mu = kNegInf;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            float l = x[t][k];
+            if (PEN) {
+                c[k] += tk.tok[t] == v0 + k ? 1 : 0;
+                l = __builtin_fmaf(-f, (float)c[k], l) - (c[k] > 0 ? r : 0.0f);
+            }
+            y[k] = (FULL || v0 + k < V) ? l * scale2 : kNegInf;
+            mu = fmaxf(mu, y[k]);
+        }
+        float su = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            su += fast_exp2(y[k] - mu);
+        join_finite(m[t], s[t], mu, su);
+        if (t == R - 1) {
+            // noise of the last row: two Philox blocks cover the unit's 8 entries
+            const U4 g0 = philox(U4{(uint32_t)(v0 >> 2), (uint32_t)t, (uint32_t)b, 0u}, p.k0, p.k1);
+            const U4 g1 = philox(U4{(uint32_t)(v0 >> 2) + 1u, (uint32_t)t, (uint32_t)b, 0u}, p.k0, p.k1);
+            const uint32_t gw[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const float key = y[k] + gumbel2(gw[k]);
+                if ((FULL || v0 + k < V) && better(key, v0 + k, bk, bi)) {
+                    bk = key;
+                    bi = v0 + k;
+                }
+            }
+        }
+    }
+}
+
+// Grid (splits, requests); the workgroups of one launch all take the same
+// path: PEN when the call has penalty arrays (zero penalties through it are
+// exact), FULL for the splits that lie wholly inside the vocabulary with
+// 16-byte aligned rows (the ragged last split gets a launch of its own).
+template <int R, typename L, bool PEN, bool FULL>
+__global__ __launch_bounds__(kSampleThreads) void gdn_sample_stats_kernel(const SampleParams p, int split0)
+{
+    __shared__ float2 sh_ms[R][kSampleThreads / 64];
     __shared__ float2 sh_best[kSampleThreads / 64];
-    const int split = blockIdx.x, b = blockIdx.y;
-    const int R = p.R, V = p.V, S = p.S;
+    const int split = split0 + blockIdx.x, b = blockIdx.y;
+    const int V = p.V, S = p.S;
     const int tid = threadIdx.x;
     if (padding(p, b))
         return;
@@ -256,58 +384,27 @@ __global__ __launch_bounds__(kSampleThreads) void gdn_sample_stats_kernel(const 
     const float f = p.freq ? p.freq[b] : 0.0f, r = p.pres ? p.pres[b] : 0.0f;
     const L *lg = static_cast<const L *>(p.logits) + (size_t)b * R * V;
 
-    float m[kMaxSampleRows], s[kMaxSampleRows];
+    float m[R], s[R];
 #pragma unroll
-    for (int t = 0; t < kMaxSampleRows; ++t) {
+    for (int t = 0; t < R; ++t) {
         m[t] = kNegInf;
         s[t] = 0.0f;
     }
     float bk = kNegInf;
     int bi = 0x7fffffff;
     const int base = split * kSampleChunk;
-#pragma unroll
+#pragma unroll 1
     for (int u = 0; u < kPerThread / 8; ++u) {
         const int v0 = base + (u * kSampleThreads + tid) * 8;
-        if (v0 >= V)
-            break;
-        int pc[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-            pc[k] = (p.prior && v0 + k < V) ? p.prior[(size_t)b * V + v0 + k] : 0;
-        // noise of the last row: two Philox blocks cover the unit's 8 entries
-        const U4 g0 = philox(U4{(uint32_t)(v0 >> 2), (uint32_t)(R - 1), (uint32_t)b, 0u}, p.k0, p.k1);
-        const U4 g1 = philox(U4{(uint32_t)(v0 >> 2) + 1u, (uint32_t)(R - 1), (uint32_t)b, 0u}, p.k0, p.k1);
-        const uint32_t gw[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-#pragma unroll
-        for (int t = 0; t < kMaxSampleRows; ++t) {
-            if (t < R) {
-                float x[8];
-                load_unit<L>(lg + (size_t)t * V, v0, V, x);
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    if (v0 + k < V) {
-                        const float y = penalised2(x[k], pc[k], tk, t, v0 + k, f, r, scale2);
-                        combine_ms(m[t], s[t], y, 1.0f);
-                        if (t == R - 1) {
-                            const float key = y + gumbel2(gw[k]);
-                            if (better(key, v0 + k, bk, bi)) {
-                                bk = key;
-                                bi = v0 + k;
-                            }
-                        }
-                    }
-                }
-            }
-        }
+        if (FULL || v0 < V)
+            stats_unit<R, L, PEN, FULL>(p, lg, tk, b, v0, f, r, scale2, m, s, bk, bi);
     }
     const int wave = tid >> 6, lane = tid & 63;
 #pragma unroll
-    for (int t = 0; t < kMaxSampleRows; ++t) {
-        if (t < R) {
-            wave_ms(m[t], s[t]);
-            if (lane == 0)
-                sh_ms[t][wave] = float2{m[t], s[t]};
-        }
+    for (int t = 0; t < R; ++t) {
+        wave_ms(m[t], s[t]);
+        if (lane == 0)
+            sh_ms[t][wave] = float2{m[t], s[t]};
     }
     group_best(bk, bi, sh_best);   // includes a barrier after the sh_ms stores
     if (tid < R) {
@@ -323,14 +420,15 @@ __global__ __launch_bounds__(kSampleThreads) void gdn_sample_stats_kernel(const 
 
 // ---- residual kernel --------------------------------------------------------
 
-template <typename L>
+template <int R, typename L>
 __global__ __launch_bounds__(kSampleThreads) void gdn_sample_residual_kernel(const SampleParams p)
 {
     __shared__ float2 row_ms[kMaxSampleRows];
     __shared__ int acc[kMaxSampleRows];
     __shared__ float2 sh_best[kSampleThreads / 64];
+    __shared__ float2 parts[kMaxSampleRows * kMaxSplits];
     const int split = blockIdx.x, b = blockIdx.y;
-    const int R = p.R, V = p.V, S = p.S;
+    const int V = p.V, S = p.S;
     const int tid = threadIdx.x;
     if (padding(p, b))
         return;
@@ -340,22 +438,26 @@ __global__ __launch_bounds__(kSampleThreads) void gdn_sample_residual_kernel(con
     const L *lg = static_cast<const L *>(p.logits) + (size_t)b * R * V;
 
     // row t's softmax statistics, combined over the splits in index order, and
-    // the acceptance of draft t+1 (the same arithmetic in every workgroup)
+    // the acceptance of draft t+1 (the same arithmetic in every workgroup);
+    // the partial pairs come in through LDS, every thread loading some
+    for (int i = tid; i < R * S; i += kSampleThreads)
+        parts[i] = p.stats[(size_t)b * R * S + i];
+    __syncthreads();
     if (tid < R) {
         const int t = tid;
         float mm = kNegInf, ss = 0.0f;
         for (int i = 0; i < S; ++i) {
-            const float2 ms = p.stats[((size_t)b * R + t) * S + i];
+            const float2 ms = parts[t * S + i];
             combine_ms(mm, ss, ms.x, ms.y);
         }
         row_ms[t] = float2{mm, ss};
         int ok = 1;
         if (t < R - 1) {
-            const int d = min(max(tk.tok[t + 1], 0), V - 1);   // out of range: flagged by the final kernel
+            const int d = min(max(p.draft[(size_t)b * (R - 1) + t], 0), V - 1);   // out of range: flagged later
             const int pc = p.prior ? p.prior[(size_t)b * V + d] : 0;
             const float y = penalised2(load_logit(static_cast<const L *>(p.logits), ((size_t)b * R + t) * V + d), pc,
                                        tk, t, d, f, r, scale2);
-            const float pd = exp2f(y - mm) / ss;
+            const float pd = fast_exp2(y - mm) / ss;
             const float qd = p.dprob ? p.dprob[((size_t)b * (R - 1) + t) * V + d] : 1.0f;
             const U4 w = philox(U4{0u, (uint32_t)t, (uint32_t)b, 1u}, p.k0, p.k1);
             ok = unit_uniform(w.x) * qd <= pd ? 1 : 0;
@@ -377,7 +479,7 @@ __global__ __launch_bounds__(kSampleThreads) void gdn_sample_residual_kernel(con
     // residual max(0, p - q) of row n-1 over this workgroup's entries
     const int t = n - 1;
     const float mm = row_ms[t].x, inv = 1.0f / row_ms[t].y;
-    const int d = tk.tok[t + 1];
+    const int d = p.draft[(size_t)b * (R - 1) + t];
     const float *q = p.dprob ? p.dprob + ((size_t)b * (R - 1) + t) * V : nullptr;
     float bk = kNegInf;
     int bi = 0x7fffffff;
@@ -394,21 +496,24 @@ __global__ __launch_bounds__(kSampleThreads) void gdn_sample_residual_kernel(con
         const U4 g0 = philox(U4{(uint32_t)(v0 >> 2), (uint32_t)t, (uint32_t)b, 0u}, p.k0, p.k1);
         const U4 g1 = philox(U4{(uint32_t)(v0 >> 2) + 1u, (uint32_t)t, (uint32_t)b, 0u}, p.k0, p.k1);
         const uint32_t gw[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+        int c[8];
+        const bool pen = f != 0.0f || r != 0.0f;
+        prior_unit(p, b, v0, V, pen, c);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const int v = v0 + k;
-            if (v >= V)
-                continue;
-            const int pc = p.prior ? p.prior[(size_t)b * V + v] : 0;
-            const float pv = exp2f(penalised2(x[k], pc, tk, t, v, f, r, scale2) - mm) * inv;
+            if (v < V) {
+            const float y = penalised2(x[k], c[k], tk, t, v, f, r, scale2);
+            const float pv = fast_exp2(y - mm) * inv;
             const float qq = q ? qv[k] : (v == d ? 1.0f : 0.0f);
             const float res = pv - qq;
             if (res > 0.0f) {
-                const float key = __log2f(res) + gumbel2(gw[k]);
+                const float key = fast_log2(res) + gumbel2(gw[k]);
                 if (better(key, v, bk, bi)) {
                     bk = key;
                     bi = v;
                 }
+            }
             }
         }
     }
@@ -419,14 +524,16 @@ __global__ __launch_bounds__(kSampleThreads) void gdn_sample_residual_kernel(con
 
 // ---- final kernel -----------------------------------------------------------
 
-__global__ __launch_bounds__(kSampleThreads) void gdn_sample_final_kernel(const SampleParams p)
+// One wave per request: the lanes take the splits' best keys in turn, then the
+// wave's best (ties to the smaller index) is the next token.
+__global__ __launch_bounds__(64) void gdn_sample_final_kernel(const SampleParams p)
 {
-    const int b = blockIdx.x * kSampleThreads + threadIdx.x;
-    if (b >= p.B)
-        return;
+    const int b = blockIdx.x, lane = threadIdx.x;
     if (padding(p, b)) {
-        p.accept[b] = 0;
-        p.next[b] = -1;
+        if (lane == 0) {
+            p.accept[b] = 0;
+            p.next[b] = -1;
+        }
         return;
     }
     const int R = p.R, V = p.V, S = p.S;
@@ -438,23 +545,66 @@ __global__ __launch_bounds__(kSampleThreads) void gdn_sample_final_kernel(const 
         bad |= d < 0 || d >= V;
     }
     if (bad) {
-        if (p.err)
-            atomicOr(p.err, 8);
-        p.accept[b] = 0;
-        p.next[b] = -1;
+        if (lane == 0) {
+            if (p.err)
+                atomicOr(p.err, 8);
+            p.accept[b] = 0;
+            p.next[b] = -1;
+        }
         return;
     }
     const int n = p.nacc[b];
     const float2 *src = (n == R ? p.bonus : p.resid) + (size_t)b * S;
     float bk = kNegInf;
     int bi = 0x7fffffff;
-    for (int i = 0; i < S; ++i)
+    for (int i = lane; i < S; i += 64)
         if (better(src[i].x, __float_as_int(src[i].y), bk, bi)) {
             bk = src[i].x;
             bi = __float_as_int(src[i].y);
         }
-    p.accept[b] = n;
-    p.next[b] = bi;
+    wave_best(bk, bi);
+    if (lane == 0) {
+        p.accept[b] = n;
+        // an empty residual (every p <= q after rounding) keeps the rejected draft
+        p.next[b] = bi != 0x7fffffff ? bi : (n < R ? p.draft[(size_t)b * (R - 1) + n - 1] : 0);
+    }
+}
+
+template <int R, typename L, bool PEN> void launch_stats(const SampleParams &p, hipStream_t st)
+{
+    const bool aligned = ((size_t)p.V * sizeof(L)) % 16 == 0 && (reinterpret_cast<uintptr_t>(p.logits) & 15) == 0 &&
+                         (reinterpret_cast<uintptr_t>(p.prior) & 15) == 0;
+    const int full = aligned ? p.V / kSampleChunk : 0;   // splits wholly inside the vocabulary
+    if (full > 0)
+        hipLaunchKernelGGL((gdn_sample_stats_kernel<R, L, PEN, true>), dim3((unsigned)full, (unsigned)p.B),
+                           dim3(kSampleThreads), 0, st, p, 0);
+    if (full < p.S)
+        hipLaunchKernelGGL((gdn_sample_stats_kernel<R, L, PEN, false>), dim3((unsigned)(p.S - full), (unsigned)p.B),
+                           dim3(kSampleThreads), 0, st, p, full);
+}
+
+template <int R, typename L> void launch_sample_kernels(dim3 grid, const SampleParams &p, hipStream_t st)
+{
+    if (p.pres || p.freq)
+        launch_stats<R, L, true>(p, st);
+    else
+        launch_stats<R, L, false>(p, st);
+    hipLaunchKernelGGL((gdn_sample_residual_kernel<R, L>), grid, dim3(kSampleThreads), 0, st, p);
+}
+
+template <typename L> void launch_rows(int rows, dim3 grid, const SampleParams &p, hipStream_t st)
+{
+    switch (rows) {
+    case 1: launch_sample_kernels<1, L>(grid, p, st); break;
+    case 2: launch_sample_kernels<2, L>(grid, p, st); break;
+    case 3: launch_sample_kernels<3, L>(grid, p, st); break;
+    case 4: launch_sample_kernels<4, L>(grid, p, st); break;
+    case 5: launch_sample_kernels<5, L>(grid, p, st); break;
+    case 6: launch_sample_kernels<6, L>(grid, p, st); break;
+    case 7: launch_sample_kernels<7, L>(grid, p, st); break;
+    case 8: launch_sample_kernels<8, L>(grid, p, st); break;
+    default: launch_sample_kernels<9, L>(grid, p, st); break;
+    }
 }
 
 struct SampleLayout {
@@ -468,7 +618,7 @@ gdn_status sample_layout(int batch, int rows, int vocab, SampleLayout *l)
 {
     if (batch < 0 || rows < 1 || rows > kMaxSampleRows || vocab < 1)
         return GDN_ERR_INVALID_ARG;
-    if ((size_t)batch * rows * vocab > ((size_t)1 << 40) || vocab > (1 << 30))
+    if (vocab > kMaxSplits * kSampleChunk)
         return GDN_ERR_UNSUPPORTED;
     l->S = (vocab + kSampleChunk - 1) / kSampleChunk;
     size_t off = 0;
@@ -543,15 +693,11 @@ gdn_status gdn_spec_accept_sample(const gdn_sample_inputs *in, int32_t logits_dt
     p.err = err_flag;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const dim3 grid((unsigned)l.S, (unsigned)batch);
-    if (logits_dtype == GDN_F32) {
-        hipLaunchKernelGGL(gdn_sample_stats_kernel<float>, grid, dim3(kSampleThreads), 0, st, p);
-        hipLaunchKernelGGL(gdn_sample_residual_kernel<float>, grid, dim3(kSampleThreads), 0, st, p);
-    } else {
-        hipLaunchKernelGGL(gdn_sample_stats_kernel<uint16_t>, grid, dim3(kSampleThreads), 0, st, p);
-        hipLaunchKernelGGL(gdn_sample_residual_kernel<uint16_t>, grid, dim3(kSampleThreads), 0, st, p);
-    }
-    hipLaunchKernelGGL(gdn_sample_final_kernel, dim3((batch + kSampleThreads - 1) / kSampleThreads),
-                       dim3(kSampleThreads), 0, st, p);
+    if (logits_dtype == GDN_F32)
+        launch_rows<float>(rows, grid, p, st);
+    else
+        launch_rows<uint16_t>(rows, grid, p, st);
+    hipLaunchKernelGGL(gdn_sample_final_kernel, dim3((unsigned)batch), dim3(64), 0, st, p);
     return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 

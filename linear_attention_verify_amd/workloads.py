@@ -258,3 +258,46 @@ def draw_attention(w: AttnWorkload):
     kc = to_storage(rng.standard_normal((pages, s.page_size, s.num_kv_heads, D), dtype=f32), "bf16")
     vc = to_storage(rng.standard_normal((pages, s.page_size, s.num_kv_heads, D), dtype=f32), "bf16")
     return {"seq_lens": seq, "block_table": table, "q": q, "k_cache": kc, "v_cache": vc}
+
+
+# ---- speculative sampling of the verify rows' logits ----
+
+@dataclass(frozen=True)
+class SampleWorkload:
+    name: str
+    batch: int
+    rows: int
+    vocab: int
+    draft_probs: bool = False     # a drafter that reports its distribution (else greedy)
+    penalties: bool = True
+    seed: int = 0
+    boost: float = 15.0           # logit added to each row's likely token
+    agree: float = 0.8            # chance that a draft is the previous row's likely token
+
+
+SAMPLE_WORKLOADS = {
+    # Qwen-sized vocabulary, the saturated batch's 64 requests x 9 rows
+    "sample-b64": SampleWorkload("sample-b64", batch=64, rows=9, vocab=151936, seed=21),
+}
+
+
+def draw_sample(w: SampleWorkload):
+    """Logits [B][R][V] ~ N(0, 4) rounded to bf16, with a likely token per row
+    (logit + boost); drafts [B][R-1] equal to the previous row's likely token
+    with probability `agree`, else uniform; temperatures U(0.7, 1.3);
+    presence U(0, 1), frequency U(0, 0.5); prior counts mostly 0, else 1..3;
+    pending tokens uniform. All int32 / fp32 numpy arrays, logits as bf16 bits."""
+    rng = np.random.default_rng([w.seed, 97])
+    B, R, V = w.batch, w.rows, w.vocab
+    logits = 2.0 * rng.standard_normal((B, R, V), dtype=np.float32)
+    likely = rng.integers(0, V, (B, R))
+    np.put_along_axis(logits, likely[..., None], np.take_along_axis(logits, likely[..., None], 2) + w.boost, 2)
+    draft = np.where(rng.random((B, R - 1)) < w.agree, likely[:, :R - 1], rng.integers(0, V, (B, R - 1)))
+    d = {"logits": f32_to_bf16_bits(logits), "draft": draft.astype(np.int32),
+         "temperature": rng.uniform(0.7, 1.3, B).astype(np.float32),
+         "pending": rng.integers(0, V, B).astype(np.int32)}
+    if w.penalties:
+        d["presence"] = rng.uniform(0.0, 1.0, B).astype(np.float32)
+        d["frequency"] = rng.uniform(0.0, 0.5, B).astype(np.float32)
+        d["prior_counts"] = np.where(rng.random((B, V)) < 0.95, 0, rng.integers(1, 4, (B, V))).astype(np.int32)
+    return d
