@@ -22,17 +22,19 @@
 //   stats     grid (splits, requests): each workgroup takes 4096 vocabulary
 //             entries of every row of its request, forms the penalised and
 //             tempered logits in base 2 and leaves, per row, the running
-//             maximum and sum of 2^x (online softmax), plus the best Gumbel
-//             key of the last row (the bonus draw).
+//             maximum and sum of 2^x (online softmax). No random numbers.
 //   residual  grid (splits, requests): every workgroup of a request combines
 //             the partial sums in the same order, so all of them reach the
 //             same acceptance of every draft and the same accept length n;
-//             if a draft was rejected, each takes the best Gumbel key of the
-//             residual max(0, p - q) over its entries of row n - 1.
-//   final     one thread per request: the best key over the splits gives the
+//             each then takes the best Gumbel key over its entries of row
+//             n - 1: of the residual max(0, p - q) after a rejection, of p
+//             when every draft was kept (the bonus token).
+//   final     one wave per request: the best key over the splits gives the
 //             next token; accept_len and next_token are written.
 
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 
 #include <math.h>
 #include <stddef.h>
@@ -46,10 +48,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kSampleThreads = 256;
-constexpr int kSampleChunk = 4096;                        // vocabulary entries per workgroup
-constexpr int kPerThread = kSampleChunk / kSampleThreads;  // 16: two units of 8
+constexpr int kColumn = kSampleThreads * 8;   // entries of one step of a workgroup: a unit of 8 per thread
 constexpr int kMaxSampleRows = 9;
-constexpr int kMaxSplits = 256;                            // vocabulary up to 2^20 entries
+constexpr int kMaxSplits = 256;               // workgroups per request in either pass
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_huge_valf();
 
@@ -101,11 +102,12 @@ struct SampleParams {
     const float *pres;
     const float *freq;
     const int32_t *slot_ids;
-    int B, R, V, S;
+    int B, R, V;
+    int S, U;     // stats pass: splits per request, units (columns) per thread in a split
+    int Sd, Ud;   // draw pass: the same
     uint32_t k0, k1;
     float2 *stats;   // [B][R][S]: running maximum (base 2) and sum of 2^(x - max)
-    float2 *bonus;   // [B][S]: best key of the last row and its index (bits)
-    float2 *resid;   // [B][S]: best key of the residual and its index (bits)
+    float2 *resid;   // [B][Sd]: best key of the draw (residual or bonus) and its index (bits)
     int32_t *nacc;   // [B]: accept length
     int32_t *accept;
     int32_t *next;
@@ -115,40 +117,16 @@ struct SampleParams {
 __device__ __forceinline__ float load_logit(const float *p, size_t i) { return p[i]; }
 __device__ __forceinline__ float load_logit(const uint16_t *p, size_t i) { return __uint_as_float((uint32_t)p[i] << 16); }
 
-template <typename L> __device__ __forceinline__ void load_unit(const L *row, int v0, int V, float (&x)[8]);
-
-template <> __device__ __forceinline__ void load_unit<float>(const float *row, int v0, int V, float (&x)[8])
+// Per-request values that every lane of a workgroup reads: scalar loads
+// through the constant address space (the sampling kernels never write
+// these inputs), whose waits do not drain the vector loads in flight.
+__device__ __forceinline__ int32_t ld_scalar(const int32_t *ptr, size_t i)
 {
-    if (v0 + 8 <= V && ((uintptr_t)(row + v0) & 15u) == 0) {
-        const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row + v0));
-        const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row + v0) + 1);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            x[k] = a[k];
-            x[4 + k] = b[k];
-        }
-    } else {
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-            x[k] = v0 + k < V ? row[v0 + k] : 0.0f;
-    }
+    return ((const __attribute__((address_space(4))) int32_t *)ptr)[i];
 }
-
-template <> __device__ __forceinline__ void load_unit<uint16_t>(const uint16_t *row, int v0, int V, float (&x)[8])
+__device__ __forceinline__ float ld_scalar(const float *ptr, size_t i)
 {
-    if (v0 + 8 <= V && ((uintptr_t)(row + v0) & 15u) == 0) {
-        const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(row + v0));
-        const uint32_t w[4] = {a[0], a[1], a[2], a[3]};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            x[2 * k] = __uint_as_float(w[k] << 16);
-            x[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
-        }
-    } else {
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-            x[k] = v0 + k < V ? __uint_as_float((uint32_t)row[v0 + k] << 16) : 0.0f;
-    }
+    return ((const __attribute__((address_space(4))) float *)ptr)[i];
 }
 
 // A request's tokens in row order: the pending token (or -1), then the drafts.
@@ -159,10 +137,10 @@ struct Tokens {
 __device__ __forceinline__ Tokens request_tokens(const SampleParams &p, int b)
 {
     Tokens t;
-    t.tok[0] = p.pending ? p.pending[b] : -1;
+    t.tok[0] = p.pending ? ld_scalar(p.pending, b) : -1;
 #pragma unroll
     for (int s = 1; s < kMaxSampleRows; ++s)
-        t.tok[s] = s < p.R ? p.draft[(size_t)b * (p.R - 1) + s - 1] : -1;
+        t.tok[s] = s < p.R ? ld_scalar(p.draft, (size_t)b * (p.R - 1) + s - 1) : -1;
     return t;
 }
 
@@ -206,14 +184,31 @@ __device__ __forceinline__ void wave_best(float &k, int &i)
     }
 }
 
-__device__ __forceinline__ void wave_ms(float &m, float &s)
+__device__ __forceinline__ float wave_max(float x)
 {
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const float m2 = __shfl_xor(m, off, 64);
-        const float s2 = __shfl_xor(s, off, 64);
-        combine_ms(m, s, m2, s2);
-    }
+    for (int off = 32; off >= 1; off >>= 1)
+        x = fmaxf(x, __shfl_xor(x, off, 64));
+    return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+// The wave's (max, sum of 2^(x - max)) from every lane's pair: the maximum
+// first, then each lane's sum rescaled to it once, then the sum. Every lane
+// gets the result.
+__device__ __forceinline__ void wave_ms(float &m, float &s)
+{
+    const float mm = wave_max(m);
+    const float ref = mm == kNegInf ? 0.0f : mm;
+    s = wave_sum(s * fast_exp2(m - ref));
+    m = mm;
 }
 
 // Workgroup best key; every thread gets the same result.
@@ -235,178 +230,358 @@ __device__ __forceinline__ void group_best(float &k, int &i, float2 *sh)
     __syncthreads();
 }
 
-__device__ __forceinline__ bool padding(const SampleParams &p, int b) { return p.slot_ids && p.slot_ids[b] == -1; }
+__device__ __forceinline__ bool padding(const SampleParams &p, int b) { return p.slot_ids && ld_scalar(p.slot_ids, b) == -1; }
 
 __device__ __forceinline__ float temperature_scale(const SampleParams &p, int b)
 {
-    const float T = p.temp[b];
+    const float T = ld_scalar(p.temp, b);
     return (T > 0.0f && T <= 3.0e38f) ? kLog2e / T : 0.0f;   // invalid temperatures are flagged by the final kernel
 }
 
-// Prior counts of a unit's 8 entries (zero without penalties or counts).
-__device__ __forceinline__ void prior_unit(const SampleParams &p, int b, int v0, int V, bool pen, int (&c)[8])
+// ---- unit loads ---------------------------------------------------------------
+//
+// A thread's unit is 8 consecutive vocabulary entries. With `vec` (the unit lies
+// inside the vocabulary and its row is 16-byte aligned) a row's unit is one or
+// two 16-byte loads; otherwise each entry is loaded on its own from a clamped
+// (always valid) index and entries past the vocabulary read as -inf logits,
+// zero counts and zero draft probabilities (the `fill` of a float row).
+
+template <typename L> struct Unit;
+template <> struct Unit<uint16_t> {   // bf16 pairs, low half first
+    u32x4 w;
+    __device__ __forceinline__ float at(int k) const
+    {
+        return __uint_as_float((k & 1) ? (w[k >> 1] & 0xffff0000u) : (w[k >> 1] << 16));
+    }
+    __device__ __forceinline__ void clear(int k)   // entry k := -inf
+    {
+        w[k >> 1] = (k & 1) ? ((w[k >> 1] & 0xffffu) | 0xff800000u) : ((w[k >> 1] & 0xffff0000u) | 0xff80u);
+    }
+};
+template <> struct Unit<float> {
+    f32x4 a, b;
+    __device__ __forceinline__ float at(int k) const { return k < 4 ? a[k] : b[k - 4]; }
+    __device__ __forceinline__ void clear(int k)
+    {
+        if (k < 4)
+            a[k] = kNegInf;
+        else
+            b[k - 4] = kNegInf;
+    }
+};
+
+__device__ __forceinline__ Unit<uint16_t> load_unit(const uint16_t *row, int v0, int V, bool vec)
 {
-    if (pen && p.prior && v0 + 8 <= V && (((size_t)b * V + v0) & 3) == 0) {
-        const int4 a = *reinterpret_cast<const int4 *>(p.prior + (size_t)b * V + v0);
-        const int4 d = *reinterpret_cast<const int4 *>(p.prior + (size_t)b * V + v0 + 4);
+    Unit<uint16_t> u;
+    if (vec) {
+        u.w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(row + v0));
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int i = v0 + 2 * k;
+            const uint32_t lo = row[min(i, V - 1)], hi = row[min(i + 1, V - 1)];   // clamped: always valid
+            u.w[k] = (i < V ? lo : 0xff80u) | ((i + 1 < V ? hi : 0xff80u) << 16);   // bf16 -inf past the end
+        }
+    }
+    return u;
+}
+
+__device__ __forceinline__ Unit<float> load_unit(const float *row, int v0, int V, bool vec, float fill = kNegInf)
+{
+    Unit<float> u;
+    if (vec) {
+        u.a = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row + v0));
+        u.b = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row + v0) + 1);
+    } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float x = row[min(v0 + k, V - 1)];
+            const float y = v0 + k < V ? x : fill;
+            if (k < 4)
+                u.a[k] = y;
+            else
+                u.b[k - 4] = y;
+        }
+    }
+    return u;
+}
+
+__device__ __forceinline__ void load_counts(const int32_t *row, int v0, int V, bool vec, int (&c)[8])
+{
+    if (vec) {
+        const int4 a = *reinterpret_cast<const int4 *>(row + v0);
+        const int4 d = *reinterpret_cast<const int4 *>(row + v0 + 4);
         c[0] = a.x; c[1] = a.y; c[2] = a.z; c[3] = a.w; c[4] = d.x; c[5] = d.y; c[6] = d.z; c[7] = d.w;
     } else {
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
-            c[k] = (pen && p.prior && v0 + k < V) ? p.prior[(size_t)b * V + v0 + k] : 0;
+        for (int k = 0; k < 8; ++k) {
+            const int x = row[min(v0 + k, V - 1)];
+            c[k] = v0 + k < V ? x : 0;
+        }
     }
+}
+
+// Which rows may take 16-byte loads (whole units only): bit 0 the logits,
+// bit 1 the prior counts, bit 2 the draft probabilities.
+enum : int { kVecLogits = 1, kVecPrior = 2, kVecProbs = 4 };
+
+// Penalty of an entry with count c, in tempered base-2 units.
+__device__ __forceinline__ float penalty2(int c, float f, float r, float scale2)
+{
+    return __builtin_fmaf(f, (float)c, c > 0 ? r : 0.0f) * scale2;
+}
+
+// True when one of tokens 0..last lies in [v0, v0 + 8).
+__device__ __forceinline__ bool unit_holds_token(const Tokens &tk, int last, int v0)
+{
+    bool hit = false;
+#pragma unroll
+    for (int j = 0; j < kMaxSampleRows; ++j)
+        hit |= j <= last && (uint32_t)tk.tok[j] - (uint32_t)v0 < 8u;
+    return hit;
 }
 
 // ---- stats kernel -----------------------------------------------------------
 //
-// Per thread, two units of 8 consecutive entries. For each unit all R rows
-// are loaded first (one 16-byte load per row), then row by row: with
-// penalties, the counts grow by the row's own token (c_t = c_{t-1} + [token
-// of row t == v], from the prior counts); the logits are scaled to base 2; and
-// the unit's maximum and sum of 2^(y - max) (one exp2 per entry) join the
-// thread's running pair for that row. R is a template parameter, so the row
-// loops are straight-line code.
+// Grid (splits, requests). A split is U columns of 2048 entries; each thread
+// takes one unit of 8 entries per column, for every row of its request. The
+// launch sizes U so that the whole grid is resident at once (about one round
+// of workgroups), and a thread loads the next column while it works on the
+// current one. Per row the penalised, tempered logits in base 2 are
+// y = x log2(e)/T - pen and the thread keeps a running (m, sum of 2^(y - m)):
+// the first unit sets m exactly (its maximum); later units are summed against
+// that m without a maximum of their own, and only a unit whose sum leaves the
+// safe range (a value far above m, or m still -inf) joins exactly instead.
+// The penalty comes from the prior counts alone, except at the entries of the
+// request's own tokens, whose counts grow from row to row: a unit that holds
+// one (rare, and a thread's own branch) joins those entries to every row on
+// their own first and then drops them from the unit.
 
-// FULL: all 8 entries inside the vocabulary and the rows 16-byte aligned, so
-// the loads are plain 16-byte loads and no entry needs a range check.
-template <bool FULL, typename L> __device__ __forceinline__ void load8(const L *row, int v0, int V, float (&x)[8])
+// The running pair (m, s) of one row joined exactly by a unit's 8 values.
+__device__ __forceinline__ void join_unit(float &m, float &s, const float (&y)[8])
 {
-    if constexpr (FULL) {
-        if constexpr (sizeof(L) == 4) {
-            const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row + v0));
-            const f32x4 c = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row + v0) + 1);
+    float mu = kNegInf;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                x[k] = a[k];
-                x[4 + k] = c[k];
-            }
-        } else {
-            const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(row + v0));
+    for (int k = 0; k < 8; ++k)
+        mu = fmaxf(mu, y[k]);
+    const float mm = fmaxf(m, mu);
+    const float ref = mm == kNegInf ? 0.0f : mm;   // all -inf so far: the sum stays zero
+    float su = 0.0f;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                x[2 * k] = __uint_as_float(a[k] << 16);
-                x[2 * k + 1] = __uint_as_float(a[k] & 0xffff0000u);
+    for (int k = 0; k < 8; ++k)
+        su += fast_exp2(y[k] - ref);
+    s = __builtin_fmaf(s, fast_exp2(m - ref), su);
+    m = mm;
+}
+
+// The running pair (m, s) of one row joined by one value.
+__device__ __forceinline__ void join_one(float &m, float &s, float y)
+{
+    const float mm = fmaxf(m, y);
+    const float ref = mm == kNegInf ? 0.0f : mm;
+    s = __builtin_fmaf(s, fast_exp2(m - ref), fast_exp2(y - ref));
+    m = mm;
+}
+
+// One unit's loads: every row's 8 logits and (with penalties) the prior counts.
+template <int R, typename L, bool PEN>
+__device__ __forceinline__ void stats_fetch(const SampleParams &p, const L *lg, int b, int v0, Unit<L> (&x)[R],
+                                            int (&c)[8])
+{
+    const int V = p.V;
+#pragma unroll
+    for (int t = 0; t < R; ++t)
+        x[t] = load_unit(lg + (size_t)t * V, v0, V, true);
+    if (PEN && p.prior) {
+        load_counts(p.prior + (size_t)b * V, v0, V, true, c);
+    } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            c[k] = 0;
+    }
+}
+
+// One unit's arithmetic: every row's running pair joined by the unit, exactly
+// (EXACT) or against the running maximum.
+template <int R, typename L, bool PEN, bool EXACT>
+__device__ __forceinline__ void stats_unit(const Tokens &tk, int v0, float f, float r, float scale2, Unit<L> (&x)[R],
+                                           const int (&c)[8], float (&m)[R], float (&s)[R])
+{
+    float ps[8];
+    if (PEN) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            ps[k] = penalty2(c[k], f, r, scale2);
+        if (unit_holds_token(tk, R - 1, v0)) {
+            // entries holding one of the request's tokens: their counts grow
+            // from row to row, so they join each row on their own, exactly,
+            // and leave the unit as -inf
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                bool tok = false;
+#pragma unroll
+                for (int j = 0; j < R; ++j)
+                    tok |= tk.tok[j] == v0 + k;
+                if (tok) {
+                    int ck = c[k];
+#pragma unroll
+                    for (int t = 0; t < R; ++t) {
+                        ck += tk.tok[t] == v0 + k ? 1 : 0;
+                        join_one(m[t], s[t], __builtin_fmaf(x[t].at(k), scale2, -penalty2(ck, f, r, scale2)));
+                        x[t].clear(k);
+                    }
+                }
             }
         }
     } else {
 #pragma unroll
         for (int k = 0; k < 8; ++k)
-            x[k] = v0 + k < V ? load_logit(row, v0 + k) : 0.0f;
-    }
-}
-
-// The running pair (m, s) joined by a unit's (mu, su); mu is finite.
-__device__ __forceinline__ void join_finite(float &m, float &s, float mu, float su)
-{
-    const float mm = fmaxf(m, mu);
-    s = __builtin_fmaf(s, fast_exp2(m - mm), su * fast_exp2(mu - mm));
-    m = mm;
-}
-
-template <int R, typename L, bool PEN, bool FULL>
-__device__ __forceinline__ void stats_unit(const SampleParams &p, const L *lg, const Tokens &tk, int b, int v0,
-                                           float f, float r, float scale2, float (&m)[R], float (&s)[R], float &bk,
-                                           int &bi)
-{
-    const int V = p.V;
-    float x[R][8];
-#pragma unroll
-    for (int t = 0; t < R; ++t)
-        load8<FULL, L>(lg + (size_t)t * V, v0, V, x[t]);
-    int c[8];
-    if (PEN) {
-        if constexpr (FULL) {
-            if (p.prior) {
-                const int4 a = *reinterpret_cast<const int4 *>(p.prior + (size_t)b * V + v0);
-                const int4 d = *reinterpret_cast<const int4 *>(p.prior + (size_t)b * V + v0 + 4);
-                c[0] = a.x; c[1] = a.y; c[2] = a.z; c[3] = a.w; c[4] = d.x; c[5] = d.y; c[6] = d.z; c[7] = d.w;
-            } else {
-#pragma unroll
-                for (int k = 0; k < 8; ++k)
-                    c[k] = 0;
-            }
-        } else {
-            prior_unit(p, b, v0, V, true, c);
-        }
+            ps[k] = 0.0f;
     }
 #pragma unroll
     for (int t = 0; t < R; ++t) {
-        float y[8];
-        float mu = kNegInf;
+        if (EXACT) {
+            float y[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            float l = x[t][k];
-            if (PEN) {
-                c[k] += tk.tok[t] == v0 + k ? 1 : 0;
-                l = __builtin_fmaf(-f, (float)c[k], l) - (c[k] > 0 ? r : 0.0f);
-            }
-            y[k] = (FULL || v0 + k < V) ? l * scale2 : kNegInf;
-            mu = fmaxf(mu, y[k]);
-        }
-        float su = 0.0f;
+            for (int k = 0; k < 8; ++k)
+                y[k] = __builtin_fmaf(x[t].at(k), scale2, -ps[k]);
+            join_unit(m[t], s[t], y);
+        } else {
+            // 2^(y - m) = 2^(x log2(e)/T - (pen + m)); below 2^100 per unit the
+            // sum is safe, otherwise the unit joins exactly
+            float su = 0.0f;
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
-            su += fast_exp2(y[k] - mu);
-        join_finite(m[t], s[t], mu, su);
-        if (t == R - 1) {
-            // noise of the last row: two Philox blocks cover the unit's 8 entries
-            const U4 g0 = philox(U4{(uint32_t)(v0 >> 2), (uint32_t)t, (uint32_t)b, 0u}, p.k0, p.k1);
-            const U4 g1 = philox(U4{(uint32_t)(v0 >> 2) + 1u, (uint32_t)t, (uint32_t)b, 0u}, p.k0, p.k1);
-            const uint32_t gw[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+            for (int k = 0; k < 8; ++k)
+                su += fast_exp2(__builtin_fmaf(x[t].at(k), scale2, -(ps[k] + m[t])));
+            if (su <= 0x1p100f) {
+                s[t] += su;
+            } else {
+                float y[8];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const float key = y[k] + gumbel2(gw[k]);
-                if ((FULL || v0 + k < V) && better(key, v0 + k, bk, bi)) {
-                    bk = key;
-                    bi = v0 + k;
-                }
+                for (int k = 0; k < 8; ++k)
+                    y[k] = __builtin_fmaf(x[t].at(k), scale2, -ps[k]);
+                join_unit(m[t], s[t], y);
             }
         }
     }
 }
 
-// Grid (splits, requests); the workgroups of one launch all take the same
-// path: PEN when the call has penalty arrays (zero penalties through it are
-// exact), FULL for the splits that lie wholly inside the vocabulary with
-// 16-byte aligned rows (the ragged last split gets a launch of its own).
-template <int R, typename L, bool PEN, bool FULL>
-__global__ __launch_bounds__(kSampleThreads) void gdn_sample_stats_kernel(const SampleParams p, int split0)
+// A unit that is not whole, or whose rows are not 16-byte aligned: every
+// entry loaded on its own from a clamped index (entries past the vocabulary
+// read as -inf logits and zero counts), all rows at once.
+template <int R, typename L, bool PEN>
+__device__ __forceinline__ void stats_fetch_general(const SampleParams &p, const L *lg, int b, int v0, Unit<L> (&x)[R],
+                                                    int (&c)[8])
+{
+    const int V = p.V;
+#pragma unroll
+    for (int t = 0; t < R; ++t)
+        x[t] = load_unit(lg + (size_t)t * V, v0, V, false);
+    if (PEN && p.prior) {
+        load_counts(p.prior + (size_t)b * V, v0, V, false, c);
+    } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            c[k] = 0;
+    }
+}
+
+// Every row's (m, s) combined over the wave, the rows interleaved so that
+// their shuffles overlap: maxima first, each lane's sum rescaled once, then
+// the sums. Every lane gets the results.
+template <int R> __device__ __forceinline__ void wave_ms_rows(float (&m)[R], float (&s)[R])
+{
+    float mx[R];
+#pragma unroll
+    for (int t = 0; t < R; ++t)
+        mx[t] = m[t];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+#pragma unroll
+        for (int t = 0; t < R; ++t)
+            mx[t] = fmaxf(mx[t], __shfl_xor(mx[t], off, 64));
+#pragma unroll
+    for (int t = 0; t < R; ++t) {
+        const float ref = mx[t] == kNegInf ? 0.0f : mx[t];
+        s[t] *= fast_exp2(m[t] - ref);
+        m[t] = mx[t];
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+#pragma unroll
+        for (int t = 0; t < R; ++t)
+            s[t] += __shfl_xor(s[t], off, 64);
+}
+
+template <int R, typename L, bool PEN>
+__global__ __launch_bounds__(kSampleThreads) void gdn_sample_stats_kernel(const SampleParams p, int vec_ok)
 {
     __shared__ float2 sh_ms[R][kSampleThreads / 64];
-    __shared__ float2 sh_best[kSampleThreads / 64];
-    const int split = split0 + blockIdx.x, b = blockIdx.y;
-    const int V = p.V, S = p.S;
+    const int split = blockIdx.x, b = blockIdx.y;
+    const int V = p.V, S = p.S, U = p.U;
     const int tid = threadIdx.x;
+    const L *lg = static_cast<const L *>(p.logits) + (size_t)b * R * V;
+    const int base = split * U * kColumn;
+    const int cols = min(U, (V - base + kColumn - 1) / kColumn);   // columns inside the vocabulary
+    const bool vec = (vec_ok & kVecLogits) && (!PEN || !p.prior || (vec_ok & kVecPrior));
+    const int whole = vec ? min(cols, (V - base) / kColumn) : 0;   // columns of whole units only
+
+    // the first two columns' loads go out before the per-request values are
+    // read (rows of padding requests are still inside the logits)
+    Unit<L> x[R], xn[R];
+    int c[8], cn[8];
+    if (whole > 0) {
+        stats_fetch<R, L, PEN>(p, lg, b, base + tid * 8, x, c);
+        stats_fetch<R, L, PEN>(p, lg, b, base + (min(1, whole - 1) * kSampleThreads + tid) * 8, xn, cn);
+    }
     if (padding(p, b))
         return;
-    const Tokens tk = request_tokens(p, b);
     const float scale2 = temperature_scale(p, b);
-    const float f = p.freq ? p.freq[b] : 0.0f, r = p.pres ? p.pres[b] : 0.0f;
-    const L *lg = static_cast<const L *>(p.logits) + (size_t)b * R * V;
-
+    Tokens tk;
+    float f = 0.0f, r = 0.0f;
+    if (PEN) {
+        tk = request_tokens(p, b);
+        f = p.freq ? ld_scalar(p.freq, b) : 0.0f;
+        r = p.pres ? ld_scalar(p.pres, b) : 0.0f;
+    }
     float m[R], s[R];
 #pragma unroll
     for (int t = 0; t < R; ++t) {
         m[t] = kNegInf;
         s[t] = 0.0f;
     }
-    float bk = kNegInf;
-    int bi = 0x7fffffff;
-    const int base = split * kSampleChunk;
+    if (whole > 0) {
+        stats_unit<R, L, PEN, true>(tk, base + tid * 8, f, r, scale2, x, c, m, s);
 #pragma unroll 1
-    for (int u = 0; u < kPerThread / 8; ++u) {
-        const int v0 = base + (u * kSampleThreads + tid) * 8;
-        if (FULL || v0 < V)
-            stats_unit<R, L, PEN, FULL>(p, lg, tk, b, v0, f, r, scale2, m, s, bk, bi);
-    }
-    const int wave = tid >> 6, lane = tid & 63;
+        for (int u = 1; u + 1 < whole; ++u) {
 #pragma unroll
-    for (int t = 0; t < R; ++t) {
-        wave_ms(m[t], s[t]);
-        if (lane == 0)
+            for (int t = 0; t < R; ++t)
+                x[t] = xn[t];
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                c[k] = cn[k];
+            stats_fetch<R, L, PEN>(p, lg, b, base + ((u + 1) * kSampleThreads + tid) * 8, xn, cn);
+            stats_unit<R, L, PEN, false>(tk, base + (u * kSampleThreads + tid) * 8, f, r, scale2, x, c, m, s);
+        }
+        if (whole > 1)
+            stats_unit<R, L, PEN, false>(tk, base + ((whole - 1) * kSampleThreads + tid) * 8, f, r, scale2, xn, cn,
+                                         m, s);
+    }
+    // the ragged last column (or every column of unaligned rows)
+#pragma unroll 1
+    for (int u = whole; u < cols; ++u) {
+        const int v0 = base + (u * kSampleThreads + tid) * 8;
+        stats_fetch_general<R, L, PEN>(p, lg, b, v0, x, c);
+        stats_unit<R, L, PEN, true>(tk, v0, f, r, scale2, x, c, m, s);
+    }
+    wave_ms_rows<R>(m, s);
+    const int wave = tid >> 6, lane = tid & 63;
+    if (lane == 0) {
+#pragma unroll
+        for (int t = 0; t < R; ++t)
             sh_ms[t][wave] = float2{m[t], s[t]};
     }
-    group_best(bk, bi, sh_best);   // includes a barrier after the sh_ms stores
+    __syncthreads();
     if (tid < R) {
         float mm = kNegInf, ss = 0.0f;
 #pragma unroll
@@ -414,51 +589,163 @@ __global__ __launch_bounds__(kSampleThreads) void gdn_sample_stats_kernel(const 
             combine_ms(mm, ss, sh_ms[tid][w].x, sh_ms[tid][w].y);
         p.stats[((size_t)b * R + tid) * S + split] = float2{mm, ss};
     }
-    if (tid == 0)
-        p.bonus[(size_t)b * S + split] = float2{bk, __int_as_float(bi)};
 }
 
-// ---- residual kernel --------------------------------------------------------
+// ---- draw kernel ------------------------------------------------------------
+//
+// Grid (splits, requests), a split being Ud columns as above. Every workgroup
+// of a request combines the partial sums in the same order, so all of them
+// reach the same acceptance of every draft and the same accept length n.
+// Then each takes the best Gumbel key over its entries of row n - 1: of the
+// residual max(0, p - q) after a rejection, or of p itself when every draft
+// was kept (the bonus token). With a greedy drafter (q one on the draft, zero
+// elsewhere) the residual is p without the rejected draft, so both of those
+// draws rank y + G (y = log2 p up to a constant of the row); only a drafter
+// with probabilities needs p - q itself.
+
+struct DrawRow {   // what the draw needs of its row
+    const void *lg;     // the row's logits
+    const float *q;     // its draft probabilities (drafter with probabilities, after a rejection), or null
+    int t, d;           // the row, the draft excluded (greedy drafter after a rejection) or -1
+    float mm, inv;      // the row's softmax maximum and 1 / sum
+};
+
+template <typename L> struct DrawUnit {
+    Unit<L> x;
+    Unit<float> q;
+    int c[8];
+};
+
+// One unit's loads: 16-byte loads (VEC: a whole unit of aligned rows) or
+// entry by entry from clamped indices.
+template <typename L, bool VEC>
+__device__ __forceinline__ void draw_fetch(const SampleParams &p, const DrawRow &w, bool pen, int b, int v0,
+                                           DrawUnit<L> &u)
+{
+    const int V = p.V;
+    u.x = load_unit(static_cast<const L *>(w.lg), v0, V, VEC);
+    if (w.q)
+        u.q = load_unit(w.q, v0, V, VEC, 0.0f);
+    if (pen && p.prior) {
+        load_counts(p.prior + (size_t)b * V, v0, V, VEC, u.c);
+    } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            u.c[k] = 0;
+    }
+}
+
+template <typename L>
+__device__ __forceinline__ void draw_unit(const SampleParams &p, const DrawRow &w, const Tokens &tk, bool pen, int b,
+                                          int v0, float f, float r, float scale2, DrawUnit<L> &u, float &bk, int &bi)
+{
+    const int V = p.V, t = w.t;
+    float ps[8];
+    if (pen) {
+        if (unit_holds_token(tk, t, v0)) {
+#pragma unroll
+            for (int j = 0; j < kMaxSampleRows; ++j)
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    u.c[k] += (j <= t && tk.tok[j] == v0 + k) ? 1 : 0;
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            ps[k] = penalty2(u.c[k], f, r, scale2);
+    } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            ps[k] = 0.0f;
+    }
+    const U4 g0 = philox(U4{(uint32_t)(v0 >> 2), (uint32_t)t, (uint32_t)b, 0u}, p.k0, p.k1);
+    const U4 g1 = philox(U4{(uint32_t)(v0 >> 2) + 1u, (uint32_t)t, (uint32_t)b, 0u}, p.k0, p.k1);
+    const uint32_t gw[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int v = v0 + k;
+        const float y = __builtin_fmaf(u.x.at(k), scale2, -ps[k]);
+        float key;
+        if (w.q) {
+            const float res = fast_exp2(y - w.mm) * w.inv - u.q.at(k);
+            key = res > 0.0f ? fast_log2(res) + gumbel2(gw[k]) : kNegInf;
+        } else {
+            key = v != w.d ? y + gumbel2(gw[k]) : kNegInf;
+        }
+        if (v < V && key != kNegInf && better(key, v, bk, bi)) {
+            bk = key;
+            bi = v;
+        }
+    }
+}
 
 template <int R, typename L>
-__global__ __launch_bounds__(kSampleThreads) void gdn_sample_residual_kernel(const SampleParams p)
+__global__ __launch_bounds__(kSampleThreads) void gdn_sample_residual_kernel(const SampleParams p, int vec_ok)
 {
     __shared__ float2 row_ms[kMaxSampleRows];
     __shared__ int acc[kMaxSampleRows];
     __shared__ float2 sh_best[kSampleThreads / 64];
-    __shared__ float2 parts[kMaxSampleRows * kMaxSplits];
     const int split = blockIdx.x, b = blockIdx.y;
-    const int V = p.V, S = p.S;
+    const int V = p.V, S = p.S, U = p.Ud;
     const int tid = threadIdx.x;
     if (padding(p, b))
         return;
     const Tokens tk = request_tokens(p, b);
     const float scale2 = temperature_scale(p, b);
-    const float f = p.freq ? p.freq[b] : 0.0f, r = p.pres ? p.pres[b] : 0.0f;
+    const float f = p.freq ? ld_scalar(p.freq, b) : 0.0f, r = p.pres ? ld_scalar(p.pres, b) : 0.0f;
+    const bool pen = f != 0.0f || r != 0.0f;
     const L *lg = static_cast<const L *>(p.logits) + (size_t)b * R * V;
+    const int base = split * U * kColumn;
+    const int cols = min(U, (V - base + kColumn - 1) / kColumn);
 
-    // row t's softmax statistics, combined over the splits in index order, and
-    // the acceptance of draft t+1 (the same arithmetic in every workgroup);
-    // the partial pairs come in through LDS, every thread loading some
-    for (int i = tid; i < R * S; i += kSampleThreads)
-        parts[i] = p.stats[(size_t)b * R * S + i];
+    // thread t < R - 1 reads what the acceptance of draft t+1 needs at the
+    // draft's entry, alongside the partial sums; every thread loads (from a
+    // clamped, valid index) so that no load sits in a divergent branch
+    const int ta = R > 1 ? min(tid, R - 2) : 0;
+    int dt = tk.tok[1];
+#pragma unroll
+    for (int j = 2; j < R; ++j)
+        dt = ta == j - 1 ? tk.tok[j] : dt;
+    const int dd = min(max(dt, 0), V - 1);   // out of range: flagged by the final kernel
+    const L xd_raw = static_cast<const L *>(p.logits)[((size_t)b * R + ta) * V + dd];
+    const int pcd = p.prior ? p.prior[(size_t)b * V + dd] : 0;
+    const float qd = p.dprob ? p.dprob[((size_t)b * (R - 1) + ta) * V + dd] : 1.0f;
+
+    // row t's softmax statistics over the splits (wave t % 4, lanes taking
+    // the splits in turn), then the acceptance of draft t+1; the same
+    // arithmetic in the same order in every workgroup of the request
+    const int wave = tid >> 6, lane = tid & 63;
+    constexpr int RW = (R + kSampleThreads / 64 - 1) / (kSampleThreads / 64);   // rows per wave
+    constexpr int PL = kMaxSplits / 64;                                          // partials per lane
+    float2 part[RW][PL];
+#pragma unroll
+    for (int j = 0; j < RW; ++j) {
+        const int t = wave + j * (kSampleThreads / 64);
+#pragma unroll
+        for (int i = 0; i < PL; ++i) {
+            const int sp = lane + 64 * i;
+            const float2 v = p.stats[((size_t)b * R + min(t, R - 1)) * S + min(sp, S - 1)];
+            part[j][i] = (t < R && sp < S) ? v : float2{kNegInf, 0.0f};
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < RW; ++j) {
+        const int t = wave + j * (kSampleThreads / 64);
+        float mm = kNegInf, ss = 0.0f;
+#pragma unroll
+        for (int i = 0; i < PL; ++i)
+            combine_ms(mm, ss, part[j][i].x, part[j][i].y);
+        wave_ms(mm, ss);
+        if (lane == 0 && t < R)
+            row_ms[t] = float2{mm, ss};
+    }
     __syncthreads();
     if (tid < R) {
         const int t = tid;
-        float mm = kNegInf, ss = 0.0f;
-        for (int i = 0; i < S; ++i) {
-            const float2 ms = parts[t * S + i];
-            combine_ms(mm, ss, ms.x, ms.y);
-        }
-        row_ms[t] = float2{mm, ss};
+        const float mm = row_ms[t].x, ss = row_ms[t].y;
         int ok = 1;
         if (t < R - 1) {
-            const int d = min(max(p.draft[(size_t)b * (R - 1) + t], 0), V - 1);   // out of range: flagged later
-            const int pc = p.prior ? p.prior[(size_t)b * V + d] : 0;
-            const float y = penalised2(load_logit(static_cast<const L *>(p.logits), ((size_t)b * R + t) * V + d), pc,
-                                       tk, t, d, f, r, scale2);
+            const float y = penalised2(load_logit(&xd_raw, 0), pcd, tk, t, dd, f, r, scale2);
             const float pd = fast_exp2(y - mm) / ss;
-            const float qd = p.dprob ? p.dprob[((size_t)b * (R - 1) + t) * V + d] : 1.0f;
             const U4 w = philox(U4{0u, (uint32_t)t, (uint32_t)b, 1u}, p.k0, p.k1);
             ok = unit_uniform(w.x) * qd <= pd ? 1 : 0;
         }
@@ -473,53 +760,46 @@ __global__ __launch_bounds__(kSampleThreads) void gdn_sample_residual_kernel(con
         }
     if (split == 0 && tid == 0)
         p.nacc[b] = n;
-    if (n == R)
-        return;
 
-    // residual max(0, p - q) of row n-1 over this workgroup's entries
-    const int t = n - 1;
-    const float mm = row_ms[t].x, inv = 1.0f / row_ms[t].y;
-    const int d = p.draft[(size_t)b * (R - 1) + t];
-    const float *q = p.dprob ? p.dprob + ((size_t)b * (R - 1) + t) * V : nullptr;
+    DrawRow w;
+    w.t = n - 1;
+    const bool rejected = n < R;
+    w.d = -1;
+#pragma unroll
+    for (int j = 1; j < R; ++j)
+        w.d = rejected && w.t == j - 1 ? tk.tok[j] : w.d;
+    w.lg = lg + (size_t)w.t * V;
+    w.q = rejected && p.dprob ? p.dprob + ((size_t)b * (R - 1) + w.t) * V : nullptr;
+    w.mm = row_ms[w.t].x;
+    w.inv = 1.0f / row_ms[w.t].y;
     float bk = kNegInf;
     int bi = 0x7fffffff;
-    const int base = split * kSampleChunk;
-#pragma unroll
-    for (int u = 0; u < kPerThread / 8; ++u) {
-        const int v0 = base + (u * kSampleThreads + tid) * 8;
-        if (v0 >= V)
-            break;
-        float x[8], qv[8];
-        load_unit<L>(lg + (size_t)t * V, v0, V, x);
-        if (q)
-            load_unit<float>(q, v0, V, qv);
-        const U4 g0 = philox(U4{(uint32_t)(v0 >> 2), (uint32_t)t, (uint32_t)b, 0u}, p.k0, p.k1);
-        const U4 g1 = philox(U4{(uint32_t)(v0 >> 2) + 1u, (uint32_t)t, (uint32_t)b, 0u}, p.k0, p.k1);
-        const uint32_t gw[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-        int c[8];
-        const bool pen = f != 0.0f || r != 0.0f;
-        prior_unit(p, b, v0, V, pen, c);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int v = v0 + k;
-            if (v < V) {
-            const float y = penalised2(x[k], c[k], tk, t, v, f, r, scale2);
-            const float pv = fast_exp2(y - mm) * inv;
-            const float qq = q ? qv[k] : (v == d ? 1.0f : 0.0f);
-            const float res = pv - qq;
-            if (res > 0.0f) {
-                const float key = fast_log2(res) + gumbel2(gw[k]);
-                if (better(key, v, bk, bi)) {
-                    bk = key;
-                    bi = v;
-                }
-            }
-            }
+    // whole columns in order, the next one's loads out before the current
+    // one's arithmetic; then the ragged last column entry by entry
+    const bool vec_all = (vec_ok & kVecLogits) && (!pen || !p.prior || (vec_ok & kVecPrior)) &&
+                         (!w.q || (vec_ok & kVecProbs));
+    const int whole = vec_all ? min(cols, (V - base) / kColumn) : 0;
+    DrawUnit<L> cur, nxt;
+    if (whole > 0) {
+        draw_fetch<L, true>(p, w, pen, b, base + tid * 8, cur);
+#pragma unroll 1
+        for (int u = 0; u + 1 < whole; ++u) {
+            draw_fetch<L, true>(p, w, pen, b, base + ((u + 1) * kSampleThreads + tid) * 8, nxt);
+            draw_unit<L>(p, w, tk, pen, b, base + (u * kSampleThreads + tid) * 8, f, r, scale2, cur, bk, bi);
+            cur = nxt;
         }
+        draw_unit<L>(p, w, tk, pen, b, base + ((whole - 1) * kSampleThreads + tid) * 8, f, r, scale2, cur, bk, bi);
+    }
+#pragma unroll 1
+    for (int u = whole; u < cols; ++u) {
+        const int v0 = base + (u * kSampleThreads + tid) * 8;
+        draw_fetch<L, false>(p, w, pen, b, min(v0, V - 1), cur);
+        if (v0 < V)
+            draw_unit<L>(p, w, tk, pen, b, v0, f, r, scale2, cur, bk, bi);
     }
     group_best(bk, bi, sh_best);
     if (tid == 0)
-        p.resid[(size_t)b * S + split] = float2{bk, __int_as_float(bi)};
+        p.resid[(size_t)b * p.Sd + split] = float2{bk, __int_as_float(bi)};
 }
 
 // ---- final kernel -----------------------------------------------------------
@@ -536,7 +816,7 @@ __global__ __launch_bounds__(64) void gdn_sample_final_kernel(const SampleParams
         }
         return;
     }
-    const int R = p.R, V = p.V, S = p.S;
+    const int R = p.R, V = p.V, S = p.Sd;
     bool bad = !(p.temp[b] > 0.0f && p.temp[b] <= 3.0e38f);
     if (p.pending)
         bad |= p.pending[b] < 0 || p.pending[b] >= V;
@@ -554,7 +834,7 @@ __global__ __launch_bounds__(64) void gdn_sample_final_kernel(const SampleParams
         return;
     }
     const int n = p.nacc[b];
-    const float2 *src = (n == R ? p.bonus : p.resid) + (size_t)b * S;
+    const float2 *src = p.resid + (size_t)b * S;
     float bk = kNegInf;
     int bi = 0x7fffffff;
     for (int i = lane; i < S; i += 64)
@@ -570,46 +850,89 @@ __global__ __launch_bounds__(64) void gdn_sample_final_kernel(const SampleParams
     }
 }
 
-template <int R, typename L, bool PEN> void launch_stats(const SampleParams &p, hipStream_t st)
+// Workgroups of a kernel that one compute unit holds at once (its occupancy),
+// asked of the runtime once per kernel.
+template <typename K> int groups_per_cu(K kernel)
 {
-    const bool aligned = ((size_t)p.V * sizeof(L)) % 16 == 0 && (reinterpret_cast<uintptr_t>(p.logits) & 15) == 0 &&
-                         (reinterpret_cast<uintptr_t>(p.prior) & 15) == 0;
-    const int full = aligned ? p.V / kSampleChunk : 0;   // splits wholly inside the vocabulary
-    if (full > 0)
-        hipLaunchKernelGGL((gdn_sample_stats_kernel<R, L, PEN, true>), dim3((unsigned)full, (unsigned)p.B),
-                           dim3(kSampleThreads), 0, st, p, 0);
-    if (full < p.S)
-        hipLaunchKernelGGL((gdn_sample_stats_kernel<R, L, PEN, false>), dim3((unsigned)(p.S - full), (unsigned)p.B),
-                           dim3(kSampleThreads), 0, st, p, full);
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kSampleThreads, 0) != hipSuccess || n < 1)
+        n = 1;
+    return n;
 }
 
-template <int R, typename L> void launch_sample_kernels(dim3 grid, const SampleParams &p, hipStream_t st)
+int compute_units(hipStream_t st)
 {
-    if (p.pres || p.freq)
-        launch_stats<R, L, true>(p, st);
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipStreamGetDevice(st, &dev) != hipSuccess && hipGetDevice(&dev) != hipSuccess)
+        return 256;
+    if (dev < 0 || dev >= 64)
+        return 256;
+    if (!cached[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+// Columns per thread so that the batch's workgroups all fit on the device at
+// once: each request gets at most resident / B splits, and at most kMaxSplits.
+int columns_per_split(int B, int V, int resident)
+{
+    const int total = (V + kColumn - 1) / kColumn;
+    const int per_request = std::max(1, std::min(kMaxSplits, resident / std::max(B, 1)));
+    return std::max(1, (total + per_request - 1) / per_request);
+}
+
+template <int R, typename L> void launch_sample_kernels(SampleParams p, hipStream_t st)
+{
+    const auto row_aligned = [](const void *ptr, size_t row_bytes) {
+        return ptr && (reinterpret_cast<uintptr_t>(ptr) & 15) == 0 && row_bytes % 16 == 0;
+    };
+    const int vec = (row_aligned(p.logits, (size_t)p.V * sizeof(L)) ? kVecLogits : 0) |
+                    (row_aligned(p.prior, (size_t)p.V * sizeof(int32_t)) ? kVecPrior : 0) |
+                    (row_aligned(p.dprob, (size_t)p.V * sizeof(float)) ? kVecProbs : 0);
+    const int cus = compute_units(st);
+    const bool pen = p.pres || p.freq;
+    static const int occ_pen = groups_per_cu(gdn_sample_stats_kernel<R, L, true>);
+    static const int occ_plain = groups_per_cu(gdn_sample_stats_kernel<R, L, false>);
+    static const int occ_draw = groups_per_cu(gdn_sample_residual_kernel<R, L>);
+    p.U = columns_per_split(p.B, p.V, cus * (pen ? occ_pen : occ_plain));
+    p.S = (p.V + p.U * kColumn - 1) / (p.U * kColumn);
+    p.Ud = columns_per_split(p.B, p.V, cus * occ_draw);
+    p.Sd = (p.V + p.Ud * kColumn - 1) / (p.Ud * kColumn);
+    const dim3 block(kSampleThreads);
+    if (pen)
+        hipLaunchKernelGGL((gdn_sample_stats_kernel<R, L, true>), dim3((unsigned)p.S, (unsigned)p.B), block, 0, st, p,
+                           vec);
     else
-        launch_stats<R, L, false>(p, st);
-    hipLaunchKernelGGL((gdn_sample_residual_kernel<R, L>), grid, dim3(kSampleThreads), 0, st, p);
+        hipLaunchKernelGGL((gdn_sample_stats_kernel<R, L, false>), dim3((unsigned)p.S, (unsigned)p.B), block, 0, st,
+                           p, vec);
+    hipLaunchKernelGGL((gdn_sample_residual_kernel<R, L>), dim3((unsigned)p.Sd, (unsigned)p.B), block, 0, st, p, vec);
+    hipLaunchKernelGGL(gdn_sample_final_kernel, dim3((unsigned)p.B), dim3(64), 0, st, p);
 }
 
-template <typename L> void launch_rows(int rows, dim3 grid, const SampleParams &p, hipStream_t st)
+template <typename L> void launch_rows(int rows, const SampleParams &p, hipStream_t st)
 {
     switch (rows) {
-    case 1: launch_sample_kernels<1, L>(grid, p, st); break;
-    case 2: launch_sample_kernels<2, L>(grid, p, st); break;
-    case 3: launch_sample_kernels<3, L>(grid, p, st); break;
-    case 4: launch_sample_kernels<4, L>(grid, p, st); break;
-    case 5: launch_sample_kernels<5, L>(grid, p, st); break;
-    case 6: launch_sample_kernels<6, L>(grid, p, st); break;
-    case 7: launch_sample_kernels<7, L>(grid, p, st); break;
-    case 8: launch_sample_kernels<8, L>(grid, p, st); break;
-    default: launch_sample_kernels<9, L>(grid, p, st); break;
+    case 1: launch_sample_kernels<1, L>(p, st); break;
+    case 2: launch_sample_kernels<2, L>(p, st); break;
+    case 3: launch_sample_kernels<3, L>(p, st); break;
+    case 4: launch_sample_kernels<4, L>(p, st); break;
+    case 5: launch_sample_kernels<5, L>(p, st); break;
+    case 6: launch_sample_kernels<6, L>(p, st); break;
+    case 7: launch_sample_kernels<7, L>(p, st); break;
+    case 8: launch_sample_kernels<8, L>(p, st); break;
+    default: launch_sample_kernels<9, L>(p, st); break;
     }
 }
 
+// Scratch: partial pairs [B][R][splits], draw keys [B][splits], accept
+// lengths [B], sized for the most splits any launch may use.
 struct SampleLayout {
-    size_t stats, bonus, resid, nacc, total;
-    int S;
+    size_t stats, resid, nacc, total;
 };
 
 size_t align256(size_t v) { return (v + 255) / 256 * 256; }
@@ -618,16 +941,14 @@ gdn_status sample_layout(int batch, int rows, int vocab, SampleLayout *l)
 {
     if (batch < 0 || rows < 1 || rows > kMaxSampleRows || vocab < 1)
         return GDN_ERR_INVALID_ARG;
-    if (vocab > kMaxSplits * kSampleChunk)
+    if (vocab > (1 << 20))
         return GDN_ERR_UNSUPPORTED;
-    l->S = (vocab + kSampleChunk - 1) / kSampleChunk;
+    const size_t splits = std::min<size_t>(kMaxSplits, (vocab + kColumn - 1) / kColumn);
     size_t off = 0;
     l->stats = off;
-    off = align256(off + (size_t)batch * rows * l->S * sizeof(float2));
-    l->bonus = off;
-    off = align256(off + (size_t)batch * l->S * sizeof(float2));
+    off = align256(off + (size_t)batch * rows * splits * sizeof(float2));
     l->resid = off;
-    off = align256(off + (size_t)batch * l->S * sizeof(float2));
+    off = align256(off + (size_t)batch * splits * sizeof(float2));
     l->nacc = off;
     off = align256(off + (size_t)batch * sizeof(int32_t));
     l->total = off;
@@ -681,23 +1002,19 @@ gdn_status gdn_spec_accept_sample(const gdn_sample_inputs *in, int32_t logits_dt
     p.B = batch;
     p.R = rows;
     p.V = vocab;
-    p.S = l.S;
     p.k0 = (uint32_t)(seed & 0xffffffffu);
     p.k1 = (uint32_t)(seed >> 32);
     p.stats = reinterpret_cast<float2 *>(base + l.stats);
-    p.bonus = reinterpret_cast<float2 *>(base + l.bonus);
     p.resid = reinterpret_cast<float2 *>(base + l.resid);
     p.nacc = reinterpret_cast<int32_t *>(base + l.nacc);
     p.accept = accept_len;
     p.next = next_token;
     p.err = err_flag;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const dim3 grid((unsigned)l.S, (unsigned)batch);
     if (logits_dtype == GDN_F32)
-        launch_rows<float>(rows, grid, p, st);
+        launch_rows<float>(rows, p, st);
     else
-        launch_rows<uint16_t>(rows, grid, p, st);
-    hipLaunchKernelGGL(gdn_sample_final_kernel, dim3((unsigned)batch), dim3(64), 0, st, p);
+        launch_rows<uint16_t>(rows, p, st);
     return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
