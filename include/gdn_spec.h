@@ -232,7 +232,9 @@ gdn_status gdn_spec_accept_greedy(const int32_t *draft, const int32_t *target,
  * that is not finite and > 0, or a draft or pending token outside [0, V), gets
  * accept_len 0 and next_token -1, and bit 3 is OR-ed into *err_flag.
  * scratch: gdn_spec_sample_scratch_bytes() bytes, 16-byte aligned, used
- * within the call only. Host checks return a status before any launch.
+ * within the call only; it needs no clearing (the call resets what it uses),
+ * and calls in flight at the same time need buffers of their own. Host checks
+ * return a status before any launch.
  */
 typedef struct {
     const void *logits;

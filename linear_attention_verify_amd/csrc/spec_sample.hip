@@ -18,19 +18,19 @@
 // v & 3, for the noise of row t at entry v; (0, t, b, 1), word 0, for row t's
 // acceptance uniform. U = (2 (word >> 9) + 1) / 2^24, exact in fp32.
 //
-// Three kernels, all over the logits in HBM order:
-//   stats     grid (splits, requests): each workgroup takes 4096 vocabulary
-//             entries of every row of its request, forms the penalised and
-//             tempered logits in base 2 and leaves, per row, the running
-//             maximum and sum of 2^x (online softmax). No random numbers.
-//   residual  grid (splits, requests): every workgroup of a request combines
+// Two kernels, both over the logits in HBM order:
+//   stats     grid (splits, requests): each workgroup takes its columns of
+//             every row of its request, forms the penalised and tempered
+//             logits in base 2 and leaves, per row, the running maximum and
+//             sum of 2^x (online softmax). No random numbers.
+//   draw      grid (splits, requests): every workgroup of a request combines
 //             the partial sums in the same order, so all of them reach the
 //             same acceptance of every draft and the same accept length n;
 //             each then takes the best Gumbel key over its entries of row
 //             n - 1: of the residual max(0, p - q) after a rejection, of p
-//             when every draft was kept (the bonus token).
-//   final     one wave per request: the best key over the splits gives the
-//             next token; accept_len and next_token are written.
+//             when every draft was kept (the bonus token). The workgroups
+//             fold their bests into one word per request with atomics; the
+//             last of them to finish writes accept_len and next_token.
 
 #include <hip/hip_runtime.h>
 
@@ -107,8 +107,8 @@ struct SampleParams {
     int Sd, Ud;   // draw pass: the same
     uint32_t k0, k1;
     float2 *stats;   // [B][R][S]: running maximum (base 2) and sum of 2^(x - max)
-    float2 *resid;   // [B][Sd]: best key of the draw (residual or bonus) and its index (bits)
-    int32_t *nacc;   // [B]: accept length
+    unsigned long long *best;   // [B]: best (key, index) of the draw so far, as one ordered word
+    int32_t *done;              // [B]: draw workgroups finished
     int32_t *accept;
     int32_t *next;
     int32_t *err;
@@ -159,6 +159,16 @@ __device__ __forceinline__ float penalised2(float l, int prior_c, const Tokens &
 
 // Best (key, index) with ties to the smaller index.
 __device__ __forceinline__ bool better(float k, int i, float bk, int bi) { return k > bk || (k == bk && i < bi); }
+
+// (key, index) as one word that orders like better(): the key's bits made
+// monotonic in the high half, the complemented index in the low half. A NaN
+// key counts as -inf, so the word is never all ones.
+__device__ __forceinline__ unsigned long long order_key(float k, int i)
+{
+    const uint32_t u = __float_as_uint(k == k ? k : kNegInf);
+    const uint32_t hi = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((unsigned long long)hi << 32) | (uint32_t)~(uint32_t)i;
+}
 
 // ---- reductions ------------------------------------------------------------
 
@@ -526,6 +536,10 @@ __global__ __launch_bounds__(kSampleThreads) void gdn_sample_stats_kernel(const 
     const bool vec = (vec_ok & kVecLogits) && (!PEN || !p.prior || (vec_ok & kVecPrior));
     const int whole = vec ? min(cols, (V - base) / kColumn) : 0;   // columns of whole units only
 
+    if (split == 0 && tid == 0) {   // the draw pass of this call gathers its result here
+        p.best[b] = 0ull;
+        p.done[b] = 0;
+    }
     // the first two columns' loads go out before the per-request values are
     // read (rows of padding requests are still inside the logits)
     Unit<L> x[R], xn[R];
@@ -635,11 +649,14 @@ __device__ __forceinline__ void draw_fetch(const SampleParams &p, const DrawRow 
     }
 }
 
+// One unit's keys. A thread visits its entries in increasing index order, so
+// among equal keys the first one seen (the smaller index) is kept by a plain
+// greater-than; entries past the vocabulary have -inf keys.
 template <typename L>
 __device__ __forceinline__ void draw_unit(const SampleParams &p, const DrawRow &w, const Tokens &tk, bool pen, int b,
-                                          int v0, float f, float r, float scale2, DrawUnit<L> &u, float &bk, int &bi)
+                                          int v0, float f2, float r2, float scale2, DrawUnit<L> &u, float &bk, int &bi)
 {
-    const int V = p.V, t = w.t;
+    const int t = w.t;
     float ps[8];
     if (pen) {
         if (unit_holds_token(tk, t, v0)) {
@@ -651,7 +668,7 @@ __device__ __forceinline__ void draw_unit(const SampleParams &p, const DrawRow &
         }
 #pragma unroll
         for (int k = 0; k < 8; ++k)
-            ps[k] = penalty2(u.c[k], f, r, scale2);
+            ps[k] = __builtin_fmaf(f2, (float)u.c[k], u.c[k] > 0 ? r2 : 0.0f);
     } else {
 #pragma unroll
         for (int k = 0; k < 8; ++k)
@@ -662,18 +679,17 @@ __device__ __forceinline__ void draw_unit(const SampleParams &p, const DrawRow &
     const uint32_t gw[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-        const int v = v0 + k;
         const float y = __builtin_fmaf(u.x.at(k), scale2, -ps[k]);
         float key;
         if (w.q) {
             const float res = fast_exp2(y - w.mm) * w.inv - u.q.at(k);
             key = res > 0.0f ? fast_log2(res) + gumbel2(gw[k]) : kNegInf;
         } else {
-            key = v != w.d ? y + gumbel2(gw[k]) : kNegInf;
+            key = v0 + k != w.d ? y + gumbel2(gw[k]) : kNegInf;
         }
-        if (v < V && key != kNegInf && better(key, v, bk, bi)) {
+        if (key > bk) {
             bk = key;
-            bi = v;
+            bi = v0 + k;
         }
     }
 }
@@ -684,14 +700,21 @@ __global__ __launch_bounds__(kSampleThreads) void gdn_sample_residual_kernel(con
     __shared__ float2 row_ms[kMaxSampleRows];
     __shared__ int acc[kMaxSampleRows];
     __shared__ float2 sh_best[kSampleThreads / 64];
+    __shared__ int last;
     const int split = blockIdx.x, b = blockIdx.y;
     const int V = p.V, S = p.S, U = p.Ud;
     const int tid = threadIdx.x;
-    if (padding(p, b))
+    if (padding(p, b)) {
+        if (split == 0 && tid == 0) {
+            p.accept[b] = 0;
+            p.next[b] = -1;
+        }
         return;
+    }
     const Tokens tk = request_tokens(p, b);
     const float scale2 = temperature_scale(p, b);
     const float f = p.freq ? ld_scalar(p.freq, b) : 0.0f, r = p.pres ? ld_scalar(p.pres, b) : 0.0f;
+    const float f2 = f * scale2, r2 = r * scale2;
     const bool pen = f != 0.0f || r != 0.0f;
     const L *lg = static_cast<const L *>(p.logits) + (size_t)b * R * V;
     const int base = split * U * kColumn;
@@ -758,8 +781,6 @@ __global__ __launch_bounds__(kSampleThreads) void gdn_sample_residual_kernel(con
             n = t + 1;
             break;
         }
-    if (split == 0 && tid == 0)
-        p.nacc[b] = n;
 
     DrawRow w;
     w.t = n - 1;
@@ -785,68 +806,51 @@ __global__ __launch_bounds__(kSampleThreads) void gdn_sample_residual_kernel(con
 #pragma unroll 1
         for (int u = 0; u + 1 < whole; ++u) {
             draw_fetch<L, true>(p, w, pen, b, base + ((u + 1) * kSampleThreads + tid) * 8, nxt);
-            draw_unit<L>(p, w, tk, pen, b, base + (u * kSampleThreads + tid) * 8, f, r, scale2, cur, bk, bi);
+            draw_unit<L>(p, w, tk, pen, b, base + (u * kSampleThreads + tid) * 8, f2, r2, scale2, cur, bk, bi);
             cur = nxt;
         }
-        draw_unit<L>(p, w, tk, pen, b, base + ((whole - 1) * kSampleThreads + tid) * 8, f, r, scale2, cur, bk, bi);
+        draw_unit<L>(p, w, tk, pen, b, base + ((whole - 1) * kSampleThreads + tid) * 8, f2, r2, scale2, cur, bk,
+                     bi);
     }
 #pragma unroll 1
     for (int u = whole; u < cols; ++u) {
         const int v0 = base + (u * kSampleThreads + tid) * 8;
         draw_fetch<L, false>(p, w, pen, b, min(v0, V - 1), cur);
         if (v0 < V)
-            draw_unit<L>(p, w, tk, pen, b, v0, f, r, scale2, cur, bk, bi);
+            draw_unit<L>(p, w, tk, pen, b, v0, f2, r2, scale2, cur, bk, bi);
     }
     group_best(bk, bi, sh_best);
-    if (tid == 0)
-        p.resid[(size_t)b * p.Sd + split] = float2{bk, __int_as_float(bi)};
-}
 
-// ---- final kernel -----------------------------------------------------------
-
-// One wave per request: the lanes take the splits' best keys in turn, then the
-// wave's best (ties to the smaller index) is the next token.
-__global__ __launch_bounds__(64) void gdn_sample_final_kernel(const SampleParams p)
-{
-    const int b = blockIdx.x, lane = threadIdx.x;
-    if (padding(p, b)) {
-        if (lane == 0) {
-            p.accept[b] = 0;
-            p.next[b] = -1;
-        }
-        return;
+    // every workgroup folds its best into the request's word with an atomic
+    // maximum, then counts itself done; the count waits for the maximum's
+    // returned value, so it is performed after it. The last to count reads
+    // the word back: the best over all splits. Only atomics cross workgroups.
+    if (tid == 0) {
+        const unsigned long long prev = atomicMax(&p.best[b], order_key(bk, bi));
+        last = atomicAdd(&p.done[b], prev == ~0ull ? 2 : 1) == p.Sd - 1;   // never ~0: see order_key
     }
-    const int R = p.R, V = p.V, S = p.Sd;
-    bool bad = !(p.temp[b] > 0.0f && p.temp[b] <= 3.0e38f);
+    __syncthreads();
+    if (!last || tid != 0)
+        return;
+    const unsigned long long fin = atomicOr(&p.best[b], 0ull);
+    const int ci = (int)~(uint32_t)fin;
+    bool bad = !(scale2 > 0.0f);
     if (p.pending)
-        bad |= p.pending[b] < 0 || p.pending[b] >= V;
-    for (int s = 0; s < R - 1; ++s) {
-        const int d = p.draft[(size_t)b * (R - 1) + s];
-        bad |= d < 0 || d >= V;
-    }
+        bad |= tk.tok[0] < 0 || tk.tok[0] >= V;
+#pragma unroll
+    for (int j = 1; j < R; ++j)
+        bad |= tk.tok[j] < 0 || tk.tok[j] >= V;
     if (bad) {
-        if (lane == 0) {
-            if (p.err)
-                atomicOr(p.err, 8);
-            p.accept[b] = 0;
-            p.next[b] = -1;
-        }
+        if (p.err)
+            atomicOr(p.err, 8);
+        p.accept[b] = 0;
+        p.next[b] = -1;
         return;
     }
-    const int n = p.nacc[b];
-    const float2 *src = p.resid + (size_t)b * S;
-    float bk = kNegInf;
-    int bi = 0x7fffffff;
-    for (int i = lane; i < S; i += 64)
-        if (better(src[i].x, __float_as_int(src[i].y), bk, bi)) {
-            bk = src[i].x;
-            bi = __float_as_int(src[i].y);
-        }
-    wave_best(bk, bi);
-    if (lane == 0) {
+    {
         p.accept[b] = n;
         // an empty residual (every p <= q after rounding) keeps the rejected draft
-        p.next[b] = bi != 0x7fffffff ? bi : (n < R ? p.draft[(size_t)b * (R - 1) + n - 1] : 0);
+        p.next[b] = ci != 0x7fffffff ? ci : (n < R ? w.d : 0);
     }
 }
 
@@ -911,7 +915,6 @@ template <int R, typename L> void launch_sample_kernels(SampleParams p, hipStrea
         hipLaunchKernelGGL((gdn_sample_stats_kernel<R, L, false>), dim3((unsigned)p.S, (unsigned)p.B), block, 0, st,
                            p, vec);
     hipLaunchKernelGGL((gdn_sample_residual_kernel<R, L>), dim3((unsigned)p.Sd, (unsigned)p.B), block, 0, st, p, vec);
-    hipLaunchKernelGGL(gdn_sample_final_kernel, dim3((unsigned)p.B), dim3(64), 0, st, p);
 }
 
 template <typename L> void launch_rows(int rows, const SampleParams &p, hipStream_t st)
@@ -929,10 +932,10 @@ template <typename L> void launch_rows(int rows, const SampleParams &p, hipStrea
     }
 }
 
-// Scratch: partial pairs [B][R][splits], draw keys [B][splits], accept
-// lengths [B], sized for the most splits any launch may use.
+// Scratch: partial pairs [B][R][splits] (sized for the most splits any
+// launch may use), the draw's best word [B] and finished-workgroup counts [B].
 struct SampleLayout {
-    size_t stats, resid, nacc, total;
+    size_t stats, best, done, total;
 };
 
 size_t align256(size_t v) { return (v + 255) / 256 * 256; }
@@ -947,9 +950,9 @@ gdn_status sample_layout(int batch, int rows, int vocab, SampleLayout *l)
     size_t off = 0;
     l->stats = off;
     off = align256(off + (size_t)batch * rows * splits * sizeof(float2));
-    l->resid = off;
-    off = align256(off + (size_t)batch * splits * sizeof(float2));
-    l->nacc = off;
+    l->best = off;
+    off = align256(off + (size_t)batch * sizeof(unsigned long long));
+    l->done = off;
     off = align256(off + (size_t)batch * sizeof(int32_t));
     l->total = off;
     return GDN_OK;
@@ -1005,8 +1008,8 @@ gdn_status gdn_spec_accept_sample(const gdn_sample_inputs *in, int32_t logits_dt
     p.k0 = (uint32_t)(seed & 0xffffffffu);
     p.k1 = (uint32_t)(seed >> 32);
     p.stats = reinterpret_cast<float2 *>(base + l.stats);
-    p.resid = reinterpret_cast<float2 *>(base + l.resid);
-    p.nacc = reinterpret_cast<int32_t *>(base + l.nacc);
+    p.best = reinterpret_cast<unsigned long long *>(base + l.best);
+    p.done = reinterpret_cast<int32_t *>(base + l.done);
     p.accept = accept_len;
     p.next = next_token;
     p.err = err_flag;

@@ -141,6 +141,37 @@ def test_sample_accept_length_spread():
     assert set(acc_r.tolist()) == {1, 2, 3, 4}
 
 
+def test_scratch_reused_across_calls():
+    """One scratch buffer for several calls in a row (the call resets its own
+    counters): a full batch, then a smaller one with another vocabulary, then
+    the first again with a new seed; each against the oracle."""
+    big = make_inputs(24, 9, 30000, seed=77, dtype="bf16", probs=False, penalties=True)
+    small = make_inputs(5, 4, 4500, seed=78, dtype="f32", probs=True, penalties=False)
+    nbytes = max(bd.gdn_spec_sample_scratch_bytes(24, 9, 30000), bd.gdn_spec_sample_scratch_bytes(5, 4, 4500))
+    scratch = torch.full((nbytes,), 0x5A, dtype=torch.uint8, device=DEV)   # not cleared: garbage to start
+    for d, seed, dtype in ((big, 11, "bf16"), (small, 12, "f32"), (big, 13, "bf16")):
+        B, R, V = d["logits"].shape
+        print("sample reuse B=%d R=%d V=%d seed=%d" % (B, R, V, seed), flush=True)
+        t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+        lg = torch.from_numpy(d["logits"]).to(DEV)
+        lg = lg.to(torch.bfloat16) if dtype == "bf16" else lg
+        acc = torch.full((B,), -7, dtype=torch.int32, device=DEV)
+        nxt = torch.full((B,), -7, dtype=torch.int32, device=DEV)
+        err = torch.zeros(1, dtype=torch.int32, device=DEV)
+        bd.gdn_spec_accept_sample(lg, t(d["draft"]), t(d["temperature"]), seed, acc, nxt, scratch,
+                                  draft_probs=t(d.get("draft_probs")), pending=t(d.get("pending")),
+                                  prior_counts=t(d.get("prior_counts")), presence=t(d.get("presence")),
+                                  frequency=t(d.get("frequency")), slot_ids=t(d.get("slot_ids")), err_flag=err)
+        torch.cuda.synchronize()
+        acc_r, nxt_r, info = run_oracle(d, seed)
+        assert int(err.item()) == 0
+        clear = [min(i["accept_margins"][:acc_r[b]] or [1.0]) > ACCEPT_TIE and i["argmax_gap"] > KEY_TIE
+                 for b, i in enumerate(info)]
+        a, n = acc.cpu().numpy(), nxt.cpu().numpy()
+        assert all((a[b] == acc_r[b] and n[b] == nxt_r[b]) or not clear[b] for b in range(B)), (a, acc_r, n, nxt_r)
+        assert sum(not c for c in clear) <= max(1, B // 20)
+
+
 def test_bad_inputs_are_flagged():
     d = make_inputs(6, 4, 100, seed=9, dtype="f32", probs=False, penalties=True)
     d["temperature"][1] = 0.0
