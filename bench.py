@@ -37,6 +37,7 @@ HBM_PEAK_GBPS = 8000.0
 COPY_BYTES = 256 << 20
 KERNEL_SOURCE = os.path.join(ROOT, "linear_attention_verify_amd", "csrc", "gdn_spec.hip")
 ATTN_SOURCE = os.path.join(ROOT, "linear_attention_verify_amd", "csrc", "spec_attention.hip")
+SAMPLE_SOURCE = os.path.join(ROOT, "linear_attention_verify_amd", "csrc", "spec_sample.hip")
 
 # HBM bytes per launch read from rocprofv3 counters: FETCH_SIZE and WRITE_SIZE
 # (KiB per dispatch, one run each) of every launch of the kernel, averaged,
@@ -46,15 +47,22 @@ ATTN_SOURCE = os.path.join(ROOT, "linear_attention_verify_amd", "csrc", "spec_at
 # reports null.
 MEASURED_TRAFFIC = [
     {"source": KERNEL_SOURCE,
-     "source_sha256": "f0436b5cecf214df6802988cbdc20b3b72b7597e3ed04699adba958ace1e0189",
+     "source_sha256": "23952e152fc9e8d397b96d8b83ea886765a59149fc5314e0a37ae3125d20ec19",
      "bytes": {   # (workload, mode, kernel) -> bytes per launch
-         ("saturated-b64", "replay", "verify"): 176085313,
-         ("saturated-b64", "replay", "commit"): 282700576,
+         ("saturated-b64", "replay", "verify"): 176086659,
+         ("saturated-b64", "replay", "commit"): 282684671,
+         ("saturated-b64", "snapshot", "verify"): 1384335766,
+         ("saturated-b64", "snapshot", "commit"): 274773215,
      }},
     {"source": ATTN_SOURCE,
-     "source_sha256": "48053594bb5c23d84287f0f2482f4eed15c191f19f7704bebaaaec6088e44d2a",
+     "source_sha256": "f254bc77bc855d9281a6304db619d063533d81c6e4ed714c46000f8b555346f6",
      "bytes": {   # one call: split kernel + combine kernel
-         ("attn-b64", "-", "attn_verify"): 681306111,
+         ("attn-b64", "-", "attn_verify"): 681347947,
+     }},
+    {"source": SAMPLE_SOURCE,
+     "source_sha256": "47b36fd82f912081bbe5a0497b820ee1e28bcf243d08da4bd71e42cc043d9642",
+     "bytes": {   # one call: stats kernel + draw kernel
+         ("sample-b64", "-", "accept_sample"): 275200735,
      }},
 ]
 
@@ -349,6 +357,8 @@ def run_sample(args, w):
 
     if args.graph or args.accept != "given" or args.mode != "replay":
         raise SystemExit("--graph, --accept and --mode apply to GDN workloads")
+    if args.calibrate_copy:
+        calibration_copy()
     d = wl.draw_sample(w)
     dev = "cuda"
     t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
@@ -397,7 +407,7 @@ def run_sample(args, w):
                    "accept_mean": acc_mean, "rotating_copies": M},
         "gbps": nb * args.steps / wall / 1e9, "hbm_frac": nb * args.steps / wall / 1e9 / HBM_PEAK_GBPS,
         "kernels": {"accept_sample": {"avg_us": tcall * 1e6, "bytes": nb, "gbps": ach}},
-        "roofline": {"bound": "hbm", "kernel": "accept_sample (stats + residual + final)", "achieved": ach,
+        "roofline": {"bound": "hbm", "kernel": "accept_sample (stats + draw kernels)", "achieved": ach,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS,
                      "traffic": measured_traffic(w.name, "-", "accept_sample")},
     }

@@ -695,7 +695,7 @@ __device__ __forceinline__ void draw_unit(const SampleParams &p, const DrawRow &
 }
 
 template <int R, typename L>
-__global__ __launch_bounds__(kSampleThreads) void gdn_sample_residual_kernel(const SampleParams p, int vec_ok)
+__global__ __launch_bounds__(kSampleThreads) void gdn_sample_draw_kernel(const SampleParams p, int vec_ok)
 {
     __shared__ float2 row_ms[kMaxSampleRows];
     __shared__ int acc[kMaxSampleRows];
@@ -902,7 +902,7 @@ template <int R, typename L> void launch_sample_kernels(SampleParams p, hipStrea
     const bool pen = p.pres || p.freq;
     static const int occ_pen = groups_per_cu(gdn_sample_stats_kernel<R, L, true>);
     static const int occ_plain = groups_per_cu(gdn_sample_stats_kernel<R, L, false>);
-    static const int occ_draw = groups_per_cu(gdn_sample_residual_kernel<R, L>);
+    static const int occ_draw = groups_per_cu(gdn_sample_draw_kernel<R, L>);
     p.U = columns_per_split(p.B, p.V, cus * (pen ? occ_pen : occ_plain));
     p.S = (p.V + p.U * kColumn - 1) / (p.U * kColumn);
     p.Ud = columns_per_split(p.B, p.V, cus * occ_draw);
@@ -914,7 +914,7 @@ template <int R, typename L> void launch_sample_kernels(SampleParams p, hipStrea
     else
         hipLaunchKernelGGL((gdn_sample_stats_kernel<R, L, false>), dim3((unsigned)p.S, (unsigned)p.B), block, 0, st,
                            p, vec);
-    hipLaunchKernelGGL((gdn_sample_residual_kernel<R, L>), dim3((unsigned)p.Sd, (unsigned)p.B), block, 0, st, p, vec);
+    hipLaunchKernelGGL((gdn_sample_draw_kernel<R, L>), dim3((unsigned)p.Sd, (unsigned)p.B), block, 0, st, p, vec);
 }
 
 template <typename L> void launch_rows(int rows, const SampleParams &p, hipStream_t st)
