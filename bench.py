@@ -14,6 +14,16 @@ copy the other copies move several GB, so nothing of it (state, inputs, or
 the stash the commit reads back) is still in the 256 MB Infinity Cache: every
 kernel runs cold. All inputs are resident in HBM before the timed region.
 
+Schedule (--schedule, reported in the line): serial (the default) issues
+everything on one stream. overlap issues a group's commits on a second stream
+once the whole group is verified, and a copy's next verify waits for that
+copy's commit, as a serving loop that starts the next step's layers while the
+last step's states are committed would; every data dependency of the serial
+order holds. It pays in long runs of large replay batches (one kernel's ramp
+and tail take the other's work); over a few steps the pipeline's fill and
+drain and the per-launch stream waits cost more than it gains. Per-kernel
+durations are always timed serially, each kernel's launches back to back.
+
 Prints one JSON line. value = verify rows per second (batch x rows per step);
 gbps = algorithmic HBM bytes per second: per request, verify reads the state,
 the conv history, x and the gates and writes o and a stash of the rows' raw
@@ -525,6 +535,11 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="time replays of a captured HIP graph of each group of steps instead of "
                          "eager launches (steps and warmup must be multiples of --copies)")
+    ap.add_argument("--schedule", default="serial", choices=["serial", "overlap"],
+                    help="serial: every launch on one stream; overlap: a group's commits on a second "
+                         "stream, each copy's next verify waiting for its own commit, so one group's "
+                         "commits run beside the next group's verifies (pays in long runs of large "
+                         "replay batches; the pipeline's fill and drain cost more over a few steps)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 256 MiB device copy (the reference dispatch for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -563,6 +578,15 @@ def main():
     prepared = [bd.Prepared(c.desc, c.ssm, c.conv, c.conv_w, c.x, c.alpha, c.beta, c.slot_ids,
                             c.accept, w.rows, c.mode, c.scratch, c.out, c.err, stream)
                 for c in cases]
+    overlap = args.schedule == "overlap"
+    if overlap and args.graph:
+        raise SystemExit("--graph captures one stream: use --schedule serial")
+    vstream, cstream = (torch.cuda.Stream(), torch.cuda.Stream()) if overlap else (stream, stream)
+    pv = [bd.Prepared(c.desc, c.ssm, c.conv, c.conv_w, c.x, c.alpha, c.beta, c.slot_ids, c.accept, w.rows,
+                      c.mode, c.scratch, c.out, c.err, vstream) for c in cases] if overlap else prepared
+    pc = [bd.Prepared(c.desc, c.ssm, c.conv, c.conv_w, c.x, c.alpha, c.beta, c.slot_ids, c.accept, w.rows,
+                      c.mode, c.scratch, c.out, c.err, cstream) for c in cases] if overlap else prepared
+    committed = [torch.cuda.Event() for _ in range(M)]
     accepts = [None] * M
     if args.accept == "greedy":
         draft, target = wl.draw_tokens(w, base.accept_np)
@@ -571,7 +595,9 @@ def main():
             tt = torch.from_numpy(target).cuda()
             nxt = torch.empty(w.batch, dtype=torch.int32, device="cuda")
             c.accept.zero_()
-            accepts[k] = bd.PreparedAccept(dt, tt, c.slot_ids, w.rows, c.accept, nxt, stream)
+            accepts[k] = bd.PreparedAccept(dt, tt, c.slot_ids, w.rows, c.accept, nxt, cstream)
+    accepts_serial = [None if a is None or not overlap else
+                      bd.PreparedAccept(*a._keep[:3], w.rows, *a._keep[3:], stream) for a in accepts]
     torch.cuda.synchronize()
 
     graph = None
@@ -595,14 +621,41 @@ def main():
                 p.commit()
         torch.cuda.synchronize()
 
+    def run_overlapped(nsteps):
+        """nsteps steps in groups of M copies on two streams: the group's
+        verifies on one, then (once every verify of the group is done, as
+        sampling needs the last layer) its acceptances and commits on the
+        other; a copy's next verify waits for that copy's commit. So one
+        group's commits run beside the next group's verifies, and every data
+        dependency of the serial order is kept."""
+        s = 0
+        while s < nsteps:
+            group = list(range(s, min(s + M, nsteps)))
+            for k in group:
+                vstream.wait_event(committed[k % M])
+                pv[k % M].verify()
+            verified = torch.cuda.Event()
+            verified.record(vstream)
+            cstream.wait_event(verified)
+            for k in group:
+                if accepts[k % M] is not None:
+                    accepts[k % M]()
+            for k in group:
+                pc[k % M].commit()
+                committed[k % M].record(cstream)
+            s += len(group)
+
     def run(nsteps, marks=None):
         """nsteps steps in groups of M copies: the group's verifies, then its
         acceptances (if any), then its commits. With `marks`, HIP events on the
-        launch stream bracket each of the three phases of every group."""
+        launch stream bracket each of the three phases of every group (always
+        one stream: each kernel's launches back to back)."""
         if graph is not None and marks is None:
             for _ in range(nsteps // M):
                 graph.replay()
             return
+        if overlap and marks is None:
+            return run_overlapped(nsteps)
         s = 0
         while s < nsteps:
             group = list(range(s, min(s + M, nsteps)))
@@ -619,7 +672,7 @@ def main():
             mark()
             for k in group:
                 if accepts[k % M] is not None:
-                    accepts[k % M]()
+                    (accepts_serial[k % M] or accepts[k % M])()
             mark()
             for k in group:
                 prepared[k % M].commit()
@@ -629,6 +682,7 @@ def main():
             s += len(group)
 
     run(args.warmup)
+    torch.cuda.synchronize()
 
     # timed region: exactly K steps, wall clock bracketed by synchronisation.
     # The device error flags are read after the timed passes (they are
@@ -685,7 +739,7 @@ def main():
                    "storage": w.shape.dtype, "state": "f32", "pool_slots": w.num_slots,
                    "commit_mode": args.mode, "accept_mean": float(np.mean(base.accept_np)),
                    "rotating_copies": M, "launch": "hip graph" if args.graph else "eager",
-                   "accept": args.accept},
+                   "schedule": "overlap" if overlap else "serial", "accept": args.accept},
         "gbps": gbps,
         "hbm_frac": gbps / HBM_PEAK_GBPS,
         "kernels": kernels,
