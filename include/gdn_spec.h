@@ -168,6 +168,53 @@ gdn_status gdn_spec_commit_layers(const gdn_layer_desc *desc, const gdn_pool *po
                                   void *stream);
 
 /*
+ * Another per-slot state a commit restores after the accepted rows: a window
+ * of the last `length` entries of a stream (FreeToken PR #844 "MTP drafts for
+ * the Qwen3.5 family and Flash-Next", Design: besides the GDN state a slot
+ * carries a second conv history and an n-gram context of token ids; the
+ * verify stages, per verify row, the entry that row appends, and the commit
+ * restores each state as it stands after the accepted rows, with the same
+ * upload of the slot and count indices). For request b with slot s and accept
+ * length n >= 1, state[s] becomes entries n .. n+length-1 of
+ * [state[s] (length entries, oldest first) | rows[b][0..n-1]]; n = 0 leaves it
+ * as it is. The GDN conv history is such a window (entries of C channels,
+ * length W-1).
+ *
+ *  state        [num_slots][length][entry_bytes], device, 4-byte aligned,
+ *               updated in place
+ *  rows         [batch][rows][entry_bytes], device, 4-byte aligned: row t of
+ *               request b is the entry verify row t appends
+ *  entry_bytes  a positive multiple of 4
+ */
+typedef struct {
+    void *state;
+    const void *rows;
+    int32_t num_slots;
+    int32_t length;
+    int32_t entry_bytes;
+} gdn_slot_window;
+
+/*
+ * Commit every GDN layer of a hybrid stack and every window state in one
+ * launch, all sharing slot_ids and accept_len (FreeToken PR #844, Design: the
+ * GDN commit and then every other slot state's commit, with one upload of the
+ * slot and count indices). The GDN layers are as in gdn_spec_commit_layers
+ * (0..64 of them; with none, desc, pools and scratch are not read); the
+ * windows (0..16, at least one layer or window in all) follow the rule above.
+ * Per request, a slot id outside [-1, num_slots) of a window sets bit 0 of
+ * *err_flag and an accept length outside [0, rows] bit 1, and that window of
+ * that request is left as it is. No window may overlap a pool, a scratch
+ * buffer or another window. Host checks return a status before any launch:
+ * GDN_ERR_INVALID_ARG for counts out of range, missing or misaligned
+ * pointers, entry_bytes not a positive multiple of 4; GDN_ERR_UNSUPPORTED for
+ * a window whose words do not fit an int32 index.
+ */
+gdn_status gdn_spec_commit_all(const gdn_layer_desc *desc, const gdn_pool *pools, void *const *scratch,
+                               int32_t layers, const gdn_slot_window *windows, int32_t num_windows,
+                               const int32_t *slot_ids, const int32_t *accept_len, int32_t batch, int32_t rows,
+                               gdn_commit_mode mode, size_t scratch_bytes, int32_t *err_flag, void *stream);
+
+/*
  * Greedy acceptance on the device, producing the accept_len that
  * gdn_spec_commit reads. Verify row 0 of request b holds the pending token and
  * row t (1 <= t < rows) the draft token draft[b][t-1]; target[b][t] is the

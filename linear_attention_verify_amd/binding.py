@@ -29,7 +29,7 @@ GDN_ACT_NONE = 1
 MODES = {"replay": GDN_COMMIT_REPLAY, "snapshot": GDN_COMMIT_SNAPSHOT}
 
 EXPORTS = ("gdn_spec_scratch_bytes", "gdn_spec_verify", "gdn_spec_commit", "gdn_spec_commit_layers",
-           "gdn_spec_accept_greedy", "gdn_strerror", "gdn_spec_attn_scratch_bytes", "gdn_spec_attn_verify",
+           "gdn_spec_commit_all", "gdn_spec_accept_greedy", "gdn_strerror", "gdn_spec_attn_scratch_bytes", "gdn_spec_attn_verify",
            "gdn_spec_attn_verify_static", "gdn_spec_sample_scratch_bytes", "gdn_spec_accept_sample")
 
 # bytes of the device array behind gdn_spec_attn_verify_static (GDN_SPEC_ATTN_STATIC_SCRATCH_BYTES)
@@ -55,6 +55,16 @@ class GdnPool(ctypes.Structure):
         ("ssm", ctypes.c_void_p),
         ("conv", ctypes.c_void_p),
         ("num_slots", ctypes.c_int32),
+    ]
+
+
+class GdnSlotWindow(ctypes.Structure):
+    _fields_ = [
+        ("state", ctypes.c_void_p),
+        ("rows", ctypes.c_void_p),
+        ("num_slots", ctypes.c_int32),
+        ("length", ctypes.c_int32),
+        ("entry_bytes", ctypes.c_int32),
     ]
 
 
@@ -105,6 +115,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.gdn_spec_commit_layers.restype = ctypes.c_int
     lib.gdn_spec_commit_layers.argtypes = [pdesc, ppool, ctypes.POINTER(vp), i32, vp, vp, i32, i32,
                                            ctypes.c_int, sz, vp, vp]
+    lib.gdn_spec_commit_all.restype = ctypes.c_int
+    lib.gdn_spec_commit_all.argtypes = [pdesc, ppool, ctypes.POINTER(vp), i32, ctypes.POINTER(GdnSlotWindow), i32,
+                                        vp, vp, i32, i32, ctypes.c_int, sz, vp, vp]
     lib.gdn_spec_accept_greedy.restype = ctypes.c_int
     lib.gdn_spec_accept_greedy.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp]
     pattn = ctypes.POINTER(GdnAttnDesc)
@@ -362,6 +375,72 @@ def gdn_spec_commit_layers(desc, layers, slot_ids, accept_len, rows, mode, err_f
                            host_slot_ids=None):
     """Commit every layer in one launch; layers = [(ssm, conv, scratch), ...] device tensors."""
     PreparedCommitLayers(desc, layers, slot_ids, accept_len, rows, mode, err_flag, stream, host_slot_ids)()
+
+
+def _check_window(state, rows_t, B, R, device):
+    """A window state [P][L][...] and its staged rows [B][R][...]: same dtype
+    and entry shape, entries a multiple of 4 bytes; returns the descriptor."""
+    torch = _torch()
+    if not isinstance(state, torch.Tensor) or state.dim() < 2:
+        raise ValueError("window state must be a tensor [slots][length][...]")
+    _check(state, "window state", state.dtype, tuple(state.shape), device=device)
+    _check(rows_t, "window rows", state.dtype, (B, R) + tuple(state.shape[2:]), device=device)
+    entry = state.element_size()
+    for e in state.shape[2:]:
+        entry *= int(e)
+    if entry % 4 or entry == 0:
+        raise ValueError("window entries are %d bytes, a positive multiple of 4 is needed" % entry)
+    return GdnSlotWindow(_ptr(state), _ptr(rows_t), int(state.shape[0]), int(state.shape[1]), entry)
+
+
+class PreparedCommitAll:
+    """gdn_spec_commit_all: GDN layers [(ssm, conv, scratch), ...] and window
+    states [(state, rows), ...] committed in one launch, checked and turned
+    into ctypes arguments once."""
+
+    def __init__(self, desc, layers, windows, slot_ids, accept_len, rows, mode, err_flag=None, stream=None,
+                 host_slot_ids=None):
+        torch = _torch()
+        if not layers and not windows:
+            raise ValueError("nothing to commit")
+        B = dev = None
+        for ssm, conv, sc in layers:
+            B = _check_commit_args(desc, ssm, conv, slot_ids, accept_len, sc, err_flag)
+            dev = ssm.device
+            if host_slot_ids is not None:
+                check_slot_ids_host(host_slot_ids, int(ssm.shape[0]))
+        if B is None:
+            B = _check_slot_table(slot_ids, None)
+            dev = slot_ids.device
+            _check(accept_len, "accept_len", torch.int32, (B,), device=dev)
+            _check(err_flag, "err_flag", torch.int32, (None,), device=dev, optional=True)
+        wins = [_check_window(st, rw, B, rows, dev) for st, rw in windows]
+        if host_slot_ids is not None:
+            for st, _ in windows:
+                check_slot_ids_host(host_slot_ids, int(st.shape[0]))
+        self.lib = load_library()
+        self._keep = (layers, windows, slot_ids, accept_len, err_flag)
+        self.desc = desc
+        L = len(layers)
+        self.pools = (GdnPool * max(L, 1))(*[make_pool(ssm, conv) for ssm, conv, _ in layers])
+        self.scratch = (ctypes.c_void_p * max(L, 1))(*[_ptr(sc) for _, _, sc in layers])
+        self.windows = (GdnSlotWindow * max(len(wins), 1))(*wins)
+        nbytes = min(_nbytes(sc) for _, _, sc in layers) if layers else 0
+        self.args = (ctypes.byref(self.desc) if desc is not None else None, self.pools if L else None,
+                     self.scratch if L else None, L, self.windows if wins else None, len(wins), _ptr(slot_ids),
+                     _ptr(accept_len), B, rows, _mode(mode), nbytes, _ptr(err_flag), _stream(stream))
+
+    def __call__(self):
+        st = self.lib.gdn_spec_commit_all(*self.args)
+        if st != GDN_OK:
+            raise GdnError(st, "gdn_spec_commit_all")
+
+
+def gdn_spec_commit_all(desc, layers, windows, slot_ids, accept_len, rows, mode, err_flag=None, stream=None,
+                        host_slot_ids=None):
+    """Commit GDN layers [(ssm, conv, scratch), ...] and window states
+    [(state [P][L][...], rows [B][R][...]), ...] in one launch."""
+    PreparedCommitAll(desc, layers, windows, slot_ids, accept_len, rows, mode, err_flag, stream, host_slot_ids)()
 
 
 def _check_accept_args(draft, target, slot_ids, rows, accept_len, next_token):

@@ -2031,11 +2031,81 @@ struct StackLayer {
 struct CommitStack {
     StackLayer l[kMaxLayers];
     size_t xs, es, ks, as, snap;   // scratch part offsets, the same in every layer
+    int layers;
 };
 
-template <int D, typename T, bool SNAP, int NPART>
-__global__ __launch_bounds__(kThreads) void gdn_commit_stack_kernel(const CommitParams<T> p0, const CommitStack st)
+// Other per-slot states committed in the same launch: windows of the last L
+// entries of a stream, rolled by the accept length over the rows the verify
+// staged (FreeToken PR #844, Design: the commit restores every slot state as
+// it stands after the accepted rows, all of them with one upload of the slot
+// and count indices).
+constexpr int kMaxWindows = 16;
+
+struct WindowSet {
+    gdn_slot_window w[kMaxWindows];
+    int count;
+};
+
+// Request b's window in window state w: new word u (of L * entry words) is
+// word u + n * entry of [old window | staged rows], so every source lies ahead
+// of its destination. The roll runs in chunks of one word per thread, each
+// chunk read completely before any of it is written (a barrier between), and
+// a chunk's sources lie beyond every word written before it: in place with no
+// staging buffer. Whole-workgroup path (barriers inside).
+__device__ __forceinline__ void commit_window(const gdn_slot_window &w, const int32_t *slot_ids,
+                                              const int32_t *accept, int R, int32_t *err, int b)
 {
+    const int slot = slot_ids[b], n = accept[b];
+    if (slot == -1)
+        return;
+    if (slot < -1 || slot >= w.num_slots || n < 0 || n > R) {
+        if (threadIdx.x == 0 && err)
+            atomicOr(err, (slot < -1 || slot >= w.num_slots) ? 1 : 2);
+        return;
+    }
+    if (n == 0)
+        return;
+    const int ew = w.entry_bytes / 4;
+    const int words = w.length * ew, shift = n * ew;
+    uint32_t *state = static_cast<uint32_t *>(w.state) + (size_t)slot * words;
+    const uint32_t *rows = static_cast<const uint32_t *>(w.rows) + (size_t)b * R * ew;
+    for (int c = 0; c < words; c += kThreads) {
+        const int u = c + (int)threadIdx.x;
+        uint32_t v = 0;
+        if (u < words) {
+            const int src = u + shift;   // < words + n * ew <= words + R * ew
+            v = src < words ? state[src] : rows[src - words];
+        }
+        __syncthreads();
+        if (u < words)
+            state[u] = v;
+        __syncthreads();
+    }
+}
+
+__device__ __forceinline__ void commit_windows(const WindowSet &ws, const int32_t *slot_ids, const int32_t *accept,
+                                               int B, int R, int32_t *err)
+{
+    const int items = ws.count * B;
+    for (int i = blockIdx.x; i < items; i += gridDim.x)
+        commit_window(ws.w[i / B], slot_ids, accept, R, err, i % B);
+}
+
+__global__ __launch_bounds__(kThreads) void gdn_commit_windows_kernel(const WindowSet ws, const int32_t *slot_ids,
+                                                                      const int32_t *accept, int B, int R,
+                                                                      int32_t *err)
+{
+    commit_windows(ws, slot_ids, accept, B, R, err);
+}
+
+template <int D, typename T, bool SNAP, int NPART>
+__global__ __launch_bounds__(kThreads) void gdn_commit_stack_kernel(const CommitParams<T> p0, const CommitStack st,
+                                                                    const WindowSet ws)
+{
+    if ((int)blockIdx.y == st.layers) {   // the grid row after the layers: the window states
+        commit_windows(ws, p0.slot_ids, p0.accept, p0.B, p0.R, p0.err);
+        return;
+    }
     CommitParams<T> p = p0;
     const StackLayer &l = st.l[blockIdx.y];
     p.ssm = l.ssm;
@@ -2209,34 +2279,36 @@ hipError_t verify_typed(const Checked &c, const gdn_layer_desc *d, const gdn_poo
 
 template <int D, typename T, bool SNAP, int NPART>
 hipError_t launch_commit_parts(const CommitParams<T> &cp, const CommitStack *stack, int layers, int blocks,
-                               hipStream_t st)
+                               hipStream_t st, const WindowSet *ws)
 {
     const int groups = (blocks + kXcds - 1) / kXcds;
-    const dim3 grid(groups * kXcds * NPART, layers);
-    if (stack)
-        hipLaunchKernelGGL((gdn_commit_stack_kernel<D, T, SNAP, NPART>), grid, dim3(kThreads), 0, st, cp, *stack);
-    else
+    const dim3 grid(groups * kXcds * NPART, layers + (ws && ws->count > 0 ? 1 : 0));
+    if (stack) {
+        WindowSet none = {};
+        hipLaunchKernelGGL((gdn_commit_stack_kernel<D, T, SNAP, NPART>), grid, dim3(kThreads), 0, st, cp, *stack,
+                           ws ? *ws : none);
+    } else
         hipLaunchKernelGGL((gdn_commit_kernel<D, T, SNAP, NPART>), grid, dim3(kThreads), 0, st, cp);
     return hipGetLastError();
 }
 
 template <int D, typename T, bool SNAP>
 hipError_t launch_commit(const CommitParams<T> &cp, const CommitStack *stack, int layers, int blocks,
-                         hipStream_t st)
+                         hipStream_t st, const WindowSet *ws)
 {
     // 8 KiB parts at every batch size: 16 KiB parts for 16 requests and 4 KiB
     // parts for one request measured no faster
-    return launch_commit_parts<D, T, SNAP, commit_parts<D>()>(cp, stack, layers, blocks, st);
+    return launch_commit_parts<D, T, SNAP, commit_parts<D>()>(cp, stack, layers, blocks, st, ws);
 }
 
 template <typename T, bool SNAP>
 hipError_t commit_dim(int D, const CommitParams<T> &cp, const CommitStack *stack, int layers, int blocks,
-                      hipStream_t st)
+                      hipStream_t st, const WindowSet *ws)
 {
     switch (D) {
-    case 32: return launch_commit<32, T, SNAP>(cp, stack, layers, blocks, st);
-    case 64: return launch_commit<64, T, SNAP>(cp, stack, layers, blocks, st);
-    case 128: return launch_commit<128, T, SNAP>(cp, stack, layers, blocks, st);
+    case 32: return launch_commit<32, T, SNAP>(cp, stack, layers, blocks, st, ws);
+    case 64: return launch_commit<64, T, SNAP>(cp, stack, layers, blocks, st, ws);
+    case 128: return launch_commit<128, T, SNAP>(cp, stack, layers, blocks, st, ws);
     default: return hipErrorInvalidValue;
     }
 }
@@ -2245,7 +2317,7 @@ template <typename T>
 hipError_t commit_typed(const Checked &c, const gdn_pool *pool, const int32_t *slot_ids,
                         const int32_t *accept, int batch, int rows, bool snapshot,
                         const void *scratch, const ScratchLayout &L, int32_t *err, hipStream_t st,
-                        const CommitStack *stack = nullptr, int layers = 1)
+                        const CommitStack *stack = nullptr, int layers = 1, const WindowSet *ws = nullptr)
 {
     CommitParams<T> cp;
     const char *base = static_cast<const char *>(scratch);
@@ -2266,8 +2338,8 @@ hipError_t commit_typed(const Checked &c, const gdn_pool *pool, const int32_t *s
     cp.R = rows;
     cp.B = batch;
     const int blocks = batch * c.HV;
-    return snapshot ? commit_dim<T, true>(c.D, cp, stack, layers, blocks, st)
-                    : commit_dim<T, false>(c.D, cp, stack, layers, blocks, st);
+    return snapshot ? commit_dim<T, true>(c.D, cp, stack, layers, blocks, st, ws)
+                    : commit_dim<T, false>(c.D, cp, stack, layers, blocks, st, ws);
 }
 
 gdn_status check_common(const gdn_layer_desc *desc, const gdn_pool *pool, int32_t batch,
@@ -2365,8 +2437,33 @@ gdn_status gdn_spec_commit_layers(const gdn_layer_desc *desc, const gdn_pool *po
                                   gdn_commit_mode mode, size_t scratch_bytes, int32_t *err_flag,
                                   void *stream)
 {
-    if (!pools || !scratch || layers < 1 || layers > kMaxLayers)
+    if (layers < 1)
         return GDN_ERR_INVALID_ARG;
+    return gdn_spec_commit_all(desc, pools, scratch, layers, nullptr, 0, slot_ids, accept_len, batch, rows, mode,
+                               scratch_bytes, err_flag, stream);
+}
+
+gdn_status gdn_spec_commit_all(const gdn_layer_desc *desc, const gdn_pool *pools, void *const *scratch,
+                               int32_t layers, const gdn_slot_window *windows, int32_t num_windows,
+                               const int32_t *slot_ids, const int32_t *accept_len, int32_t batch, int32_t rows,
+                               gdn_commit_mode mode, size_t scratch_bytes, int32_t *err_flag, void *stream)
+{
+    if (layers < 0 || layers > kMaxLayers || num_windows < 0 || num_windows > kMaxWindows ||
+        layers + num_windows < 1 || (layers > 0 && (!pools || !scratch)) || (num_windows > 0 && !windows))
+        return GDN_ERR_INVALID_ARG;
+    if (batch < 0 || rows < 1 || rows > kMaxRows)
+        return GDN_ERR_INVALID_ARG;
+    WindowSet ws = {};
+    for (int i = 0; i < num_windows; ++i) {
+        const gdn_slot_window &w = windows[i];
+        if (!w.state || !w.rows || w.num_slots < 1 || w.length < 1 || w.entry_bytes < 4 || w.entry_bytes % 4 ||
+            (reinterpret_cast<uintptr_t>(w.state) & 3) || (reinterpret_cast<uintptr_t>(w.rows) & 3))
+            return GDN_ERR_INVALID_ARG;
+        if ((int64_t)w.length * w.entry_bytes + (int64_t)kMaxRows * w.entry_bytes > 0x7fffffff)
+            return GDN_ERR_UNSUPPORTED;
+        ws.w[i] = w;
+    }
+    ws.count = num_windows;
     Checked c;
     ScratchLayout L;
     for (int l = 0; l < layers; ++l) {
@@ -2378,6 +2475,13 @@ gdn_status gdn_spec_commit_layers(const gdn_layer_desc *desc, const gdn_pool *po
         return GDN_OK;
     if (!slot_ids || !accept_len)
         return GDN_ERR_INVALID_ARG;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (layers == 0) {
+        const int items = num_windows * batch;
+        hipLaunchKernelGGL(gdn_commit_windows_kernel, dim3(items < 4096 ? items : 4096), dim3(kThreads), 0, st, ws,
+                           slot_ids, accept_len, batch, rows, err_flag);
+        return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+    }
     CommitStack stack = {};
     for (int l = 0; l < layers; ++l)
         stack.l[l] = StackLayer{pools[l].ssm, pools[l].conv, static_cast<const char *>(scratch[l]),
@@ -2387,14 +2491,14 @@ gdn_status gdn_spec_commit_layers(const gdn_layer_desc *desc, const gdn_pool *po
     stack.ks = L.ks;
     stack.as = L.as;
     stack.snap = L.snap;
-    hipStream_t st = static_cast<hipStream_t>(stream);
+    stack.layers = layers;
     const bool snap = mode == GDN_COMMIT_SNAPSHOT;
     // layer 0's pointers fill the shared parameters; each grid row swaps in its own
     hipError_t e = desc->dtype == GDN_F32
         ? commit_typed<float>(c, &pools[0], slot_ids, accept_len, batch, rows, snap, scratch[0], L, err_flag, st,
-                              &stack, layers)
+                              &stack, layers, &ws)
         : commit_typed<bf16_t>(c, &pools[0], slot_ids, accept_len, batch, rows, snap, scratch[0], L, err_flag, st,
-                               &stack, layers);
+                               &stack, layers, &ws);
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 

@@ -155,6 +155,36 @@ def test_commit_layers_arguments_are_refused(lib):
     assert _status_commit_layers(lib, d, [p, p], [4096, 4096], 2, batch=0) == bd.GDN_OK
 
 
+def test_commit_all_arguments_are_refused(lib):
+    """gdn_spec_commit_all (GDN layers and window states in one launch) refuses
+    counts out of range, missing or misaligned window pointers and entries
+    that are not a positive multiple of 4 bytes, before any launch."""
+    INV, UNS = bd.GDN_ERR_INVALID_ARG, bd.GDN_ERR_UNSUPPORTED
+    fake = 0x100000   # never dereferenced: every call below is refused first
+
+    def call(windows, nw, layers=0, batch=2, rows=3):
+        arr = (bd.GdnSlotWindow * max(len(windows), 1))(*windows)
+        return lib.gdn_spec_commit_all(None, None, None, layers, arr if windows else None, nw, fake, fake, batch,
+                                       rows, 0, 0, None, None)
+
+    good = bd.GdnSlotWindow(fake, fake, 4, 3, 16)
+    assert call([], 0) == INV                                          # nothing to commit
+    assert call([good] * 17, 17) == INV                                # more than 16 windows
+    assert call([good], 1, layers=-1) == INV
+    assert call([good], 1, layers=65) == INV
+    assert call([good], 1, layers=1) == INV                            # layers without pools
+    assert call([good], 1, rows=0) == INV
+    assert call([good], 1, rows=10) == INV
+    assert call([good], 1, batch=-1) == INV
+    for bad in (bd.GdnSlotWindow(None, fake, 4, 3, 16), bd.GdnSlotWindow(fake, None, 4, 3, 16),
+                bd.GdnSlotWindow(fake + 2, fake, 4, 3, 16), bd.GdnSlotWindow(fake, fake + 1, 4, 3, 16),
+                bd.GdnSlotWindow(fake, fake, 0, 3, 16), bd.GdnSlotWindow(fake, fake, 4, 0, 16),
+                bd.GdnSlotWindow(fake, fake, 4, 3, 6), bd.GdnSlotWindow(fake, fake, 4, 3, 0)):
+        assert call([good, bad], 2) == INV
+    assert call([bd.GdnSlotWindow(fake, fake, 4, 1 << 20, 1 << 12)], 1) == UNS   # words past an int32 index
+    assert call([good], 1, batch=0) == bd.GDN_OK                       # empty batch: nothing launched
+
+
 def test_accept_greedy_arguments_are_refused(lib):
     inv = bd.GDN_ERR_INVALID_ARG
     f = lib.gdn_spec_accept_greedy
