@@ -393,8 +393,8 @@ __device__ __forceinline__ void join_one(float &m, float &s, float y)
     m = mm;
 }
 
-// One unit's loads: every row's 8 logits and (with penalties) the prior counts.
-template <int R, typename L, bool PEN>
+// One unit's loads: every row's 8 logits and (PRIOR) the prior counts.
+template <int R, typename L, bool PRIOR>
 __device__ __forceinline__ void stats_fetch(const SampleParams &p, const L *lg, int b, int v0, Unit<L> (&x)[R],
                                             int (&c)[8])
 {
@@ -402,7 +402,7 @@ __device__ __forceinline__ void stats_fetch(const SampleParams &p, const L *lg, 
 #pragma unroll
     for (int t = 0; t < R; ++t)
         x[t] = load_unit(lg + (size_t)t * V, v0, V, true);
-    if (PEN && p.prior) {
+    if (PRIOR) {
         load_counts(p.prior + (size_t)b * V, v0, V, true, c);
     } else {
 #pragma unroll
@@ -412,11 +412,16 @@ __device__ __forceinline__ void stats_fetch(const SampleParams &p, const L *lg, 
 }
 
 // One unit's arithmetic: every row's running pair joined by the unit, exactly
-// (EXACT) or against the running maximum.
-template <int R, typename L, bool PEN, bool EXACT>
-__device__ __forceinline__ void stats_unit(const Tokens &tk, int v0, float f, float r, float scale2, Unit<L> (&x)[R],
-                                           const int (&c)[8], float (&m)[R], float (&s)[R])
+// (EXACT) or against the running maximum. With RELOAD, each row's registers
+// take the same row of the next unit (at vn) as soon as the row is consumed,
+// and the counts take the next unit's once the penalties are formed: one unit
+// of lookahead in the registers of one.
+template <int R, typename L, bool PEN, bool PRIOR, bool EXACT, bool RELOAD>
+__device__ __forceinline__ void stats_unit(const SampleParams &p, const L *lg, int b, int vn, const Tokens &tk, int v0,
+                                           float f, float r, float scale2, Unit<L> (&x)[R], int (&c)[8],
+                                           float (&m)[R], float (&s)[R])
 {
+    const int V = p.V;
     float ps[8];
     if (PEN) {
 #pragma unroll
@@ -448,6 +453,8 @@ __device__ __forceinline__ void stats_unit(const Tokens &tk, int v0, float f, fl
         for (int k = 0; k < 8; ++k)
             ps[k] = 0.0f;
     }
+    if (PRIOR && RELOAD)
+        load_counts(p.prior + (size_t)b * V, vn, V, true, c);
 #pragma unroll
     for (int t = 0; t < R; ++t) {
         if (EXACT) {
@@ -473,13 +480,15 @@ __device__ __forceinline__ void stats_unit(const Tokens &tk, int v0, float f, fl
                 join_unit(m[t], s[t], y);
             }
         }
+        if (RELOAD)
+            x[t] = load_unit(lg + (size_t)t * V, vn, V, true);
     }
 }
 
 // A unit that is not whole, or whose rows are not 16-byte aligned: every
 // entry loaded on its own from a clamped index (entries past the vocabulary
 // read as -inf logits and zero counts), all rows at once.
-template <int R, typename L, bool PEN>
+template <int R, typename L, bool PRIOR>
 __device__ __forceinline__ void stats_fetch_general(const SampleParams &p, const L *lg, int b, int v0, Unit<L> (&x)[R],
                                                     int (&c)[8])
 {
@@ -487,7 +496,7 @@ __device__ __forceinline__ void stats_fetch_general(const SampleParams &p, const
 #pragma unroll
     for (int t = 0; t < R; ++t)
         x[t] = load_unit(lg + (size_t)t * V, v0, V, false);
-    if (PEN && p.prior) {
+    if (PRIOR) {
         load_counts(p.prior + (size_t)b * V, v0, V, false, c);
     } else {
 #pragma unroll
@@ -523,7 +532,7 @@ template <int R> __device__ __forceinline__ void wave_ms_rows(float (&m)[R], flo
             s[t] += __shfl_xor(s[t], off, 64);
 }
 
-template <int R, typename L, bool PEN>
+template <int R, typename L, bool PEN, bool PRIOR>
 __global__ __launch_bounds__(kSampleThreads) void gdn_sample_stats_kernel(const SampleParams p, int vec_ok)
 {
     __shared__ float2 sh_ms[R][kSampleThreads / 64];
@@ -533,21 +542,19 @@ __global__ __launch_bounds__(kSampleThreads) void gdn_sample_stats_kernel(const 
     const L *lg = static_cast<const L *>(p.logits) + (size_t)b * R * V;
     const int base = split * U * kColumn;
     const int cols = min(U, (V - base + kColumn - 1) / kColumn);   // columns inside the vocabulary
-    const bool vec = (vec_ok & kVecLogits) && (!PEN || !p.prior || (vec_ok & kVecPrior));
+    const bool vec = (vec_ok & kVecLogits) && (!PRIOR || (vec_ok & kVecPrior));
     const int whole = vec ? min(cols, (V - base) / kColumn) : 0;   // columns of whole units only
 
     if (split == 0 && tid == 0) {   // the draw pass of this call gathers its result here
         p.best[b] = 0ull;
         p.done[b] = 0;
     }
-    // the first two columns' loads go out before the per-request values are
-    // read (rows of padding requests are still inside the logits)
-    Unit<L> x[R], xn[R];
-    int c[8], cn[8];
-    if (whole > 0) {
-        stats_fetch<R, L, PEN>(p, lg, b, base + tid * 8, x, c);
-        stats_fetch<R, L, PEN>(p, lg, b, base + (min(1, whole - 1) * kSampleThreads + tid) * 8, xn, cn);
-    }
+    // the first column's loads go out before the per-request values are read
+    // (rows of padding requests are still inside the logits)
+    Unit<L> x[R];
+    int c[8];
+    if (whole > 0)
+        stats_fetch<R, L, PRIOR>(p, lg, b, base + tid * 8, x, c);
     if (padding(p, b))
         return;
     const float scale2 = temperature_scale(p, b);
@@ -564,29 +571,21 @@ __global__ __launch_bounds__(kSampleThreads) void gdn_sample_stats_kernel(const 
         m[t] = kNegInf;
         s[t] = 0.0f;
     }
-    if (whole > 0) {
-        stats_unit<R, L, PEN, true>(tk, base + tid * 8, f, r, scale2, x, c, m, s);
+    const auto col = [&](int u) { return base + (u * kSampleThreads + tid) * 8; };
+    if (whole > 1) {
+        stats_unit<R, L, PEN, PRIOR, true, true>(p, lg, b, col(1), tk, col(0), f, r, scale2, x, c, m, s);
 #pragma unroll 1
-        for (int u = 1; u + 1 < whole; ++u) {
-#pragma unroll
-            for (int t = 0; t < R; ++t)
-                x[t] = xn[t];
-#pragma unroll
-            for (int k = 0; k < 8; ++k)
-                c[k] = cn[k];
-            stats_fetch<R, L, PEN>(p, lg, b, base + ((u + 1) * kSampleThreads + tid) * 8, xn, cn);
-            stats_unit<R, L, PEN, false>(tk, base + (u * kSampleThreads + tid) * 8, f, r, scale2, x, c, m, s);
-        }
-        if (whole > 1)
-            stats_unit<R, L, PEN, false>(tk, base + ((whole - 1) * kSampleThreads + tid) * 8, f, r, scale2, xn, cn,
-                                         m, s);
+        for (int u = 1; u + 1 < whole; ++u)
+            stats_unit<R, L, PEN, PRIOR, false, true>(p, lg, b, col(u + 1), tk, col(u), f, r, scale2, x, c, m, s);
+        stats_unit<R, L, PEN, PRIOR, false, false>(p, lg, b, 0, tk, col(whole - 1), f, r, scale2, x, c, m, s);
+    } else if (whole == 1) {
+        stats_unit<R, L, PEN, PRIOR, true, false>(p, lg, b, 0, tk, col(0), f, r, scale2, x, c, m, s);
     }
     // the ragged last column (or every column of unaligned rows)
 #pragma unroll 1
     for (int u = whole; u < cols; ++u) {
-        const int v0 = base + (u * kSampleThreads + tid) * 8;
-        stats_fetch_general<R, L, PEN>(p, lg, b, v0, x, c);
-        stats_unit<R, L, PEN, true>(tk, v0, f, r, scale2, x, c, m, s);
+        stats_fetch_general<R, L, PRIOR>(p, lg, b, col(u), x, c);
+        stats_unit<R, L, PEN, PRIOR, true, false>(p, lg, b, 0, tk, col(u), f, r, scale2, x, c, m, s);
     }
     wave_ms_rows<R>(m, s);
     const int wave = tid >> 6, lane = tid & 63;
@@ -631,16 +630,16 @@ template <typename L> struct DrawUnit {
 };
 
 // One unit's loads: 16-byte loads (VEC: a whole unit of aligned rows) or
-// entry by entry from clamped indices.
-template <typename L, bool VEC>
-__device__ __forceinline__ void draw_fetch(const SampleParams &p, const DrawRow &w, bool pen, int b, int v0,
-                                           DrawUnit<L> &u)
+// entry by entry from clamped indices. Q: the row's draft probabilities are
+// read (a drafter with probabilities after a rejection); PRIOR: the prior counts.
+template <typename L, bool VEC, bool Q, bool PRIOR>
+__device__ __forceinline__ void draw_fetch(const SampleParams &p, const DrawRow &w, int b, int v0, DrawUnit<L> &u)
 {
     const int V = p.V;
     u.x = load_unit(static_cast<const L *>(w.lg), v0, V, VEC);
-    if (w.q)
+    if (Q)
         u.q = load_unit(w.q, v0, V, VEC, 0.0f);
-    if (pen && p.prior) {
+    if (PRIOR) {
         load_counts(p.prior + (size_t)b * V, v0, V, VEC, u.c);
     } else {
 #pragma unroll
@@ -651,14 +650,15 @@ __device__ __forceinline__ void draw_fetch(const SampleParams &p, const DrawRow 
 
 // One unit's keys. A thread visits its entries in increasing index order, so
 // among equal keys the first one seen (the smaller index) is kept by a plain
-// greater-than; entries past the vocabulary have -inf keys.
-template <typename L>
-__device__ __forceinline__ void draw_unit(const SampleParams &p, const DrawRow &w, const Tokens &tk, bool pen, int b,
-                                          int v0, float f2, float r2, float scale2, DrawUnit<L> &u, float &bk, int &bi)
+// greater-than; entries past the vocabulary have -inf keys. PEN: the row has
+// penalties (its counts are the prior counts, when given, plus its tokens).
+template <typename L, bool Q, bool PEN>
+__device__ __forceinline__ void draw_unit(const SampleParams &p, const DrawRow &w, const Tokens &tk, int b, int v0,
+                                          float f2, float r2, float scale2, DrawUnit<L> &u, float &bk, int &bi)
 {
     const int t = w.t;
     float ps[8];
-    if (pen) {
+    if (PEN) {
         if (unit_holds_token(tk, t, v0)) {
 #pragma unroll
             for (int j = 0; j < kMaxSampleRows; ++j)
@@ -669,19 +669,15 @@ __device__ __forceinline__ void draw_unit(const SampleParams &p, const DrawRow &
 #pragma unroll
         for (int k = 0; k < 8; ++k)
             ps[k] = __builtin_fmaf(f2, (float)u.c[k], u.c[k] > 0 ? r2 : 0.0f);
-    } else {
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-            ps[k] = 0.0f;
     }
     const U4 g0 = philox(U4{(uint32_t)(v0 >> 2), (uint32_t)t, (uint32_t)b, 0u}, p.k0, p.k1);
     const U4 g1 = philox(U4{(uint32_t)(v0 >> 2) + 1u, (uint32_t)t, (uint32_t)b, 0u}, p.k0, p.k1);
     const uint32_t gw[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-        const float y = __builtin_fmaf(u.x.at(k), scale2, -ps[k]);
+        const float y = PEN ? __builtin_fmaf(u.x.at(k), scale2, -ps[k]) : u.x.at(k) * scale2;
         float key;
-        if (w.q) {
+        if (Q) {
             const float res = fast_exp2(y - w.mm) * w.inv - u.q.at(k);
             key = res > 0.0f ? fast_log2(res) + gumbel2(gw[k]) : kNegInf;
         } else {
@@ -691,6 +687,35 @@ __device__ __forceinline__ void draw_unit(const SampleParams &p, const DrawRow &
             bk = key;
             bi = v0 + k;
         }
+    }
+}
+
+// The workgroup's columns of the draw's row: whole columns in order, the
+// next one's loads out before the current one's arithmetic; then the ragged
+// last column entry by entry.
+template <typename L, bool Q, bool PEN, bool PRIOR>
+__device__ __forceinline__ void draw_columns(const SampleParams &p, const DrawRow &w, const Tokens &tk, int b, int base,
+                                             int cols, int whole, float f2, float r2, float scale2, float &bk, int &bi)
+{
+    const int V = p.V, tid = threadIdx.x;
+    DrawUnit<L> cur, nxt;
+    if (whole > 0) {
+        draw_fetch<L, true, Q, PRIOR>(p, w, b, base + tid * 8, cur);
+#pragma unroll 1
+        for (int u = 0; u + 1 < whole; ++u) {
+            draw_fetch<L, true, Q, PRIOR>(p, w, b, base + ((u + 1) * kSampleThreads + tid) * 8, nxt);
+            draw_unit<L, Q, PEN>(p, w, tk, b, base + (u * kSampleThreads + tid) * 8, f2, r2, scale2, cur, bk, bi);
+            cur = nxt;
+        }
+        draw_unit<L, Q, PEN>(p, w, tk, b, base + ((whole - 1) * kSampleThreads + tid) * 8, f2, r2, scale2, cur, bk,
+                             bi);
+    }
+#pragma unroll 1
+    for (int u = whole; u < cols; ++u) {
+        const int v0 = base + (u * kSampleThreads + tid) * 8;
+        draw_fetch<L, false, Q, PRIOR>(p, w, b, min(v0, V - 1), cur);
+        if (v0 < V)
+            draw_unit<L, Q, PEN>(p, w, tk, b, v0, f2, r2, scale2, cur, bk, bi);
     }
 }
 
@@ -739,27 +764,52 @@ __global__ __launch_bounds__(kSampleThreads) void gdn_sample_draw_kernel(const S
     const int wave = tid >> 6, lane = tid & 63;
     constexpr int RW = (R + kSampleThreads / 64 - 1) / (kSampleThreads / 64);   // rows per wave
     constexpr int PL = kMaxSplits / 64;                                          // partials per lane
-    float2 part[RW][PL];
+    // one partial per lane when the splits fit a wave (the usual case), else
+    // up to PL per lane; the branch is uniform and every load in it is
+    // unconditional
+    float mrow[RW], srow[RW];
+    if (S <= 64) {
+        float2 part[RW];
 #pragma unroll
-    for (int j = 0; j < RW; ++j) {
-        const int t = wave + j * (kSampleThreads / 64);
+        for (int j = 0; j < RW; ++j) {
+            const int t = wave + j * (kSampleThreads / 64);
+            const float2 v = p.stats[((size_t)b * R + min(t, R - 1)) * S + min(lane, S - 1)];
+            part[j] = (t < R && lane < S) ? v : float2{kNegInf, 0.0f};
+        }
 #pragma unroll
-        for (int i = 0; i < PL; ++i) {
-            const int sp = lane + 64 * i;
-            const float2 v = p.stats[((size_t)b * R + min(t, R - 1)) * S + min(sp, S - 1)];
-            part[j][i] = (t < R && sp < S) ? v : float2{kNegInf, 0.0f};
+        for (int j = 0; j < RW; ++j) {
+            mrow[j] = part[j].x;
+            srow[j] = part[j].y;
+        }
+    } else {
+        float2 part[RW][PL];
+#pragma unroll
+        for (int j = 0; j < RW; ++j) {
+            const int t = wave + j * (kSampleThreads / 64);
+#pragma unroll
+            for (int i = 0; i < PL; ++i) {
+                const int sp = lane + 64 * i;
+                const float2 v = p.stats[((size_t)b * R + min(t, R - 1)) * S + min(sp, S - 1)];
+                part[j][i] = (t < R && sp < S) ? v : float2{kNegInf, 0.0f};
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < RW; ++j) {
+            mrow[j] = kNegInf;
+            srow[j] = 0.0f;
+#pragma unroll
+            for (int i = 0; i < PL; ++i)
+                combine_ms(mrow[j], srow[j], part[j][i].x, part[j][i].y);
         }
     }
+    wave_ms_rows<RW>(mrow, srow);
+    if (lane == 0) {
 #pragma unroll
-    for (int j = 0; j < RW; ++j) {
-        const int t = wave + j * (kSampleThreads / 64);
-        float mm = kNegInf, ss = 0.0f;
-#pragma unroll
-        for (int i = 0; i < PL; ++i)
-            combine_ms(mm, ss, part[j][i].x, part[j][i].y);
-        wave_ms(mm, ss);
-        if (lane == 0 && t < R)
-            row_ms[t] = float2{mm, ss};
+        for (int j = 0; j < RW; ++j) {
+            const int t = wave + j * (kSampleThreads / 64);
+            if (t < R)
+                row_ms[t] = float2{mrow[j], srow[j]};
+        }
     }
     __syncthreads();
     if (tid < R) {
@@ -795,29 +845,26 @@ __global__ __launch_bounds__(kSampleThreads) void gdn_sample_draw_kernel(const S
     w.inv = 1.0f / row_ms[w.t].y;
     float bk = kNegInf;
     int bi = 0x7fffffff;
-    // whole columns in order, the next one's loads out before the current
-    // one's arithmetic; then the ragged last column entry by entry
     const bool vec_all = (vec_ok & kVecLogits) && (!pen || !p.prior || (vec_ok & kVecPrior)) &&
                          (!w.q || (vec_ok & kVecProbs));
     const int whole = vec_all ? min(cols, (V - base) / kColumn) : 0;
-    DrawUnit<L> cur, nxt;
-    if (whole > 0) {
-        draw_fetch<L, true>(p, w, pen, b, base + tid * 8, cur);
-#pragma unroll 1
-        for (int u = 0; u + 1 < whole; ++u) {
-            draw_fetch<L, true>(p, w, pen, b, base + ((u + 1) * kSampleThreads + tid) * 8, nxt);
-            draw_unit<L>(p, w, tk, pen, b, base + (u * kSampleThreads + tid) * 8, f2, r2, scale2, cur, bk, bi);
-            cur = nxt;
-        }
-        draw_unit<L>(p, w, tk, pen, b, base + ((whole - 1) * kSampleThreads + tid) * 8, f2, r2, scale2, cur, bk,
-                     bi);
-    }
-#pragma unroll 1
-    for (int u = whole; u < cols; ++u) {
-        const int v0 = base + (u * kSampleThreads + tid) * 8;
-        draw_fetch<L, false>(p, w, pen, b, min(v0, V - 1), cur);
-        if (v0 < V)
-            draw_unit<L>(p, w, tk, pen, b, v0, f2, r2, scale2, cur, bk, bi);
+    // one path per workgroup (uniform branches): drafter probabilities or
+    // not, penalties or not
+    const int pm = !pen ? 0 : p.prior ? 2 : 1;   // penalties: none, tokens only, prior counts and tokens
+    if (w.q) {
+        if (pm == 2)
+            draw_columns<L, true, true, true>(p, w, tk, b, base, cols, whole, f2, r2, scale2, bk, bi);
+        else if (pm == 1)
+            draw_columns<L, true, true, false>(p, w, tk, b, base, cols, whole, f2, r2, scale2, bk, bi);
+        else
+            draw_columns<L, true, false, false>(p, w, tk, b, base, cols, whole, f2, r2, scale2, bk, bi);
+    } else {
+        if (pm == 2)
+            draw_columns<L, false, true, true>(p, w, tk, b, base, cols, whole, f2, r2, scale2, bk, bi);
+        else if (pm == 1)
+            draw_columns<L, false, true, false>(p, w, tk, b, base, cols, whole, f2, r2, scale2, bk, bi);
+        else
+            draw_columns<L, false, false, false>(p, w, tk, b, base, cols, whole, f2, r2, scale2, bk, bi);
     }
     group_best(bk, bi, sh_best);
 
@@ -900,20 +947,22 @@ template <int R, typename L> void launch_sample_kernels(SampleParams p, hipStrea
                     (row_aligned(p.dprob, (size_t)p.V * sizeof(float)) ? kVecProbs : 0);
     const int cus = compute_units(st);
     const bool pen = p.pres || p.freq;
-    static const int occ_pen = groups_per_cu(gdn_sample_stats_kernel<R, L, true>);
-    static const int occ_plain = groups_per_cu(gdn_sample_stats_kernel<R, L, false>);
+    static const int occ_prior = groups_per_cu(gdn_sample_stats_kernel<R, L, true, true>);
+    static const int occ_pen = groups_per_cu(gdn_sample_stats_kernel<R, L, true, false>);
+    static const int occ_plain = groups_per_cu(gdn_sample_stats_kernel<R, L, false, false>);
     static const int occ_draw = groups_per_cu(gdn_sample_draw_kernel<R, L>);
-    p.U = columns_per_split(p.B, p.V, cus * (pen ? occ_pen : occ_plain));
+    p.U = columns_per_split(p.B, p.V, cus * (!pen ? occ_plain : p.prior ? occ_prior : occ_pen));
     p.S = (p.V + p.U * kColumn - 1) / (p.U * kColumn);
     p.Ud = columns_per_split(p.B, p.V, cus * occ_draw);
     p.Sd = (p.V + p.Ud * kColumn - 1) / (p.Ud * kColumn);
     const dim3 block(kSampleThreads);
-    if (pen)
-        hipLaunchKernelGGL((gdn_sample_stats_kernel<R, L, true>), dim3((unsigned)p.S, (unsigned)p.B), block, 0, st, p,
-                           vec);
+    const dim3 grid((unsigned)p.S, (unsigned)p.B);
+    if (pen && p.prior)
+        hipLaunchKernelGGL((gdn_sample_stats_kernel<R, L, true, true>), grid, block, 0, st, p, vec);
+    else if (pen)
+        hipLaunchKernelGGL((gdn_sample_stats_kernel<R, L, true, false>), grid, block, 0, st, p, vec);
     else
-        hipLaunchKernelGGL((gdn_sample_stats_kernel<R, L, false>), dim3((unsigned)p.S, (unsigned)p.B), block, 0, st,
-                           p, vec);
+        hipLaunchKernelGGL((gdn_sample_stats_kernel<R, L, false, false>), grid, block, 0, st, p, vec);
     hipLaunchKernelGGL((gdn_sample_draw_kernel<R, L>), dim3((unsigned)p.Sd, (unsigned)p.B), block, 0, st, p, vec);
 }
 
