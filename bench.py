@@ -136,6 +136,19 @@ def algorithmic_bytes(w, accept, mode="replay"):
     return verify, commit
 
 
+def fused_bytes(w, accept):
+    """Bytes per commit-verify launch: one step's verify and the previous
+    step's commit of the same requests, less what the two share. The state
+    and the conv history are read once for both, so a request with n > 0
+    pending rows moves its state once in each direction (replay mode)."""
+    vbytes, cbytes = algorithmic_bytes(w, accept, "replay")
+    s = w.shape
+    state = s.num_v_heads * s.d_k * s.d_v * 4
+    hist = (s.conv_width - 1) * s.conv_channels * s.elem_bytes
+    shared = sum(state + hist for n in accept if n > 0)
+    return vbytes + cbytes - shared
+
+
 # Worker threads for the oracle leg: a host serving one GPU gives this process
 # a share of 16 cores, whatever the affinity mask shows, so the oracle uses at
 # most 16 threads; the affinity count is reported beside it.
@@ -535,11 +548,14 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="time replays of a captured HIP graph of each group of steps instead of "
                          "eager launches (steps and warmup must be multiples of --copies)")
-    ap.add_argument("--schedule", default="serial", choices=["serial", "overlap"],
+    ap.add_argument("--schedule", default="serial", choices=["serial", "overlap", "fused"],
                     help="serial: every launch on one stream; overlap: a group's commits on a second "
                          "stream, each copy's next verify waiting for its own commit, so one group's "
                          "commits run beside the next group's verifies (pays in long runs of large "
-                         "replay batches; the pipeline's fill and drain cost more over a few steps)")
+                         "replay batches; the pipeline's fill and drain cost more over a few steps); "
+                         "fused: each step is one gdn_spec_commit_verify launch that commits the copy's "
+                         "previous step into the state on its way into this step's verify (replay; "
+                         "every step still commits one batch and verifies one)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 256 MiB device copy (the reference dispatch for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -579,8 +595,11 @@ def main():
                             c.accept, w.rows, c.mode, c.scratch, c.out, c.err, stream)
                 for c in cases]
     overlap = args.schedule == "overlap"
+    fused = args.schedule == "fused"
     if overlap and args.graph:
         raise SystemExit("--graph captures one stream: use --schedule serial")
+    if fused and (args.graph or args.mode != "replay"):
+        raise SystemExit("--schedule fused: replay mode, eager launches")
     vstream, cstream = (torch.cuda.Stream(), torch.cuda.Stream()) if overlap else (stream, stream)
     pv = [bd.Prepared(c.desc, c.ssm, c.conv, c.conv_w, c.x, c.alpha, c.beta, c.slot_ids, c.accept, w.rows,
                       c.mode, c.scratch, c.out, c.err, vstream) for c in cases] if overlap else prepared
@@ -598,7 +617,25 @@ def main():
             accepts[k] = bd.PreparedAccept(dt, tt, c.slot_ids, w.rows, c.accept, nxt, cstream)
     accepts_serial = [None if a is None or not overlap else
                       bd.PreparedAccept(*a._keep[:3], w.rows, *a._keep[3:], stream) for a in accepts]
+    # fused schedule: two scratch buffers per copy, alternating between the
+    # step that is verified and the step whose commit is pending; each
+    # copy's first verify (untimed, before the warmup) leaves a pending commit
+    fsteps = []
+    if fused:
+        ident = torch.arange(w.batch, dtype=torch.int32, device="cuda")
+        for c, p in zip(cases, prepared):
+            alt = torch.empty_like(c.scratch)
+            pair = [bd.PreparedCommitVerify(c.desc, c.ssm, c.conv, c.conv_w, c.x, c.alpha, c.beta, c.slot_ids,
+                                            w.rows, dst, ident, src, c.slot_ids, c.accept, c.out, c.err, stream)
+                    for dst, src in ((alt, c.scratch), (c.scratch, alt))]
+            fsteps.append([pair, 0])
+            p.verify()
     torch.cuda.synchronize()
+
+    def fused_step(k):
+        pair, i = fsteps[k]
+        pair[i]()
+        fsteps[k][1] = 1 - i
 
     graph = None
     if args.graph:
@@ -668,14 +705,18 @@ def main():
                     ev.append(e)
             mark()
             for k in group:
-                prepared[k % M].verify()
+                if fused:
+                    fused_step(k % M)
+                else:
+                    prepared[k % M].verify()
             mark()
             for k in group:
                 if accepts[k % M] is not None:
                     (accepts_serial[k % M] or accepts[k % M])()
             mark()
             for k in group:
-                prepared[k % M].commit()
+                if not fused:
+                    prepared[k % M].commit()
             mark()
             if marks is not None:
                 marks.append((len(group), ev))
@@ -709,16 +750,23 @@ def main():
     vbytes, cbytes = algorithmic_bytes(w, base.accept_np, args.mode)
     rows_per_step = w.batch * w.rows
     value = rows_per_step * args.steps / wall
-    gbps = (vbytes + cbytes) * args.steps / wall / 1e9
-    kernels = {
-        "verify": {"avg_us": float(tv.mean() * 1e6), "bytes": vbytes,
-                   "gbps": float(vbytes / tv.mean() / 1e9)},
-        "commit": {"avg_us": float(tc.mean() * 1e6), "bytes": cbytes,
-                   "gbps": float(cbytes / tc.mean() / 1e9)},
-    }
+    if fused:
+        fbytes = fused_bytes(w, base.accept_np)
+        gbps = fbytes * args.steps / wall / 1e9
+        kernels = {"commit_verify": {"avg_us": float(tv.mean() * 1e6), "bytes": fbytes,
+                                     "gbps": float(fbytes / tv.mean() / 1e9)}}
+        dom = "commit_verify"
+    else:
+        gbps = (vbytes + cbytes) * args.steps / wall / 1e9
+        kernels = {
+            "verify": {"avg_us": float(tv.mean() * 1e6), "bytes": vbytes,
+                       "gbps": float(vbytes / tv.mean() / 1e9)},
+            "commit": {"avg_us": float(tc.mean() * 1e6), "bytes": cbytes,
+                       "gbps": float(cbytes / tc.mean() / 1e9)},
+        }
+        dom = "verify" if tv.mean() >= tc.mean() else "commit"
     if args.accept == "greedy":
         kernels["accept_greedy"] = {"avg_us": float(ta * 1e6)}
-    dom = "verify" if tv.mean() >= tc.mean() else "commit"
     ach = kernels[dom]["gbps"]
     line = {
         "metric": METRIC,
@@ -739,7 +787,7 @@ def main():
                    "storage": w.shape.dtype, "state": "f32", "pool_slots": w.num_slots,
                    "commit_mode": args.mode, "accept_mean": float(np.mean(base.accept_np)),
                    "rotating_copies": M, "launch": "hip graph" if args.graph else "eager",
-                   "schedule": "overlap" if overlap else "serial", "accept": args.accept},
+                   "schedule": args.schedule, "accept": args.accept},
         "gbps": gbps,
         "hbm_frac": gbps / HBM_PEAK_GBPS,
         "kernels": kernels,

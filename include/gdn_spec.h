@@ -145,6 +145,49 @@ gdn_status gdn_spec_commit(const gdn_layer_desc *desc, const gdn_pool *pool,
                            size_t scratch_bytes, int32_t *err_flag, void *stream);
 
 /*
+ * Commit the previous step's accepted rows and verify this step's rows, in one
+ * launch (replay mode). A layer's commit of step s and its verify of step s+1
+ * are adjacent in a serving loop: the verify must read the committed state,
+ * and nothing else reads that layer's state in between (FreeToken issue
+ * #828, Design: the verify only reads the state and the commit replays the
+ * accepted rows; lmdeploy PR #5006, Verification path: a gated-delta-rule
+ * verify-and-commit kernel mode). Here each state chunk takes the pending
+ * rows' update on its way into the verify and goes back to the pool from
+ * there, so the state is read once per step instead of twice. The pool and
+ * the outputs are bit for bit those of gdn_spec_commit (previous step)
+ * followed by gdn_spec_verify (this step) on the one-round kernel.
+ *
+ * Arguments as for gdn_spec_verify (batch, rows, slot_ids, x, alpha, beta,
+ * scratch, out), plus the previous step's verify:
+ *  src_row        int32 [batch]: the previous batch row whose accepted rows
+ *                 are still to be committed to slot_ids[b], or -1 (nothing
+ *                 pending: the state is read as it is). Ignored for padding
+ *                 requests. Distinct within one call.
+ *  prev_scratch   the scratch of the previous step's verify (same desc and
+ *                 rows, batch prev_batch), prev_scratch_bytes long; must not
+ *                 overlap `scratch`. Each buffer holds at least its batch's
+ *                 gdn_spec_scratch_bytes(..., GDN_COMMIT_REPLAY).
+ *  prev_slot_ids  int32 [prev_batch], the previous step's slot table;
+ *                 prev_slot_ids[src_row[b]] must equal slot_ids[b].
+ *  prev_accept_len int32 [prev_batch], its accept lengths (0..rows).
+ *  err_flag       bit 0: slot id outside [-1, num_slots); bit 1: accept
+ *                 length outside [0, rows]; bit 2: src_row[b] outside
+ *                 [-1, prev_batch) or naming another slot. Such a request is
+ *                 skipped: no commit, zero outputs.
+ * Rows of the previous batch that no src_row names are not committed here
+ * (gdn_spec_commit does that). Requires bf16 storage, d_k = d_v = 128 and
+ * HV = 2*HK (GDN_ERR_UNSUPPORTED otherwise): every workgroup then owns the
+ * conv channels it commits.
+ */
+gdn_status gdn_spec_commit_verify(const gdn_layer_desc *desc, const gdn_pool *pool, const void *conv_w,
+                                  const void *x, const void *alpha, const void *beta,
+                                  const int32_t *slot_ids, int32_t batch, int32_t rows, void *scratch,
+                                  size_t scratch_bytes, const int32_t *src_row, const void *prev_scratch,
+                                  size_t prev_scratch_bytes, const int32_t *prev_slot_ids,
+                                  const int32_t *prev_accept_len, int32_t prev_batch, void *out, int32_t *err_flag,
+                                  void *stream);
+
+/*
  * Commit every GDN layer of a hybrid stack in one launch. Layer l's pool is
  * pools[l] and scratch[l] is the scratch its last gdn_spec_verify used; all
  * layers were verified with the same desc, batch, rows, mode and slot_ids,

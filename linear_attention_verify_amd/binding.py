@@ -28,7 +28,8 @@ GDN_ACT_NONE = 1
 
 MODES = {"replay": GDN_COMMIT_REPLAY, "snapshot": GDN_COMMIT_SNAPSHOT}
 
-EXPORTS = ("gdn_spec_scratch_bytes", "gdn_spec_verify", "gdn_spec_commit", "gdn_spec_commit_layers",
+EXPORTS = ("gdn_spec_scratch_bytes", "gdn_spec_verify", "gdn_spec_commit", "gdn_spec_commit_verify",
+           "gdn_spec_commit_layers",
            "gdn_spec_commit_all", "gdn_spec_accept_greedy", "gdn_strerror", "gdn_spec_attn_scratch_bytes", "gdn_spec_attn_verify",
            "gdn_spec_attn_verify_static", "gdn_spec_sample_scratch_bytes", "gdn_spec_accept_sample")
 
@@ -112,6 +113,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                                     vp, sz, vp, vp, vp]
     lib.gdn_spec_commit.restype = ctypes.c_int
     lib.gdn_spec_commit.argtypes = [pdesc, ppool, vp, vp, i32, i32, ctypes.c_int, vp, sz, vp, vp]
+    lib.gdn_spec_commit_verify.restype = ctypes.c_int
+    lib.gdn_spec_commit_verify.argtypes = [pdesc, ppool, vp, vp, vp, vp, vp, i32, i32, vp, sz, vp, vp, sz, vp, vp, i32,
+                                           vp, vp, vp]
     lib.gdn_spec_commit_layers.restype = ctypes.c_int
     lib.gdn_spec_commit_layers.argtypes = [pdesc, ppool, ctypes.POINTER(vp), i32, vp, vp, i32, i32,
                                            ctypes.c_int, sz, vp, vp]
@@ -341,6 +345,61 @@ def gdn_spec_commit(desc, ssm, conv, slot_ids, accept_len, rows, mode, scratch, 
         _mode(mode), _ptr(scratch), _nbytes(scratch) if B else 0, _ptr(err_flag), _stream(stream))
     if st != GDN_OK:
         raise GdnError(st, "gdn_spec_commit")
+
+
+def _check_commit_verify_args(desc, ssm, conv, conv_w, x, alpha, beta, slot_ids, rows, scratch, src_row,
+                              prev_scratch, prev_slot_ids, prev_accept_len, out, err_flag):
+    """A commit-verify call: this step's verify tensors, the source-row table
+    and the previous step's slot table, accept lengths and scratch. Returns
+    (batch, previous batch)."""
+    torch = _torch()
+    B = _check_verify_args(desc, ssm, conv, conv_w, x, alpha, beta, slot_ids, rows, scratch, out, err_flag)
+    dev = ssm.device
+    Bp = 0 if prev_slot_ids is None else _check_slot_table(prev_slot_ids, dev)
+    if B > 0:
+        _check(src_row, "src_row", torch.int32, (B,), device=dev)
+    if Bp > 0:
+        _check(prev_accept_len, "prev_accept_len", torch.int32, (Bp,), device=dev)
+        _check(prev_scratch, "prev_scratch", torch.uint8, device=dev)
+    return B, Bp
+
+
+class PreparedCommitVerify:
+    """gdn_spec_commit_verify on fixed device tensors: commits the previous
+    step's accepted rows (prev_slot_ids, prev_accept_len, prev_scratch) into
+    the slots src_row maps them to, then verifies this step's rows, in one
+    launch. Checked and turned into ctypes arguments once."""
+
+    def __init__(self, desc, ssm, conv, conv_w, x, alpha, beta, slot_ids, rows, scratch, src_row, prev_scratch,
+                 prev_slot_ids, prev_accept_len, out, err_flag=None, stream=None, host_slot_ids=None):
+        B, Bp = _check_commit_verify_args(desc, ssm, conv, conv_w, x, alpha, beta, slot_ids, rows, scratch, src_row,
+                                          prev_scratch, prev_slot_ids, prev_accept_len, out, err_flag)
+        if host_slot_ids is not None:
+            check_slot_ids_host(host_slot_ids, int(ssm.shape[0]))
+        self.lib = load_library()
+        self._keep = (ssm, conv, conv_w, x, alpha, beta, slot_ids, scratch, src_row, prev_scratch, prev_slot_ids,
+                      prev_accept_len, out, err_flag)
+        self.desc = desc
+        self.pool = make_pool(ssm, conv)
+        self.args = (ctypes.byref(self.desc), ctypes.byref(self.pool), _ptr(conv_w), _ptr(x), _ptr(alpha),
+                     _ptr(beta), _ptr(slot_ids), B, rows, _ptr(scratch), _nbytes(scratch) if B else 0, _ptr(src_row),
+                     _ptr(prev_scratch) if Bp else None, _nbytes(prev_scratch) if Bp else 0,
+                     _ptr(prev_slot_ids) if Bp else None, _ptr(prev_accept_len) if Bp else None, Bp, _ptr(out),
+                     _ptr(err_flag), _stream(stream))
+
+    def __call__(self):
+        st = self.lib.gdn_spec_commit_verify(*self.args)
+        if st != GDN_OK:
+            raise GdnError(st, "gdn_spec_commit_verify")
+
+
+def gdn_spec_commit_verify(desc, ssm, conv, conv_w, x, alpha, beta, slot_ids, rows, scratch, src_row, prev_scratch,
+                           prev_slot_ids, prev_accept_len, out, err_flag=None, stream=None, host_slot_ids=None):
+    """Commit the previous step's accepted rows and verify this step's rows in
+    one launch (replay mode); src_row[b] names the previous batch row pending
+    on slot_ids[b], or -1."""
+    PreparedCommitVerify(desc, ssm, conv, conv_w, x, alpha, beta, slot_ids, rows, scratch, src_row, prev_scratch,
+                         prev_slot_ids, prev_accept_len, out, err_flag, stream, host_slot_ids)()
 
 
 class PreparedCommitLayers:

@@ -101,6 +101,22 @@ __device__ __forceinline__ f32x4 buf_stream_load_f4(__amdgpu_buffer_rsrc_t r, ui
     return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, kStreamPolicy));
 }
 
+__device__ __forceinline__ void buf_stream_store_f4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, f32x4 v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) uint32_t, v), r,
+                                           (int)voff, (int)soff, kStreamPolicy);
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane i's bytes land
+// at lds + 16 i (lds uniform across the wave). The host pass never sees the
+// builtin: parsed there, it drops the host stub of every kernel that uses it.
+__device__ __forceinline__ void lds_dma16(const float *src, float *lds)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+#endif
+}
+
 __device__ __forceinline__ float4 stream_load(const float *ptr)
 {
     const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(ptr));
@@ -252,6 +268,19 @@ template <typename T> struct VerifyParams {
     int HK, HV, C, P;
     int act;
     float scale, eps;
+    // commit of the previous step ahead of this verify (commit-verify only):
+    // src_row[b] is the previous batch row whose accepted rows are still to
+    // be applied to slot_ids[b] (-1: none), read from that step's stash
+    float *ssm_out;
+    T *hist_out;
+    const int32_t *src_row;
+    const int32_t *prev_slots;
+    const int32_t *prev_accept;
+    const T *pxs;
+    const float *pes;
+    const float *pks;
+    const float *pas;
+    int Bp;
 };
 
 // Inputs of one conv channel: taps, history (oldest first) and the verify rows.
@@ -663,6 +692,19 @@ __device__ __forceinline__ void load_chunk(f32x4 (&sc)[CK], __amdgpu_buffer_rsrc
     asm volatile("" ::: "memory");
 }
 
+// The same, with the chunk offset in the per-lane offset, which the
+// resource's range check covers (the uniform offset is not checked): a chunk
+// past the end of the state returns zeros and moves no bytes.
+template <int CK>
+__device__ __forceinline__ void load_chunk_checked(f32x4 (&sc)[CK], __amdgpu_buffer_rsrc_t rs, uint32_t soff, int c)
+{
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int k = 0; k < CK; ++k)
+        sc[k] = buf_stream_load_f4(rs, soff + (uint32_t)(c * CK + k) * 4 * 128 * 4, 0);
+    asm volatile("" ::: "memory");
+}
+
 // Chunk c of the state against the column table: four tiles on the matrix
 // cores, and the two VALU columns (NVL = 2) as per-lane partial sums.
 template <int CK, int NVL, int MS>
@@ -687,9 +729,10 @@ __device__ __forceinline__ void mfma_chunk(const f32x4 (&sc)[CK], int c, int kg,
     }
 }
 
-template <int NR, typename T, bool SNAP>
+template <int NR, typename T, bool SNAP, bool FUSED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void gdn_verify_d128_kernel(const VerifyParams<T> p)
 {
+    static_assert(!FUSED || (sizeof(T) == 2 && !SNAP), "commit-verify: bf16 storage, replay");
     constexpr int D = 128;
     constexpr int NC = 2 * NR;
     constexpr int NMF = NC < 16 ? NC : 16;   // columns on the matrix cores
@@ -715,6 +758,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     __shared__ float4 cpark[4][64];                 // per wave: each lane's coefficients during the stream
     __shared__ float gp[4][NR * NC + NR];           // wave w's share: (M^T M)[u][c], u < NR; then |q_t|^2
     __shared__ float al[2][NR], be[2][NR];
+    __shared__ float alo[2][FUSED ? NR : 1];         // commit-verify: the previous step's a_t
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -726,6 +770,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const int h0 = 2 * (blockIdx.x % npair);
     const int kh = h0 / G;
     const int slot_in = p.slot_ids[b];   // its latency overlaps the slot-free loads below
+    int src = -1;
+    if constexpr (FUSED)
+        src = p.src_row[b];
 
     // Small loads first, branch-free, so they retire ahead of the state
     // stream; those that need no slot (gates, verify rows, taps) go before the
@@ -765,19 +812,44 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     }
     // then the loads that need the slot: a bad slot id reads slot 0's history
     // (any address inside the pool) and the workgroup leaves before the state
-    const bool bad = slot_in < 0 || slot_in >= p.P;
+    bool bad = slot_in < 0 || slot_in >= p.P;
+    int errbits = bad && slot_in != -1 ? 1 : 0;
+    // commit-verify: n accepted rows of the previous step's row src go into
+    // the state before it is read (a padding request ignores src)
+    int n = 0;
+    if constexpr (FUSED) {
+        if (!bad && src != -1) {
+            if (src < 0 || src >= p.Bp || p.prev_slots[src] != slot_in) {
+                bad = true;
+                errbits |= 4;
+            } else {
+                n = p.prev_accept[src];
+                if (n < 0 || n > NR) {
+                    bad = true;
+                    errbits |= 2;
+                    n = 0;
+                }
+            }
+        }
+    }
     const int slot = bad ? 0 : slot_in;
     if constexpr (STAGED) {
         const int u = min(tid, (kWidth - 1) * UPR - 1);
-        hu = *reinterpret_cast<const uint4 *>(p.conv + ((size_t)slot * (kWidth - 1) + u / UPR) * p.C +
-                                              unit_channel(u % UPR));
+        const int r = u / UPR;
+        // (commit-verify: the committed history, entry n + r of [history |
+        // previous rows]; n = 0 without a pending commit)
+        const int e = r + n;
+        const T *from = e < kWidth - 1
+            ? p.conv + ((size_t)slot * (kWidth - 1) + e) * p.C + unit_channel(u % UPR)
+            : p.pxs + ((size_t)src * NR + e - (kWidth - 1)) * p.C + unit_channel(u % UPR);
+        hu = *reinterpret_cast<const uint4 *>(from);
     } else {
         cinA = load_channel<NR>(p, slot, b, chA);
         cinV = load_channel<NR>(p, slot, b, chV);
     }
     if (bad) {
-        if (slot_in != -1 && tid == 0 && p.err)
-            atomicOr(p.err, 1);
+        if (errbits && tid == 0 && p.err)
+            atomicOr(p.err, errbits);
         zero_outputs(p, b, h0, NR, D);
         zero_outputs(p, b, h0 + 1, NR, D);
         return;
@@ -789,7 +861,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const int rb = 64 * (wave & 1);                  // and its 64-row block
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.ssm + ((size_t)slot * HV + h0 + hh) * D * D, D * D * 4);
     const uint32_t soff = (kg * D + rb + 4 * m) * 4;  // lane byte offset within each K-step block
-    f32x4 c0[CK], c1[CK], c2[CK];
+    // chunks in flight: three; two in the commit-verify, whose stream is a
+    // rolled loop over chunk pairs (unrolled, its replay loops keep too many
+    // values live for four workgroups per compute unit)
+    constexpr int DEPTH = FUSED ? 2 : 3;
+    f32x4 c0[CK], c1[CK], c2[DEPTH == 3 ? CK : 1];
     load_chunk(c0, rs, soff, 0);
     load_chunk(c1, rs, soff, 1);
     __builtin_amdgcn_sched_barrier(0);
@@ -821,6 +897,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         if constexpr (NXU > 2)
             stage_xunit(2, xu2);
         lds_barrier();
+        if constexpr (FUSED) {
+            // the committed history goes to the pool (q/k units by the key
+            // head's first pair only); after the barrier, since a history row
+            // one wave overwrites may be another wave's source
+            const int k = tid % UPR;
+            if (n > 0 && tid < (kWidth - 1) * UPR && (k >= 32 || owner))
+                out_store(reinterpret_cast<uint4 *>(p.hist_out + ((size_t)slot * (kWidth - 1) + tid / UPR) * p.C +
+                                                    unit_channel(k)),
+                          hu);
+        }
         const T *Xt = reinterpret_cast<const T *>(P);
         auto tap = [](uint2 w, int k) {
             return T{(uint16_t)(((k < 2 ? w.x : w.y) >> (16 * (k & 1))) & 0xffffu)};
@@ -867,9 +953,38 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         }
     }
     __builtin_amdgcn_sched_barrier(0);
-    load_chunk(c2, rs, soff, 2);
+    if constexpr (DEPTH == 3)
+        load_chunk(c2, rs, soff, 2);
     __builtin_amdgcn_sched_barrier(0);
     lds_barrier();   // the column table and the gates are complete
+
+    // commit-verify: the previous step's stash of this key head and value-head
+    // pair (n rows of k^_t, e_t, a_t) goes straight from HBM into P, which is
+    // free until the product tables: k^ rows at P[t*D], e rows at
+    // P[NR*D + (2t + pair head)*D] (a row's two heads are contiguous in the
+    // stash as well), in 1 KiB pieces, one per wave instruction, with no
+    // registers held across the Gram matrix. The gates come through one
+    // register (a zero-size resource when nothing is pending: zeros).
+    float sa = 0.0f;
+    if constexpr (FUSED) {
+        const int sr = src < 0 ? 0 : src;
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.pas + (size_t)sr * HV * NR, n > 0 ? HV * NR * 4 : 0);
+        sa = buf_load<float>(ra, (uint32_t)((h0 + min(tid / NR, 1)) * NR + tid % NR) * 4, 0);
+        if (n > 0) {
+            const float *kb = p.pks + ((size_t)src * HK + kh) * NR * D;
+            const int nk = (n * D + 255) / 256;
+            for (int i = wave; i < nk + n; i += 4) {
+                if (i < nk) {
+                    const int f = i * 256 + lane * 4;
+                    if (f < n * D)
+                        lds_dma16(kb + f, P + i * 256);
+                } else {
+                    const int t = i - nk;
+                    lds_dma16(p.pes + (((size_t)src * NR + t) * HV + h0) * D + lane * 4, P + NR * D + t * 2 * D);
+                }
+            }
+        }
+    }
 
     float *Pw = P + wave * 64 * PS;
     float *invw = invs[wave];
@@ -910,6 +1025,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
                 g[NR * NC + NMF - NR + 1] = dv[1];
             }
         }
+    }
+    if constexpr (FUSED) {
+        if (tid < 2 * NR)
+            alo[tid / NR][tid % NR] = sa;
+        // vmcnt(0): this wave's stash pieces are in LDS (the state chunks
+        // requested before them have arrived too, as loads return in order)
+        __builtin_amdgcn_s_waitcnt(0x0f70);
     }
     lds_barrier();   // from here on each wave finishes its rows alone
     auto gram = [&](int idx) { return (gp[0][idx] + gp[1][idx]) + (gp[2][idx] + gp[3][idx]); };
@@ -957,22 +1079,72 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         acc[q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         pv[q][0] = pv[q][1] = 0.0f;
     }
+    // commit-verify: each chunk takes the n accepted rows (the replay
+    // commit's update, in its order) and goes back to the pool before its
+    // products, so the verify reads the committed state
+    // (stores through a resource that is empty when nothing is pending: no
+    // branch around them)
+    const __amdgpu_buffer_rsrc_t rw =
+        make_rsrc(FUSED ? p.ssm_out + ((size_t)slot * HV + h0 + hh) * D * D : nullptr, FUSED && n > 0 ? D * D * 4 : 0);
+    auto commit_chunk = [&](f32x4 (&sc)[CK], int c) {
+        if constexpr (FUSED) {
+            {
+                const float *Pe = P + NR * D + hh * D;
+#pragma unroll 1
+                for (int t = 0; t < n; ++t) {
+                    const float a = alo[hh][t];
+                    const float4 ev = *reinterpret_cast<const float4 *>(&Pe[t * 2 * D + rb + 4 * m]);
+#pragma unroll
+                    for (int k = 0; k < CK; ++k) {
+                        const float kk = P[t * D + 4 * (c * CK + k) + kg];
+                        sc[k][0] = row_update(sc[k][0], a, ev.x, kk);
+                        sc[k][1] = row_update(sc[k][1], a, ev.y, kk);
+                        sc[k][2] = row_update(sc[k][2], a, ev.z, kk);
+                        sc[k][3] = row_update(sc[k][3], a, ev.w, kk);
+                    }
+                }
+#pragma unroll
+                for (int k = 0; k < CK; ++k)
+                    buf_stream_store_f4(rw, soff, (uint32_t)(c * CK + k) * 4 * D * 4, sc[k]);
+            }
+        }
+    };
+    if constexpr (FUSED) {
+        // the loads past the last chunk fall outside the state's resource:
+        // they return zeros and move no bytes
+        static_assert(NCHUNK % 2 == 0, "chunks go in pairs");
+#pragma unroll 1
+        for (int c = 0; c < NCHUNK; c += 2) {
+            commit_chunk(c0, c);
+            mfma_chunk<CK, NVL, MS>(c0, c, kg, m, Mt, acc, pv);
+            load_chunk_checked(c0, rs, soff, c + 2);
+            commit_chunk(c1, c + 1);
+            mfma_chunk<CK, NVL, MS>(c1, c + 1, kg, m, Mt, acc, pv);
+            load_chunk_checked(c1, rs, soff, c + 3);
+        }
+    } else {
 #pragma unroll
     for (int c = 0; c < NCHUNK; ++c) {
         if (c % 3 == 0) {
+            commit_chunk(c0, c);
             mfma_chunk<CK, NVL, MS>(c0, c, kg, m, Mt, acc, pv);
             if (c + 3 < NCHUNK)
                 load_chunk(c0, rs, soff, c + 3);
         } else if (c % 3 == 1) {
+            commit_chunk(c1, c);
             mfma_chunk<CK, NVL, MS>(c1, c, kg, m, Mt, acc, pv);
             if (c + 3 < NCHUNK)
                 load_chunk(c1, rs, soff, c + 3);
         } else {
+            commit_chunk(c2, c);
             mfma_chunk<CK, NVL, MS>(c2, c, kg, m, Mt, acc, pv);
             if (c + 3 < NCHUNK)
                 load_chunk(c2, rs, soff, c + 3);
         }
     }
+    }
+    if constexpr (FUSED)
+        lds_barrier();   // every wave is done with the staged stash before the product tables overwrite it
 
     // (S_0 M^)[i][c] = (S_0 M)[i][c] inv_c. Tile v, register q of lane (kg, m):
     // row 16kg + 4q + v of the block, column m.
@@ -2208,7 +2380,8 @@ hipError_t launch_verify(const VerifyParams<T> &vp, const VerifyLaunch &l)
             }
         }
         if (!done)
-            hipLaunchKernelGGL((gdn_verify_d128_kernel<NR, T, SNAP>), dim3(units), dim3(kThreads), 0, l.st, vp);
+            hipLaunchKernelGGL((gdn_verify_d128_kernel<NR, T, SNAP, false>), dim3(units), dim3(kThreads), 0, l.st,
+                               vp);
     } else {
         hipLaunchKernelGGL((gdn_verify_kernel<D, NR, T, SNAP>), dim3(l.batch * l.HV), dim3(kThreads),
                            0, l.st, vp);
@@ -2245,12 +2418,11 @@ hipError_t verify_dim(int D, int rows, const VerifyParams<T> &vp, const VerifyLa
 }
 
 template <typename T>
-hipError_t verify_typed(const Checked &c, const gdn_layer_desc *d, const gdn_pool *pool,
-                        const void *conv_w, const void *x, const void *alpha, const void *beta,
-                        const int32_t *slot_ids, int batch, int rows, bool snapshot, void *scratch,
-                        const ScratchLayout &L, void *out, int32_t *err, hipStream_t st)
+VerifyParams<T> verify_params(const Checked &c, const gdn_layer_desc *d, const gdn_pool *pool, const void *conv_w,
+                              const void *x, const void *alpha, const void *beta, const int32_t *slot_ids,
+                              bool snapshot, void *scratch, const ScratchLayout &L, void *out, int32_t *err)
 {
-    VerifyParams<T> vp;
+    VerifyParams<T> vp = {};
     char *base = static_cast<char *>(scratch);
     vp.ssm = pool->ssm;
     vp.conv = static_cast<const T *>(pool->conv);
@@ -2273,8 +2445,44 @@ hipError_t verify_typed(const Checked &c, const gdn_layer_desc *d, const gdn_poo
     vp.act = d->act;
     vp.scale = d->scale;
     vp.eps = d->l2_eps;
+    return vp;
+}
+
+template <typename T>
+hipError_t verify_typed(const Checked &c, const gdn_layer_desc *d, const gdn_pool *pool,
+                        const void *conv_w, const void *x, const void *alpha, const void *beta,
+                        const int32_t *slot_ids, int batch, int rows, bool snapshot, void *scratch,
+                        const ScratchLayout &L, void *out, int32_t *err, hipStream_t st)
+{
+    const VerifyParams<T> vp =
+        verify_params<T>(c, d, pool, conv_w, x, alpha, beta, slot_ids, snapshot, scratch, L, out, err);
     const VerifyLaunch l{batch, c.HK, c.HV, st};
     return snapshot ? verify_dim<T, true>(c.D, rows, vp, l) : verify_dim<T, false>(c.D, rows, vp, l);
+}
+
+// Commit-verify: the one-round d = 128 kernel (every batch size), with the
+// previous step's commit applied to each state chunk on its way in.
+template <int NR> hipError_t launch_commit_verify(const VerifyParams<bf16_t> &vp, int batch, int HV, hipStream_t st)
+{
+    hipLaunchKernelGGL((gdn_verify_d128_kernel<NR, bf16_t, false, true>), dim3(batch * (HV / 2)), dim3(kThreads), 0,
+                       st, vp);
+    return hipGetLastError();
+}
+
+hipError_t commit_verify_rows(int rows, const VerifyParams<bf16_t> &vp, int batch, int HV, hipStream_t st)
+{
+    switch (rows) {
+    case 1: return launch_commit_verify<1>(vp, batch, HV, st);
+    case 2: return launch_commit_verify<2>(vp, batch, HV, st);
+    case 3: return launch_commit_verify<3>(vp, batch, HV, st);
+    case 4: return launch_commit_verify<4>(vp, batch, HV, st);
+    case 5: return launch_commit_verify<5>(vp, batch, HV, st);
+    case 6: return launch_commit_verify<6>(vp, batch, HV, st);
+    case 7: return launch_commit_verify<7>(vp, batch, HV, st);
+    case 8: return launch_commit_verify<8>(vp, batch, HV, st);
+    case 9: return launch_commit_verify<9>(vp, batch, HV, st);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 template <int D, typename T, bool SNAP, int NPART>
@@ -2406,6 +2614,58 @@ gdn_status gdn_spec_verify(const gdn_layer_desc *desc, const gdn_pool *pool, con
                               scratch, L, out, err_flag, st)
         : verify_typed<bf16_t>(c, desc, pool, conv_w, x, alpha, beta, slot_ids, batch, rows, snap,
                                scratch, L, out, err_flag, st);
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+gdn_status gdn_spec_commit_verify(const gdn_layer_desc *desc, const gdn_pool *pool, const void *conv_w,
+                                  const void *x, const void *alpha, const void *beta,
+                                  const int32_t *slot_ids, int32_t batch, int32_t rows, void *scratch,
+                                  size_t scratch_bytes, const int32_t *src_row, const void *prev_scratch,
+                                  size_t prev_scratch_bytes, const int32_t *prev_slot_ids,
+                                  const int32_t *prev_accept_len, int32_t prev_batch, void *out, int32_t *err_flag,
+                                  void *stream)
+{
+    Checked c;
+    ScratchLayout L;
+    gdn_status s = check_common(desc, pool, batch, rows, GDN_COMMIT_REPLAY, scratch, scratch_bytes, &c, &L);
+    if (s != GDN_OK)
+        return s;
+    if (prev_batch < 0)
+        return GDN_ERR_INVALID_ARG;
+    if (desc->dtype != GDN_BF16 || c.D != 128 || c.HV != 2 * c.HK)
+        return GDN_ERR_UNSUPPORTED;
+    if ((size_t)prev_batch * c.HV > 0x7fffffffu)
+        return GDN_ERR_UNSUPPORTED;
+    const ScratchLayout Lp = scratch_layout(c.HK, c.HV, c.D, c.C, c.esize, prev_batch, rows, false);
+    if (prev_batch > 0) {
+        if (!prev_scratch || !aligned16(prev_scratch) || !prev_slot_ids || !prev_accept_len)
+            return GDN_ERR_INVALID_ARG;
+        if (prev_scratch_bytes < Lp.total)
+            return GDN_ERR_SCRATCH_TOO_SMALL;
+        // this step's stash must not land on the one being committed
+        const uintptr_t a0 = reinterpret_cast<uintptr_t>(scratch), a1 = a0 + L.total;
+        const uintptr_t b0 = reinterpret_cast<uintptr_t>(prev_scratch), b1 = b0 + Lp.total;
+        if (batch > 0 && a0 < b1 && b0 < a1)
+            return GDN_ERR_INVALID_ARG;
+    }
+    if (batch == 0)
+        return GDN_OK;
+    if (!conv_w || !x || !alpha || !beta || !slot_ids || !src_row || !out || !aligned16(conv_w) || !aligned16(x))
+        return GDN_ERR_INVALID_ARG;
+    VerifyParams<bf16_t> vp =
+        verify_params<bf16_t>(c, desc, pool, conv_w, x, alpha, beta, slot_ids, false, scratch, L, out, err_flag);
+    const char *pb = static_cast<const char *>(prev_scratch);
+    vp.ssm_out = pool->ssm;
+    vp.hist_out = static_cast<bf16_t *>(pool->conv);
+    vp.src_row = src_row;
+    vp.prev_slots = prev_slot_ids;
+    vp.prev_accept = prev_accept_len;
+    vp.pxs = prev_batch > 0 ? reinterpret_cast<const bf16_t *>(pb + Lp.xs) : nullptr;
+    vp.pes = prev_batch > 0 ? reinterpret_cast<const float *>(pb + Lp.es) : nullptr;
+    vp.pks = prev_batch > 0 ? reinterpret_cast<const float *>(pb + Lp.ks) : nullptr;
+    vp.pas = prev_batch > 0 ? reinterpret_cast<const float *>(pb + Lp.as) : nullptr;
+    vp.Bp = prev_batch;
+    const hipError_t e = commit_verify_rows(rows, vp, batch, c.HV, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 

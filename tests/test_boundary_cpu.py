@@ -321,3 +321,38 @@ def test_sample_arguments_are_refused(lib):
     assert f(scratch=4104) == inv                                        # misaligned
     assert f(nbytes=need - 1) == bd.GDN_ERR_SCRATCH_TOO_SMALL
     assert f(batch=0, inputs=None, scratch=None, acc=None, nxt=None) == bd.GDN_OK
+
+
+def _status_commit_verify(lib, desc, pool, batch=2, rows=3, scratch=0x100000, prev=0x200000, prev_batch=2,
+                          nbytes=1 << 16, pnbytes=1 << 16, src=4096, prev_slots=4096, prev_acc=4096, ptr=4096):
+    return lib.gdn_spec_commit_verify(ctypes.byref(desc), ctypes.byref(pool), ptr, ptr, ptr, ptr, ptr, batch, rows,
+                                      scratch, nbytes, src, prev, pnbytes, prev_slots, prev_acc, prev_batch, ptr, None,
+                                      None)
+
+
+def test_commit_verify_arguments_are_refused(lib):
+    """gdn_spec_commit_verify runs only where every workgroup owns the conv
+    channels it commits (bf16, d = 128, HV = 2 HK), and refuses a missing
+    source table or previous step, a negative previous batch and a scratch
+    that overlaps the previous step's, before any launch."""
+    INV, UNS = bd.GDN_ERR_INVALID_ARG, bd.GDN_ERR_UNSUPPORTED
+    q = bd.layer_desc(wl.LayerShape(num_k_heads=2, num_v_heads=4, d_k=128, d_v=128, dtype="bf16"))
+    p = good_pool()
+    assert _status_commit_verify(lib, good_desc(), p) == UNS                        # fp32 storage
+    d64 = bd.layer_desc(wl.LayerShape(num_k_heads=2, num_v_heads=4, d_k=64, d_v=64, dtype="bf16"))
+    assert _status_commit_verify(lib, d64, p) == UNS                                # d = 64
+    g4 = bd.layer_desc(wl.LayerShape(num_k_heads=1, num_v_heads=4, d_k=128, d_v=128, dtype="bf16"))
+    assert _status_commit_verify(lib, g4, p) == UNS                                 # four value heads per key head
+    assert _status_commit_verify(lib, q, p, prev_batch=-1) == INV
+    assert _status_commit_verify(lib, q, p, src=None) == INV
+    assert _status_commit_verify(lib, q, p, prev=None) == INV
+    assert _status_commit_verify(lib, q, p, prev=0x100008) == INV                    # misaligned previous scratch
+    assert _status_commit_verify(lib, q, p, prev_slots=None) == INV
+    assert _status_commit_verify(lib, q, p, prev_acc=None) == INV
+    assert _status_commit_verify(lib, q, p, prev=0x100000 + 256) == INV              # overlaps this step's scratch
+    assert _status_commit_verify(lib, q, p, nbytes=256) == bd.GDN_ERR_SCRATCH_TOO_SMALL
+    assert _status_commit_verify(lib, q, p, pnbytes=256) == bd.GDN_ERR_SCRATCH_TOO_SMALL
+    assert _status_commit_verify(lib, q, p, batch=0, prev=None, prev_slots=None, prev_acc=None, pnbytes=0,
+                                 prev_batch=0) == bd.GDN_OK                       # no previous step needs no buffers
+    assert _status_commit_verify(lib, q, p, rows=10) == INV
+    assert _status_commit_verify(lib, q, p, batch=0) == bd.GDN_OK                    # nothing launched

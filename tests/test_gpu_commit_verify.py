@@ -1,0 +1,206 @@
+"""Commit-verify (gdn_spec_commit_verify): one launch that commits the
+previous step's accepted rows into the state on its way into this step's
+verify (FreeToken issue #828, Design: the verify only reads the state, the
+commit replays the accepted rows; lmdeploy PR #5006, Verification path: a
+gated-delta-rule verify-and-commit kernel mode).
+
+Checked bit for bit against gdn_spec_commit followed by gdn_spec_verify
+(pool, history, outputs and the new stash), with batches rearranged between
+the steps (a request leaving, one joining, padding, a permuted order), and
+against the oracle's commit then verify."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+import gpu_harness as gh  # noqa: E402
+import oracle  # noqa: E402
+from linear_attention_verify_amd import binding as bd  # noqa: E402
+from linear_attention_verify_amd import workloads as wl  # noqa: E402
+
+DEV = "cuda"
+QWEN = wl.LayerShape(num_k_heads=16, num_v_heads=32, d_k=128, d_v=128, dtype="bf16")
+
+
+def _zero_scratch(desc, B, R):
+    return torch.zeros(max(bd.gdn_spec_scratch_bytes(desc, B, R, "replay"), 16), dtype=torch.uint8, device=DEV)
+
+
+def _plan(sid1, P, seed):
+    """The next step's batch: every step-1 request but one, shuffled, plus a
+    request on a free slot and a padding row. Returns (slot ids, source rows,
+    the step-1 rows left behind)."""
+    rng = np.random.default_rng(seed)
+    B1 = len(sid1)
+    keep = np.sort(rng.choice(B1, B1 - 1, replace=False))
+    dropped = np.setdiff1d(np.arange(B1), keep)
+    new_slot = int(rng.choice(np.setdiff1d(np.arange(P), sid1)))
+    order = [int(r) for r in keep] + [-1, -2]
+    rng.shuffle(order)
+    sid2, src = [], []
+    for r in order:
+        if r >= 0:
+            sid2.append(int(sid1[r]))
+            src.append(r)
+        elif r == -1:
+            sid2.append(new_slot)
+            src.append(-1)
+        else:
+            sid2.append(-1)
+            src.append(int(rng.integers(0, B1)))   # a padding row's source is ignored
+    return np.array(sid2, np.int32), np.array(src, np.int32), dropped, new_slot
+
+
+def _two_steps(R, B1, seed, accept_edges=True):
+    w = wl.small_workload(QWEN, batch=B1, rows=R, num_slots=3 * B1, seed=seed)
+    sid1, acc1 = wl.draw_requests(w)
+    if accept_edges:
+        acc1[0], acc1[1] = 0, R                    # nothing accepted; every row accepted
+    c = gh.make_case(w, slot_ids=sid1, accept=acc1)
+    sid2, src, dropped, new_slot = _plan(sid1, w.num_slots, seed + 1)
+    w2 = wl.small_workload(QWEN, batch=len(sid2), rows=R, num_slots=w.num_slots, seed=seed + 2)
+    d2 = wl.draw_layer(w2, 0)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(seed)
+    c.ssm[new_slot] = torch.randn(c.ssm[new_slot].shape, generator=gen, device=DEV)
+    c.conv[new_slot] = torch.randn(c.conv[new_slot].shape, generator=gen, device=DEV).to(torch.bfloat16)
+    return c, w2, d2, sid2, src, dropped
+
+
+def _step2(c, w2, d2, sid2):
+    s = c.w.shape
+    ins = {k: gh.storage_tensor(d2[k], s.dtype) for k in ("x", "alpha", "beta")}
+    out = torch.full((w2.batch, w2.rows, s.num_v_heads, s.d_v), float("nan"), dtype=torch.bfloat16, device=DEV)
+    return ins, out, torch.from_numpy(sid2).to(DEV)
+
+
+def _run_both(c, w2, d2, sid2, src, dropped):
+    """Returns (reference, fused) tuples of (ssm, conv, out, new scratch, err)."""
+    R = c.w.rows
+    gh.verify(c)                                    # step 1, the previous step's stash in c.scratch
+    torch.cuda.synchronize()
+    ssm0, conv0 = c.ssm.clone(), c.conv.clone()
+    ins, out, sid2_t = _step2(c, w2, d2, sid2)
+
+    # commit, then verify
+    gh.commit(c)
+    sb = _zero_scratch(c.desc, w2.batch, R)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    bd.gdn_spec_verify(c.desc, c.ssm, c.conv, c.conv_w, ins["x"], ins["alpha"], ins["beta"], sid2_t, R, "replay",
+                       sb, out, err)
+    torch.cuda.synchronize()
+    ref = (c.ssm.clone(), c.conv.clone(), out.clone(), sb.clone(), int(err.item()) | int(c.err.item()))
+
+    # the rows left behind committed on their own, the rest with the verify
+    c.ssm.copy_(ssm0)
+    c.conv.copy_(conv0)
+    c.err.zero_()
+    lone = np.full_like(c.slot_ids_np, -1)
+    lone[dropped] = c.slot_ids_np[dropped]
+    bd.gdn_spec_commit(c.desc, c.ssm, c.conv, torch.from_numpy(lone).to(DEV), c.accept, R, "replay", c.scratch,
+                       c.err)
+    sb2 = _zero_scratch(c.desc, w2.batch, R)
+    out.fill_(float("nan"))
+    err2 = torch.zeros(1, dtype=torch.int32, device=DEV)
+    print("commit-verify B=%d->%d R=%d" % (c.w.batch, w2.batch, R), flush=True)
+    bd.gdn_spec_commit_verify(c.desc, c.ssm, c.conv, c.conv_w, ins["x"], ins["alpha"], ins["beta"], sid2_t, R, sb2,
+                              torch.from_numpy(src).to(DEV), c.scratch, c.slot_ids, c.accept, out, err2,
+                              host_slot_ids=sid2)
+    torch.cuda.synchronize()
+    fused = (c.ssm.clone(), c.conv.clone(), out.clone(), sb2.clone(), int(err2.item()) | int(c.err.item()))
+    return ref, fused
+
+
+def _bits_equal(a, b):
+    return torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8))
+
+
+@pytest.mark.parametrize("R", [4, 9])
+def test_commit_verify_equals_commit_then_verify(R):
+    c, w2, d2, sid2, src, dropped = _two_steps(R, B1=16, seed=900 + R)
+    ref, fused = _run_both(c, w2, d2, sid2, src, dropped)
+    assert ref[4] == 0 and fused[4] == 0
+    for name, a, b in zip(("state", "history", "outputs", "stash"), ref[:4], fused[:4]):
+        assert _bits_equal(a, b), name
+
+
+def test_commit_verify_at_the_saturated_batch():
+    """64 requests x 9 rows, every request continued in place (the serving
+    loop's usual case and the benchmark's launch), bit for bit."""
+    w = wl.WORKLOADS["saturated-b64"]
+    c = gh.make_case(w)
+    d2 = wl.draw_layer(w, 1)
+    ident = np.arange(w.batch, dtype=np.int32)
+    ref, fused = _run_both(c, w, d2, c.slot_ids_np, ident, np.zeros(0, np.int64))
+    assert ref[4] == 0 and fused[4] == 0
+    for name, a, b in zip(("state", "history", "outputs", "stash"), ref[:4], fused[:4]):
+        assert _bits_equal(a, b), name
+
+
+def test_commit_verify_matches_the_oracle():
+    """The oracle's commit of step 1 then its verify of step 2, on the whole
+    pool: outputs to the bf16 tolerance, states to the fp32 one, conv
+    histories bit for bit."""
+    R = 4
+    c, w2, d2, sid2, src, dropped = _two_steps(R, B1=16, seed=950)
+    s = c.w.shape
+    host_ssm = c.ssm.cpu().numpy().copy()
+    host_conv = gh.to_storage_numpy(c.conv, s.dtype).copy()
+    _, fused = _run_both(c, w2, d2, sid2, src, dropped)
+    assert fused[4] == 0
+    orc = oracle.Oracle()
+    d1 = c.draw
+    assert orc.commit(s, host_ssm, host_conv, d1["conv_w"], d1["x"], d1["alpha"], d1["beta"], c.slot_ids_np,
+                      c.accept_np, R, nthreads=16) == 0
+    o_ref, _, err = orc.verify(s, host_ssm, host_conv, d1["conv_w"], d2["x"], d2["alpha"], d2["beta"], sid2, R,
+                               nthreads=16)
+    assert err == 0
+    atol, rtol = gh.tolerances(s)
+    np.testing.assert_allclose(gh.tensor_f64(fused[2], s.dtype), o_ref, atol=atol, rtol=rtol)
+    touched = np.unique(np.concatenate([c.slot_ids_np, sid2[sid2 >= 0]]))
+    satol, srtol = gh.state_tolerances(s)
+    np.testing.assert_allclose(fused[0].cpu().numpy()[touched], host_ssm[touched], atol=satol, rtol=srtol)
+    conv_gpu = gh.to_storage_numpy(fused[1], s.dtype)
+    assert np.array_equal(conv_gpu[touched], host_conv[touched])
+
+
+def test_commit_verify_errors_skip_the_request():
+    """A source row outside the previous batch or naming another slot (bit 2),
+    an accept length outside [0, rows] (bit 1) and a slot outside the pool
+    (bit 0): each such request gets zero outputs and its slot keeps its state;
+    the others are committed and verified as usual."""
+    R = 4
+    c, w2, d2, sid2, src, dropped = _two_steps(R, B1=16, seed=970, accept_edges=False)
+    gh.verify(c)
+    torch.cuda.synchronize()
+    live = np.flatnonzero((sid2 >= 0) & (src >= 0))
+    b_far, b_other, b_acc, b_slot = live[:4]
+    src = src.copy()
+    sid2 = sid2.copy()
+    src[b_far] = c.w.batch + 3                                   # outside the previous batch
+    src[b_other] = src[live[4]]                                  # names another request's row
+    acc = c.accept_np.copy()
+    acc[src[b_acc]] = R + 1                                      # accept length out of range
+    c.accept.copy_(torch.from_numpy(acc))
+    bad_slot_owner = sid2[b_slot]
+    sid2[b_slot] = c.w.num_slots + 5                             # slot outside the pool
+    ins, out, sid2_t = _step2(c, w2, d2, sid2)
+    before_ssm, before_conv = c.ssm.clone(), c.conv.clone()
+    sb = _zero_scratch(c.desc, w2.batch, R)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    bd.gdn_spec_commit_verify(c.desc, c.ssm, c.conv, c.conv_w, ins["x"], ins["alpha"], ins["beta"], sid2_t, R, sb,
+                              torch.from_numpy(src).to(DEV), c.scratch, c.slot_ids, c.accept, out, err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 7
+    for b in (b_far, b_other, b_acc, b_slot):
+        assert bool((out[b].float() == 0).all()), b
+    for b in (b_far, b_other, b_acc):
+        s_ = int(sid2[b])
+        assert _bits_equal(c.ssm[s_], before_ssm[s_]) and _bits_equal(c.conv[s_], before_conv[s_]), b
+    s_ = int(bad_slot_owner)                                     # its request never reached the pool
+    assert _bits_equal(c.ssm[s_], before_ssm[s_])
+    ok = np.setdiff1d(live, [b_far, b_other, b_acc, b_slot])
+    changed = [int(sid2[b]) for b in ok if c.accept_np[src[b]] > 0]
+    assert changed and all(not _bits_equal(c.ssm[s_], before_ssm[s_]) for s_ in changed)
