@@ -442,7 +442,9 @@ def run_sample(args, w):
 def run_stack(args, w):
     """A hybrid stack slice: every step verifies the batch through each of the
     w.layers GDN layers (one pool per layer) and then commits all layers, one
-    launch per layer (the default) or all in one launch (--stack-commit fused)."""
+    launch per layer or all in one launch (--stack-commit fused); with the
+    fused schedule, each layer's commit of the previous step runs inside its
+    verify of this one (one gdn_spec_commit_verify launch per layer)."""
     import numpy as np
     import torch
 
@@ -460,16 +462,40 @@ def run_stack(args, w):
     c0 = layers[0]
     fused = bd.PreparedCommitLayers(c0.desc, [(c.ssm, c.conv, c.scratch) for c in layers], c0.slot_ids,
                                     c0.accept, w.rows, args.mode, c0.err, stream)
+    cv = args.schedule == "fused"
+    csteps = []
+    if cv:
+        ident = torch.arange(w.batch, dtype=torch.int32, device="cuda")
+        for c, p in zip(layers, prepared):
+            alt = torch.empty_like(c.scratch)
+            csteps.append([[bd.PreparedCommitVerify(c.desc, c.ssm, c.conv, c.conv_w, c.x, c.alpha, c.beta,
+                                                    c.slot_ids, w.rows, dst, ident, src, c.slot_ids, c.accept,
+                                                    c.out, c.err, stream)
+                            for dst, src in ((alt, c.scratch), (c.scratch, alt))], 0])
+            p.verify()   # the step before the first: its commit is pending
     torch.cuda.synchronize()
 
-    def step():
-        for p in prepared:
-            p.verify()
+    def verifies():
+        for k, p in enumerate(prepared):
+            if cv:
+                pair, i = csteps[k]
+                pair[i]()
+                csteps[k][1] = 1 - i
+            else:
+                p.verify()
+
+    def commits():
+        if cv:
+            return
         if args.stack_commit == "fused":
             fused()
         else:
             for p in prepared:
                 p.commit()
+
+    def step():
+        verifies()
+        commits()
 
     for _ in range(args.warmup):
         step()
@@ -487,14 +513,9 @@ def run_stack(args, w):
     for _ in range(args.steps):
         a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
         a.record(stream)
-        for p in prepared:
-            p.verify()
+        verifies()
         b.record(stream)
-        if args.stack_commit == "fused":
-            fused()
-        else:
-            for p in prepared:
-                p.commit()
+        commits()
         c.record(stream)
         ev_v.append((a, b))
         ev_c.append((b, c))
@@ -504,11 +525,18 @@ def run_stack(args, w):
     vb, cb = algorithmic_bytes(w, acc, args.mode)
     L = w.layers
     rows_per_step = w.batch * w.rows * L
-    gbps = (vb + cb) * L * args.steps / wall / 1e9
-    kernels = {"verify": {"avg_us": float(tv.mean() * 1e6), "bytes": vb, "gbps": float(vb / tv.mean() / 1e9)},
-               "commit_all_layers": {"avg_us": float(tc.mean() * 1e6), "bytes": cb * L,
-                                     "gbps": float(cb * L / tc.mean() / 1e9)}}
-    dom = "commit_all_layers" if tc.mean() >= tv.mean() * L else "verify"
+    if cv:
+        fb = fused_bytes(w, acc)
+        gbps = fb * L * args.steps / wall / 1e9
+        kernels = {"commit_verify": {"avg_us": float(tv.mean() * 1e6), "bytes": fb,
+                                     "gbps": float(fb / tv.mean() / 1e9)}}
+        dom = "commit_verify"
+    else:
+        gbps = (vb + cb) * L * args.steps / wall / 1e9
+        kernels = {"verify": {"avg_us": float(tv.mean() * 1e6), "bytes": vb, "gbps": float(vb / tv.mean() / 1e9)},
+                   "commit_all_layers": {"avg_us": float(tc.mean() * 1e6), "bytes": cb * L,
+                                         "gbps": float(cb * L / tc.mean() / 1e9)}}
+        dom = "commit_all_layers" if tc.mean() >= tv.mean() * L else "verify"
     line = {
         "metric": METRIC, "value": rows_per_step * args.steps / wall, "unit": "rows/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3,
@@ -518,7 +546,8 @@ def run_stack(args, w):
                    "key_heads": w.shape.num_k_heads, "value_heads": w.shape.num_v_heads,
                    "head_dim": w.shape.d_k, "conv_width": w.shape.conv_width, "storage": w.shape.dtype,
                    "state": "f32", "pool_slots": w.num_slots, "commit_mode": args.mode,
-                   "commit_launch": args.stack_commit, "accept_mean": float(np.mean(acc))},
+                   "commit_launch": "with each verify" if cv else args.stack_commit,
+                   "schedule": args.schedule, "accept_mean": float(np.mean(acc))},
         "gbps": gbps, "hbm_frac": gbps / HBM_PEAK_GBPS, "kernels": kernels,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["gbps"], "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": kernels[dom]["gbps"] / HBM_PEAK_GBPS,
@@ -548,18 +577,21 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="time replays of a captured HIP graph of each group of steps instead of "
                          "eager launches (steps and warmup must be multiples of --copies)")
-    ap.add_argument("--schedule", default="serial", choices=["serial", "overlap", "fused"],
+    ap.add_argument("--schedule", default=None, choices=["serial", "overlap", "fused"],
                     help="serial: every launch on one stream; overlap: a group's commits on a second "
                          "stream, each copy's next verify waiting for its own commit, so one group's "
                          "commits run beside the next group's verifies (pays in long runs of large "
                          "replay batches; the pipeline's fill and drain cost more over a few steps); "
                          "fused: each step is one gdn_spec_commit_verify launch that commits the copy's "
                          "previous step into the state on its way into this step's verify (replay; "
-                         "every step still commits one batch and verifies one)")
+                         "every step still commits one batch and verifies one). Default: fused in "
+                         "replay mode with eager launches, serial otherwise")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 256 MiB device copy (the reference dispatch for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
     args = ap.parse_args()
+    if args.schedule is None:
+        args.schedule = "fused" if args.mode == "replay" and not args.graph else "serial"
 
     if args.gpus != 1:
         print("bench.py runs on one GPU: the verify/commit path has no cross-GPU step "
