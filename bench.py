@@ -57,12 +57,13 @@ SAMPLE_SOURCE = os.path.join(ROOT, "linear_attention_verify_amd", "csrc", "spec_
 # reports null.
 MEASURED_TRAFFIC = [
     {"source": KERNEL_SOURCE,
-     "source_sha256": "23952e152fc9e8d397b96d8b83ea886765a59149fc5314e0a37ae3125d20ec19",
+     "source_sha256": "52736e5eb2c00455af960da8265f8cb60472694936cb6dfb87092d577b054703",
      "bytes": {   # (workload, mode, kernel) -> bytes per launch
-         ("saturated-b64", "replay", "verify"): 176086659,
-         ("saturated-b64", "replay", "commit"): 282684671,
-         ("saturated-b64", "snapshot", "verify"): 1384335766,
-         ("saturated-b64", "snapshot", "commit"): 274773215,
+         ("saturated-b64", "replay", "commit_verify"): 319378794,
+         ("saturated-b64", "replay", "verify"): 176086092,
+         ("saturated-b64", "replay", "commit"): 282700947,
+         ("saturated-b64", "snapshot", "verify"): 1384336321,
+         ("saturated-b64", "snapshot", "commit"): 274771354,
      }},
     {"source": ATTN_SOURCE,
      "source_sha256": "f254bc77bc855d9281a6304db619d063533d81c6e4ed714c46000f8b555346f6",
@@ -70,9 +71,9 @@ MEASURED_TRAFFIC = [
          ("attn-b64", "-", "attn_verify"): 681347947,
      }},
     {"source": SAMPLE_SOURCE,
-     "source_sha256": "47b36fd82f912081bbe5a0497b820ee1e28bcf243d08da4bd71e42cc043d9642",
+     "source_sha256": "efe9de2a538f6b01887b342eff1afa6650fcceddd1d855fb42a42a7e920bffab",
      "bytes": {   # one call: stats kernel + draw kernel
-         ("sample-b64", "-", "accept_sample"): 275200735,
+         ("sample-b64", "-", "accept_sample"): 275209893,
      }},
 ]
 
@@ -585,13 +586,12 @@ def main():
                          "fused: each step is one gdn_spec_commit_verify launch that commits the copy's "
                          "previous step into the state on its way into this step's verify (replay; "
                          "every step still commits one batch and verifies one). Default: fused in "
-                         "replay mode with eager launches, serial otherwise")
+                         "replay mode with eager launches where the batch fills the chip (at least one "
+                         "(request, value-head pair) per compute unit), serial otherwise")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 256 MiB device copy (the reference dispatch for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
     args = ap.parse_args()
-    if args.schedule is None:
-        args.schedule = "fused" if args.mode == "replay" and not args.graph else "serial"
 
     if args.gpus != 1:
         print("bench.py runs on one GPU: the verify/commit path has no cross-GPU step "
@@ -612,6 +612,11 @@ def main():
     if args.workload in wl.SAMPLE_WORKLOADS:
         return run_sample(args, wl.SAMPLE_WORKLOADS[args.workload])
     w = wl.WORKLOADS[args.workload]
+    if args.schedule is None:
+        s = w.shape
+        fits = (s.dtype == "bf16" and s.d_k == 128 and s.num_v_heads == 2 * s.num_k_heads
+                and w.batch * s.num_v_heads // 2 >= 256)
+        args.schedule = "fused" if args.mode == "replay" and not args.graph and fits else "serial"
     if w.layers != 1:
         return run_stack(args, w)
     if args.calibrate_copy:
