@@ -586,8 +586,8 @@ def main():
                          "fused: each step is one gdn_spec_commit_verify launch that commits the copy's "
                          "previous step into the state on its way into this step's verify (replay; "
                          "every step still commits one batch and verifies one). Default: fused in "
-                         "replay mode with eager launches where the batch fills the chip (at least one "
-                         "(request, value-head pair) per compute unit), serial otherwise")
+                         "replay mode with eager launches on the layers it serves (bf16, d = 128, an even "
+                         "number of value heads per key head), serial otherwise")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 256 MiB device copy (the reference dispatch for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -614,8 +614,7 @@ def main():
     w = wl.WORKLOADS[args.workload]
     if args.schedule is None:
         s = w.shape
-        fits = (s.dtype == "bf16" and s.d_k == 128 and s.num_v_heads == 2 * s.num_k_heads
-                and w.batch * s.num_v_heads // 2 >= 256)
+        fits = s.dtype == "bf16" and s.d_k == 128 and (s.num_v_heads // s.num_k_heads) % 2 == 0
         args.schedule = "fused" if args.mode == "replay" and not args.graph and fits else "serial"
     if w.layers != 1:
         return run_stack(args, w)

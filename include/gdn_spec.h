@@ -175,9 +175,12 @@ gdn_status gdn_spec_commit(const gdn_layer_desc *desc, const gdn_pool *pool,
  *                 [-1, prev_batch) or naming another slot. Such a request is
  *                 skipped: no commit, zero outputs.
  * Rows of the previous batch that no src_row names are not committed here
- * (gdn_spec_commit does that). Requires bf16 storage, d_k = d_v = 128 and
- * HV = 2*HK (GDN_ERR_UNSUPPORTED otherwise): every workgroup then owns the
- * conv channels it commits.
+ * (gdn_spec_commit does that). The previous step must have been a
+ * replay-mode gdn_spec_verify or a gdn_spec_commit_verify: their scratch
+ * also keeps the conv history they read, from which the committed history is
+ * built, so no workgroup reads pool history that another is rewriting.
+ * Requires bf16 storage, d_k = d_v = 128 and an even number of value heads
+ * per key head (GDN_ERR_UNSUPPORTED otherwise).
  */
 gdn_status gdn_spec_commit_verify(const gdn_layer_desc *desc, const gdn_pool *pool, const void *conv_w,
                                   const void *x, const void *alpha, const void *beta,

@@ -216,7 +216,7 @@ __device__ __forceinline__ void tri_decode(int idx, int &t, int &u)
 __host__ __device__ constexpr int coef_count(int R) { return 3 * R + 2 * R * R; }
 
 struct ScratchLayout {
-    size_t xs, es, ks, as, snap, total;
+    size_t xs, es, ks, as, xh, snap, total;
 };
 
 __host__ __device__ inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -226,6 +226,10 @@ __host__ __device__ inline size_t align_up(size_t v) { return (v + kAlign - 1) /
 //   es   [B][R][HV][D]      fp32 correction vector e_t of each row and value head
 //   ks   [B][HK][R][D]      fp32 normalised k_t of each row and key head
 //   as   [B][HV][R]         fp32 decay gate a_t
+//   xh   [B][W-1][C]        the conv history the verify read (storage type;
+//                           written by the replay-mode bf16 d = 128 kernels,
+//                           so that a commit-verify of the next step builds
+//                           the committed history from scratch alone)
 //   snap [B][HV][R][D][D]   fp32 S_t after each row (snapshot mode only), same
 //                           per-head layout as the pool
 __host__ inline ScratchLayout scratch_layout(int HK, int HV, int D, int C, size_t esize, int B,
@@ -241,6 +245,8 @@ __host__ inline ScratchLayout scratch_layout(int HK, int HV, int D, int C, size_
     off = align_up(off + (size_t)B * HK * R * D * sizeof(float));
     L.as = off;
     off = align_up(off + (size_t)B * HV * R * sizeof(float));
+    L.xh = off;
+    off = align_up(off + (size_t)B * (kWidth - 1) * C * esize);
     L.snap = off;
     if (snapshot)
         off = align_up(off + (size_t)B * R * HV * D * D * sizeof(float));
@@ -280,7 +286,9 @@ template <typename T> struct VerifyParams {
     const float *pes;
     const float *pks;
     const float *pas;
+    const T *pxh;
     int Bp;
+    T *xh;
 };
 
 // Inputs of one conv channel: taps, history (oldest first) and the verify rows.
@@ -836,12 +844,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     if constexpr (STAGED) {
         const int u = min(tid, (kWidth - 1) * UPR - 1);
         const int r = u / UPR;
-        // (commit-verify: the committed history, entry n + r of [history |
-        // previous rows]; n = 0 without a pending commit)
+        // (commit-verify with n > 0 pending rows: the committed history,
+        // entry n + r of [the history the previous verify read | its rows],
+        // all from the previous step's scratch, so no workgroup reads pool
+        // history that another one is overwriting)
         const int e = r + n;
-        const T *from = e < kWidth - 1
-            ? p.conv + ((size_t)slot * (kWidth - 1) + e) * p.C + unit_channel(u % UPR)
-            : p.pxs + ((size_t)src * NR + e - (kWidth - 1)) * p.C + unit_channel(u % UPR);
+        const T *from = n == 0 ? p.conv + ((size_t)slot * (kWidth - 1) + r) * p.C + unit_channel(u % UPR)
+            : e < kWidth - 1 ? p.pxh + ((size_t)src * (kWidth - 1) + e) * p.C + unit_channel(u % UPR)
+                             : p.pxs + ((size_t)src * NR + e - (kWidth - 1)) * p.C + unit_channel(u % UPR);
         hu = *reinterpret_cast<const uint4 *>(from);
     } else {
         cinA = load_channel<NR>(p, slot, b, chA);
@@ -897,15 +907,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         if constexpr (NXU > 2)
             stage_xunit(2, xu2);
         lds_barrier();
-        if constexpr (FUSED) {
-            // the committed history goes to the pool (q/k units by the key
-            // head's first pair only); after the barrier, since a history row
-            // one wave overwrites may be another wave's source
+        if constexpr (!SNAP) {
+            // the history this verify used, for the next step's commit-verify;
+            // with a commit pending, the committed history also goes to the
+            // pool (q/k units by the key head's first pair only)
             const int k = tid % UPR;
-            if (n > 0 && tid < (kWidth - 1) * UPR && (k >= 32 || owner))
-                out_store(reinterpret_cast<uint4 *>(p.hist_out + ((size_t)slot * (kWidth - 1) + tid / UPR) * p.C +
-                                                    unit_channel(k)),
-                          hu);
+            if (tid < (kWidth - 1) * UPR && (k >= 32 || owner)) {
+                const size_t hoff = (size_t)(tid / UPR) * p.C + unit_channel(k);
+                out_store(reinterpret_cast<uint4 *>(p.xh + (size_t)b * (kWidth - 1) * p.C + hoff), hu);
+                if (FUSED && n > 0)
+                    out_store(reinterpret_cast<uint4 *>(p.hist_out + (size_t)slot * (kWidth - 1) * p.C + hoff), hu);
+            }
         }
         const T *Xt = reinterpret_cast<const T *>(P);
         auto tap = [](uint2 w, int k) {
@@ -1279,9 +1291,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 // In snapshot mode each wave then applies every row's update to its two
 // chunks, still in registers, and stores its part of S_1..S_R. Both modes
 // form the products in the same order, so they agree bit for bit.
-template <int NR, bool SNAP>
+template <int NR, bool SNAP, bool FUSED>
 __global__ __launch_bounds__(kThreads) void gdn_verify_d128_split_kernel(const VerifyParams<bf16_t> p)
 {
+    static_assert(!(SNAP && FUSED), "commit-verify: replay");
     using T = bf16_t;
     constexpr int D = 128;
     constexpr int NC = 2 * NR;
@@ -1300,7 +1313,11 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_d128_split_kernel(const V
     static_assert(NUT <= 2, "staged units per thread");
     constexpr int XFLOATS = NROWS * UPR * 4;               // staged rows, as floats
     constexpr int RFLOATS = 4 * 64 * PS;                    // per-wave partial products
-    constexpr int PFLOATS = XFLOATS > RFLOATS ? XFLOATS : RFLOATS;
+    // commit-verify: the previous step's stash sits beyond the staged inputs
+    // (k^ [t][j] for the key head, then e [t][64] of the block's rows) until
+    // the partial products overwrite it
+    constexpr int SFLOATS = FUSED ? NR * D + NR * 64 : 0;
+    constexpr int PFLOATS = XFLOATS + SFLOATS > RFLOATS ? XFLOATS + SFLOATS : RFLOATS;
 
     __shared__ __align__(16) float Mt[D * MS];
     __shared__ __align__(16) float P[PFLOATS];   // staged inputs; then the four waves' partial products
@@ -1308,6 +1325,7 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_d128_split_kernel(const V
     __shared__ float gp[4][NR * NC + NR];
     __shared__ float al[NR], be[NR];
     __shared__ float eb[SNAP ? NR * 64 : 1];   // e_t of the block's rows, for the snapshots
+    __shared__ float alo[FUSED ? NR : 1];      // commit-verify: the previous step's a_t of head h
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1324,6 +1342,9 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_d128_split_kernel(const V
     const int kh = h0 / G;
     const bool owner = (h0 % G) == 0;    // the key head's first pair stores its q/k inputs
     const int slot_in = p.slot_ids[b];
+    int src = -1;
+    if constexpr (FUSED)
+        src = p.src_row[b];
 
     // staged unit k of a row: q units 0..15, k units 16..31, then the block's
     // value channels rb..rb+63 of head h; unit k starts at local channel 8k
@@ -1339,21 +1360,46 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_d128_split_kernel(const V
     const int chV = 2 * HK * D + h * D + rb + min(tid, 63);
     const uint2 wA = *reinterpret_cast<const uint2 *>(p.conv_w + (size_t)chA * kWidth);
     const uint2 wV = *reinterpret_cast<const uint2 *>(p.conv_w + (size_t)chV * kWidth);
-    const bool bad = slot_in < 0 || slot_in >= p.P;
+    bool bad = slot_in < 0 || slot_in >= p.P;
+    int errbits = bad && slot_in != -1 ? 1 : 0;
+    // commit-verify: n accepted rows of the previous step's row src go into
+    // the state before it is read (a padding request ignores src)
+    int n = 0;
+    if constexpr (FUSED) {
+        if (!bad && src != -1) {
+            if (src < 0 || src >= p.Bp || p.prev_slots[src] != slot_in) {
+                bad = true;
+                errbits |= 4;
+            } else {
+                n = p.prev_accept[src];
+                if (n < 0 || n > NR) {
+                    bad = true;
+                    errbits |= 2;
+                    n = 0;
+                }
+            }
+        }
+    }
     const int slot = bad ? 0 : slot_in;
-    // staged rows: history (from the pool) then the verify rows
+    // staged rows: history then the verify rows. The history is the pool's,
+    // or with n > 0 pending rows the committed one, entry n + r of [the
+    // history the previous verify read | its rows], from the previous step's
+    // scratch (the pool's history of this slot is being rewritten)
     uint4 su[NUT];
 #pragma unroll
     for (int q = 0; q < NUT; ++q) {
         const int uu = min(q * kThreads + tid, NU - 1);
         const int r = uu / UPR, k = uu % UPR;
-        const T *row = r < kWidth - 1 ? p.conv + ((size_t)slot * (kWidth - 1) + r) * p.C
-                                      : p.x + ((size_t)b * NR + (r - (kWidth - 1))) * p.C;
+        const int e = r + n;
+        const T *row = r >= kWidth - 1 ? p.x + ((size_t)b * NR + (r - (kWidth - 1))) * p.C
+            : n == 0                   ? p.conv + ((size_t)slot * (kWidth - 1) + r) * p.C
+            : e < kWidth - 1           ? p.pxh + ((size_t)src * (kWidth - 1) + e) * p.C
+                                       : p.pxs + ((size_t)src * NR + e - (kWidth - 1)) * p.C;
         su[q] = *reinterpret_cast<const uint4 *>(row + unit_channel(k));
     }
     if (bad) {
-        if (slot_in != -1 && tid == 0 && blk == 0 && p.err)
-            atomicOr(p.err, 1);
+        if (errbits && tid == 0 && blk == 0 && p.err)
+            atomicOr(p.err, errbits);
         for (int idx = tid; idx < NR * 64; idx += kThreads) {
             const int t = idx / 64, i = idx % 64;
             out_store(&p.out[(((size_t)b * NR + t) * HV + h) * D + rb + i], from_f32<T>(0.0f));
@@ -1370,6 +1416,36 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_d128_split_kernel(const V
     load_chunk(c0, rs, soff, 2 * wave);
     load_chunk(c1, rs, soff, 2 * wave + 1);
     __builtin_amdgcn_sched_barrier(0);
+
+    // commit-verify: the previous step's stash straight into LDS beyond the
+    // staged inputs, 16 bytes per lane (k^ rows of the key head, 1 KiB per
+    // wave instruction; e of the block's 64 rows, four rows per instruction),
+    // and the gates of head h through one register
+    float sa = 0.0f;
+    float *const Sk = P + XFLOATS;
+    float *const Se = P + XFLOATS + NR * D;
+    if constexpr (FUSED) {
+        const int sr = src < 0 ? 0 : src;
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.pas + (size_t)sr * HV * NR, n > 0 ? HV * NR * 4 : 0);
+        sa = buf_load<float>(ra, (uint32_t)(h * NR + min(tid, NR - 1)) * 4, 0);
+        if (n > 0) {
+            const float *kb = p.pks + ((size_t)src * HK + kh) * NR * D;
+            const int nk = (n * D + 255) / 256;
+            const int ne = (n + 3) / 4;
+            for (int i = wave; i < nk + ne; i += 4) {
+                if (i < nk) {
+                    const int f = i * 256 + lane * 4;
+                    if (f < n * D)
+                        lds_dma16(kb + f, Sk + i * 256);
+                } else {
+                    const int q = i - nk;
+                    const int t = 4 * q + lane / 16;
+                    if (t < n)
+                        lds_dma16(p.pes + (((size_t)src * NR + t) * HV + h) * D + rb + (lane % 16) * 4, Se + q * 256);
+                }
+            }
+        }
+    }
 
     if (tid < NR) {
         al[tid] = to_f32(ga);
@@ -1391,6 +1467,20 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_d128_split_kernel(const V
         }
     }
     lds_barrier();
+    if constexpr (!SNAP) {
+        // the history this verify used, for the next step's commit-verify
+        // (the block's value channels; the key head's q/k channels from the
+        // first block of its first pair); with a commit pending, the
+        // committed history goes to the pool by the same writers
+        static_assert((kWidth - 1) * UPR <= kThreads, "history units in the first pass");
+        const int k = tid % UPR;
+        if (tid < (kWidth - 1) * UPR && (k >= 32 || (owner && blk == 0))) {
+            const size_t hoff = (size_t)(tid / UPR) * p.C + unit_channel(k);
+            out_store(reinterpret_cast<uint4 *>(p.xh + (size_t)b * (kWidth - 1) * p.C + hoff), su[0]);
+            if (FUSED && n > 0)
+                out_store(reinterpret_cast<uint4 *>(p.hist_out + (size_t)slot * (kWidth - 1) * p.C + hoff), su[0]);
+        }
+    }
     float v[NR];   // value channel rb + tid of head h (threads < 64)
     {
         ChanIn<NR, T> cinA, cinV;
@@ -1471,6 +1561,38 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_d128_split_kernel(const V
     for (int q = 0; q < 4; ++q) {
         acc[q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         pv[q][0] = pv[q][1] = 0.0f;
+    }
+    if constexpr (FUSED) {
+        // this wave's two chunks take the n accepted rows (the replay
+        // commit's update, in its order) and go back to the pool before
+        // their products; stores through a resource that is empty when
+        // nothing is pending
+        if (tid < NR)
+            alo[tid] = sa;
+        __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's stash pieces are in LDS
+        lds_barrier();
+        const __amdgpu_buffer_rsrc_t rw =
+            make_rsrc(p.ssm_out + ((size_t)slot * HV + h) * D * D, n > 0 ? D * D * 4 : 0);
+        auto commit_chunk = [&](f32x4 (&sc)[CK], int c) {
+#pragma unroll 1
+            for (int t = 0; t < n; ++t) {
+                const float a = alo[t];
+                const float4 ev = *reinterpret_cast<const float4 *>(&Se[t * 64 + 4 * m]);
+#pragma unroll
+                for (int kk4 = 0; kk4 < CK; ++kk4) {
+                    const float kk = Sk[t * D + 4 * (c * CK + kk4) + kg];
+                    sc[kk4][0] = row_update(sc[kk4][0], a, ev.x, kk);
+                    sc[kk4][1] = row_update(sc[kk4][1], a, ev.y, kk);
+                    sc[kk4][2] = row_update(sc[kk4][2], a, ev.z, kk);
+                    sc[kk4][3] = row_update(sc[kk4][3], a, ev.w, kk);
+                }
+            }
+#pragma unroll
+            for (int kk4 = 0; kk4 < CK; ++kk4)
+                buf_stream_store_f4(rw, soff, (uint32_t)(c * CK + kk4) * 4 * D * 4, sc[kk4]);
+        };
+        commit_chunk(c0, 2 * wave);
+        commit_chunk(c1, 2 * wave + 1);
     }
     mfma_chunk<CK, NVL, MS>(c0, 2 * wave, kg, m, Mt, acc, pv);
     mfma_chunk<CK, NVL, MS>(c1, 2 * wave + 1, kg, m, Mt, acc, pv);
@@ -2368,7 +2490,7 @@ hipError_t launch_verify(const VerifyParams<T> &vp, const VerifyLaunch &l)
             // 11.0 us). One threshold for both modes keeps their products in the
             // same order, so replay and snapshot agree bit for bit
             if (units < kComputeUnits) {
-                hipLaunchKernelGGL((gdn_verify_d128_split_kernel<NR, SNAP>), dim3(units * 4), dim3(kThreads), 0,
+                hipLaunchKernelGGL((gdn_verify_d128_split_kernel<NR, SNAP, false>), dim3(units * 4), dim3(kThreads), 0,
                                    l.st, vp);
                 done = true;
             } else if constexpr (SNAP) {
@@ -2437,6 +2559,7 @@ VerifyParams<T> verify_params(const Checked &c, const gdn_layer_desc *d, const g
     vp.es = reinterpret_cast<float *>(base + L.es);
     vp.ks = reinterpret_cast<float *>(base + L.ks);
     vp.as = reinterpret_cast<float *>(base + L.as);
+    vp.xh = reinterpret_cast<T *>(base + L.xh);
     vp.snap = snapshot ? reinterpret_cast<float *>(base + L.snap) : nullptr;
     vp.HK = c.HK;
     vp.HV = c.HV;
@@ -2460,12 +2583,18 @@ hipError_t verify_typed(const Checked &c, const gdn_layer_desc *d, const gdn_poo
     return snapshot ? verify_dim<T, true>(c.D, rows, vp, l) : verify_dim<T, false>(c.D, rows, vp, l);
 }
 
-// Commit-verify: the one-round d = 128 kernel (every batch size), with the
-// previous step's commit applied to each state chunk on its way in.
+// Commit-verify: the d = 128 verify kernels of the same batch sizes (the
+// split kernel below one unit per compute unit, the one-round kernel from
+// there), with the previous step's commit applied to each state chunk on its
+// way in.
 template <int NR> hipError_t launch_commit_verify(const VerifyParams<bf16_t> &vp, int batch, int HV, hipStream_t st)
 {
-    hipLaunchKernelGGL((gdn_verify_d128_kernel<NR, bf16_t, false, true>), dim3(batch * (HV / 2)), dim3(kThreads), 0,
-                       st, vp);
+    const int units = batch * (HV / 2);
+    if (units < kComputeUnits)
+        hipLaunchKernelGGL((gdn_verify_d128_split_kernel<NR, false, true>), dim3(units * 4), dim3(kThreads), 0, st,
+                           vp);
+    else
+        hipLaunchKernelGGL((gdn_verify_d128_kernel<NR, bf16_t, false, true>), dim3(units), dim3(kThreads), 0, st, vp);
     return hipGetLastError();
 }
 
@@ -2632,7 +2761,7 @@ gdn_status gdn_spec_commit_verify(const gdn_layer_desc *desc, const gdn_pool *po
         return s;
     if (prev_batch < 0)
         return GDN_ERR_INVALID_ARG;
-    if (desc->dtype != GDN_BF16 || c.D != 128 || c.HV != 2 * c.HK)
+    if (desc->dtype != GDN_BF16 || c.D != 128 || (c.HV / c.HK) % 2 != 0)
         return GDN_ERR_UNSUPPORTED;
     if ((size_t)prev_batch * c.HV > 0x7fffffffu)
         return GDN_ERR_UNSUPPORTED;
@@ -2664,6 +2793,7 @@ gdn_status gdn_spec_commit_verify(const gdn_layer_desc *desc, const gdn_pool *po
     vp.pes = prev_batch > 0 ? reinterpret_cast<const float *>(pb + Lp.es) : nullptr;
     vp.pks = prev_batch > 0 ? reinterpret_cast<const float *>(pb + Lp.ks) : nullptr;
     vp.pas = prev_batch > 0 ? reinterpret_cast<const float *>(pb + Lp.as) : nullptr;
+    vp.pxh = prev_batch > 0 ? reinterpret_cast<const bf16_t *>(pb + Lp.xh) : nullptr;
     vp.Bp = prev_batch;
     const hipError_t e = commit_verify_rows(rows, vp, batch, c.HV, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;

@@ -56,9 +56,9 @@ def test_scratch_bytes(lib, name, mode):
     w = wl.WORKLOADS[name]
     s = w.shape
     B, R, HK, HV, D, C = w.batch, w.rows, s.num_k_heads, s.num_v_heads, s.d_k, s.conv_channels
-    # raw row inputs, e_t per value head, k_t per key head, a_t per value head
+    # raw row inputs, e_t per value head, k_t per key head, a_t per value head, the history read
     want = (_align(B * R * C * s.elem_bytes) + _align(B * R * HV * D * 4) + _align(B * HK * R * D * 4)
-            + _align(B * HV * R * 4))
+            + _align(B * HV * R * 4) + _align(B * (s.conv_width - 1) * C * s.elem_bytes))
     if mode == "snapshot":
         want += _align(B * R * HV * D * D * 4)
     assert bd.gdn_spec_scratch_bytes(bd.layer_desc(s), B, R, mode) == want
@@ -331,8 +331,8 @@ def _status_commit_verify(lib, desc, pool, batch=2, rows=3, scratch=0x100000, pr
 
 
 def test_commit_verify_arguments_are_refused(lib):
-    """gdn_spec_commit_verify runs only where every workgroup owns the conv
-    channels it commits (bf16, d = 128, HV = 2 HK), and refuses a missing
+    """gdn_spec_commit_verify runs on the d = 128 bf16 kernels (an even number
+    of value heads per key head), and refuses a missing
     source table or previous step, a negative previous batch and a scratch
     that overlaps the previous step's, before any launch."""
     INV, UNS = bd.GDN_ERR_INVALID_ARG, bd.GDN_ERR_UNSUPPORTED
@@ -341,8 +341,8 @@ def test_commit_verify_arguments_are_refused(lib):
     assert _status_commit_verify(lib, good_desc(), p) == UNS                        # fp32 storage
     d64 = bd.layer_desc(wl.LayerShape(num_k_heads=2, num_v_heads=4, d_k=64, d_v=64, dtype="bf16"))
     assert _status_commit_verify(lib, d64, p) == UNS                                # d = 64
-    g4 = bd.layer_desc(wl.LayerShape(num_k_heads=1, num_v_heads=4, d_k=128, d_v=128, dtype="bf16"))
-    assert _status_commit_verify(lib, g4, p) == UNS                                 # four value heads per key head
+    g1 = bd.layer_desc(wl.LayerShape(num_k_heads=2, num_v_heads=2, d_k=128, d_v=128, dtype="bf16"))
+    assert _status_commit_verify(lib, g1, p) == UNS                                 # one value head per key head
     assert _status_commit_verify(lib, q, p, prev_batch=-1) == INV
     assert _status_commit_verify(lib, q, p, src=None) == INV
     assert _status_commit_verify(lib, q, p, prev=None) == INV

@@ -22,6 +22,8 @@ from linear_attention_verify_amd import workloads as wl  # noqa: E402
 
 DEV = "cuda"
 QWEN = wl.LayerShape(num_k_heads=16, num_v_heads=32, d_k=128, d_v=128, dtype="bf16")
+# four value heads per key head: two workgroups (pairs) share a key head's q/k channels
+GQA4 = wl.LayerShape(num_k_heads=8, num_v_heads=32, d_k=128, d_v=128, dtype="bf16")
 
 
 def _zero_scratch(desc, B, R):
@@ -29,12 +31,12 @@ def _zero_scratch(desc, B, R):
 
 
 def _plan(sid1, P, seed):
-    """The next step's batch: every step-1 request but one, shuffled, plus a
-    request on a free slot and a padding row. Returns (slot ids, source rows,
-    the step-1 rows left behind)."""
+    """The next step's batch: every step-1 request but one (all of them in a
+    batch of one or two), shuffled, plus a request on a free slot and a
+    padding row. Returns (slot ids, source rows, the step-1 rows left behind)."""
     rng = np.random.default_rng(seed)
     B1 = len(sid1)
-    keep = np.sort(rng.choice(B1, B1 - 1, replace=False))
+    keep = np.sort(rng.choice(B1, B1 - 1 if B1 > 2 else B1, replace=False))
     dropped = np.setdiff1d(np.arange(B1), keep)
     new_slot = int(rng.choice(np.setdiff1d(np.arange(P), sid1)))
     order = [int(r) for r in keep] + [-1, -2]
@@ -53,14 +55,16 @@ def _plan(sid1, P, seed):
     return np.array(sid2, np.int32), np.array(src, np.int32), dropped, new_slot
 
 
-def _two_steps(R, B1, seed, accept_edges=True):
-    w = wl.small_workload(QWEN, batch=B1, rows=R, num_slots=3 * B1, seed=seed)
+def _two_steps(R, B1, seed, accept_edges=True, shape=QWEN):
+    w = wl.small_workload(shape, batch=B1, rows=R, num_slots=3 * B1 + 2, seed=seed)
     sid1, acc1 = wl.draw_requests(w)
     if accept_edges:
-        acc1[0], acc1[1] = 0, R                    # nothing accepted; every row accepted
+        acc1[0] = R                                # every row accepted
+        if B1 > 1:
+            acc1[1] = 0                            # nothing accepted
     c = gh.make_case(w, slot_ids=sid1, accept=acc1)
     sid2, src, dropped, new_slot = _plan(sid1, w.num_slots, seed + 1)
-    w2 = wl.small_workload(QWEN, batch=len(sid2), rows=R, num_slots=w.num_slots, seed=seed + 2)
+    w2 = wl.small_workload(shape, batch=len(sid2), rows=R, num_slots=w.num_slots, seed=seed + 2)
     d2 = wl.draw_layer(w2, 0)
     gen = torch.Generator(device=DEV)
     gen.manual_seed(seed)
@@ -117,9 +121,13 @@ def _bits_equal(a, b):
     return torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8))
 
 
-@pytest.mark.parametrize("R", [4, 9])
-def test_commit_verify_equals_commit_then_verify(R):
-    c, w2, d2, sid2, src, dropped = _two_steps(R, B1=16, seed=900 + R)
+@pytest.mark.parametrize("R,B1,shape", [
+    (4, 16, QWEN), (9, 16, QWEN),              # the one-round kernel (a unit per compute unit or more)
+    (3, 1, QWEN), (9, 1, QWEN), (4, 6, QWEN),  # the split kernel (fewer)
+    (4, 16, GQA4), (3, 2, GQA4),               # a key head shared by two pairs, both kernels
+])
+def test_commit_verify_equals_commit_then_verify(R, B1, shape):
+    c, w2, d2, sid2, src, dropped = _two_steps(R, B1=B1, seed=900 + 10 * R + B1, shape=shape)
     ref, fused = _run_both(c, w2, d2, sid2, src, dropped)
     assert ref[4] == 0 and fused[4] == 0
     for name, a, b in zip(("state", "history", "outputs", "stash"), ref[:4], fused[:4]):
@@ -139,12 +147,13 @@ def test_commit_verify_at_the_saturated_batch():
         assert _bits_equal(a, b), name
 
 
-def test_commit_verify_matches_the_oracle():
+@pytest.mark.parametrize("B1", [16, 3])
+def test_commit_verify_matches_the_oracle(B1):
     """The oracle's commit of step 1 then its verify of step 2, on the whole
     pool: outputs to the bf16 tolerance, states to the fp32 one, conv
-    histories bit for bit."""
+    histories bit for bit (both kernels)."""
     R = 4
-    c, w2, d2, sid2, src, dropped = _two_steps(R, B1=16, seed=950)
+    c, w2, d2, sid2, src, dropped = _two_steps(R, B1=B1, seed=950 + B1)
     s = c.w.shape
     host_ssm = c.ssm.cpu().numpy().copy()
     host_conv = gh.to_storage_numpy(c.conv, s.dtype).copy()
@@ -166,13 +175,14 @@ def test_commit_verify_matches_the_oracle():
     assert np.array_equal(conv_gpu[touched], host_conv[touched])
 
 
-def test_commit_verify_errors_skip_the_request():
+@pytest.mark.parametrize("B1", [16, 8])
+def test_commit_verify_errors_skip_the_request(B1):
     """A source row outside the previous batch or naming another slot (bit 2),
     an accept length outside [0, rows] (bit 1) and a slot outside the pool
     (bit 0): each such request gets zero outputs and its slot keeps its state;
-    the others are committed and verified as usual."""
+    the others are committed and verified as usual (both kernels)."""
     R = 4
-    c, w2, d2, sid2, src, dropped = _two_steps(R, B1=16, seed=970, accept_edges=False)
+    c, w2, d2, sid2, src, dropped = _two_steps(R, B1=B1, seed=970 + B1, accept_edges=False)
     gh.verify(c)
     torch.cuda.synchronize()
     live = np.flatnonzero((sid2 >= 0) & (src >= 0))
