@@ -57,13 +57,13 @@ SAMPLE_SOURCE = os.path.join(ROOT, "linear_attention_verify_amd", "csrc", "spec_
 # reports null.
 MEASURED_TRAFFIC = [
     {"source": KERNEL_SOURCE,
-     "source_sha256": "52736e5eb2c00455af960da8265f8cb60472694936cb6dfb87092d577b054703",
+     "source_sha256": "81bdd8bdada7539d093e40d839246a8be2bc9401069033b02d9e6c9db698278f",
      "bytes": {   # (workload, mode, kernel) -> bytes per launch
-         ("saturated-b64", "replay", "commit_verify"): 319378794,
-         ("saturated-b64", "replay", "verify"): 176086092,
-         ("saturated-b64", "replay", "commit"): 282700947,
-         ("saturated-b64", "snapshot", "verify"): 1384336321,
-         ("saturated-b64", "snapshot", "commit"): 274771354,
+         ("saturated-b64", "replay", "commit_verify"): 322532611,
+         ("saturated-b64", "replay", "verify"): 179234206,
+         ("saturated-b64", "replay", "commit"): 282700563,
+         ("saturated-b64", "snapshot", "verify"): 1384334161,
+         ("saturated-b64", "snapshot", "commit"): 274772581,
      }},
     {"source": ATTN_SOURCE,
      "source_sha256": "f254bc77bc855d9281a6304db619d063533d81c6e4ed714c46000f8b555346f6",
