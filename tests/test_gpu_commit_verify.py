@@ -214,3 +214,63 @@ def test_commit_verify_errors_skip_the_request(B1):
     ok = np.setdiff1d(live, [b_far, b_other, b_acc, b_slot])
     changed = [int(sid2[b]) for b in ok if c.accept_np[src[b]] > 0]
     assert changed and all(not _bits_equal(c.ssm[s_], before_ssm[s_]) for s_ in changed)
+
+
+def test_commit_verify_replays_from_a_graph():
+    """Two consecutive commit-verify steps (the scratch buffers trading
+    places) captured in one HIP graph replay to the bits of the eager
+    launches, three times, with eager work between the replays (FreeToken PR
+    #844, Tests: a captured verify replays bitwise; the call only enqueues
+    kernels on the caller's stream)."""
+    w = wl.small_workload(QWEN, batch=16, rows=4, num_slots=40, seed=990)
+    c = gh.make_case(w)
+    s = c.w.shape
+    d2, d3 = wl.draw_layer(w, 1), wl.draw_layer(w, 2)
+    ins2 = [gh.storage_tensor(d2[k], s.dtype) for k in ("x", "alpha", "beta")]
+    ins3 = [gh.storage_tensor(d3[k], s.dtype) for k in ("x", "alpha", "beta")]
+    gh.verify(c)                                       # step 1: scratch A holds its stash
+    torch.cuda.synchronize()
+    sa_, sb_ = c.scratch.clone(), _zero_scratch(c.desc, w.batch, w.rows)
+    ident = torch.arange(w.batch, dtype=torch.int32, device=DEV)
+    out = torch.empty_like(c.out)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    steps = [bd.PreparedCommitVerify(c.desc, c.ssm, c.conv, c.conv_w, *ins2, c.slot_ids, w.rows, sb_, ident, sa_,
+                                     c.slot_ids, c.accept, out, err),
+             bd.PreparedCommitVerify(c.desc, c.ssm, c.conv, c.conv_w, *ins3, c.slot_ids, w.rows, sa_, ident, sb_,
+                                     c.slot_ids, c.accept, out, err)]
+    ssm0, conv0, a0 = c.ssm.clone(), c.conv.clone(), sa_.clone()
+
+    def restore():
+        c.ssm.copy_(ssm0)
+        c.conv.copy_(conv0)
+        sa_.copy_(a0)
+        sb_.zero_()
+        out.fill_(float("nan"))
+        err.zero_()
+
+    restore()
+    for st in steps:
+        st()
+    torch.cuda.synchronize()
+    want = (c.ssm.clone(), c.conv.clone(), out.clone(), sa_.clone())
+    assert int(err.item()) == 0
+
+    restore()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for st in steps:
+            st.args = st.args[:-1] + (torch.cuda.current_stream().cuda_stream,)
+            st()
+    torch.cuda.synchronize()
+    junk = torch.randn(1 << 20, device=DEV)
+    for rep in range(3):
+        restore()
+        junk.mul_(1.5)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = (c.ssm, c.conv, out, sa_)
+        for name, a, b in zip(("state", "history", "outputs", "stash"), want, got):
+            assert _bits_equal(a, b), (rep, name)
+        assert int(err.item()) == 0
