@@ -255,6 +255,30 @@ def check_slot_ids_host(slot_ids, num_slots):
         raise ValueError("slot %d is shared by requests %s" % (s, reqs))
 
 
+def check_src_rows_host(src_row, prev_batch):
+    """Opt-in check of a host copy of a commit-verify's source-row table:
+    every entry is -1 or a row of the previous batch [0, prev_batch), and no
+    previous row is named twice (its accepted rows would be committed twice).
+    Raises ValueError."""
+    import numpy as np
+    if hasattr(src_row, "detach"):
+        if src_row.is_cuda:
+            raise ValueError("check_src_rows_host takes the host copy of the source-row table")
+        src_row = src_row.detach().numpy()
+    a = np.asarray(src_row)
+    if a.ndim != 1 or not np.issubdtype(a.dtype, np.integer):
+        raise ValueError("source-row table must be a 1-D integer array")
+    bad = (a < -1) | (a >= prev_batch)
+    if bad.any():
+        i = int(np.flatnonzero(bad)[0])
+        raise ValueError("source row %d of request %d is outside [-1, %d)" % (int(a[i]), i, prev_batch))
+    live = a[a >= 0]
+    uniq, counts = np.unique(live, return_counts=True)
+    if (counts > 1).any():
+        r = int(uniq[np.flatnonzero(counts > 1)[0]])
+        raise ValueError("previous row %d is named by requests %s" % (r, np.flatnonzero(a == r).tolist()))
+
+
 def _stream(stream):
     if stream is None:
         import torch
@@ -371,11 +395,14 @@ class PreparedCommitVerify:
     launch. Checked and turned into ctypes arguments once."""
 
     def __init__(self, desc, ssm, conv, conv_w, x, alpha, beta, slot_ids, rows, scratch, src_row, prev_scratch,
-                 prev_slot_ids, prev_accept_len, out, err_flag=None, stream=None, host_slot_ids=None):
+                 prev_slot_ids, prev_accept_len, out, err_flag=None, stream=None, host_slot_ids=None,
+                 host_src_row=None):
         B, Bp = _check_commit_verify_args(desc, ssm, conv, conv_w, x, alpha, beta, slot_ids, rows, scratch, src_row,
                                           prev_scratch, prev_slot_ids, prev_accept_len, out, err_flag)
         if host_slot_ids is not None:
             check_slot_ids_host(host_slot_ids, int(ssm.shape[0]))
+        if host_src_row is not None:
+            check_src_rows_host(host_src_row, Bp)
         self.lib = load_library()
         self._keep = (ssm, conv, conv_w, x, alpha, beta, slot_ids, scratch, src_row, prev_scratch, prev_slot_ids,
                       prev_accept_len, out, err_flag)
@@ -394,12 +421,14 @@ class PreparedCommitVerify:
 
 
 def gdn_spec_commit_verify(desc, ssm, conv, conv_w, x, alpha, beta, slot_ids, rows, scratch, src_row, prev_scratch,
-                           prev_slot_ids, prev_accept_len, out, err_flag=None, stream=None, host_slot_ids=None):
+                           prev_slot_ids, prev_accept_len, out, err_flag=None, stream=None, host_slot_ids=None,
+                           host_src_row=None):
     """Commit the previous step's accepted rows and verify this step's rows in
     one launch (replay mode); src_row[b] names the previous batch row pending
-    on slot_ids[b], or -1."""
+    on slot_ids[b], or -1. With host copies of the slot and source-row tables
+    (host_slot_ids, host_src_row), those are checked too."""
     PreparedCommitVerify(desc, ssm, conv, conv_w, x, alpha, beta, slot_ids, rows, scratch, src_row, prev_scratch,
-                         prev_slot_ids, prev_accept_len, out, err_flag, stream, host_slot_ids)()
+                         prev_slot_ids, prev_accept_len, out, err_flag, stream, host_slot_ids, host_src_row)()
 
 
 class PreparedCommitLayers:

@@ -124,3 +124,25 @@ def test_duplicate_slots_stop_the_call_before_the_library(no_library, monkeypatc
     with pytest.raises(ValueError, match="shared"):
         bd.gdn_spec_commit(desc, t["ssm"], t["conv"], t["slot_ids"], t["accept"], R, "replay", t["scratch"],
                            host_slot_ids=[2, 0, 2])
+
+
+def test_commit_verify_refuses_host_tensors_and_bad_tables(no_library):
+    """The commit-verify's extra tables (source rows, the previous slot table
+    and accept lengths) are checked like the others; a host copy of the
+    source-row table is checked for range and for a previous row named twice."""
+    desc, R, t = _host_case()
+    i32 = dict(dtype=torch.int32)
+    args = (desc, t["ssm"], t["conv"], t["conv_w"], t["x"], t["alpha"], t["beta"], t["slot_ids"], R, t["scratch"])
+    with pytest.raises(ValueError, match="GPU memory"):
+        bd.gdn_spec_commit_verify(*args, torch.zeros(3, **i32), t["scratch"], torch.zeros(2, **i32),
+                                  torch.zeros(2, **i32), t["out"], t["err"])
+    bd.check_src_rows_host([1, -1, 0], 2)
+    bd.check_src_rows_host(np.array([], np.int64), 0)
+    with pytest.raises(ValueError, match="named by requests \\[0, 2\\]"):
+        bd.check_src_rows_host([1, -1, 1], 2)
+    with pytest.raises(ValueError, match="outside"):
+        bd.check_src_rows_host([2], 2)
+    with pytest.raises(ValueError, match="outside"):
+        bd.check_src_rows_host([-3], 2)
+    with pytest.raises(ValueError):
+        bd.check_src_rows_host(torch.zeros(2, dtype=torch.float32), 2)
