@@ -137,12 +137,13 @@ def algorithmic_bytes(w, accept, mode="replay"):
     return verify, commit
 
 
-def fused_bytes(w, accept):
+def fused_bytes(w, accept, mode="replay"):
     """Bytes per commit-verify launch: one step's verify and the previous
     step's commit of the same requests, less what the two share. The state
-    and the conv history are read once for both, so a request with n > 0
-    pending rows moves its state once in each direction (replay mode)."""
-    vbytes, cbytes = algorithmic_bytes(w, accept, "replay")
+    (replay) or the saved S_n (snapshot) and the conv history are read once
+    for both, so a request with n > 0 pending rows reads its state once and
+    writes it once."""
+    vbytes, cbytes = algorithmic_bytes(w, accept, mode)
     s = w.shape
     state = s.num_v_heads * s.d_k * s.d_v * 4
     hist = (s.conv_width - 1) * s.conv_channels * s.elem_bytes
@@ -471,7 +472,7 @@ def run_stack(args, w):
             alt = torch.empty_like(c.scratch)
             csteps.append([[bd.PreparedCommitVerify(c.desc, c.ssm, c.conv, c.conv_w, c.x, c.alpha, c.beta,
                                                     c.slot_ids, w.rows, dst, ident, src, c.slot_ids, c.accept,
-                                                    c.out, c.err, stream)
+                                                    c.out, c.err, stream, mode=args.mode)
                             for dst, src in ((alt, c.scratch), (c.scratch, alt))], 0])
             p.verify()   # the step before the first: its commit is pending
     torch.cuda.synchronize()
@@ -527,7 +528,7 @@ def run_stack(args, w):
     L = w.layers
     rows_per_step = w.batch * w.rows * L
     if cv:
-        fb = fused_bytes(w, acc)
+        fb = fused_bytes(w, acc, args.mode)
         gbps = fb * L * args.steps / wall / 1e9
         kernels = {"commit_verify": {"avg_us": float(tv.mean() * 1e6), "bytes": fb,
                                      "gbps": float(fb / tv.mean() / 1e9)}}
@@ -584,10 +585,10 @@ def main():
                          "commits run beside the next group's verifies (pays in long runs of large "
                          "replay batches; the pipeline's fill and drain cost more over a few steps); "
                          "fused: each step is one gdn_spec_commit_verify launch that commits the copy's "
-                         "previous step into the state on its way into this step's verify (replay; "
-                         "every step still commits one batch and verifies one). Default: fused in "
-                         "replay mode with eager launches on the layers it serves (bf16, d = 128, an even "
-                         "number of value heads per key head), serial otherwise")
+                         "previous step into the state on its way into this step's verify ("
+                         "every step still commits one batch and verifies one). Default: fused with eager "
+                         "launches on the layers it serves (bf16, d = 128, an even number of value heads "
+                         "per key head), serial otherwise")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 256 MiB device copy (the reference dispatch for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -615,7 +616,7 @@ def main():
     if args.schedule is None:
         s = w.shape
         fits = s.dtype == "bf16" and s.d_k == 128 and (s.num_v_heads // s.num_k_heads) % 2 == 0
-        args.schedule = "fused" if args.mode == "replay" and not args.graph and fits else "serial"
+        args.schedule = "fused" if not args.graph and fits else "serial"
     if w.layers != 1:
         return run_stack(args, w)
     if args.calibrate_copy:
@@ -634,8 +635,8 @@ def main():
     fused = args.schedule == "fused"
     if overlap and args.graph:
         raise SystemExit("--graph captures one stream: use --schedule serial")
-    if fused and (args.graph or args.mode != "replay"):
-        raise SystemExit("--schedule fused: replay mode, eager launches")
+    if fused and args.graph:
+        raise SystemExit("--schedule fused: eager launches")
     vstream, cstream = (torch.cuda.Stream(), torch.cuda.Stream()) if overlap else (stream, stream)
     pv = [bd.Prepared(c.desc, c.ssm, c.conv, c.conv_w, c.x, c.alpha, c.beta, c.slot_ids, c.accept, w.rows,
                       c.mode, c.scratch, c.out, c.err, vstream) for c in cases] if overlap else prepared
@@ -662,7 +663,8 @@ def main():
         for c, p in zip(cases, prepared):
             alt = torch.empty_like(c.scratch)
             pair = [bd.PreparedCommitVerify(c.desc, c.ssm, c.conv, c.conv_w, c.x, c.alpha, c.beta, c.slot_ids,
-                                            w.rows, dst, ident, src, c.slot_ids, c.accept, c.out, c.err, stream)
+                                            w.rows, dst, ident, src, c.slot_ids, c.accept, c.out, c.err, stream,
+                                            mode=args.mode)
                     for dst, src in ((alt, c.scratch), (c.scratch, alt))]
             fsteps.append([pair, 0])
             p.verify()
@@ -787,7 +789,7 @@ def main():
     rows_per_step = w.batch * w.rows
     value = rows_per_step * args.steps / wall
     if fused:
-        fbytes = fused_bytes(w, base.accept_np)
+        fbytes = fused_bytes(w, base.accept_np, args.mode)
         gbps = fbytes * args.steps / wall / 1e9
         kernels = {"commit_verify": {"avg_us": float(tv.mean() * 1e6), "bytes": fbytes,
                                      "gbps": float(fbytes / tv.mean() / 1e9)}}

@@ -146,19 +146,20 @@ gdn_status gdn_spec_commit(const gdn_layer_desc *desc, const gdn_pool *pool,
 
 /*
  * Commit the previous step's accepted rows and verify this step's rows, in one
- * launch (replay mode). A layer's commit of step s and its verify of step s+1
+ * launch. A layer's commit of step s and its verify of step s+1
  * are adjacent in a serving loop: the verify must read the committed state,
  * and nothing else reads that layer's state in between (FreeToken issue
  * #828, Design: the verify only reads the state and the commit replays the
  * accepted rows; lmdeploy PR #5006, Verification path: a gated-delta-rule
  * verify-and-commit kernel mode). Here each state chunk takes the pending
- * rows' update on its way into the verify and goes back to the pool from
- * there, so the state is read once per step instead of twice. The pool and
- * the outputs are bit for bit those of gdn_spec_commit (previous step)
- * followed by gdn_spec_verify (this step) on the one-round kernel.
+ * rows' update on its way into the verify (replay mode), or is the previous
+ * step's saved S_n to begin with (snapshot mode), and goes back to the pool
+ * from there, so the state is read once per step instead of twice. The pool,
+ * the outputs and the new scratch are bit for bit those of gdn_spec_commit
+ * (previous step) followed by gdn_spec_verify (this step) in the same mode.
  *
- * Arguments as for gdn_spec_verify (batch, rows, slot_ids, x, alpha, beta,
- * scratch, out), plus the previous step's verify:
+ * Arguments as for gdn_spec_verify (batch, rows, mode, slot_ids, x, alpha,
+ * beta, scratch, out), plus the previous step's verify:
  *  src_row        int32 [batch]: the previous batch row whose accepted rows
  *                 are still to be committed to slot_ids[b], or -1 (nothing
  *                 pending: the state is read as it is). Ignored for padding
@@ -166,7 +167,7 @@ gdn_status gdn_spec_commit(const gdn_layer_desc *desc, const gdn_pool *pool,
  *  prev_scratch   the scratch of the previous step's verify (same desc and
  *                 rows, batch prev_batch), prev_scratch_bytes long; must not
  *                 overlap `scratch`. Each buffer holds at least its batch's
- *                 gdn_spec_scratch_bytes(..., GDN_COMMIT_REPLAY).
+ *                 gdn_spec_scratch_bytes(..., mode).
  *  prev_slot_ids  int32 [prev_batch], the previous step's slot table;
  *                 prev_slot_ids[src_row[b]] must equal slot_ids[b].
  *  prev_accept_len int32 [prev_batch], its accept lengths (0..rows).
@@ -176,7 +177,7 @@ gdn_status gdn_spec_commit(const gdn_layer_desc *desc, const gdn_pool *pool,
  *                 skipped: no commit, zero outputs.
  * Rows of the previous batch that no src_row names are not committed here
  * (gdn_spec_commit does that). The previous step must have been a
- * replay-mode gdn_spec_verify or a gdn_spec_commit_verify: their scratch
+ * gdn_spec_verify or gdn_spec_commit_verify in the same mode: their scratch
  * also keeps the conv history they read, from which the committed history is
  * built, so no workgroup reads pool history that another is rewriting.
  * Requires bf16 storage, d_k = d_v = 128 and an even number of value heads
@@ -184,9 +185,9 @@ gdn_status gdn_spec_commit(const gdn_layer_desc *desc, const gdn_pool *pool,
  */
 gdn_status gdn_spec_commit_verify(const gdn_layer_desc *desc, const gdn_pool *pool, const void *conv_w,
                                   const void *x, const void *alpha, const void *beta,
-                                  const int32_t *slot_ids, int32_t batch, int32_t rows, void *scratch,
-                                  size_t scratch_bytes, const int32_t *src_row, const void *prev_scratch,
-                                  size_t prev_scratch_bytes, const int32_t *prev_slot_ids,
+                                  const int32_t *slot_ids, int32_t batch, int32_t rows, gdn_commit_mode mode,
+                                  void *scratch, size_t scratch_bytes, const int32_t *src_row,
+                                  const void *prev_scratch, size_t prev_scratch_bytes, const int32_t *prev_slot_ids,
                                   const int32_t *prev_accept_len, int32_t prev_batch, void *out, int32_t *err_flag,
                                   void *stream);
 

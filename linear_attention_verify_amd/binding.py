@@ -114,8 +114,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.gdn_spec_commit.restype = ctypes.c_int
     lib.gdn_spec_commit.argtypes = [pdesc, ppool, vp, vp, i32, i32, ctypes.c_int, vp, sz, vp, vp]
     lib.gdn_spec_commit_verify.restype = ctypes.c_int
-    lib.gdn_spec_commit_verify.argtypes = [pdesc, ppool, vp, vp, vp, vp, vp, i32, i32, vp, sz, vp, vp, sz, vp, vp, i32,
-                                           vp, vp, vp]
+    lib.gdn_spec_commit_verify.argtypes = [pdesc, ppool, vp, vp, vp, vp, vp, i32, i32, ctypes.c_int, vp, sz, vp, vp,
+                                           sz, vp, vp, i32, vp, vp, vp]
     lib.gdn_spec_commit_layers.restype = ctypes.c_int
     lib.gdn_spec_commit_layers.argtypes = [pdesc, ppool, ctypes.POINTER(vp), i32, vp, vp, i32, i32,
                                            ctypes.c_int, sz, vp, vp]
@@ -255,19 +255,28 @@ def check_slot_ids_host(slot_ids, num_slots):
         raise ValueError("slot %d is shared by requests %s" % (s, reqs))
 
 
-def check_src_rows_host(src_row, prev_batch):
+def check_src_rows_host(src_row, prev_batch, slot_ids=None):
     """Opt-in check of a host copy of a commit-verify's source-row table:
     every entry is -1 or a row of the previous batch [0, prev_batch), and no
     previous row is named twice (its accepted rows would be committed twice).
-    Raises ValueError."""
+    With the host slot table, padding requests (slot -1), whose source is
+    ignored, are left out. Raises ValueError."""
     import numpy as np
-    if hasattr(src_row, "detach"):
-        if src_row.is_cuda:
-            raise ValueError("check_src_rows_host takes the host copy of the source-row table")
-        src_row = src_row.detach().numpy()
-    a = np.asarray(src_row)
+
+    def host(t, what):
+        if hasattr(t, "detach"):
+            if t.is_cuda:
+                raise ValueError("check_src_rows_host takes the host copy of the %s" % what)
+            t = t.detach().numpy()
+        return np.asarray(t)
+    a = host(src_row, "source-row table")
     if a.ndim != 1 or not np.issubdtype(a.dtype, np.integer):
         raise ValueError("source-row table must be a 1-D integer array")
+    if slot_ids is not None:
+        sl = host(slot_ids, "slot table")
+        if sl.shape != a.shape:
+            raise ValueError("slot table and source-row table differ in length")
+        a = np.where(sl == -1, -1, a)
     bad = (a < -1) | (a >= prev_batch)
     if bad.any():
         i = int(np.flatnonzero(bad)[0])
@@ -396,20 +405,21 @@ class PreparedCommitVerify:
 
     def __init__(self, desc, ssm, conv, conv_w, x, alpha, beta, slot_ids, rows, scratch, src_row, prev_scratch,
                  prev_slot_ids, prev_accept_len, out, err_flag=None, stream=None, host_slot_ids=None,
-                 host_src_row=None):
+                 host_src_row=None, mode="replay"):
         B, Bp = _check_commit_verify_args(desc, ssm, conv, conv_w, x, alpha, beta, slot_ids, rows, scratch, src_row,
                                           prev_scratch, prev_slot_ids, prev_accept_len, out, err_flag)
         if host_slot_ids is not None:
             check_slot_ids_host(host_slot_ids, int(ssm.shape[0]))
         if host_src_row is not None:
-            check_src_rows_host(host_src_row, Bp)
+            check_src_rows_host(host_src_row, Bp, host_slot_ids)
         self.lib = load_library()
         self._keep = (ssm, conv, conv_w, x, alpha, beta, slot_ids, scratch, src_row, prev_scratch, prev_slot_ids,
                       prev_accept_len, out, err_flag)
         self.desc = desc
         self.pool = make_pool(ssm, conv)
         self.args = (ctypes.byref(self.desc), ctypes.byref(self.pool), _ptr(conv_w), _ptr(x), _ptr(alpha),
-                     _ptr(beta), _ptr(slot_ids), B, rows, _ptr(scratch), _nbytes(scratch) if B else 0, _ptr(src_row),
+                     _ptr(beta), _ptr(slot_ids), B, rows, _mode(mode), _ptr(scratch), _nbytes(scratch) if B else 0,
+                     _ptr(src_row),
                      _ptr(prev_scratch) if Bp else None, _nbytes(prev_scratch) if Bp else 0,
                      _ptr(prev_slot_ids) if Bp else None, _ptr(prev_accept_len) if Bp else None, Bp, _ptr(out),
                      _ptr(err_flag), _stream(stream))
@@ -422,13 +432,13 @@ class PreparedCommitVerify:
 
 def gdn_spec_commit_verify(desc, ssm, conv, conv_w, x, alpha, beta, slot_ids, rows, scratch, src_row, prev_scratch,
                            prev_slot_ids, prev_accept_len, out, err_flag=None, stream=None, host_slot_ids=None,
-                           host_src_row=None):
+                           host_src_row=None, mode="replay"):
     """Commit the previous step's accepted rows and verify this step's rows in
-    one launch (replay mode); src_row[b] names the previous batch row pending
-    on slot_ids[b], or -1. With host copies of the slot and source-row tables
-    (host_slot_ids, host_src_row), those are checked too."""
+    one launch (replay or snapshot mode); src_row[b] names the previous batch
+    row pending on slot_ids[b], or -1. With host copies of the slot and
+    source-row tables (host_slot_ids, host_src_row), those are checked too."""
     PreparedCommitVerify(desc, ssm, conv, conv_w, x, alpha, beta, slot_ids, rows, scratch, src_row, prev_scratch,
-                         prev_slot_ids, prev_accept_len, out, err_flag, stream, host_slot_ids, host_src_row)()
+                         prev_slot_ids, prev_accept_len, out, err_flag, stream, host_slot_ids, host_src_row, mode)()
 
 
 class PreparedCommitLayers:

@@ -287,6 +287,7 @@ template <typename T> struct VerifyParams {
     const float *pks;
     const float *pas;
     const T *pxh;
+    const float *psnap;   // snapshot mode: the previous step's S_1..S_R
     int Bp;
     T *xh;
 };
@@ -907,7 +908,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         if constexpr (NXU > 2)
             stage_xunit(2, xu2);
         lds_barrier();
-        if constexpr (!SNAP) {
+        {
             // the history this verify used, for the next step's commit-verify;
             // with a commit pending, the committed history also goes to the
             // pool (q/k units by the key head's first pair only)
@@ -1294,7 +1295,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 template <int NR, bool SNAP, bool FUSED>
 __global__ __launch_bounds__(kThreads) void gdn_verify_d128_split_kernel(const VerifyParams<bf16_t> p)
 {
-    static_assert(!(SNAP && FUSED), "commit-verify: replay");
     using T = bf16_t;
     constexpr int D = 128;
     constexpr int NC = 2 * NR;
@@ -1316,7 +1316,7 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_d128_split_kernel(const V
     // commit-verify: the previous step's stash sits beyond the staged inputs
     // (k^ [t][j] for the key head, then e [t][64] of the block's rows) until
     // the partial products overwrite it
-    constexpr int SFLOATS = FUSED ? NR * D + NR * 64 : 0;
+    constexpr int SFLOATS = FUSED && !SNAP ? NR * D + NR * 64 : 0;
     constexpr int PFLOATS = XFLOATS + SFLOATS > RFLOATS ? XFLOATS + SFLOATS : RFLOATS;
 
     __shared__ __align__(16) float Mt[D * MS];
@@ -1410,7 +1410,11 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_d128_split_kernel(const V
     // this wave's two chunks: K-steps 8w .. 8w + 7 of the block
     const int kg = lane >> 4;
     const int m = lane & 15;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.ssm + ((size_t)slot * HV + h) * D * D, D * D * 4);
+    // (commit-verify in snapshot mode: with n > 0 pending rows, S_0 is the
+    // previous step's S_n of this head, which also goes to the pool)
+    const __amdgpu_buffer_rsrc_t rs =
+        FUSED && SNAP && n > 0 ? make_rsrc(p.psnap + (((size_t)src * HV + h) * NR + (n - 1)) * D * D, D * D * 4)
+                               : make_rsrc(p.ssm + ((size_t)slot * HV + h) * D * D, D * D * 4);
     const uint32_t soff = (kg * D + rb + 4 * m) * 4;
     f32x4 c0[CK], c1[CK];
     load_chunk(c0, rs, soff, 2 * wave);
@@ -1424,7 +1428,7 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_d128_split_kernel(const V
     float sa = 0.0f;
     float *const Sk = P + XFLOATS;
     float *const Se = P + XFLOATS + NR * D;
-    if constexpr (FUSED) {
+    if constexpr (FUSED && !SNAP) {
         const int sr = src < 0 ? 0 : src;
         const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.pas + (size_t)sr * HV * NR, n > 0 ? HV * NR * 4 : 0);
         sa = buf_load<float>(ra, (uint32_t)(h * NR + min(tid, NR - 1)) * 4, 0);
@@ -1467,7 +1471,7 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_d128_split_kernel(const V
         }
     }
     lds_barrier();
-    if constexpr (!SNAP) {
+    {
         // the history this verify used, for the next step's commit-verify
         // (the block's value channels; the key head's q/k channels from the
         // first block of its first pair); with a commit pending, the
@@ -1563,19 +1567,21 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_d128_split_kernel(const V
         pv[q][0] = pv[q][1] = 0.0f;
     }
     if constexpr (FUSED) {
-        // this wave's two chunks take the n accepted rows (the replay
-        // commit's update, in its order) and go back to the pool before
-        // their products; stores through a resource that is empty when
-        // nothing is pending
-        if (tid < NR)
-            alo[tid] = sa;
-        __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's stash pieces are in LDS
-        lds_barrier();
+        // this wave's two chunks take the n accepted rows (replay: the
+        // commit's update, in its order; snapshot: they are S_n already) and
+        // go back to the pool before their products; stores through a
+        // resource that is empty when nothing is pending
+        if constexpr (!SNAP) {
+            if (tid < NR)
+                alo[tid] = sa;
+            __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's stash pieces are in LDS
+            lds_barrier();
+        }
         const __amdgpu_buffer_rsrc_t rw =
             make_rsrc(p.ssm_out + ((size_t)slot * HV + h) * D * D, n > 0 ? D * D * 4 : 0);
         auto commit_chunk = [&](f32x4 (&sc)[CK], int c) {
 #pragma unroll 1
-            for (int t = 0; t < n; ++t) {
+            for (int t = 0; t < (SNAP ? 0 : n); ++t) {
                 const float a = alo[t];
                 const float4 ev = *reinterpret_cast<const float4 *>(&Se[t * 64 + 4 * m]);
 #pragma unroll
@@ -1757,7 +1763,7 @@ __device__ __forceinline__ int load_uniform(const int32_t *ptr, int idx)
     return ((const __attribute__((address_space(4))) int32_t *)ptr)[idx];
 }
 
-template <int NR>
+template <int NR, bool FUSED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(snapshot_groups_per_cu<NR>())))
 void gdn_verify_d128_snapshot_kernel(const VerifyParams<bf16_t> p, int units)
 {
@@ -1808,14 +1814,32 @@ void gdn_verify_d128_snapshot_kernel(const VerifyParams<bf16_t> p, int units)
         return k < 16 ? kh * D + 8 * k : (k < 32 ? HK * D + kh * D + 8 * (k - 16) : 2 * HK * D + h0 * D + 8 * (k - 32));
     };
 
-    // one unit's inputs, held in registers from their request to the conv
-    int slot_in;
+    // one unit's inputs, held in registers from their request to the conv;
+    // with a commit pending (commit-verify), its source row src_in, its n_in
+    // accepted rows and any error bits
+    int slot_in, src_in = -1, n_in = 0, err_in = 0;
     T ga, gb;
     uint4 xu0 = {}, xu1 = {}, xu2 = {}, hu = {};
     uint2 wA = {}, wV = {};
     auto load_inputs = [&](int u) {
         const int b = u / npair, h0 = 2 * (u % npair), kh = h0 / G;
         slot_in = load_uniform(p.slot_ids, b);
+        err_in = (slot_in < -1 || slot_in >= p.P) ? 1 : 0;
+        n_in = 0;
+        if constexpr (FUSED) {
+            src_in = load_uniform(p.src_row, b);
+            if (err_in == 0 && slot_in != -1 && src_in != -1) {
+                if (src_in < 0 || src_in >= p.Bp || load_uniform(p.prev_slots, src_in) != slot_in) {
+                    err_in = 4;
+                } else {
+                    n_in = load_uniform(p.prev_accept, src_in);
+                    if (n_in < 0 || n_in > NR) {
+                        err_in = 2;
+                        n_in = 0;
+                    }
+                }
+            }
+        }
         const size_t gi = ((size_t)b * NR + gtt) * HV + h0 + ghh;
         ga = p.alpha[gi];
         gb = p.beta[gi];
@@ -1833,15 +1857,24 @@ void gdn_verify_d128_snapshot_kernel(const VerifyParams<bf16_t> p, int units)
         const int chV = 2 * HK * D + h0 * D + tid;
         wA = *reinterpret_cast<const uint2 *>(p.conv_w + (size_t)chA * kWidth);
         wV = *reinterpret_cast<const uint2 *>(p.conv_w + (size_t)chV * kWidth);
-        // a slot id outside the pool reads slot 0's history (inside the pool)
+        // a slot id outside the pool reads slot 0's history (inside the pool);
+        // with n_in > 0 pending rows the committed history, entry n_in + r of
+        // [the history the previous verify read | its rows], from the previous
+        // step's scratch
         const int sl = (slot_in < 0 || slot_in >= p.P) ? 0 : slot_in;
         const int uh = min(tid, (kWidth - 1) * UPR - 1);
-        hu = *reinterpret_cast<const uint4 *>(p.conv + ((size_t)sl * (kWidth - 1) + uh / UPR) * p.C +
-                                              unit_channel(kh, h0, uh % UPR));
+        const int r = uh / UPR, e = r + n_in;
+        const T *from = n_in == 0 ? p.conv + ((size_t)sl * (kWidth - 1) + r) * p.C
+            : e < kWidth - 1      ? p.pxh + ((size_t)src_in * (kWidth - 1) + e) * p.C
+                                  : p.pxs + ((size_t)src_in * NR + e - (kWidth - 1)) * p.C;
+        hu = *reinterpret_cast<const uint4 *>(from + unit_channel(kh, h0, uh % UPR));
     };
-    // this wave's head of unit u; an empty resource for a unit that streams nothing
-    auto state_rsrc = [&](int u, bool valid, int slot) {
+    // this wave's head of unit u; an empty resource for a unit that streams
+    // nothing; with n > 0 pending rows, the previous step's S_n
+    auto state_rsrc = [&](int u, bool valid, int slot, int src, int n) {
         const int h0 = 2 * (u % npair);
+        if (FUSED && valid && n > 0)
+            return make_rsrc(p.psnap + (((size_t)src * HV + h0 + hh) * NR + (n - 1)) * D * D, D * D * 4);
         return valid ? make_rsrc(p.ssm + ((size_t)slot * HV + h0 + hh) * D * D, D * D * 4)
                      : make_rsrc(p.ssm, 0);
     };
@@ -1851,9 +1884,10 @@ void gdn_verify_d128_snapshot_kernel(const VerifyParams<bf16_t> p, int units)
         return;
     f32x4 S[NCHUNK][CK];
     load_inputs(u);
-    bool valid = slot_in >= 0 && slot_in < p.P;
+    bool valid = slot_in >= 0 && slot_in < p.P && err_in == 0;
+    int slot = slot_in, n = n_in, errs = err_in;
     {
-        const __amdgpu_buffer_rsrc_t rs = state_rsrc(u, valid, slot_in);
+        const __amdgpu_buffer_rsrc_t rs = state_rsrc(u, valid, slot_in, src_in, n_in);
 #pragma unroll
         for (int c = 0; c < NCHUNK; ++c)
             load_chunk(S[c], rs, soff, c);
@@ -1864,8 +1898,8 @@ void gdn_verify_d128_snapshot_kernel(const VerifyParams<bf16_t> p, int units)
         const bool owner = (h0 % G) == 0;
         const int nxt = u + (int)gridDim.x;
         const bool has_next = nxt < units;
-        if (!valid && slot_in != -1 && tid == 0 && p.err)
-            atomicOr(p.err, 1);
+        if (errs && tid == 0 && p.err)
+            atomicOr(p.err, errs);
 
         if (tid < 2 * NR) {
             al[ghh][gtt] = to_f32(ga);
@@ -1893,6 +1927,18 @@ void gdn_verify_d128_snapshot_kernel(const VerifyParams<bf16_t> p, int units)
         if constexpr (NXU > 2)
             stage_xunit(2, xu2);
         lds_barrier();
+        {
+            // the history this verify used, for the next step's commit-verify;
+            // with a commit pending, the committed history also goes to the
+            // pool (q/k units by the key head's first pair only)
+            const int k = tid % UPR;
+            if (valid && tid < (kWidth - 1) * UPR && (k >= 32 || owner)) {
+                const size_t hoff = (size_t)(tid / UPR) * p.C + unit_channel(kh, h0, k);
+                out_store(reinterpret_cast<uint4 *>(p.xh + (size_t)b * (kWidth - 1) * p.C + hoff), hu);
+                if (FUSED && n > 0)
+                    out_store(reinterpret_cast<uint4 *>(p.hist_out + (size_t)slot * (kWidth - 1) * p.C + hoff), hu);
+            }
+        }
 
         float v[NR];   // value channel tid = row rb + lane of head h0 + hh
         {
@@ -1931,7 +1977,7 @@ void gdn_verify_d128_snapshot_kernel(const VerifyParams<bf16_t> p, int units)
         // the next unit's inputs load while this one is finished
         if (has_next)
             load_inputs(nxt);
-        const bool nvalid = has_next && slot_in >= 0 && slot_in < p.P;
+        const bool nvalid = has_next && slot_in >= 0 && slot_in < p.P && err_in == 0;
         lds_barrier();   // the column table and the gates are complete
 
         float *Pw = P + wave * 64 * PS;
@@ -1995,8 +2041,19 @@ void gdn_verify_d128_snapshot_kernel(const VerifyParams<bf16_t> p, int units)
             cpark[wave][lane] = float4{cA, cB, gt, bew[tt]};
         }
 
+        // commit-verify: S_n goes to the pool (stores through a resource that
+        // is empty when nothing is pending)
+        if constexpr (FUSED) {
+            const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.ssm_out + ((size_t)slot * HV + h0 + hh) * D * D,
+                                                        valid && n > 0 ? D * D * 4 : 0);
+#pragma unroll
+            for (int c = 0; c < NCHUNK; ++c)
+#pragma unroll
+                for (int kk4 = 0; kk4 < CK; ++kk4)
+                    buf_stream_store_f4(rw, soff, (uint32_t)(c * CK + kk4) * 4 * D * 4, S[c][kk4]);
+        }
         // products with the column table
-        const __amdgpu_buffer_rsrc_t nrs = state_rsrc(nxt, nvalid, slot_in);
+        const __amdgpu_buffer_rsrc_t nrs = state_rsrc(nxt, nvalid, slot_in, src_in, n_in);
         f32x4 acc[4];
         float pv[4][2];
 #pragma unroll
@@ -2119,6 +2176,9 @@ void gdn_verify_d128_snapshot_kernel(const VerifyParams<bf16_t> p, int units)
             break;
         u = nxt;
         valid = nvalid;
+        slot = slot_in;
+        n = n_in;
+        errs = err_in;
         lds_barrier();   // every wave is done with this unit's LDS
     }
 }
@@ -2496,8 +2556,8 @@ hipError_t launch_verify(const VerifyParams<T> &vp, const VerifyLaunch &l)
             } else if constexpr (SNAP) {
                 const int cap = kComputeUnits * snapshot_groups_per_cu<NR>();
                 const int grid = units < cap ? units : cap;
-                hipLaunchKernelGGL((gdn_verify_d128_snapshot_kernel<NR>), dim3(grid), dim3(kThreads), 0, l.st, vp,
-                                   units);
+                hipLaunchKernelGGL((gdn_verify_d128_snapshot_kernel<NR, false>), dim3(grid), dim3(kThreads), 0, l.st,
+                                   vp, units);
                 done = true;
             }
         }
@@ -2587,29 +2647,36 @@ hipError_t verify_typed(const Checked &c, const gdn_layer_desc *d, const gdn_poo
 // split kernel below one unit per compute unit, the one-round kernel from
 // there), with the previous step's commit applied to each state chunk on its
 // way in.
-template <int NR> hipError_t launch_commit_verify(const VerifyParams<bf16_t> &vp, int batch, int HV, hipStream_t st)
+template <int NR, bool SNAP>
+hipError_t launch_commit_verify(const VerifyParams<bf16_t> &vp, int batch, int HV, hipStream_t st)
 {
     const int units = batch * (HV / 2);
-    if (units < kComputeUnits)
-        hipLaunchKernelGGL((gdn_verify_d128_split_kernel<NR, false, true>), dim3(units * 4), dim3(kThreads), 0, st,
+    if (units < kComputeUnits) {
+        hipLaunchKernelGGL((gdn_verify_d128_split_kernel<NR, SNAP, true>), dim3(units * 4), dim3(kThreads), 0, st,
                            vp);
-    else
+    } else if constexpr (SNAP) {
+        const int cap = kComputeUnits * snapshot_groups_per_cu<NR>();
+        hipLaunchKernelGGL((gdn_verify_d128_snapshot_kernel<NR, true>), dim3(units < cap ? units : cap),
+                           dim3(kThreads), 0, st, vp, units);
+    } else {
         hipLaunchKernelGGL((gdn_verify_d128_kernel<NR, bf16_t, false, true>), dim3(units), dim3(kThreads), 0, st, vp);
+    }
     return hipGetLastError();
 }
 
+template <bool SNAP>
 hipError_t commit_verify_rows(int rows, const VerifyParams<bf16_t> &vp, int batch, int HV, hipStream_t st)
 {
     switch (rows) {
-    case 1: return launch_commit_verify<1>(vp, batch, HV, st);
-    case 2: return launch_commit_verify<2>(vp, batch, HV, st);
-    case 3: return launch_commit_verify<3>(vp, batch, HV, st);
-    case 4: return launch_commit_verify<4>(vp, batch, HV, st);
-    case 5: return launch_commit_verify<5>(vp, batch, HV, st);
-    case 6: return launch_commit_verify<6>(vp, batch, HV, st);
-    case 7: return launch_commit_verify<7>(vp, batch, HV, st);
-    case 8: return launch_commit_verify<8>(vp, batch, HV, st);
-    case 9: return launch_commit_verify<9>(vp, batch, HV, st);
+    case 1: return launch_commit_verify<1, SNAP>(vp, batch, HV, st);
+    case 2: return launch_commit_verify<2, SNAP>(vp, batch, HV, st);
+    case 3: return launch_commit_verify<3, SNAP>(vp, batch, HV, st);
+    case 4: return launch_commit_verify<4, SNAP>(vp, batch, HV, st);
+    case 5: return launch_commit_verify<5, SNAP>(vp, batch, HV, st);
+    case 6: return launch_commit_verify<6, SNAP>(vp, batch, HV, st);
+    case 7: return launch_commit_verify<7, SNAP>(vp, batch, HV, st);
+    case 8: return launch_commit_verify<8, SNAP>(vp, batch, HV, st);
+    case 9: return launch_commit_verify<9, SNAP>(vp, batch, HV, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -2748,15 +2815,15 @@ gdn_status gdn_spec_verify(const gdn_layer_desc *desc, const gdn_pool *pool, con
 
 gdn_status gdn_spec_commit_verify(const gdn_layer_desc *desc, const gdn_pool *pool, const void *conv_w,
                                   const void *x, const void *alpha, const void *beta,
-                                  const int32_t *slot_ids, int32_t batch, int32_t rows, void *scratch,
-                                  size_t scratch_bytes, const int32_t *src_row, const void *prev_scratch,
-                                  size_t prev_scratch_bytes, const int32_t *prev_slot_ids,
+                                  const int32_t *slot_ids, int32_t batch, int32_t rows, gdn_commit_mode mode,
+                                  void *scratch, size_t scratch_bytes, const int32_t *src_row,
+                                  const void *prev_scratch, size_t prev_scratch_bytes, const int32_t *prev_slot_ids,
                                   const int32_t *prev_accept_len, int32_t prev_batch, void *out, int32_t *err_flag,
                                   void *stream)
 {
     Checked c;
     ScratchLayout L;
-    gdn_status s = check_common(desc, pool, batch, rows, GDN_COMMIT_REPLAY, scratch, scratch_bytes, &c, &L);
+    gdn_status s = check_common(desc, pool, batch, rows, mode, scratch, scratch_bytes, &c, &L);
     if (s != GDN_OK)
         return s;
     if (prev_batch < 0)
@@ -2765,7 +2832,8 @@ gdn_status gdn_spec_commit_verify(const gdn_layer_desc *desc, const gdn_pool *po
         return GDN_ERR_UNSUPPORTED;
     if ((size_t)prev_batch * c.HV > 0x7fffffffu)
         return GDN_ERR_UNSUPPORTED;
-    const ScratchLayout Lp = scratch_layout(c.HK, c.HV, c.D, c.C, c.esize, prev_batch, rows, false);
+    const bool snap = mode == GDN_COMMIT_SNAPSHOT;
+    const ScratchLayout Lp = scratch_layout(c.HK, c.HV, c.D, c.C, c.esize, prev_batch, rows, snap);
     if (prev_batch > 0) {
         if (!prev_scratch || !aligned16(prev_scratch) || !prev_slot_ids || !prev_accept_len)
             return GDN_ERR_INVALID_ARG;
@@ -2782,7 +2850,7 @@ gdn_status gdn_spec_commit_verify(const gdn_layer_desc *desc, const gdn_pool *po
     if (!conv_w || !x || !alpha || !beta || !slot_ids || !src_row || !out || !aligned16(conv_w) || !aligned16(x))
         return GDN_ERR_INVALID_ARG;
     VerifyParams<bf16_t> vp =
-        verify_params<bf16_t>(c, desc, pool, conv_w, x, alpha, beta, slot_ids, false, scratch, L, out, err_flag);
+        verify_params<bf16_t>(c, desc, pool, conv_w, x, alpha, beta, slot_ids, snap, scratch, L, out, err_flag);
     const char *pb = static_cast<const char *>(prev_scratch);
     vp.ssm_out = pool->ssm;
     vp.hist_out = static_cast<bf16_t *>(pool->conv);
@@ -2794,8 +2862,10 @@ gdn_status gdn_spec_commit_verify(const gdn_layer_desc *desc, const gdn_pool *po
     vp.pks = prev_batch > 0 ? reinterpret_cast<const float *>(pb + Lp.ks) : nullptr;
     vp.pas = prev_batch > 0 ? reinterpret_cast<const float *>(pb + Lp.as) : nullptr;
     vp.pxh = prev_batch > 0 ? reinterpret_cast<const bf16_t *>(pb + Lp.xh) : nullptr;
+    vp.psnap = prev_batch > 0 && snap ? reinterpret_cast<const float *>(pb + Lp.snap) : nullptr;
     vp.Bp = prev_batch;
-    const hipError_t e = commit_verify_rows(rows, vp, batch, c.HV, static_cast<hipStream_t>(stream));
+    const hipError_t e = snap ? commit_verify_rows<true>(rows, vp, batch, c.HV, static_cast<hipStream_t>(stream))
+                              : commit_verify_rows<false>(rows, vp, batch, c.HV, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 

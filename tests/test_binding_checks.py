@@ -146,3 +146,6 @@ def test_commit_verify_refuses_host_tensors_and_bad_tables(no_library):
         bd.check_src_rows_host([-3], 2)
     with pytest.raises(ValueError):
         bd.check_src_rows_host(torch.zeros(2, dtype=torch.float32), 2)
+    bd.check_src_rows_host([1, 1, 0], 2, slot_ids=[4, -1, 5])        # a padding request's source is ignored
+    with pytest.raises(ValueError, match="differ in length"):
+        bd.check_src_rows_host([1, 0], 2, slot_ids=[4])

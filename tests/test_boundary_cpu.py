@@ -324,10 +324,11 @@ def test_sample_arguments_are_refused(lib):
 
 
 def _status_commit_verify(lib, desc, pool, batch=2, rows=3, scratch=0x100000, prev=0x200000, prev_batch=2,
-                          nbytes=1 << 16, pnbytes=1 << 16, src=4096, prev_slots=4096, prev_acc=4096, ptr=4096):
+                          nbytes=1 << 16, pnbytes=1 << 16, src=4096, prev_slots=4096, prev_acc=4096, ptr=4096,
+                          mode=0):
     return lib.gdn_spec_commit_verify(ctypes.byref(desc), ctypes.byref(pool), ptr, ptr, ptr, ptr, ptr, batch, rows,
-                                      scratch, nbytes, src, prev, pnbytes, prev_slots, prev_acc, prev_batch, ptr, None,
-                                      None)
+                                      mode, scratch, nbytes, src, prev, pnbytes, prev_slots, prev_acc, prev_batch, ptr,
+                                      None, None)
 
 
 def test_commit_verify_arguments_are_refused(lib):
@@ -355,4 +356,6 @@ def test_commit_verify_arguments_are_refused(lib):
     assert _status_commit_verify(lib, q, p, batch=0, prev=None, prev_slots=None, prev_acc=None, pnbytes=0,
                                  prev_batch=0) == bd.GDN_OK                       # no previous step needs no buffers
     assert _status_commit_verify(lib, q, p, rows=10) == INV
+    assert _status_commit_verify(lib, q, p, mode=2) == INV
+    assert _status_commit_verify(lib, q, p, mode=1) == bd.GDN_ERR_SCRATCH_TOO_SMALL   # snapshot scratch is larger
     assert _status_commit_verify(lib, q, p, batch=0) == bd.GDN_OK                    # nothing launched

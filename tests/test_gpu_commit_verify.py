@@ -26,8 +26,8 @@ QWEN = wl.LayerShape(num_k_heads=16, num_v_heads=32, d_k=128, d_v=128, dtype="bf
 GQA4 = wl.LayerShape(num_k_heads=8, num_v_heads=32, d_k=128, d_v=128, dtype="bf16")
 
 
-def _zero_scratch(desc, B, R):
-    return torch.zeros(max(bd.gdn_spec_scratch_bytes(desc, B, R, "replay"), 16), dtype=torch.uint8, device=DEV)
+def _zero_scratch(desc, B, R, mode="replay"):
+    return torch.zeros(max(bd.gdn_spec_scratch_bytes(desc, B, R, mode), 16), dtype=torch.uint8, device=DEV)
 
 
 def _plan(sid1, P, seed):
@@ -55,14 +55,14 @@ def _plan(sid1, P, seed):
     return np.array(sid2, np.int32), np.array(src, np.int32), dropped, new_slot
 
 
-def _two_steps(R, B1, seed, accept_edges=True, shape=QWEN):
+def _two_steps(R, B1, seed, accept_edges=True, shape=QWEN, mode="replay"):
     w = wl.small_workload(shape, batch=B1, rows=R, num_slots=3 * B1 + 2, seed=seed)
     sid1, acc1 = wl.draw_requests(w)
     if accept_edges:
         acc1[0] = R                                # every row accepted
         if B1 > 1:
             acc1[1] = 0                            # nothing accepted
-    c = gh.make_case(w, slot_ids=sid1, accept=acc1)
+    c = gh.make_case(w, slot_ids=sid1, accept=acc1, mode=mode)
     sid2, src, dropped, new_slot = _plan(sid1, w.num_slots, seed + 1)
     w2 = wl.small_workload(shape, batch=len(sid2), rows=R, num_slots=w.num_slots, seed=seed + 2)
     d2 = wl.draw_layer(w2, 0)
@@ -90,9 +90,9 @@ def _run_both(c, w2, d2, sid2, src, dropped):
 
     # commit, then verify
     gh.commit(c)
-    sb = _zero_scratch(c.desc, w2.batch, R)
+    sb = _zero_scratch(c.desc, w2.batch, R, c.mode)
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
-    bd.gdn_spec_verify(c.desc, c.ssm, c.conv, c.conv_w, ins["x"], ins["alpha"], ins["beta"], sid2_t, R, "replay",
+    bd.gdn_spec_verify(c.desc, c.ssm, c.conv, c.conv_w, ins["x"], ins["alpha"], ins["beta"], sid2_t, R, c.mode,
                        sb, out, err)
     torch.cuda.synchronize()
     ref = (c.ssm.clone(), c.conv.clone(), out.clone(), sb.clone(), int(err.item()) | int(c.err.item()))
@@ -103,15 +103,15 @@ def _run_both(c, w2, d2, sid2, src, dropped):
     c.err.zero_()
     lone = np.full_like(c.slot_ids_np, -1)
     lone[dropped] = c.slot_ids_np[dropped]
-    bd.gdn_spec_commit(c.desc, c.ssm, c.conv, torch.from_numpy(lone).to(DEV), c.accept, R, "replay", c.scratch,
+    bd.gdn_spec_commit(c.desc, c.ssm, c.conv, torch.from_numpy(lone).to(DEV), c.accept, R, c.mode, c.scratch,
                        c.err)
-    sb2 = _zero_scratch(c.desc, w2.batch, R)
+    sb2 = _zero_scratch(c.desc, w2.batch, R, c.mode)
     out.fill_(float("nan"))
     err2 = torch.zeros(1, dtype=torch.int32, device=DEV)
-    print("commit-verify B=%d->%d R=%d" % (c.w.batch, w2.batch, R), flush=True)
+    print("commit-verify %s B=%d->%d R=%d" % (c.mode, c.w.batch, w2.batch, R), flush=True)
     bd.gdn_spec_commit_verify(c.desc, c.ssm, c.conv, c.conv_w, ins["x"], ins["alpha"], ins["beta"], sid2_t, R, sb2,
                               torch.from_numpy(src).to(DEV), c.scratch, c.slot_ids, c.accept, out, err2,
-                              host_slot_ids=sid2)
+                              host_slot_ids=sid2, host_src_row=src, mode=c.mode)
     torch.cuda.synchronize()
     fused = (c.ssm.clone(), c.conv.clone(), out.clone(), sb2.clone(), int(err2.item()) | int(c.err.item()))
     return ref, fused
@@ -121,24 +121,26 @@ def _bits_equal(a, b):
     return torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8))
 
 
+@pytest.mark.parametrize("mode", ["replay", "snapshot"])
 @pytest.mark.parametrize("R,B1,shape", [
-    (4, 16, QWEN), (9, 16, QWEN),              # the one-round kernel (a unit per compute unit or more)
+    (4, 16, QWEN), (9, 16, QWEN),              # one unit per compute unit or more (one-round / snapshot kernel)
     (3, 1, QWEN), (9, 1, QWEN), (4, 6, QWEN),  # the split kernel (fewer)
     (4, 16, GQA4), (3, 2, GQA4),               # a key head shared by two pairs, both kernels
 ])
-def test_commit_verify_equals_commit_then_verify(R, B1, shape):
-    c, w2, d2, sid2, src, dropped = _two_steps(R, B1=B1, seed=900 + 10 * R + B1, shape=shape)
+def test_commit_verify_equals_commit_then_verify(R, B1, shape, mode):
+    c, w2, d2, sid2, src, dropped = _two_steps(R, B1=B1, seed=900 + 10 * R + B1, shape=shape, mode=mode)
     ref, fused = _run_both(c, w2, d2, sid2, src, dropped)
     assert ref[4] == 0 and fused[4] == 0
     for name, a, b in zip(("state", "history", "outputs", "stash"), ref[:4], fused[:4]):
         assert _bits_equal(a, b), name
 
 
-def test_commit_verify_at_the_saturated_batch():
+@pytest.mark.parametrize("mode", ["replay", "snapshot"])
+def test_commit_verify_at_the_saturated_batch(mode):
     """64 requests x 9 rows, every request continued in place (the serving
     loop's usual case and the benchmark's launch), bit for bit."""
     w = wl.WORKLOADS["saturated-b64"]
-    c = gh.make_case(w)
+    c = gh.make_case(w, mode=mode)
     d2 = wl.draw_layer(w, 1)
     ident = np.arange(w.batch, dtype=np.int32)
     ref, fused = _run_both(c, w, d2, c.slot_ids_np, ident, np.zeros(0, np.int64))
@@ -147,13 +149,14 @@ def test_commit_verify_at_the_saturated_batch():
         assert _bits_equal(a, b), name
 
 
+@pytest.mark.parametrize("mode", ["replay", "snapshot"])
 @pytest.mark.parametrize("B1", [16, 3])
-def test_commit_verify_matches_the_oracle(B1):
+def test_commit_verify_matches_the_oracle(B1, mode):
     """The oracle's commit of step 1 then its verify of step 2, on the whole
     pool: outputs to the bf16 tolerance, states to the fp32 one, conv
-    histories bit for bit (both kernels)."""
+    histories bit for bit (both kernels, both modes)."""
     R = 4
-    c, w2, d2, sid2, src, dropped = _two_steps(R, B1=B1, seed=950 + B1)
+    c, w2, d2, sid2, src, dropped = _two_steps(R, B1=B1, seed=950 + B1, mode=mode)
     s = c.w.shape
     host_ssm = c.ssm.cpu().numpy().copy()
     host_conv = gh.to_storage_numpy(c.conv, s.dtype).copy()
@@ -175,14 +178,15 @@ def test_commit_verify_matches_the_oracle(B1):
     assert np.array_equal(conv_gpu[touched], host_conv[touched])
 
 
+@pytest.mark.parametrize("mode", ["replay", "snapshot"])
 @pytest.mark.parametrize("B1", [16, 8])
-def test_commit_verify_errors_skip_the_request(B1):
+def test_commit_verify_errors_skip_the_request(B1, mode):
     """A source row outside the previous batch or naming another slot (bit 2),
     an accept length outside [0, rows] (bit 1) and a slot outside the pool
     (bit 0): each such request gets zero outputs and its slot keeps its state;
     the others are committed and verified as usual (both kernels)."""
     R = 4
-    c, w2, d2, sid2, src, dropped = _two_steps(R, B1=B1, seed=970 + B1, accept_edges=False)
+    c, w2, d2, sid2, src, dropped = _two_steps(R, B1=B1, seed=970 + B1, accept_edges=False, mode=mode)
     gh.verify(c)
     torch.cuda.synchronize()
     live = np.flatnonzero((sid2 >= 0) & (src >= 0))
@@ -198,10 +202,10 @@ def test_commit_verify_errors_skip_the_request(B1):
     sid2[b_slot] = c.w.num_slots + 5                             # slot outside the pool
     ins, out, sid2_t = _step2(c, w2, d2, sid2)
     before_ssm, before_conv = c.ssm.clone(), c.conv.clone()
-    sb = _zero_scratch(c.desc, w2.batch, R)
+    sb = _zero_scratch(c.desc, w2.batch, R, mode)
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
     bd.gdn_spec_commit_verify(c.desc, c.ssm, c.conv, c.conv_w, ins["x"], ins["alpha"], ins["beta"], sid2_t, R, sb,
-                              torch.from_numpy(src).to(DEV), c.scratch, c.slot_ids, c.accept, out, err)
+                              torch.from_numpy(src).to(DEV), c.scratch, c.slot_ids, c.accept, out, err, mode=mode)
     torch.cuda.synchronize()
     assert int(err.item()) == 7
     for b in (b_far, b_other, b_acc, b_slot):
