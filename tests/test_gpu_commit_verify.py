@@ -278,3 +278,77 @@ def test_commit_verify_replays_from_a_graph():
         for name, a, b in zip(("state", "history", "outputs", "stash"), want, got):
             assert _bits_equal(a, b), (rep, name)
         assert int(err.item()) == 0
+
+
+@pytest.mark.parametrize("mode", ["replay", "snapshot"])
+@pytest.mark.parametrize("B", [16, 3])
+def test_commit_verify_chains_over_steps(B, mode):
+    """Four steps: a plain verify, then three commit-verify launches, each
+    committing the step before it (so a fused launch commits from a fused
+    launch's scratch, including the history it kept), then a plain commit of
+    the last. The pool and every step's outputs equal those of verify then
+    commit at every step, bit for bit, and the oracle's sequence of commits
+    and verifies within tolerance."""
+    R = 4
+    w = wl.small_workload(QWEN, batch=B, rows=R, num_slots=2 * B + 1, seed=1200 + B)
+    c = gh.make_case(w, mode=mode)
+    s = c.w.shape
+    rng = np.random.default_rng(1300 + B)
+    draws = [c.draw] + [wl.draw_layer(w, k) for k in (1, 2, 3)]
+    accepts = [rng.integers(0, R + 1, B).astype(np.int32) for _ in range(4)]
+    host_ssm = c.ssm.cpu().numpy().copy()
+    host_conv = gh.to_storage_numpy(c.conv, s.dtype).copy()
+    ssm0, conv0 = c.ssm.clone(), c.conv.clone()
+    ident = torch.arange(B, dtype=torch.int32, device=DEV)
+
+    def inputs(d):
+        return [gh.storage_tensor(d[k], s.dtype) for k in ("x", "alpha", "beta")]
+
+    # serial: verify, commit at every step
+    outs_serial = []
+    sc = _zero_scratch(c.desc, B, R, mode)
+    for d, acc in zip(draws, accepts):
+        out = torch.empty_like(c.out)
+        bd.gdn_spec_verify(c.desc, c.ssm, c.conv, c.conv_w, *inputs(d), c.slot_ids, R, mode, sc, out, c.err)
+        bd.gdn_spec_commit(c.desc, c.ssm, c.conv, c.slot_ids, torch.from_numpy(acc).to(DEV), R, mode, sc, c.err)
+        outs_serial.append(out)
+    torch.cuda.synchronize()
+    assert int(c.err.item()) == 0
+    want_ssm, want_conv = c.ssm.clone(), c.conv.clone()
+
+    # fused: a plain verify, three commit-verify launches, a plain commit
+    c.ssm.copy_(ssm0)
+    c.conv.copy_(conv0)
+    bufs = [_zero_scratch(c.desc, B, R, mode), _zero_scratch(c.desc, B, R, mode)]
+    accs = [torch.from_numpy(a).to(DEV) for a in accepts]
+    outs = []
+    out = torch.empty_like(c.out)
+    bd.gdn_spec_verify(c.desc, c.ssm, c.conv, c.conv_w, *inputs(draws[0]), c.slot_ids, R, mode, bufs[0], out, c.err)
+    outs.append(out)
+    for k in (1, 2, 3):
+        out = torch.empty_like(c.out)
+        print("chain %s B=%d step %d" % (mode, B, k), flush=True)
+        bd.gdn_spec_commit_verify(c.desc, c.ssm, c.conv, c.conv_w, *inputs(draws[k]), c.slot_ids, R, bufs[k % 2],
+                                  ident, bufs[(k - 1) % 2], c.slot_ids, accs[k - 1], out, c.err, mode=mode)
+        outs.append(out)
+    bd.gdn_spec_commit(c.desc, c.ssm, c.conv, c.slot_ids, accs[3], R, mode, bufs[1], c.err)
+    torch.cuda.synchronize()
+    assert int(c.err.item()) == 0
+    for k in range(4):
+        assert _bits_equal(outs[k], outs_serial[k]), k
+    assert _bits_equal(c.ssm, want_ssm) and _bits_equal(c.conv, want_conv)
+
+    # the oracle's steps
+    orc = oracle.Oracle()
+    atol, rtol = gh.tolerances(s)
+    for k, (d, acc) in enumerate(zip(draws, accepts)):
+        o_ref, _, e = orc.verify(s, host_ssm, host_conv, draws[0]["conv_w"], d["x"],
+                                 d["alpha"], d["beta"], c.slot_ids_np, R, nthreads=16)
+        assert e == 0
+        np.testing.assert_allclose(gh.tensor_f64(outs[k], s.dtype), o_ref, atol=atol, rtol=rtol)
+        assert orc.commit(s, host_ssm, host_conv, draws[0]["conv_w"], d["x"], d["alpha"], d["beta"], c.slot_ids_np,
+                          acc, R, nthreads=16) == 0
+    sl = c.slot_ids_np
+    satol, srtol = gh.state_tolerances(s)
+    np.testing.assert_allclose(c.ssm.cpu().numpy()[sl], host_ssm[sl], atol=satol, rtol=srtol)
+    assert np.array_equal(gh.to_storage_numpy(c.conv, s.dtype)[sl], host_conv[sl])
