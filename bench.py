@@ -1,7 +1,7 @@
 """Benchmark: GatedDeltaNet speculative verify + commit on one MI355X.
 
-A step is one pass of the whole path over one batch: gdn_spec_verify of every
-request's k+1 rows, then gdn_spec_commit of its accepted rows. The default
+A step is one pass of the whole path over one batch: the verify of every
+request's k+1 rows and the commit of its accepted rows. The default
 workload is the saturated batch: 64 requests, 9 verify rows (k = 8), a
 Qwen3-Next-shaped layer (16 key / 32 value heads, d = 128, conv width 4 over
 8192 channels, bf16 inputs, fp32 state), a 256-slot pool and geometric(0.3)
@@ -14,8 +14,13 @@ copy the other copies move several GB, so nothing of it (state, inputs, or
 the stash the commit reads back) is still in the 256 MB Infinity Cache: every
 kernel runs cold. All inputs are resident in HBM before the timed region.
 
-Schedule (--schedule, reported in the line): serial (the default) issues
-everything on one stream. overlap issues a group's commits on a second stream
+Schedule (--schedule, reported in the line): fused (the default on the layers
+it serves: bf16 storage, d = 128, an even number of value heads per key head,
+eager launches) makes each step one gdn_spec_commit_verify launch, which
+commits the copy's previous step into the state on its way into this step's
+verify; every step still verifies one batch and commits one. serial issues
+gdn_spec_verify then gdn_spec_commit on one stream (the default elsewhere).
+overlap issues a group's commits on a second stream
 once the whole group is verified, and a copy's next verify waits for that
 copy's commit, as a serving loop that starts the next step's layers while the
 last step's states are committed would; every data dependency of the serial
@@ -28,7 +33,10 @@ Prints one JSON line. value = verify rows per second (batch x rows per step);
 gbps = algorithmic HBM bytes per second: per request, verify reads the state,
 the conv history, x and the gates and writes o and a stash of the rows' raw
 inputs; commit reads and writes the state and the conv history and reads the
-accepted rows' stash.
+accepted rows' stash. A fused step reads the state and the history once for
+both (gbps counts them once); its line adds serial_equivalent, the serial
+pair's bytes over the same step time: the rate at which a verify then a
+commit would have to run to match the step (not an HBM measurement).
 """
 from __future__ import annotations
 
@@ -556,6 +564,12 @@ def run_stack(args, w):
                      "unit": "GB/s", "frac": kernels[dom]["gbps"] / HBM_PEAK_GBPS,
                      "traffic": measured_traffic(w.name, args.mode, dom)},
     }
+    if cv:
+        sb = (vb + cb) * L
+        line["serial_equivalent"] = {
+            "bytes": sb, "gbps": sb * args.steps / wall / 1e9, "frac": sb * args.steps / wall / 1e9 / HBM_PEAK_GBPS,
+            "note": "the serial verify + commit pairs' algorithmic bytes over this step's time: the rate the "
+                    "serial schedule would need to match it; the fused launches move fewer bytes (gbps, roofline)"}
     print(json.dumps(line), flush=True)
 
 
@@ -834,6 +848,12 @@ def main():
                      "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS,
                      "traffic": measured_traffic(w.name, args.mode, dom)},
     }
+    if fused:
+        sb = vbytes + cbytes
+        line["serial_equivalent"] = {
+            "bytes": sb, "gbps": sb * args.steps / wall / 1e9, "frac": sb * args.steps / wall / 1e9 / HBM_PEAK_GBPS,
+            "note": "the serial verify + commit pair's algorithmic bytes over this step's time: the rate a verify "
+                    "then a commit would need to match it; the fused launch moves fewer bytes (gbps, roofline)"}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(line), flush=True)
