@@ -1278,21 +1278,71 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     }
 }
 
-// ---- verify, d = 128, small batches: a unit split over four workgroups --------
+// ---- verify, d = 128, small batches: a unit split over several workgroups ----
 //
 // With fewer (request, pair of value heads) units than compute units, one
 // workgroup per unit leaves most of the chip idle and each
 // workgroup streams 128 KiB in a long dependent chain. Here a workgroup takes
-// one 64-row block of one value head (a quarter of a unit), and its four waves
-// split the block's 128 key indices: wave w streams K-steps 8w..8w+7 (8 KiB,
-// both chunks requested at the start) into partial products of all 64 rows,
-// which are summed through LDS before wave 0 solves the 64 rows. Each
-// workgroup repeats the unit's conv of the key head and its Gram matrix: more
-// arithmetic, no more HBM traffic (the repeated input loads hit the caches).
-// In snapshot mode each wave then applies every row's update to its two
-// chunks, still in registers, and stores its part of S_1..S_R. Both modes
-// form the products in the same order, so they agree bit for bit.
-template <int NR, bool SNAP, bool FUSED>
+// one block of RB = 16 RPL rows of one value head (RPL state rows per lane:
+// 64-row blocks, four workgroups per unit, down to 16-row blocks, sixteen per
+// unit, on the smallest batches), and its four waves split the block's 128
+// key indices: wave w streams K-steps 8w..8w+7 (both chunks requested at the
+// start) into partial products of all the block's rows, which are summed
+// through LDS before wave 0 solves them. Each workgroup repeats the unit's
+// conv of the key head and its Gram matrix: more arithmetic, no more HBM
+// traffic (the repeated input loads hit the caches). From the column table
+// on, each phase runs at the rate of one SIMD, so smaller blocks on more
+// compute units shorten it. In snapshot mode each wave then applies every
+// row's update to its two chunks, still in registers, and stores its part of
+// S_1..S_R. Every result element takes the same operations in the same order
+// whatever the block size and the mode, so all of them agree bit for bit.
+template <int RPL> struct RowBits;
+template <> struct RowBits<4> {
+    static __device__ __forceinline__ void load(float (&d)[4], __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+    {
+        const f32x4 v = buf_stream_load_f4(r, voff, soff);
+        d[0] = v[0]; d[1] = v[1]; d[2] = v[2]; d[3] = v[3];
+    }
+    static __device__ __forceinline__ void store(const float (&s)[4], __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+    {
+        buf_stream_store_f4(r, voff, soff, f32x4{s[0], s[1], s[2], s[3]});
+    }
+    static __device__ __forceinline__ void put(float *dst, const float (&s)[4])
+    {
+        *reinterpret_cast<f32x4 *>(dst) = f32x4{s[0], s[1], s[2], s[3]};
+    }
+};
+template <> struct RowBits<2> {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+    static __device__ __forceinline__ void load(float (&d)[2], __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+    {
+        const f2 v = __builtin_bit_cast(f2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, kStreamPolicy));
+        d[0] = v[0]; d[1] = v[1];
+    }
+    static __device__ __forceinline__ void store(const float (&s)[2], __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+    {
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2, f2{s[0], s[1]}), r, (int)voff, (int)soff,
+                                              kStreamPolicy);
+    }
+    static __device__ __forceinline__ void put(float *dst, const float (&s)[2])
+    {
+        *reinterpret_cast<f2 *>(dst) = f2{s[0], s[1]};
+    }
+};
+template <> struct RowBits<1> {
+    static __device__ __forceinline__ void load(float (&d)[1], __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+    {
+        d[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, kStreamPolicy));
+    }
+    static __device__ __forceinline__ void store(const float (&s)[1], __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+    {
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, s[0]), r, (int)voff, (int)soff, kStreamPolicy);
+    }
+    static __device__ __forceinline__ void put(float *dst, const float (&s)[1]) { *dst = s[0]; }
+};
+
+template <int NR, bool SNAP, bool FUSED, int RPL>
 __global__ __launch_bounds__(kThreads) void gdn_verify_d128_split_kernel(const VerifyParams<bf16_t> p)
 {
     using T = bf16_t;
@@ -1306,17 +1356,22 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_d128_split_kernel(const V
     constexpr int CK = 4;
     constexpr int NT = NR * (NR + 1) / 2;
     static_assert(NT <= 64, "one coefficient pair per lane");
+    static_assert(RPL == 1 || RPL == 2 || RPL == 4, "state rows per lane");
+    constexpr int RB = 16 * RPL;          // rows per block
+    constexpr int BPH = D / RB;           // blocks per value head
+    constexpr int WPU = 2 * BPH;          // workgroups per unit
+    constexpr int LPRW = RB / 4;          // lanes per e row in the stash copy
     constexpr int NROWS = kWidth - 1 + NR;
-    constexpr int UPR = 40;   // 16-byte units per staged row: q 16 | k 16 | v 8 (64 channels)
+    constexpr int UPR = 32 + RB / 8;   // 16-byte units per staged row: q 16 | k 16 | v RB / 8 (RB channels)
     constexpr int NU = NROWS * UPR;
     constexpr int NUT = (NU + kThreads - 1) / kThreads;   // staged units per thread
     static_assert(NUT <= 2, "staged units per thread");
     constexpr int XFLOATS = NROWS * UPR * 4;               // staged rows, as floats
-    constexpr int RFLOATS = 4 * 64 * PS;                    // per-wave partial products
+    constexpr int RFLOATS = 4 * RB * PS;                    // per-wave partial products
     // commit-verify: the previous step's stash sits beyond the staged inputs
-    // (k^ [t][j] for the key head, then e [t][64] of the block's rows) until
+    // (k^ [t][j] for the key head, then e [t][RB] of the block's rows) until
     // the partial products overwrite it
-    constexpr int SFLOATS = FUSED && !SNAP ? NR * D + NR * 64 : 0;
+    constexpr int SFLOATS = FUSED && !SNAP ? NR * D + NR * RB : 0;
     constexpr int PFLOATS = XFLOATS + SFLOATS > RFLOATS ? XFLOATS + SFLOATS : RFLOATS;
 
     __shared__ __align__(16) float Mt[D * MS];
@@ -1324,7 +1379,7 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_d128_split_kernel(const V
     __shared__ float invs[NC];
     __shared__ float gp[4][NR * NC + NR];
     __shared__ float al[NR], be[NR];
-    __shared__ float eb[SNAP ? NR * 64 : 1];   // e_t of the block's rows, for the snapshots
+    __shared__ float eb[SNAP ? NR * RB : 1];   // e_t of the block's rows, for the snapshots
     __shared__ float alo[FUSED ? NR : 1];      // commit-verify: the previous step's a_t of head h
 
     const int tid = threadIdx.x;
@@ -1333,12 +1388,12 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_d128_split_kernel(const V
     const int HV = p.HV, HK = p.HK;
     const int G = HV / HK;
     const int npair = HV / 2;
-    const int b = blockIdx.x / (npair * 4);
-    const int rem = blockIdx.x % (npair * 4);
-    const int h0 = 2 * (rem / 4);
-    const int blk = rem % 4;
-    const int h = h0 + (blk >> 1);       // this workgroup's value head
-    const int rb = 64 * (blk & 1);       // and its 64-row block
+    const int b = blockIdx.x / (npair * WPU);
+    const int rem = blockIdx.x % (npair * WPU);
+    const int h0 = 2 * (rem / WPU);
+    const int blk = rem % WPU;
+    const int h = h0 + blk / BPH;        // this workgroup's value head
+    const int rb = RB * (blk % BPH);     // and its block of rows
     const int kh = h0 / G;
     const bool owner = (h0 % G) == 0;    // the key head's first pair stores its q/k inputs
     const int slot_in = p.slot_ids[b];
@@ -1347,7 +1402,7 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_d128_split_kernel(const V
         src = p.src_row[b];
 
     // staged unit k of a row: q units 0..15, k units 16..31, then the block's
-    // value channels rb..rb+63 of head h; unit k starts at local channel 8k
+    // value channels rb..rb+RB-1 of head h; unit k starts at local channel 8k
     auto unit_channel = [&](int k) {
         return k < 16 ? kh * D + 8 * k : (k < 32 ? HK * D + kh * D + 8 * (k - 16) : 2 * HK * D + h * D + rb + 8 * (k - 32));
     };
@@ -1357,7 +1412,7 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_d128_split_kernel(const V
     const int jc = tid & (D - 1);
     const bool isq = tid < D;
     const int chA = isq ? kh * D + jc : HK * D + kh * D + jc;
-    const int chV = 2 * HK * D + h * D + rb + min(tid, 63);
+    const int chV = 2 * HK * D + h * D + rb + min(tid, RB - 1);
     const uint2 wA = *reinterpret_cast<const uint2 *>(p.conv_w + (size_t)chA * kWidth);
     const uint2 wV = *reinterpret_cast<const uint2 *>(p.conv_w + (size_t)chV * kWidth);
     bool bad = slot_in < 0 || slot_in >= p.P;
@@ -1400,8 +1455,8 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_d128_split_kernel(const V
     if (bad) {
         if (errbits && tid == 0 && blk == 0 && p.err)
             atomicOr(p.err, errbits);
-        for (int idx = tid; idx < NR * 64; idx += kThreads) {
-            const int t = idx / 64, i = idx % 64;
+        for (int idx = tid; idx < NR * RB; idx += kThreads) {
+            const int t = idx / RB, i = idx % RB;
             out_store(&p.out[(((size_t)b * NR + t) * HV + h) * D + rb + i], from_f32<T>(0.0f));
         }
         return;
@@ -1415,16 +1470,24 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_d128_split_kernel(const V
     const __amdgpu_buffer_rsrc_t rs =
         FUSED && SNAP && n > 0 ? make_rsrc(p.psnap + (((size_t)src * HV + h) * NR + (n - 1)) * D * D, D * D * 4)
                                : make_rsrc(p.ssm + ((size_t)slot * HV + h) * D * D, D * D * 4);
-    const uint32_t soff = (kg * D + rb + 4 * m) * 4;
-    f32x4 c0[CK], c1[CK];
-    load_chunk(c0, rs, soff, 2 * wave);
-    load_chunk(c1, rs, soff, 2 * wave + 1);
+    const uint32_t soff = (kg * D + rb + RPL * m) * 4;
+    // lane (kg, m) holds rows rb + RPL m .. + RPL - 1 of key index 4 K-step + kg
+    float c0[CK][RPL], c1[CK][RPL];
+    auto load_rows = [&](float (&sc)[CK][RPL], int c) {
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int k = 0; k < CK; ++k)
+            RowBits<RPL>::load(sc[k], rs, soff, (uint32_t)(c * CK + k) * 4 * D * 4);
+        asm volatile("" ::: "memory");
+    };
+    load_rows(c0, 2 * wave);
+    load_rows(c1, 2 * wave + 1);
     __builtin_amdgcn_sched_barrier(0);
 
     // commit-verify: the previous step's stash straight into LDS beyond the
     // staged inputs, 16 bytes per lane (k^ rows of the key head, 1 KiB per
-    // wave instruction; e of the block's 64 rows, four rows per instruction),
-    // and the gates of head h through one register
+    // wave instruction; e of the block's RB rows, 256 / RB rows per
+    // instruction), and the gates of head h through one register
     float sa = 0.0f;
     float *const Sk = P + XFLOATS;
     float *const Se = P + XFLOATS + NR * D;
@@ -1435,7 +1498,7 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_d128_split_kernel(const V
         if (n > 0) {
             const float *kb = p.pks + ((size_t)src * HK + kh) * NR * D;
             const int nk = (n * D + 255) / 256;
-            const int ne = (n + 3) / 4;
+            const int ne = (n * LPRW + 63) / 64;
             for (int i = wave; i < nk + ne; i += 4) {
                 if (i < nk) {
                     const int f = i * 256 + lane * 4;
@@ -1443,9 +1506,9 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_d128_split_kernel(const V
                         lds_dma16(kb + f, Sk + i * 256);
                 } else {
                     const int q = i - nk;
-                    const int t = 4 * q + lane / 16;
+                    const int t = (64 / LPRW) * q + lane / LPRW;
                     if (t < n)
-                        lds_dma16(p.pes + (((size_t)src * NR + t) * HV + h) * D + rb + (lane % 16) * 4, Se + q * 256);
+                        lds_dma16(p.pes + (((size_t)src * NR + t) * HV + h) * D + rb + (lane % LPRW) * 4, Se + q * 256);
                 }
             }
         }
@@ -1485,7 +1548,7 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_d128_split_kernel(const V
                 out_store(reinterpret_cast<uint4 *>(p.hist_out + (size_t)slot * (kWidth - 1) * p.C + hoff), su[0]);
         }
     }
-    float v[NR];   // value channel rb + tid of head h (threads < 64)
+    float v[NR];   // value channel rb + tid of head h (threads < RB)
     {
         ChanIn<NR, T> cinA, cinV;
         const T *Xt = reinterpret_cast<const T *>(P);
@@ -1497,7 +1560,7 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_d128_split_kernel(const V
             cinA.w[k] = tap(wA, k);
             cinV.w[k] = tap(wV, k);
         }
-        const int cv = 256 + min(tid, 63);   // local channel of the value input
+        const int cv = 256 + min(tid, RB - 1);   // local channel of the value input
 #pragma unroll
         for (int r = 0; r < kWidth - 1; ++r) {
             cinA.hist[r] = Xt[r * UPR * 8 + tid];
@@ -1558,14 +1621,33 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_d128_split_kernel(const V
         }
     }
 
-    // partial products of this wave's K-steps: all 64 rows, every column
-    f32x4 acc[4];
-    float pv[4][2];
+    // partial products of this wave's K-steps: all the block's rows, every
+    // column (tile v holds rows rb + RPL m + v)
+    f32x4 acc[RPL];
+    float pv[RPL][2];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < RPL; ++q) {
         acc[q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         pv[q][0] = pv[q][1] = 0.0f;
     }
+    auto mfma_rows = [&](const float (&sc)[CK][RPL], int c) {
+#pragma unroll
+        for (int k = 0; k < CK; ++k) {
+            const int j = 4 * (c * CK + k) + kg;
+            const float bm = Mt[j * MS + m];
+#pragma unroll
+            for (int v = 0; v < RPL; ++v)
+                acc[v] = __builtin_amdgcn_mfma_f32_16x16x4f32(sc[k][v], bm, acc[v], 0, 0, 0);
+            if (NVL) {
+                const float2 mv = *reinterpret_cast<const float2 *>(&Mt[j * MS + 16]);
+#pragma unroll
+                for (int v = 0; v < RPL; ++v) {
+                    pv[v][0] = __builtin_fmaf(sc[k][v], mv.x, pv[v][0]);
+                    pv[v][1] = __builtin_fmaf(sc[k][v], mv.y, pv[v][1]);
+                }
+            }
+        }
+    };
     if constexpr (FUSED) {
         // this wave's two chunks take the n accepted rows (replay: the
         // commit's update, in its order; snapshot: they are S_n already) and
@@ -1579,41 +1661,44 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_d128_split_kernel(const V
         }
         const __amdgpu_buffer_rsrc_t rw =
             make_rsrc(p.ssm_out + ((size_t)slot * HV + h) * D * D, n > 0 ? D * D * 4 : 0);
-        auto commit_chunk = [&](f32x4 (&sc)[CK], int c) {
+        auto commit_chunk = [&](float (&sc)[CK][RPL], int c) {
 #pragma unroll 1
             for (int t = 0; t < (SNAP ? 0 : n); ++t) {
                 const float a = alo[t];
-                const float4 ev = *reinterpret_cast<const float4 *>(&Se[t * 64 + 4 * m]);
+                float ev[RPL];
+#pragma unroll
+                for (int v = 0; v < RPL; ++v)
+                    ev[v] = Se[t * RB + RPL * m + v];
 #pragma unroll
                 for (int kk4 = 0; kk4 < CK; ++kk4) {
                     const float kk = Sk[t * D + 4 * (c * CK + kk4) + kg];
-                    sc[kk4][0] = row_update(sc[kk4][0], a, ev.x, kk);
-                    sc[kk4][1] = row_update(sc[kk4][1], a, ev.y, kk);
-                    sc[kk4][2] = row_update(sc[kk4][2], a, ev.z, kk);
-                    sc[kk4][3] = row_update(sc[kk4][3], a, ev.w, kk);
+#pragma unroll
+                    for (int v = 0; v < RPL; ++v)
+                        sc[kk4][v] = row_update(sc[kk4][v], a, ev[v], kk);
                 }
             }
 #pragma unroll
             for (int kk4 = 0; kk4 < CK; ++kk4)
-                buf_stream_store_f4(rw, soff, (uint32_t)(c * CK + kk4) * 4 * D * 4, sc[kk4]);
+                RowBits<RPL>::store(sc[kk4], rw, soff, (uint32_t)(c * CK + kk4) * 4 * D * 4);
         };
         commit_chunk(c0, 2 * wave);
         commit_chunk(c1, 2 * wave + 1);
     }
-    mfma_chunk<CK, NVL, MS>(c0, 2 * wave, kg, m, Mt, acc, pv);
-    mfma_chunk<CK, NVL, MS>(c1, 2 * wave + 1, kg, m, Mt, acc, pv);
+    mfma_rows(c0, 2 * wave);
+    mfma_rows(c1, 2 * wave + 1);
     lds_barrier();   // the Gram shares are in; the staged inputs are no longer read
-    float *Pw = P + wave * 64 * PS;
+    float *Pw = P + wave * RB * PS;
     if (m < NMF) {
+        // tile v, register q of lane (kg, m): row RPL (4 kg + q) + v of the block, column m
 #pragma unroll
-        for (int v4 = 0; v4 < 4; ++v4)
+        for (int v4 = 0; v4 < RPL; ++v4)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                Pw[(16 * kg + 4 * q + v4) * PS + m] = acc[v4][q];
+                Pw[(RPL * (4 * kg + q) + v4) * PS + m] = acc[v4][q];
     }
     if (NVL) {
 #pragma unroll
-        for (int v4 = 0; v4 < 4; ++v4)
+        for (int v4 = 0; v4 < RPL; ++v4)
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
                 float x = pv[v4][c];
@@ -1623,9 +1708,9 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_d128_split_kernel(const V
             }
         if (kg == 0) {
 #pragma unroll
-            for (int v4 = 0; v4 < 4; ++v4) {
-                Pw[(4 * m + v4) * PS + NMF] = pv[v4][0];
-                Pw[(4 * m + v4) * PS + NMF + 1] = pv[v4][1];
+            for (int v4 = 0; v4 < RPL; ++v4) {
+                Pw[(RPL * m + v4) * PS + NMF] = pv[v4][0];
+                Pw[(RPL * m + v4) * PS + NMF + 1] = pv[v4][1];
             }
         }
     }
@@ -1657,14 +1742,16 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_d128_split_kernel(const V
             cG = g;
             cb = be[tt];
         }
-        // row rb + lane: the four waves' partial products, scaled by the norms
+        // row rb + lane (lanes < RB; the others only hold coefficients): the
+        // four waves' partial products, scaled by the norms
+        const int lr = min(lane, RB - 1);
         float pr[NC];
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             float s = 0.0f;
 #pragma unroll
             for (int w = 0; w < 4; ++w)
-                s += P[(w * 64 + lane) * PS + c];
+                s += P[(w * RB + lr) * PS + c];
             pr[c] = s * invs[c];
         }
         float e[NR];
@@ -1683,11 +1770,13 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_d128_split_kernel(const V
 #pragma unroll
             for (int uu = 0; uu <= t; ++uu)
                 s = __builtin_fmaf(lane_value(cB, t * (t + 1) / 2 + uu), e[uu], s);
-            const size_t oi = (((size_t)b * NR + t) * HV + h) * D + rb + lane;
-            out_store(&p.out[oi], from_f32<T>(p.scale * s));
-            out_store(&p.es[oi], e[t]);
-            if (SNAP)
-                eb[t * 64 + lane] = e[t];
+            if (lane < RB) {
+                const size_t oi = (((size_t)b * NR + t) * HV + h) * D + rb + lane;
+                out_store(&p.out[oi], from_f32<T>(p.scale * s));
+                out_store(&p.es[oi], e[t]);
+                if (SNAP)
+                    eb[t * RB + lane] = e[t];
+            }
         }
     } else if (owner && blk == 0) {
         // normalised keys for the commit (three waves of the key head's first block)
@@ -1704,20 +1793,20 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_d128_split_kernel(const V
         for (int t = 0; t < NR; ++t) {
             const float a = al[t];
             const float it = invs[t];
-            float ev[4];
+            float ev[RPL];
 #pragma unroll
-            for (int v4 = 0; v4 < 4; ++v4)
-                ev[v4] = eb[t * 64 + 4 * m + v4];
+            for (int v4 = 0; v4 < RPL; ++v4)
+                ev[v4] = eb[t * RB + RPL * m + v4];
             float *dst = snap_h + (size_t)t * D * D;
-            auto snap_chunk = [&](f32x4 (&sc)[CK], int c) {
+            auto snap_chunk = [&](float (&sc)[CK][RPL], int c) {
 #pragma unroll
                 for (int k = 0; k < CK; ++k) {
                     const int j = 4 * (c * CK + k) + kg;
                     const float kk = Mt[j * MS + t] * it;
 #pragma unroll
-                    for (int v4 = 0; v4 < 4; ++v4)
+                    for (int v4 = 0; v4 < RPL; ++v4)
                         sc[k][v4] = row_update(sc[k][v4], a, ev[v4], kk);
-                    *reinterpret_cast<f32x4 *>(dst + (size_t)j * D + rb + 4 * m) = sc[k];
+                    RowBits<RPL>::put(dst + (size_t)j * D + rb + RPL * m, sc[k]);
                 }
             };
             snap_chunk(c0, 2 * wave);
@@ -2537,6 +2626,24 @@ struct VerifyLaunch {
     hipStream_t st;
 };
 
+// The split kernel's block size: 16- or 32-row blocks while the grid stays
+// within one workgroup per compute unit (the phases after the column table
+// run at one SIMD's rate, so more, smaller blocks finish sooner), 64-row
+// blocks above that. Results do not depend on the choice.
+template <int NR, bool SNAP, bool FUSED>
+void launch_split(const VerifyParams<bf16_t> &vp, int units, hipStream_t st)
+{
+    if (units * 16 <= kComputeUnits)
+        hipLaunchKernelGGL((gdn_verify_d128_split_kernel<NR, SNAP, FUSED, 1>), dim3(units * 16), dim3(kThreads), 0, st,
+                           vp);
+    else if (units * 8 <= kComputeUnits)
+        hipLaunchKernelGGL((gdn_verify_d128_split_kernel<NR, SNAP, FUSED, 2>), dim3(units * 8), dim3(kThreads), 0, st,
+                           vp);
+    else
+        hipLaunchKernelGGL((gdn_verify_d128_split_kernel<NR, SNAP, FUSED, 4>), dim3(units * 4), dim3(kThreads), 0, st,
+                           vp);
+}
+
 template <int D, int NR, typename T, bool SNAP>
 hipError_t launch_verify(const VerifyParams<T> &vp, const VerifyLaunch &l)
 {
@@ -2550,8 +2657,7 @@ hipError_t launch_verify(const VerifyParams<T> &vp, const VerifyLaunch &l)
             // 11.0 us). One threshold for both modes keeps their products in the
             // same order, so replay and snapshot agree bit for bit
             if (units < kComputeUnits) {
-                hipLaunchKernelGGL((gdn_verify_d128_split_kernel<NR, SNAP, false>), dim3(units * 4), dim3(kThreads), 0,
-                                   l.st, vp);
+                launch_split<NR, SNAP, false>(vp, units, l.st);
                 done = true;
             } else if constexpr (SNAP) {
                 const int cap = kComputeUnits * snapshot_groups_per_cu<NR>();
@@ -2652,8 +2758,7 @@ hipError_t launch_commit_verify(const VerifyParams<bf16_t> &vp, int batch, int H
 {
     const int units = batch * (HV / 2);
     if (units < kComputeUnits) {
-        hipLaunchKernelGGL((gdn_verify_d128_split_kernel<NR, SNAP, true>), dim3(units * 4), dim3(kThreads), 0, st,
-                           vp);
+        launch_split<NR, SNAP, true>(vp, units, st);
     } else if constexpr (SNAP) {
         const int cap = kComputeUnits * snapshot_groups_per_cu<NR>();
         hipLaunchKernelGGL((gdn_verify_d128_snapshot_kernel<NR, true>), dim3(units < cap ? units : cap),
