@@ -1368,14 +1368,16 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_d128_split_kernel(const V
     static_assert(NUT <= 2, "staged units per thread");
     constexpr int XFLOATS = NROWS * UPR * 4;               // staged rows, as floats
     constexpr int RFLOATS = 4 * RB * PS;                    // per-wave partial products
-    // commit-verify: the previous step's stash sits beyond the staged inputs
-    // (k^ [t][j] for the key head, then e [t][RB] of the block's rows) until
-    // the partial products overwrite it
+    // commit-verify: the previous step's stash (k^ [t][j] for the key head,
+    // then e [t][RB] of the block's rows), loaded through registers with the
+    // staged inputs, SQ float4 per thread
     constexpr int SFLOATS = FUSED && !SNAP ? NR * D + NR * RB : 0;
-    constexpr int PFLOATS = XFLOATS + SFLOATS > RFLOATS ? XFLOATS + SFLOATS : RFLOATS;
+    constexpr int SQ = (SFLOATS / 4 + kThreads - 1) / kThreads;
+    constexpr int PFLOATS = XFLOATS > RFLOATS ? XFLOATS : RFLOATS;
 
     __shared__ __align__(16) float Mt[D * MS];
     __shared__ __align__(16) float P[PFLOATS];   // staged inputs; then the four waves' partial products
+    __shared__ __align__(16) float Sst[SFLOATS > 0 ? SFLOATS : 4];   // commit-verify: the stash
     __shared__ float invs[NC];
     __shared__ float gp[4][NR * NC + NR];
     __shared__ float al[NR], be[NR];
@@ -1452,6 +1454,30 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_d128_split_kernel(const V
                                        : p.pxs + ((size_t)src * NR + e - (kWidth - 1)) * p.C;
         su[q] = *reinterpret_cast<const uint4 *>(row + unit_channel(k));
     }
+    // commit-verify: the n pending rows' stash (k^ rows of the key head, e of
+    // the block's rows) and the gates of head h, requested with the inputs
+    // (plain loads: a copy straight into LDS, pending beside ordinary loads,
+    // makes the compiler wait for every load in flight at the next use of
+    // any of them, the state chunks included)
+    float sa = 0.0f;
+    float4 stv[SQ > 0 ? SQ : 1];
+    if constexpr (FUSED && !SNAP) {
+        const int sr = src < 0 ? 0 : src;
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.pas + (size_t)sr * HV * NR, n > 0 ? HV * NR * 4 : 0);
+        sa = buf_load<float>(ra, (uint32_t)(h * NR + min(tid, NR - 1)) * 4, 0);
+        const float *kb = p.pks + ((size_t)sr * HK + kh) * NR * D;
+#pragma unroll
+        for (int q = 0; q < SQ; ++q) {
+            const int f = 4 * (q * kThreads + tid);   // float index in [k^ rows | e rows]
+            stv[q] = float4{0.0f, 0.0f, 0.0f, 0.0f};
+            if (f < n * D) {
+                stv[q] = *reinterpret_cast<const float4 *>(kb + f);
+            } else if (f >= NR * D && f - NR * D < n * RB) {
+                const int t = (f - NR * D) / RB, c = (f - NR * D) % RB;
+                stv[q] = *reinterpret_cast<const float4 *>(p.pes + (((size_t)src * NR + t) * HV + h) * D + rb + c);
+            }
+        }
+    }
     if (bad) {
         if (errbits && tid == 0 && blk == 0 && p.err)
             atomicOr(p.err, errbits);
@@ -1484,36 +1510,16 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_d128_split_kernel(const V
     load_rows(c1, 2 * wave + 1);
     __builtin_amdgcn_sched_barrier(0);
 
-    // commit-verify: the previous step's stash straight into LDS beyond the
-    // staged inputs, 16 bytes per lane (k^ rows of the key head, 1 KiB per
-    // wave instruction; e of the block's RB rows, 256 / RB rows per
-    // instruction), and the gates of head h through one register
-    float sa = 0.0f;
-    float *const Sk = P + XFLOATS;
-    float *const Se = P + XFLOATS + NR * D;
+    float *const Sk = Sst;
+    float *const Se = Sst + NR * D;
     if constexpr (FUSED && !SNAP) {
-        const int sr = src < 0 ? 0 : src;
-        const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.pas + (size_t)sr * HV * NR, n > 0 ? HV * NR * 4 : 0);
-        sa = buf_load<float>(ra, (uint32_t)(h * NR + min(tid, NR - 1)) * 4, 0);
-        if (n > 0) {
-            const float *kb = p.pks + ((size_t)src * HK + kh) * NR * D;
-            const int nk = (n * D + 255) / 256;
-            const int ne = (n * LPRW + 63) / 64;
-            for (int i = wave; i < nk + ne; i += 4) {
-                if (i < nk) {
-                    const int f = i * 256 + lane * 4;
-                    if (f < n * D)
-                        lds_dma16(kb + f, Sk + i * 256);
-                } else {
-                    const int q = i - nk;
-                    const int t = (64 / LPRW) * q + lane / LPRW;
-                    if (t < n)
-                        lds_dma16(p.pes + (((size_t)src * NR + t) * HV + h) * D + rb + (lane % LPRW) * 4, Se + q * 256);
-                }
-            }
-        }
+#pragma unroll
+        for (int q = 0; q < SQ; ++q)
+            if (4 * (q * kThreads + tid) < SFLOATS)
+                reinterpret_cast<float4 *>(Sst)[q * kThreads + tid] = stv[q];
+        if (tid < NR)
+            alo[tid] = sa;
     }
-
     if (tid < NR) {
         al[tid] = to_f32(ga);
         be[tid] = to_f32(gb);
@@ -1653,12 +1659,6 @@ __global__ __launch_bounds__(kThreads) void gdn_verify_d128_split_kernel(const V
         // commit's update, in its order; snapshot: they are S_n already) and
         // go back to the pool before their products; stores through a
         // resource that is empty when nothing is pending
-        if constexpr (!SNAP) {
-            if (tid < NR)
-                alo[tid] = sa;
-            __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's stash pieces are in LDS
-            lds_barrier();
-        }
         const __amdgpu_buffer_rsrc_t rw =
             make_rsrc(p.ssm_out + ((size_t)slot * HV + h) * D * D, n > 0 ? D * D * 4 : 0);
         auto commit_chunk = [&](float (&sc)[CK][RPL], int c) {
