@@ -65,14 +65,14 @@ SAMPLE_SOURCE = os.path.join(ROOT, "linear_attention_verify_amd", "csrc", "spec_
 # reports null.
 MEASURED_TRAFFIC = [
     {"source": KERNEL_SOURCE,
-     "source_sha256": "81dea1ad0c28d5df88671fdb5609325602b9b19be9d0667436d91fed798b4b09",
+     "source_sha256": "20972e0f456647e2e7bccd4b0e45b0b3bbf201907f65ff6507239ea2b36bbc95",
      "bytes": {   # (workload, mode, kernel) -> bytes per launch
-         ("saturated-b64", "replay", "commit_verify"): 322531864,
-         ("saturated-b64", "replay", "verify"): 179221653,
-         ("saturated-b64", "replay", "commit"): 282700307,
-         ("saturated-b64", "snapshot", "commit_verify"): 1525086066,
-         ("saturated-b64", "snapshot", "verify"): 1387484496,
-         ("saturated-b64", "snapshot", "commit"): 274756915,
+         ("saturated-b64", "replay", "commit_verify"): 322533434,
+         ("saturated-b64", "replay", "verify"): 179223169,
+         ("saturated-b64", "replay", "commit"): 282701289,
+         ("saturated-b64", "snapshot", "commit_verify"): 1525092159,
+         ("saturated-b64", "snapshot", "verify"): 1387496722,
+         ("saturated-b64", "snapshot", "commit"): 274768731,
      }},
     {"source": ATTN_SOURCE,
      "source_sha256": "f254bc77bc855d9281a6304db619d063533d81c6e4ed714c46000f8b555346f6",
