@@ -2651,11 +2651,11 @@ hipError_t launch_verify(const VerifyParams<T> &vp, const VerifyLaunch &l)
         const int units = l.batch * (l.HV / 2);
         bool done = false;
         if constexpr (sizeof(T) == 2) {
-            // fewer units than compute units: split each over four workgroups
-            // (measured: 1 request, replay 7.3 -> 6.1 us; at 16 requests, one unit
-            // per compute unit, the split was slower in replay mode, 12.0 against
-            // 11.0 us). One threshold for both modes keeps their products in the
-            // same order, so replay and snapshot agree bit for bit
+            // fewer units than compute units: split each over 4 to 16 workgroups
+            // (measured: 1 request, replay 7.3 -> 6.1 us with four; at 16 requests,
+            // one unit per compute unit, the split was slower in replay mode, 12.0
+            // against 11.0 us). One threshold for both modes keeps their products
+            // in the same order, so replay and snapshot agree bit for bit
             if (units < kComputeUnits) {
                 launch_split<NR, SNAP, false>(vp, units, l.st);
                 done = true;
