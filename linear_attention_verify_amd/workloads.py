@@ -85,8 +85,19 @@ WORKLOADS = {
     "stack36": Workload(
         "stack36", QWEN3_NEXT_LAYER, batch=128, rows=4, num_slots=512, layers=36, seed=4,
         modes=("replay",)),
+    # one rank's share of the layer under tensor parallelism over value heads
+    # at TP4 (4 key / 8 value heads, C = 2048): the saturated batch's share, and
+    # the batch at which a rank's share fills the chip as the saturated batch
+    # fills it without sharding (1,024 units)
+    "tp4-b64": Workload(
+        "tp4-b64", LayerShape(num_k_heads=4, num_v_heads=8, d_k=128, d_v=128), batch=64, rows=9,
+        num_slots=256, accept="geometric", accept_p=0.3, seed=5, modes=("replay", "snapshot")),
+    "tp4-b256": Workload(
+        "tp4-b256", LayerShape(num_k_heads=4, num_v_heads=8, d_k=128, d_v=128), batch=256, rows=9,
+        num_slots=1024, accept="geometric", accept_p=0.3, seed=6, modes=("replay", "snapshot")),
 }
 WORKLOAD_ORDER = ["tiny-fp32", "single-stream", "low-concurrency", "saturated-b64", "stack36"]
+TP_SHARES = ["tp4-b64", "tp4-b256"]
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
